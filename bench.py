@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of the draft-sampling / verification hot path on one MI355X.
+
+One step = one speculative block over the workload's batch: the four library calls
+  vt_lmhead_trimmed -> vt_softmax_temp (draft, with draws) -> vt_softmax_temp (target) -> vt_spec_verify
+on synthetic inputs already resident in HBM.  Default workload: B=1, gamma=5, hidden 3072, full
+128256-row drafter head, fp32 target logits, T=1 (config 2 of the workload recipe).
+
+Prints ONE JSON line on stdout (progress goes to stderr):
+  value        verified draft positions / s = B * gamma / (seconds per step)
+  roofline     the LM-head kernel (the dominant kernel): algorithmic bytes per launch / its average
+               duration measured live with HIP events on the launch stream, against 8 TB/s
+  cpu_baseline the float64 CPU oracle timed on a bounded sample of the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C] [--no-cpu-baseline]
+       python bench.py --copy-calibration   (a plain copy of known size, for PMC byte scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true")
+    return ap.parse_args()
+
+
+def lmhead_bytes(cfg) -> int:
+    """Algorithmic HBM bytes of one LM-head launch: kept weight rows + hidden + logits (+ keep_ids)."""
+    M = cfg.B * cfg.R
+    b = cfg.Vt * cfg.H * 2 + M * cfg.H * 2 + M * cfg.Vt * 4
+    if cfg.trimmed:
+        b += cfg.Vt * 4
+    return b
+
+
+def lmhead_flops(cfg) -> float:
+    return 2.0 * cfg.B * cfg.R * cfg.H * cfg.Vt
+
+
+def block_bytes(cfg) -> int:
+    """Algorithmic bytes of the whole block (each kernel's distinct inputs and outputs once)."""
+    M, B, g, V, Vt = cfg.B * cfg.R, cfg.B, cfg.gamma, cfg.V, cfg.Vt
+    s_t = 4 if cfg.target_dtype == "f32" else 2
+    lm = lmhead_bytes(cfg)
+    draft_sm = M * Vt * 4 + M * (8 + 4 + 4)  # read logits; write lse, ids; read u
+    target_sm = B * (g + 1) * V * s_t + B * (g + 1) * 8
+    verify = B * (V * s_t + Vt * 4 + (V * 4 if cfg.trimmed else 0) + (g + 2) * 4 + g * 4 + 4)
+    return lm + draft_sm + target_sm + verify
+
+
+def kernel_source_hash() -> str:
+    path = os.path.join(ROOT, "draft_sampling_verification_amd", "csrc", "lmhead.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload_key: str):
+    """HBM bytes per LM-head launch from a committed PMC measurement, if taken on this source."""
+    path = os.path.join(ROOT, "profiles", f"lmhead_traffic_{workload_key}.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("lmhead_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 5 copies of {n} bytes (read {n}, write {n} per copy)")
+    print(json.dumps({"copy_bytes": n, "copies": 5}))
+
+
+def cpu_baseline(cfg, wl_one, budget_s: float):
+    """Time the oracle as it stands on whole blocks of the same workload until ~budget_s."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import ref
+
+    threadpool_limits(limits=len(os.sched_getaffinity(0)))
+    used = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    blocks, t0 = 0, time.perf_counter()
+    while True:
+        ref.block(wl_one.hidden, wl_one.weight, wl_one.keep_ids, None, wl_one.target, cfg.target_dtype,
+                  wl_one.T, wl_one.u_draft, wl_one.u_acc, wl_one.u_fin, cfg.gamma, cfg.R)
+        blocks += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or blocks >= 50:
+            break
+    per_block = el / blocks
+    return {"value": wl_one.B * cfg.gamma / per_block, "unit": "verified draft positions/s",
+            "cores": int(used), "kind": "oracle",
+            "sample": f"{blocks} whole block(s) of {wl_one.B} sequence(s) of this workload, float64 numpy, "
+                      f"{el:.1f} s total, {per_block:.2f} s per block"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+
+    import draft_sampling_verification_amd as vt
+    from workloads import CONFIGS, make_workload
+
+    cfg = CONFIGS[args.config]
+    B, g, R = cfg.B, cfg.gamma, cfg.R
+    log(f"workload: {cfg.name}")
+    t0 = time.perf_counter()
+    wl = make_workload(cfg)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    def f(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    # enough copies of the inputs that the 256 MB MALL cannot serve a step from cache
+    bb = block_bytes(cfg)
+    n_sets = max(2, math.ceil(3 * MALL_BYTES / bb))
+    base = dict(weight=bf16(wl.weight), hidden=bf16(wl.hidden),
+                target=f(wl.target) if cfg.target_dtype == "f32" else bf16(wl.target),
+                u_draft=f(wl.u_draft.reshape(-1)), u_acc=f(wl.u_acc), u_fin=f(wl.u_fin))
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(n_sets - 1)]
+    keep = f(wl.keep_ids) if wl.keep_ids is not None else None
+    f2t = f(wl.full_to_trim) if wl.full_to_trim is not None else None
+    M = B * R
+    logits = torch.empty(M, cfg.Vt, dtype=torch.float32, device="cuda")
+    dlse = torch.empty(M, dtype=torch.float64, device="cuda")
+    dids = torch.empty(M, dtype=torch.int32, device="cuda")
+    tlse = torch.empty(B * (g + 1), dtype=torch.float64, device="cuda")
+    tokens = torch.empty(B, g + 1, dtype=torch.int32, device="cuda")
+    nacc = torch.empty(B, dtype=torch.int32, device="cuda")
+    ws_sm_d = vt.softmax_workspace(M, cfg.Vt)
+    ws_sm_t = vt.softmax_workspace(B * (g + 1), cfg.V)
+    ws_vf = vt.verify_workspace(B, cfg.V)
+    log(f"{n_sets} input sets on device ({bb / 1e6:.1f} MB algorithmic per step)")
+
+    ev_pairs = []
+
+    def step(s, record):
+        if record:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        vt.vt_lmhead_trimmed(s["hidden"], s["weight"], keep, logits)
+        if record:
+            e1.record()
+            ev_pairs.append((e0, e1))
+        vt.vt_softmax_temp(logits, wl.T, dlse, None, s["u_draft"], dids, workspace=ws_sm_d)
+        vt.vt_softmax_temp(s["target"].view(B * (g + 1), cfg.V), wl.T, tlse, workspace=ws_sm_t)
+        vt.vt_spec_verify(s["target"], tlse, wl.T, logits.view(B, R, cfg.Vt), dlse, wl.T, dids.view(B, R), keep,
+                          f2t, s["u_acc"], s["u_fin"], tokens, nacc, workspace=ws_vf)
+
+    for i in range(args.warmup):
+        step(sets[i % n_sets], False)
+    torch.cuda.synchronize()
+    # timed region: K steps between two synchronisations; inside it, every LM-head launch is
+    # bracketed by events on the stream it is launched on
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % n_sets], True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+    lm_ms = sum(a.elapsed_time(b) for a, b in ev_pairs) / len(ev_pairs)
+
+    value = B * g / (ms_per_step / 1e3)
+    lmb = lmhead_bytes(cfg)
+    achieved = lmb / (lm_ms / 1e3) / 1e9
+    wl_key = f"config{args.config}"
+    traffic = measured_traffic(wl_key)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "lmhead_gemv" if B * R <= 8 else "lmhead_mfma",
+            "algorithmic_bytes_per_launch": lmb, "avg_launch_ms": round(lm_ms, 5)}
+    if B * R > 8:
+        tf = lmhead_flops(cfg) / (lm_ms / 1e3) / 1e12
+        roof["mfma_tflops"] = round(tf, 1)
+        roof["mfma_frac"] = round(tf / BF16_MFMA_PEAK_TFLOPS, 4)
+    log(f"step {ms_per_step:.4f} ms, LM head {lm_ms:.4f} ms = {achieved:.0f} GB/s; "
+        f"block {bb / (ms_per_step / 1e3) / 1e9:.0f} GB/s algorithmic")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        wl_one = make_workload(cfg, B=1)
+        log("timing the CPU oracle ...")
+        cpu = cpu_baseline(cfg, wl_one, args.cpu_seconds)
+
+    out = {
+        "metric": "verified draft positions/sec + LM-head HBM GB/s (% of 8 TB/s), 1 GPU",
+        "value": round(value, 1),
+        "unit": "verified draft positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": B, "gamma": g, "hidden": cfg.H, "vocab": cfg.V,
+                   "kept_rows": cfg.Vt, "target_logits": cfg.target_dtype, "temperature": cfg.T,
+                   "weights": "bf16", "accumulate": "f32", "input_sets_rotated": n_sets,
+                   "block_algorithmic_bytes": bb,
+                   "block_gbs": round(bb / (ms_per_step / 1e3) / 1e9, 1)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,189 @@
+"""Python binding of libvt.so, the MI355X (gfx950) draft-sampling / verification library.
+
+Argument marshalling only: every function here checks tensor dtypes/shapes, passes device
+pointers and the current HIP stream to the C ABI declared in include/vt.h, and raises VtError
+on a non-OK status.  All arithmetic runs in the library's kernels.  There is no CPU fallback:
+importing works anywhere, but calling a function without the built library (or without a GPU)
+raises.
+
+Entry points (same names as the C ABI):
+  vt_lmhead_trimmed(hidden, weight, keep_ids, logits)
+  vt_softmax_temp(logits, temperature, lse, probs=None, u=None, sampled=None, workspace=None, n=None)
+  vt_spec_verify(target_logits, target_lse, target_T, draft_logits, draft_lse, draft_T, draft_ids,
+                 keep_ids, full_to_trim, u_accept, u_final, out_tokens, out_num_accepted, workspace=None)
+Helpers: softmax_workspace(rows, n), verify_workspace(B, V), lib() (the raw ctypes handle).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libvt.so")
+
+VT_OK, VT_ERR_INVALID_ARG, VT_ERR_UNSUPPORTED, VT_ERR_WORKSPACE, VT_ERR_HIP = range(5)
+VT_F32, VT_BF16 = 0, 1
+
+_lib = None
+
+
+class VtError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = lib().vt_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{fn} failed: {msg} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libvt.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m draft_sampling_verification_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, F, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
+        L.vt_lmhead_trimmed.argtypes = [P, P, P, I64, I64, I64, I64, P, P]
+        L.vt_lmhead_trimmed.restype = I
+        L.vt_softmax_temp.argtypes = [P, I, I64, I64, I64, F, P, P, P, P, P, SZ, P]
+        L.vt_softmax_temp.restype = I
+        L.vt_softmax_temp_workspace_bytes.argtypes = [I64, I64]
+        L.vt_softmax_temp_workspace_bytes.restype = SZ
+        L.vt_spec_verify.argtypes = [I64, I64, I64, I64, P, I, P, F, P, I64, P, F, P, P, P, P, P, P, P, P, SZ, P]
+        L.vt_spec_verify.restype = I
+        L.vt_spec_verify_workspace_bytes.argtypes = [I64, I64]
+        L.vt_spec_verify_workspace_bytes.restype = SZ
+        L.vt_status_string.argtypes = [I]
+        L.vt_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+EXPORTED = ("vt_lmhead_trimmed", "vt_softmax_temp", "vt_softmax_temp_workspace_bytes", "vt_spec_verify",
+            "vt_spec_verify_workspace_bytes", "vt_status_string")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t, what, dtype=None, numel=None):
+    torch = _torch()
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{what}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{what}: dtype {t.dtype}, expected {dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{what}: {t.numel()} elements, need {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check(fn, status):
+    if status != VT_OK:
+        raise VtError(fn, status)
+
+
+def _bits16(t, what):
+    """bf16 tensors are passed as their bit patterns (uint16 storage)."""
+    torch = _torch()
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{what}: expected bfloat16 (or its 16-bit patterns), got {t.dtype}")
+    return t
+
+
+def softmax_workspace(rows: int, n: int, device="cuda"):
+    """A zero-filled workspace for vt_softmax_temp (None when the shape needs none)."""
+    nbytes = lib().vt_softmax_temp_workspace_bytes(rows, n)
+    return _torch().zeros(max(nbytes, 1), dtype=_torch().uint8, device=device) if nbytes else None
+
+
+def verify_workspace(B: int, V: int, device="cuda"):
+    """A zero-filled workspace for vt_spec_verify (None when the shape needs none)."""
+    nbytes = lib().vt_spec_verify_workspace_bytes(B, V)
+    return _torch().zeros(max(nbytes, 1), dtype=_torch().uint8, device=device) if nbytes else None
+
+
+def vt_lmhead_trimmed(hidden, weight, keep_ids, logits):
+    """logits[M, Vt] = hidden[M, H] @ weight[keep_ids].T (bf16 in, fp32 out); keep_ids may be None."""
+    torch = _torch()
+    _bits16(hidden, "hidden")
+    _bits16(weight, "weight")
+    M, H = hidden.shape
+    V_rows = weight.shape[0]
+    Vt = keep_ids.numel() if keep_ids is not None else logits.shape[1]
+    if weight.shape[1] != H or tuple(logits.shape) != (M, Vt):
+        raise ValueError("vt_lmhead_trimmed: shape mismatch")
+    st = lib().vt_lmhead_trimmed(_ptr(hidden, "hidden"), _ptr(weight, "weight"),
+                                 _ptr(keep_ids, "keep_ids", torch.int32), M, H, Vt, V_rows,
+                                 _ptr(logits, "logits", torch.float32), _stream())
+    _check("vt_lmhead_trimmed", st)
+    return logits
+
+
+def vt_softmax_temp(logits, temperature, lse, probs=None, u=None, sampled=None, workspace=None, n=None):
+    """Row-wise temperature softmax of logits[rows, ld] (first n columns; default all).
+
+    lse: float64 [rows]; probs: optional float32 [rows, n]; u / sampled: optional float32 / int32
+    [rows] (draw).  logits may be float32 or bfloat16.  workspace: from softmax_workspace().
+    """
+    torch = _torch()
+    rows, ld = logits.shape
+    n = ld if n is None else n
+    if logits.dtype == torch.float32:
+        dt = VT_F32
+    else:
+        _bits16(logits, "logits")
+        dt = VT_BF16
+    if workspace is None:
+        workspace = softmax_workspace(rows, n, logits.device)
+    wsb = workspace.numel() if workspace is not None else 0
+    st = lib().vt_softmax_temp(_ptr(logits, "logits"), dt, rows, n, ld, float(temperature),
+                               _ptr(lse, "lse", torch.float64, rows), _ptr(probs, "probs", torch.float32, rows * n),
+                               _ptr(u, "u", torch.float32, rows), _ptr(sampled, "sampled", torch.int32, rows),
+                               _ptr(workspace, "workspace"), wsb, _stream())
+    _check("vt_softmax_temp", st)
+    return lse
+
+
+def vt_spec_verify(target_logits, target_lse, target_T, draft_logits, draft_lse, draft_T, draft_ids, keep_ids,
+                   full_to_trim, u_accept, u_final, out_tokens, out_num_accepted, workspace=None):
+    """Modified rejection sampling; shapes: target [B, gamma+1, V], draft [B, R, Vt], ids [B, R]."""
+    torch = _torch()
+    B, g1, V = target_logits.shape
+    gamma = g1 - 1
+    Bd, R, Vt = draft_logits.shape
+    if Bd != B or tuple(draft_ids.shape) != (B, R) or tuple(out_tokens.shape) != (B, g1):
+        raise ValueError("vt_spec_verify: shape mismatch")
+    if target_logits.dtype == torch.float32:
+        dt = VT_F32
+    else:
+        _bits16(target_logits, "target_logits")
+        dt = VT_BF16
+    if workspace is None:
+        workspace = verify_workspace(B, V, target_logits.device)
+    wsb = workspace.numel() if workspace is not None else 0
+    st = lib().vt_spec_verify(B, gamma, V, Vt, _ptr(target_logits, "target_logits"), dt,
+                              _ptr(target_lse, "target_lse", torch.float64, B * g1), float(target_T),
+                              _ptr(draft_logits, "draft_logits", torch.float32), R,
+                              _ptr(draft_lse, "draft_lse", torch.float64, B * R), float(draft_T),
+                              _ptr(draft_ids, "draft_ids", torch.int32), _ptr(keep_ids, "keep_ids", torch.int32),
+                              _ptr(full_to_trim, "full_to_trim", torch.int32, V),
+                              _ptr(u_accept, "u_accept", torch.float32, B * gamma),
+                              _ptr(u_final, "u_final", torch.float32, B),
+                              _ptr(out_tokens, "out_tokens", torch.int32),
+                              _ptr(out_num_accepted, "out_num_accepted", torch.int32, B),
+                              _ptr(workspace, "workspace"), wsb, _stream())
+    _check("vt_spec_verify", st)
+    return out_tokens, out_num_accepted

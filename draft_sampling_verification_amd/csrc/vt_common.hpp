@@ -1,0 +1,223 @@
+// Shared device helpers for the gfx950 kernels: 64-wide wavefront reductions and scans,
+// 256-thread workgroup reductions and scans through LDS, bf16 decoding, host-side status glue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <tuple>
+#include <utility>
+
+#include "vt.h"
+
+namespace vt {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;             // threads per workgroup in the row kernels
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kChunk = 4096;            // elements per chunk of a row (fixed: results never depend on B)
+constexpr int kPerThread = kChunk / kBlock;  // 16 contiguous elements per thread
+
+static_assert(kPerThread == 16, "chunk geometry");
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+__device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return static_cast<int>(threadIdx.x) / kWave; }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int wave_min_int(int v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Inclusive prefix sum across the 64 lanes of a wavefront (Hillis-Steele).
+__device__ __forceinline__ float wave_inclusive_scan(float v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    float y = __shfl_up(v, d, kWave);
+    if (lane >= d) v += y;
+  }
+  return v;
+}
+
+// Workgroup-wide reductions (all kBlock threads must call; result broadcast to every thread).
+// `red` is LDS scratch of at least kWavesPerBlock floats/ints.
+__device__ __forceinline__ float block_sum(float v, float *red) {
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane_id() == 0) red[wave_id()] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWavesPerBlock; ++w) t += red[w];
+  return t;
+}
+
+__device__ __forceinline__ float block_max(float v, float *red) {
+  v = wave_max(v);
+  __syncthreads();
+  if (lane_id() == 0) red[wave_id()] = v;
+  __syncthreads();
+  float t = red[0];
+#pragma unroll
+  for (int w = 1; w < kWavesPerBlock; ++w) t = fmaxf(t, red[w]);
+  return t;
+}
+
+__device__ __forceinline__ int block_min_int(int v, int *red) {
+  v = wave_min_int(v);
+  __syncthreads();
+  if (lane_id() == 0) red[wave_id()] = v;
+  __syncthreads();
+  int t = red[0];
+#pragma unroll
+  for (int w = 1; w < kWavesPerBlock; ++w) t = min(t, red[w]);
+  return t;
+}
+
+__device__ __forceinline__ int block_max_int(int v, int *red) {
+  v = wave_max_int(v);
+  __syncthreads();
+  if (lane_id() == 0) red[wave_id()] = v;
+  __syncthreads();
+  int t = red[0];
+#pragma unroll
+  for (int w = 1; w < kWavesPerBlock; ++w) t = max(t, red[w]);
+  return t;
+}
+
+// Inclusive prefix over the workgroup's threads in thread order.  Returns this thread's
+// inclusive value; *prev receives the previous thread's inclusive value (0 for thread 0) and
+// *total the last thread's, each formed by the very same floating-point operations as the value
+// that thread returns, so comparisons against them are mutually consistent.
+__device__ __forceinline__ float block_inclusive_scan(float v, float *red, float *prev, float *total) {
+  const int lane = lane_id(), w = wave_id();
+  const float inc = wave_inclusive_scan(v);
+  const float up = __shfl_up(inc, 1, kWave);
+  __syncthreads();
+  if (lane == kWave - 1) red[w] = inc;
+  __syncthreads();
+  float before = 0.f;
+#pragma unroll
+  for (int k = 0; k < kWavesPerBlock; ++k)
+    if (k < w) before += red[k];
+  float all = 0.f;
+#pragma unroll
+  for (int k = 0; k < kWavesPerBlock; ++k) all += red[k];
+  *prev = lane == 0 ? before : before + up;
+  *total = all;
+  return before + inc;
+}
+
+// Last-workgroup-done protocol: each workgroup of a group (a row, a sequence) publishes its
+// partial result, then bumps the group's counter; the workgroup that brings the counter to
+// `count` combines all partials and resets the counter to zero for the next call.
+__device__ __forceinline__ bool arrive_last(unsigned int *counter, unsigned int count, int *flag_lds) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned int prev = atomicAdd(counter, 1u);
+    const bool last = (prev == count - 1u);
+    if (last) *counter = 0u;
+    *flag_lds = last ? 1 : 0;
+  }
+  __syncthreads();
+  const bool last = *flag_lds != 0;
+  if (last) __threadfence();
+  return last;
+}
+
+// The 16 contiguous elements [base + 16 t, base + 16 t + 16) of a row as fp32; -inf past n.
+template <typename Tin, bool kVec>
+__device__ __forceinline__ void load16(const Tin *__restrict__ row, int64_t n, int64_t base, float (&v)[16]) {
+  const int64_t e0 = base + static_cast<int64_t>(threadIdx.x) * kPerThread;
+  if (kVec && e0 + kPerThread <= n) {
+    if constexpr (sizeof(Tin) == 4) {
+      const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(row) + e0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 f = p[q];
+        v[4 * q + 0] = f.x;
+        v[4 * q + 1] = f.y;
+        v[4 * q + 2] = f.z;
+        v[4 * q + 3] = f.w;
+      }
+    } else {
+      const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(row) + e0);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint4 b = p[q];
+        const unsigned int wds[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[8 * q + 2 * k + 0] = __uint_as_float(wds[k] << 16);
+          v[8 * q + 2 * k + 1] = __uint_as_float(wds[k] & 0xffff0000u);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int64_t e = e0 + j;
+      if (e < n) {
+        if constexpr (sizeof(Tin) == 4)
+          v[j] = reinterpret_cast<const float *>(row)[e];
+        else
+          v[j] = bf16_to_f32(reinterpret_cast<const uint16_t *>(row)[e]);
+      } else {
+        v[j] = kNegInf;
+      }
+    }
+  }
+}
+
+// Launch with an explicit status: arguments are converted to the kernel's parameter types and
+// handed to hipLaunchKernel, whose return value reports this launch alone.
+template <typename... KArgs, typename Tuple, size_t... I>
+inline hipError_t launch_packed(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t stream,
+                                Tuple &packed, std::index_sequence<I...>) {
+  void *ptrs[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1] = {static_cast<void *>(&std::get<I>(packed))...};
+  return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, ptrs, shmem, stream);
+}
+
+template <typename... KArgs, typename... Args>
+inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t stream,
+                         Args... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+  std::tuple<KArgs...> packed(static_cast<KArgs>(args)...);
+  return launch_packed(kernel, grid, block, shmem, stream, packed, std::index_sequence_for<KArgs...>{});
+}
+
+inline vt_status_t hip_status(hipError_t e) { return e == hipSuccess ? VT_OK : VT_ERR_HIP; }
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline bool finite_positive(float t) { return t > 0.f && t <= 3.4028234663852886e38f; }
+
+}  // namespace vt

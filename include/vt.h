@@ -1,0 +1,163 @@
+/*
+ * vt.h -- C ABI of the draft-sampling / verification hot path for AMD Instinct MI355X (gfx950).
+ *
+ * Three operations make one speculative-decoding block:
+ *   vt_lmhead_trimmed  drafter logits through a vocabulary-trimmed LM head
+ *   vt_softmax_temp    temperature softmax (log-normaliser, optional probabilities) with an
+ *                      optional inverse-CDF draw per row
+ *   vt_spec_verify     batched modified rejection sampling: accept scan, residual or bonus draw,
+ *                      trimmed-id -> full-id remap
+ *
+ * Pages cited (title, section):
+ *   [VT] "VocabTrim: Vocabulary Pruning for Efficient Speculative Decoding in LLMs" (arXiv 2506.22694v2)
+ *   [GL] "Speculative decoding" (glossary page)
+ *   [RR] "A rejection rule keeps speculative decoding's output exact"
+ *
+ * Conventions for every entry point
+ *   - Every array pointer is a DEVICE pointer owned by the caller.  The library never allocates,
+ *     frees or synchronises; it only enqueues kernels on `stream` (0 = the null stream) and
+ *     returns.  Outputs are valid once the caller has synchronised the stream; inputs must stay
+ *     unchanged until then.  There is no global state: calls on distinct streams (with distinct
+ *     workspaces) may overlap.
+ *   - Arguments are validated on the host before any HIP call.  A failed check returns an error
+ *     code and enqueues nothing.  Nothing is thrown across the ABI and nothing aborts.
+ *   - Random numbers the method draws are inputs: uniforms u in (0, 1].  Using u = (k+1) * 2^-24
+ *     for a 24-bit integer k keeps them exact in fp32.
+ *   - Documented but unchecked preconditions (violations give unspecified results, never an
+ *     out-of-bounds access unless stated): logits are finite or -inf with at least one finite
+ *     entry per row; keep_ids entries are distinct and in [0, V_rows); full_to_trim is the
+ *     inverse of keep_ids (-1 elsewhere); an lse passed in was produced by vt_softmax_temp from
+ *     the same logits and temperature.
+ *   - Workspaces: a caller-owned device buffer of at least the size the matching
+ *     *_workspace_bytes function returns.  It holds per-row partial results and per-row
+ *     completion counters.  Before its first use it must be zero-filled (once); every completed
+ *     call returns the counters to zero (partials are always written before they are read), so
+ *     the buffer can be reused by later calls on the same stream, for any shape it is large
+ *     enough for.  Two calls in flight at once must not share a workspace.
+ */
+#ifndef VT_H_
+#define VT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VT_OK = 0,
+  VT_ERR_INVALID_ARG = 1, /* a NULL required pointer, a size out of range, a bad temperature */
+  VT_ERR_UNSUPPORTED = 2, /* valid arguments this build does not handle (alignment, H % 8, gamma > 64) */
+  VT_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than the *_workspace_bytes size */
+  VT_ERR_HIP = 4          /* hipLaunchKernel reported an error for one of the launches */
+} vt_status_t;
+
+typedef enum { VT_F32 = 0, VT_BF16 = 1 } vt_dtype_t;
+
+/*
+ * vt_lmhead_trimmed -- drafter logits over the trimmed vocabulary.
+ *   [VT] §3, Eq. 1: the trimmed head keeps the rows of the full LM head W that belong to the kept
+ *   vocabulary (Top-K of a token-frequency count), in that order; [VT] Appendix C.1, Algorithm 2:
+ *   the trimmed drafter scores only those rows.
+ *
+ *   logits[m][j] = sum_{k < H} hidden[m][k] * weight[row(j)][k],   row(j) = keep_ids ? keep_ids[j] : j
+ *
+ *   hidden   bf16 bit patterns, row-major [M][H]
+ *   weight   bf16 bit patterns, row-major [V_rows][H] (the full head; rows are gathered through
+ *            keep_ids, so no trimmed copy is needed; pass a pre-gathered W^Trim with keep_ids=NULL)
+ *   keep_ids int32 [Vt] or NULL (then row(j) = j and Vt <= V_rows)
+ *   logits   fp32 row-major [M][Vt], written in full
+ *   Products of bf16 values are exact in fp32; sums are accumulated in fp32 in an order that does
+ *   not depend on the row, so trimmed logits equal untrimmed logits gathered at keep_ids bit for bit.
+ *   Errors: INVALID_ARG for NULL hidden/weight/logits, M, H, Vt or V_rows <= 0, Vt > V_rows when
+ *   keep_ids is NULL; UNSUPPORTED for H % 8 != 0 or a hidden/weight base not 16-byte aligned.
+ */
+vt_status_t vt_lmhead_trimmed(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep_ids,
+                              int64_t M, int64_t H, int64_t Vt, int64_t V_rows, float *logits,
+                              hipStream_t stream);
+
+/*
+ * vt_softmax_temp -- temperature softmax over each row of a [rows][n] matrix (row stride ld
+ * elements), with an optional inverse-CDF draw.
+ *   [GL] "Distributional exactness has conditions": temperature must be applied to the very
+ *   distributions the correction uses; [RR] "A target and a draft small enough to print in full":
+ *   the categorical sampler walks the tokens in index order accumulating mass.
+ *
+ *   lse[r]      = log sum_j exp(x[r][j] / T)                      (fp64 output, fp32 reduction)
+ *   probs[r][j] = exp(x[r][j] / T - lse[r])                       (optional, fp32, row stride n)
+ *   sampled[r]  = min { j : u[r] * Z <= C[j] }                    (optional, int32)
+ *     where C is the running sum of the row's weights exp((x[r][j] - max_j x[r][j]) / T) in index
+ *     order and Z is the last entry of that same running sum, so for u in (0, 1] an index exists
+ *     and a zero-weight entry is never returned.  The running sum is formed in fp32 over fixed
+ *     4096-element chunks (chunk sums, a prefix over chunks, then a prefix inside the selected
+ *     chunk), independent of rows and of the row count.  Where the two levels disagree by a
+ *     rounding step at a chunk's end, the last positive-weight entry of that chunk is returned.
+ *
+ *   logits  fp32 or bf16 (dtype), [rows][ld] with ld >= n
+ *   lse     required, fp64 [rows]
+ *   probs   optional (NULL), fp32 [rows][n]
+ *   u       optional (NULL), fp32 [rows] in (0, 1]; sampled must be non-NULL exactly when u is
+ *   workspace / workspace_bytes: see vt_softmax_temp_workspace_bytes
+ *   Errors: INVALID_ARG for NULL logits/lse, rows or n <= 0, ld < n, T not finite or <= 0,
+ *   exactly one of u/sampled NULL, an unknown dtype; WORKSPACE if the workspace is too small.
+ */
+vt_status_t vt_softmax_temp(const void *logits, vt_dtype_t dtype, int64_t rows, int64_t n, int64_t ld,
+                            float temperature, double *lse, float *probs, const float *u, int32_t *sampled,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace vt_softmax_temp needs for this shape (0 when no row spans two chunks). */
+size_t vt_softmax_temp_workspace_bytes(int64_t rows, int64_t n);
+
+/*
+ * vt_spec_verify -- modified rejection sampling for B independent sequences of gamma drafts.
+ *   [GL] "Propose a block, keep a prefix" and "Why a rejection needs a special draw";
+ *   [RR] "What the accept/reject rule has to balance" and "Extending the rule from one token to a
+ *   drafted run"; [VT] Appendix C.1, Algorithm 2 (the token index mapper back to the full vocabulary).
+ *
+ *   For each sequence b, with p_i = softmax(target row i / target_T) over the V full ids and
+ *   q_i = softmax(draft row i / draft_T) over the Vt kept ids (q_i = 0 off the kept set):
+ *     1. left to right for i < gamma: x = draft_ids[b][i] (trimmed id), y = keep_ids[x] (full id);
+ *        accept iff u_accept[b][i] <= min(1, p_i(y) / q_i(x)); n = index of the first rejection,
+ *        or gamma if none;
+ *     2. if n < gamma: final ~ max(0, p_n - q_n) over full ids 0..V-1 (if that sums to 0 in fp32:
+ *        p_n); else final ~ p_gamma (the bonus token); drawn with u_final[b] by the running-sum
+ *        rule of vt_softmax_temp over full ids, in fixed 4096-id chunks;
+ *     3. out_tokens[b] = { y_0 .. y_{n-1}, final, -1 ... } (gamma+1 entries), out_num_accepted[b] = n.
+ *   The accept ratio is evaluated in fp64 from the fp32/bf16 logits and the fp64 lse.
+ *   A draft id outside [0, Vt) (or mapping outside [0, V)) among the first gamma makes that
+ *   sequence's out_num_accepted -1 and all its tokens -1; this is checked on the device.
+ *
+ *   target_logits fp32 or bf16 (target_dtype), [B][gamma+1][V]
+ *   target_lse    fp64 [B][gamma+1]     (from vt_softmax_temp with target_T)
+ *   draft_logits  fp32 [B][R][Vt], R >= gamma (rows gamma..R-1 are not read)
+ *   draft_lse     fp64 [B][R]           (from vt_softmax_temp with draft_T)
+ *   draft_ids     int32 [B][R] trimmed ids (from vt_softmax_temp's draw)
+ *   keep_ids      int32 [Vt], full_to_trim int32 [V]: both NULL (untrimmed head, Vt == V) or both set
+ *   u_accept      fp32 [B][gamma];  u_final fp32 [B]
+ *   out_tokens    int32 [B][gamma+1];  out_num_accepted int32 [B]
+ *   Errors: INVALID_ARG for NULL required pointers, B, gamma, V, Vt <= 0, Vt > V, R < gamma,
+ *   a temperature not finite or <= 0, keep_ids/full_to_trim NULL with Vt < V or only one of them
+ *   NULL; UNSUPPORTED for gamma > 64; WORKSPACE if the workspace is too small.
+ */
+vt_status_t vt_spec_verify(int64_t B, int64_t gamma, int64_t V, int64_t Vt, const void *target_logits,
+                           vt_dtype_t target_dtype, const double *target_lse, float target_T,
+                           const float *draft_logits, int64_t R, const double *draft_lse, float draft_T,
+                           const int32_t *draft_ids, const int32_t *keep_ids, const int32_t *full_to_trim,
+                           const float *u_accept, const float *u_final, int32_t *out_tokens,
+                           int32_t *out_num_accepted, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* Bytes of workspace vt_spec_verify needs for B sequences over a V-id vocabulary. */
+size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t V);
+
+/* Static description of a status code (never NULL). */
+const char *vt_status_string(vt_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VT_H_ */

@@ -1,0 +1,141 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every function
+include/vt.h declares, and rejects bad arguments with the documented status before any HIP
+call.  Pointers here are fake, aligned addresses that validation never dereferences."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import draft_sampling_verification_amd as vt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vt.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(vt.LIB_PATH), reason="libvt.so not built")
+
+OK, INV, UNS, WS, HIP = range(5)
+F32, BF16 = 0, 1
+P = ctypes.c_void_p
+A = P(0x100000)  # 16-byte aligned fake device address
+A2 = P(0x200000)
+NUL = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(vt_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_three_operations():
+    names = declared_functions()
+    for fn in ("vt_lmhead_trimmed", "vt_softmax_temp", "vt_spec_verify"):
+        assert fn in names
+    assert set(names) == set(vt.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = vt.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", vt.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (vt_\w+)$", out, re.M))
+    for fn in declared_functions():
+        assert hasattr(L, fn), fn
+        assert fn in exported, fn
+
+
+def test_status_strings():
+    L = vt.lib()
+    seen = set()
+    for s in range(5):
+        msg = L.vt_status_string(s)
+        assert msg and msg not in seen
+        seen.add(msg)
+    assert L.vt_status_string(99) == b"unknown status"
+
+
+def test_workspace_sizes():
+    L = vt.lib()
+    assert L.vt_softmax_temp_workspace_bytes(6, 4096) == 0  # single chunk rows need none
+    assert L.vt_softmax_temp_workspace_bytes(6, 4097) > 0
+    big = L.vt_softmax_temp_workspace_bytes(2304, 128256)
+    assert big >= 2304 * 32 * 8
+    assert L.vt_spec_verify_workspace_bytes(1, 18) == 0
+    assert L.vt_spec_verify_workspace_bytes(256, 128256) >= 256 * 32 * 8
+    assert L.vt_softmax_temp_workspace_bytes(0, 10) == 0
+    assert L.vt_spec_verify_workspace_bytes(-1, 10) == 0
+
+
+# ------------------------------------------------------------------ vt_lmhead_trimmed
+
+def lm(hidden=A, weight=A2, keep=NUL, M=6, H=3072, Vt=100, V=128, logits=A):
+    return vt.lib().vt_lmhead_trimmed(hidden, weight, keep, M, H, Vt, V, logits, NUL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=NUL), INV), (dict(weight=NUL), INV), (dict(logits=NUL), INV),
+    (dict(M=0), INV), (dict(H=0), INV), (dict(Vt=0), INV), (dict(V=0), INV), (dict(M=-3), INV),
+    (dict(Vt=200, V=128), INV),                       # untrimmed head with more columns than rows
+    (dict(H=3076), UNS),                              # H % 8 != 0
+    (dict(hidden=P(0x100008)), UNS),                  # misaligned hidden
+    (dict(weight=P(0x200002)), UNS),                  # misaligned weight
+])
+def test_lmhead_rejects(kw, status):
+    assert lm(**kw) == status
+
+
+# ------------------------------------------------------------------ vt_softmax_temp
+
+def sm(logits=A, dtype=F32, rows=6, n=128256, ld=None, T=1.0, lse=A, probs=NUL, u=NUL, sampled=NUL, ws=A2,
+       wsb=1 << 30):
+    ld = n if ld is None else ld
+    return vt.lib().vt_softmax_temp(logits, dtype, rows, n, ld, T, lse, probs, u, sampled, ws, wsb, NUL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(logits=NUL), INV), (dict(lse=NUL), INV), (dict(dtype=7), INV),
+    (dict(rows=0), INV), (dict(n=0), INV), (dict(n=10, ld=9), INV),
+    (dict(T=0.0), INV), (dict(T=-1.0), INV), (dict(T=math.nan), INV), (dict(T=math.inf), INV),
+    (dict(u=A), INV), (dict(sampled=A), INV),            # u and sampled come together
+    (dict(ws=NUL), WS), (dict(wsb=16), WS),
+])
+def test_softmax_rejects(kw, status):
+    assert sm(**kw) == status
+
+
+def test_softmax_workspace_exact_size_accepted_by_validation():
+    need = vt.lib().vt_softmax_temp_workspace_bytes(6, 128256)
+    assert sm(wsb=need - 1) == WS
+
+
+# ------------------------------------------------------------------ vt_spec_verify
+
+def vf(B=4, gamma=5, V=128256, Vt=32768, target=A, tdt=F32, tlse=A, Tt=1.0, draft=A, R=6, dlse=A, Td=1.0,
+       ids=A, keep=A, f2t=A, ua=A, uf=A, tok=A, nacc=A, ws=A2, wsb=1 << 30):
+    return vt.lib().vt_spec_verify(B, gamma, V, Vt, target, tdt, tlse, Tt, draft, R, dlse, Td, ids, keep, f2t,
+                                   ua, uf, tok, nacc, ws, wsb, NUL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(target=NUL), INV), (dict(tlse=NUL), INV), (dict(draft=NUL), INV), (dict(dlse=NUL), INV),
+    (dict(ids=NUL), INV), (dict(ua=NUL), INV), (dict(uf=NUL), INV), (dict(tok=NUL), INV), (dict(nacc=NUL), INV),
+    (dict(tdt=3), INV), (dict(B=0), INV), (dict(gamma=0), INV), (dict(V=0), INV), (dict(Vt=0), INV),
+    (dict(Vt=200000), INV),                              # more kept ids than the vocabulary
+    (dict(R=4), INV),                                    # fewer draft rows than drafts
+    (dict(Tt=0.0), INV), (dict(Td=-0.5), INV), (dict(Tt=math.nan), INV), (dict(Td=math.inf), INV),
+    (dict(keep=NUL, f2t=NUL), INV),                      # trimmed head without the id maps
+    (dict(keep=NUL), INV), (dict(f2t=NUL), INV),         # only one of the two maps
+    (dict(gamma=65, R=66), UNS),
+    (dict(ws=NUL), WS), (dict(wsb=8), WS),
+])
+def test_verify_rejects(kw, status):
+    assert vf(**kw) == status
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    # the binding has no fallback: without libvt.so every call raises
+    code = ("import draft_sampling_verification_amd as vt; vt.LIB_PATH = '/nonexistent/libvt.so'\n"
+            "try:\n    vt.lib()\nexcept RuntimeError as e:\n    print('raised', 'missing' in str(e))\n")
+    out = subprocess.run(["python", "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert out.stdout.strip() == "raised True", out.stderr
