@@ -48,6 +48,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--serial", action="store_true", help="run all four calls on one stream (no overlap)")
     return ap.parse_args()
 
 
@@ -179,19 +180,31 @@ def main():
     log(f"{n_sets} input sets on device ({bb / 1e6:.1f} MB algorithmic per step)")
 
     ev_pairs = []
+    # The target's log-normalisers do not depend on the draft: they run on a second stream and
+    # overlap the LM head; verification waits for both.  (Default priority on both streams.)
+    main = torch.cuda.current_stream()
+    side = main if args.serial else torch.cuda.Stream()
+    ev_target = torch.cuda.Event()
+    ev_done = torch.cuda.Event()
+    ev_done.record(main)
 
     def step(s, record):
+        side.wait_event(ev_done)  # the previous step's verify has finished reading tlse
+        with torch.cuda.stream(side):
+            vt.vt_softmax_temp(s["target"].view(B * (g + 1), cfg.V), wl.T, tlse, workspace=ws_sm_t)
+            ev_target.record(side)
         if record:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
+            e0.record(main)
         vt.vt_lmhead_trimmed(s["hidden"], s["weight"], keep, logits)
         if record:
-            e1.record()
+            e1.record(main)
             ev_pairs.append((e0, e1))
         vt.vt_softmax_temp(logits, wl.T, dlse, None, s["u_draft"], dids, workspace=ws_sm_d)
-        vt.vt_softmax_temp(s["target"].view(B * (g + 1), cfg.V), wl.T, tlse, workspace=ws_sm_t)
+        main.wait_event(ev_target)
         vt.vt_spec_verify(s["target"], tlse, wl.T, logits.view(B, R, cfg.Vt), dlse, wl.T, dids.view(B, R), keep,
                           f2t, s["u_acc"], s["u_fin"], tokens, nacc, workspace=ws_vf)
+        ev_done.record(main)
 
     for i in range(args.warmup):
         step(sets[i % n_sets], False)
@@ -244,6 +257,7 @@ def main():
         "config": {"workload": cfg.name, "batch": B, "gamma": g, "hidden": cfg.H, "vocab": cfg.V,
                    "kept_rows": cfg.Vt, "target_logits": cfg.target_dtype, "temperature": cfg.T,
                    "weights": "bf16", "accumulate": "f32", "input_sets_rotated": n_sets,
+                   "streams": 1 if args.serial else 2,
                    "block_algorithmic_bytes": bb,
                    "block_gbs": round(bb / (ms_per_step / 1e3) / 1e9, 1)},
         "roofline": roof,

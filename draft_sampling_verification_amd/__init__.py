@@ -104,15 +104,15 @@ def _bits16(t, what):
 
 
 def softmax_workspace(rows: int, n: int, device="cuda"):
-    """A zero-filled workspace for vt_softmax_temp (None when the shape needs none)."""
+    """A workspace for vt_softmax_temp (None when the shape needs none)."""
     nbytes = lib().vt_softmax_temp_workspace_bytes(rows, n)
-    return _torch().zeros(max(nbytes, 1), dtype=_torch().uint8, device=device) if nbytes else None
+    return _torch().empty(nbytes, dtype=_torch().uint8, device=device) if nbytes else None
 
 
 def verify_workspace(B: int, V: int, device="cuda"):
-    """A zero-filled workspace for vt_spec_verify (None when the shape needs none)."""
+    """A workspace for vt_spec_verify (None when the shape needs none)."""
     nbytes = lib().vt_spec_verify_workspace_bytes(B, V)
-    return _torch().zeros(max(nbytes, 1), dtype=_torch().uint8, device=device) if nbytes else None
+    return _torch().empty(nbytes, dtype=_torch().uint8, device=device) if nbytes else None
 
 
 def vt_lmhead_trimmed(hidden, weight, keep_ids, logits):

@@ -41,34 +41,74 @@ __device__ __forceinline__ uint4 load_nt(const uint4 *p) {
   return r;
 }
 
-// Transpose-reduction of N (power of two) per-lane values across the wavefront.  Each step
-// exchanges half of the remaining values with the partner lane (lane ^ offset) and keeps the
-// sums of the other half, so the whole reduction costs about N + log2(64/N) shuffles instead of
-// 6N.  On return lane l holds the full 64-lane sum of value index (l >> (6 - log2 N)).
-template <int N>
-__device__ __forceinline__ float transpose_reduce(float (&v)[N]) {
-  const int lane = lane_id();
-  int n = N;
-  int off = kWave / 2;
+// ---- cross-lane exchange on gfx950
+// v_permlane32_swap: lanes 32..63 of the first operand trade places with lanes 0..31 of the
+// second; v_permlane16_swap does the same for the odd 16-lane rows of the first operand and the
+// even rows of the second.  Adding the two results sums each value with its partner at
+// lane ^ 32 (^ 16) while keeping the two values apart -- one instruction per pair, no selects.
+__device__ __forceinline__ void swap32(float &x, float &y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap16(float &x, float &y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+// DPP lane moves inside 16-lane rows: rotate by 8 (partner lane ^ 8), mirror within 8 lanes,
+// and the quad permutations that swap neighbours (lane ^ 1) and pairs (lane ^ 2).
+constexpr int kDppRor8 = 0x128, kDppHalfMirror = 0x141, kDppXor1 = 0xB1, kDppXor2 = 0x4E;
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Transpose-reduction of NP (1, 2, 4 or 8) per-lane partial sums over the 64 lanes.  The steps
+// at lane distance 32, 16 and 8 halve the number of values each lane carries (each lane keeps
+// the half its partner gives up), the remaining steps add within groups of 64/NP lanes.  On
+// return lane l holds the complete sum of value index l / (64 / NP).  About NP + 6 exchanges
+// instead of 6 * NP for NP separate reductions.
+template <int NP>
+__device__ __forceinline__ float transpose_reduce(float (&v)[NP]) {
+  if constexpr (NP >= 2) {
 #pragma unroll
-  for (int step = 0; step < 6; ++step) {
-    if (n > 1) {
-      const bool upper = (lane & off) != 0;
-      const int h = n / 2;
-#pragma unroll
-      for (int k = 0; k < N / 2; ++k) {
-        if (k < h) {
-          const float send = upper ? v[k] : v[k + h];
-          const float keep = upper ? v[k + h] : v[k];
-          v[k] = keep + __shfl_xor(send, off, kWave);
-        }
-      }
-      n = h;
-    } else {
-      v[0] += __shfl_xor(v[0], off, kWave);
+    for (int k = 0; k < NP / 2; ++k) {
+      float a = v[k], b = v[k + NP / 2];
+      swap32(a, b);
+      v[k] = a + b;
     }
-    off >>= 1;
+  } else {
+    float a = v[0], b = v[0];
+    swap32(a, b);
+    v[0] = a + b;
   }
+  if constexpr (NP >= 4) {
+#pragma unroll
+    for (int k = 0; k < NP / 4; ++k) {
+      float a = v[k], b = v[k + NP / 4];
+      swap16(a, b);
+      v[k] = a + b;
+    }
+  } else {
+    float a = v[0], b = v[0];
+    swap16(a, b);
+    v[0] = a + b;
+  }
+  if constexpr (NP >= 8) {
+    const bool up = (lane_id() & 8) != 0;
+#pragma unroll
+    for (int k = 0; k < NP / 8; ++k) {
+      const float send = up ? v[k] : v[k + NP / 8];
+      const float keep = up ? v[k + NP / 8] : v[k];
+      v[k] = keep + dpp<kDppRor8>(send);
+    }
+  } else {
+    v[0] += dpp<kDppRor8>(v[0]);
+  }
+  v[0] += dpp<kDppHalfMirror>(v[0]);
+  v[0] += dpp<kDppXor2>(v[0]);
+  v[0] += dpp<kDppXor1>(v[0]);
   return v[0];
 }
 
@@ -81,72 +121,85 @@ struct Pow2Ceil<1> {
   static constexpr int value = 1;
 };
 
-// One wavefront per weight row at a time; the next row's loads are issued before the current
-// row is reduced (register double buffering).  NIT = ceil(H / 512): lane l covers the 16-byte
-// pieces l + 64 * it of a row.
-template <int M, int NIT>
+#ifndef VT_GEMV_PD
+#define VT_GEMV_PD 2
+#endif
+constexpr int kGemvPrefetch = VT_GEMV_PD;  // weight rows in flight per wavefront beyond the one in use
+
+// Each wavefront walks weight rows j = w, w + W, w + 2W, ... (W = wavefronts in the grid), so at
+// any moment the grid streams one contiguous window of the head.  A ring of PD + 1 register
+// buffers keeps PD rows in flight while one is multiplied.  Every load is unconditional and in
+// bounds (row indices past the wave's last row repeat the last row, pieces past H repeat the
+// last piece and are masked), so the compiler can wait for exactly the oldest row (vmcnt(N))
+// instead of draining the queue.  FULL: H is a multiple of 512 (no masking at all).
+template <int M, int NIT, int PD, bool FULL, bool TRIM>
 __global__ __launch_bounds__(kBlock) void lmhead_gemv(const uint16_t *__restrict__ hidden,
                                                       const uint16_t *__restrict__ weight,
                                                       const int32_t *__restrict__ keep, int H, int Vt,
                                                       float *__restrict__ logits) {
   constexpr int NP = Pow2Ceil<M>::value;
+  constexpr int kGroup = kWave / NP;
   const int lane = lane_id();
   const int pieces = H >> 3;  // 16-byte pieces per row
+  auto piece = [&](int it) -> int {
+    const int p = it * kWave + lane;
+    return (FULL || it < NIT - 1) ? p : min(p, pieces - 1);
+  };
+  auto live = [&](int it) -> bool { return FULL || it < NIT - 1 || it * kWave + lane < pieces; };
+
   uint4 h[M][NIT];
 #pragma unroll
   for (int m = 0; m < M; ++m)
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      const int p = it * kWave + lane;
-      h[m][it] = p < pieces ? reinterpret_cast<const uint4 *>(hidden + static_cast<int64_t>(m) * H)[p]
-                            : make_uint4(0, 0, 0, 0);
+      const uint4 v = reinterpret_cast<const uint4 *>(hidden + static_cast<int64_t>(m) * H)[piece(it)];
+      h[m][it] = live(it) ? v : make_uint4(0, 0, 0, 0);
     }
 
-  const int nwaves = gridDim.x * kWavesPerBlock;
-  int j = blockIdx.x * kWavesPerBlock + wave_id();
-  if (j >= Vt) return;
+  const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kWavesPerBlock + wave_id());
+  const int nw = gridDim.x * kWavesPerBlock;
+  if (wv >= Vt) return;
+  const int nrows = (Vt - 1 - wv) / nw + 1;
 
-  auto row_ptr = [&](int jj) -> const uint4 * {
-    const int64_t r = keep ? static_cast<int64_t>(keep[jj]) : static_cast<int64_t>(jj);
-    return reinterpret_cast<const uint4 *>(weight + r * H);
+  auto fetch = [&](int t, uint4(&dst)[NIT]) {
+    const int j = wv + min(t, nrows - 1) * nw;  // wave-uniform
+    int64_t r = j;
+    if constexpr (TRIM) r = keep[j];
+    const uint4 *src = reinterpret_cast<const uint4 *>(weight + r * H);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) dst[it] = load_nt(src + piece(it));
   };
-  uint4 w[NIT];
-  {
-    const uint4 *src = row_ptr(j);
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int p = it * kWave + lane;
-      w[it] = p < pieces ? load_nt(src + p) : make_uint4(0, 0, 0, 0);
-    }
-  }
-  for (; j < Vt; j += nwaves) {
-    const int jn = j + nwaves;
-    uint4 wn[NIT];
-    if (jn < Vt) {
-      const uint4 *src = row_ptr(jn);
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const int p = it * kWave + lane;
-        wn[it] = p < pieces ? load_nt(src + p) : make_uint4(0, 0, 0, 0);
-      }
-    }
+  auto consume = [&](int t, const uint4(&src)[NIT]) {
     float acc[NP];
 #pragma unroll
     for (int m = 0; m < NP; ++m) acc[m] = 0.f;
 #pragma unroll
-    for (int it = 0; it < NIT; ++it)
+    for (int it = 0; it < NIT; ++it) {
+      const uint4 wv4 = live(it) ? src[it] : make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int m = 0; m < M; ++m) acc[m] = dot8(w[it], h[m][it], acc[m]);
-    const float s = transpose_reduce<NP>(acc);
-    // lane l holds the sum for hidden row l / (64 / NP)
-    constexpr int kGroup = kWave / NP;
+      for (int m = 0; m < M; ++m) acc[m] = dot8(wv4, h[m][it], acc[m]);
+    }
+    const float sum = transpose_reduce<NP>(acc);
     const int m = lane / kGroup;
-    if ((lane % kGroup) == 0 && m < M) logits[static_cast<int64_t>(m) * Vt + j] = s;
-    if (jn < Vt) {
+    if ((lane % kGroup) == 0 && m < M) logits[static_cast<int64_t>(m) * Vt + wv + t * nw] = sum;
+  };
+
+  uint4 w[PD + 1][NIT];
 #pragma unroll
-      for (int it = 0; it < NIT; ++it) w[it] = wn[it];
+  for (int s = 0; s < PD; ++s) fetch(s, w[s]);
+  // whole groups of PD + 1 rows: straight-line code, so each multiply waits only for its own row
+  int t0 = 0;
+  for (; t0 + PD < nrows; t0 += PD + 1) {
+#pragma unroll
+    for (int s = 0; s <= PD; ++s) {
+      fetch(t0 + s + PD, w[(s + PD) % (PD + 1)]);
+      consume(t0 + s, w[s]);
     }
   }
+  // the last rows (fewer than PD + 1) are already in flight
+#pragma unroll
+  for (int s = 0; s < PD; ++s)
+    if (t0 + s < nrows) consume(t0 + s, w[s]);
 }
 
 // ------------------------------------------------------------------------------ MFMA path
@@ -273,44 +326,65 @@ __global__ __launch_bounds__(kBlock) void lmhead_mfma(const uint16_t *__restrict
 // ------------------------------------------------------------------------------ dispatch
 using GemvFn = void (*)(const uint16_t *, const uint16_t *, const int32_t *, int, int, float *);
 
-template <int M, int NIT>
-constexpr GemvFn gemv_entry() {
-  return &lmhead_gemv<M, NIT>;
-}
-
 constexpr int kGemvMaxM = 8;
 constexpr int kGemvMaxNit = 8;
-constexpr int kGemvMaxRegs = 48;  // M * NIT: hidden slice kept in 4 * M * NIT VGPRs
+constexpr int kGemvMaxRegs = 48;  // M * NIT: the hidden slice lives in 4 * M * NIT VGPRs
+
+template <int M, int NIT>
+GemvFn gemv_entry(bool full, bool trim) {
+  if constexpr (M * NIT > kGemvMaxRegs) {
+    return nullptr;
+  } else {
+    if (full) return trim ? &lmhead_gemv<M, NIT, kGemvPrefetch, true, true> : &lmhead_gemv<M, NIT, kGemvPrefetch, true, false>;
+    return trim ? &lmhead_gemv<M, NIT, kGemvPrefetch, false, true> : &lmhead_gemv<M, NIT, kGemvPrefetch, false, false>;
+  }
+}
 
 template <int M>
-GemvFn gemv_for_nit(int nit) {
+GemvFn gemv_for_nit(int nit, bool full, bool trim) {
   switch (nit) {
-    case 1: return gemv_entry<M, 1>();
-    case 2: return gemv_entry<M, 2>();
-    case 3: return gemv_entry<M, 3>();
-    case 4: return gemv_entry<M, 4>();
-    case 5: return M * 5 <= kGemvMaxRegs ? gemv_entry<M, 5>() : nullptr;
-    case 6: return M * 6 <= kGemvMaxRegs ? gemv_entry<M, 6>() : nullptr;
-    case 7: return M * 7 <= kGemvMaxRegs ? gemv_entry<M, 7>() : nullptr;
-    case 8: return M * 8 <= kGemvMaxRegs ? gemv_entry<M, 8>() : nullptr;
+    case 1: return gemv_entry<M, 1>(full, trim);
+    case 2: return gemv_entry<M, 2>(full, trim);
+    case 3: return gemv_entry<M, 3>(full, trim);
+    case 4: return gemv_entry<M, 4>(full, trim);
+    case 5: return gemv_entry<M, 5>(full, trim);
+    case 6: return gemv_entry<M, 6>(full, trim);
+    case 7: return gemv_entry<M, 7>(full, trim);
+    case 8: return gemv_entry<M, 8>(full, trim);
     default: return nullptr;
   }
 }
 
-GemvFn pick_gemv(int64_t M, int64_t H) {
+GemvFn pick_gemv(int64_t M, int64_t H, bool trim) {
   const int nit = static_cast<int>((H + 511) / 512);
+  const bool full = H % 512 == 0;
   if (nit > kGemvMaxNit || M > kGemvMaxM || M * nit > kGemvMaxRegs) return nullptr;
   switch (M) {
-    case 1: return gemv_for_nit<1>(nit);
-    case 2: return gemv_for_nit<2>(nit);
-    case 3: return gemv_for_nit<3>(nit);
-    case 4: return gemv_for_nit<4>(nit);
-    case 5: return gemv_for_nit<5>(nit);
-    case 6: return gemv_for_nit<6>(nit);
-    case 7: return gemv_for_nit<7>(nit);
-    case 8: return gemv_for_nit<8>(nit);
+    case 1: return gemv_for_nit<1>(nit, full, trim);
+    case 2: return gemv_for_nit<2>(nit, full, trim);
+    case 3: return gemv_for_nit<3>(nit, full, trim);
+    case 4: return gemv_for_nit<4>(nit, full, trim);
+    case 5: return gemv_for_nit<5>(nit, full, trim);
+    case 6: return gemv_for_nit<6>(nit, full, trim);
+    case 7: return gemv_for_nit<7>(nit, full, trim);
+    case 8: return gemv_for_nit<8>(nit, full, trim);
     default: return nullptr;
   }
+}
+
+// Workgroups of a GEMV launch: as many as can be resident at once on every CU (each loops over
+// rows), but never more than there are rows for.
+int64_t gemv_blocks(GemvFn fn, int64_t Vt) {
+  int dev = 0, cus = 256, per_cu = 1;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(fn), kBlock, 0) !=
+          hipSuccess ||
+      per_cu <= 0)
+    per_cu = 1;
+  const int64_t want = static_cast<int64_t>(cus) * per_cu;
+  const int64_t need = (Vt + kWavesPerBlock - 1) / kWavesPerBlock;
+  return want < need ? want : need;
 }
 
 }  // namespace
@@ -326,13 +400,9 @@ extern "C" vt_status_t vt_lmhead_trimmed(const uint16_t *hidden, const uint16_t 
   if (M > INT32_MAX || H > INT32_MAX || Vt > INT32_MAX) return VT_ERR_UNSUPPORTED;
   if (H % 8 != 0 || !aligned16(hidden) || !aligned16(weight)) return VT_ERR_UNSUPPORTED;
 
-  const GemvFn gemv = pick_gemv(M, H);
+  const GemvFn gemv = pick_gemv(M, H, keep_ids != nullptr);
   if (gemv) {
-    // enough wavefronts to keep every CU streaming, each walking rows with a stride
-    const int64_t rows_per_block = kWavesPerBlock;
-    int64_t blocks = (Vt + rows_per_block - 1) / rows_per_block;
-    const int64_t kMaxBlocks = 256 * 4;  // 256 CUs x 4 workgroups
-    if (blocks > kMaxBlocks) blocks = kMaxBlocks;
+    const int64_t blocks = gemv_blocks(gemv, Vt);
     return hip_status(launch(gemv, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, stream, hidden, weight,
                              keep_ids, static_cast<int>(H), static_cast<int>(Vt), logits));
   }

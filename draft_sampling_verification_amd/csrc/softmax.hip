@@ -6,14 +6,15 @@
 // speculative decoding's output exact", the categorical sampler of "A target and a draft small
 // enough to print in full").
 //
-// Layout of the work: a row is cut into fixed 4096-element chunks; one 256-thread workgroup per
-// (row, chunk), each thread owning 16 contiguous elements held in registers.  Phase 1 computes
-// the chunk's (max m_c, sum s_c of exp((x - m_c)/T)); the last workgroup of the row to finish
-// (atomic counter in the workspace) combines them into M = max m_c, S_c = s_c exp((m_c - M)/T),
-// the chunk-level running sum P_c and Z = P_last, writes lse = M/T + ln Z in fp64, and, when
-// asked, draws: t = u Z, c* = first chunk with t <= P_c, then a rescan of chunk c* finds the first
-// element whose running sum reaches t.  Rows of at most one chunk finish inside their single
-// workgroup.  exp(y) is evaluated as 2^(y log2 e) on v_exp_f32 with log2(e)/T folded into one
+// Layout of the work: a row is cut into fixed 4096-element chunks, each thread of a 256-thread
+// workgroup owning 16 contiguous elements held in registers.  Rows of one chunk finish in one
+// workgroup.  Longer rows take two launches: one workgroup per (row, chunk) computes the chunk's
+// (max m_c, sum s_c of exp((x - m_c)/T)); then one workgroup per row combines them into
+// M = max m_c, S_c = s_c exp((m_c - M)/T), the chunk-level running sum P_c and Z = P_last, writes
+// lse = M/T + ln Z in fp64, and, when asked, draws: t = u Z, c* = first chunk with t <= P_c, then
+// a rescan of chunk c* finds the first element whose running sum reaches t.  The two launches
+// are ordered by the stream; no device-wide fence is used (on a multi-XCD device such a fence
+// writes back and invalidates the L2 of the issuing XCD).  exp(y) is evaluated as 2^(y log2 e) on v_exp_f32 with log2(e)/T folded into one
 // fp32 constant, and arguments are formed relative to the row max so the heavy entries carry
 // the smallest rounding.
 #include <hip/hip_runtime.h>
@@ -35,7 +36,6 @@ struct SmParams {
   float *probs;
   const float *u;
   int32_t *sampled;
-  unsigned int *counters;
   float2 *rowstat;  // (M, Z) per row, for the probability pass of multi-chunk rows
   float2 *part;     // (m_c, s_c) per (row, chunk)
   int nchunk;
@@ -84,68 +84,85 @@ __device__ __forceinline__ int chunk_find(const float (&w)[16], const ChunkScan 
   return block_max_int(last, redi);
 }
 
+// Rows of at most one chunk: the whole row lives in one workgroup.  Z is the running sum at
+// the row's last element, so the draw always finds an index.
 template <typename Tin, bool kVec>
-__global__ __launch_bounds__(kBlock) void softmax_rows(SmParams P) {
+__global__ __launch_bounds__(kBlock) void softmax_single(SmParams P) {
   __shared__ float redf[kWavesPerBlock];
   __shared__ int redi[kWavesPerBlock];
-  __shared__ int flag;
-  __shared__ float bcast[2];
+  __shared__ float bcast;
+  const int64_t r = blockIdx.x;
+  const Tin *row = reinterpret_cast<const Tin *>(P.logits) + r * P.ld;
+  float v[16], w[16];
+  load16<Tin, kVec>(row, P.n, 0, v);
+  float m = kNegInf;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) m = fmaxf(m, v[j]);
+  m = block_max(m, redf);
+  weights16(v, m, P.k2, w);
+  ChunkScan cs;
+  chunk_scan(w, 0.f, cs, redf);
+  const int last = static_cast<int>(P.n - 1);
+  if (static_cast<int>(threadIdx.x) == last / kPerThread) {
+    float z = 0.f;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j)
+      if (j == last % kPerThread) z = cs.base + cs.loc[j];
+    bcast = z;
+  }
+  __syncthreads();
+  const float Z = bcast;
+  if (threadIdx.x == 0) P.lse[r] = static_cast<double>(m) / P.T + log(static_cast<double>(Z));
+  if (P.probs) {
+    const float inv = 1.f / Z;
+    float *pr = P.probs + r * P.n;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int64_t e = static_cast<int64_t>(threadIdx.x) * kPerThread + j;
+      if (e < P.n) pr[e] = w[j] * inv;
+    }
+  }
+  if (P.u) {
+    const float t = P.u[r] * Z;
+    const int idx = chunk_find(w, cs, t, redi);
+    if (threadIdx.x == 0) P.sampled[r] = idx;
+  }
+}
 
+// Rows of several chunks, pass 1: one workgroup per (row, chunk) publishes the chunk's
+// (max m_c, sum s_c of exp((x - m_c)/T)).  The next launch reads them (kernel boundaries order
+// the two passes; no device-wide fences are needed).
+template <typename Tin, bool kVec>
+__global__ __launch_bounds__(kBlock) void softmax_partial(SmParams P) {
+  __shared__ float redf[kWavesPerBlock];
   const int64_t bid = blockIdx.x;
   const int64_t r = bid / P.nchunk;
   const int c = static_cast<int>(bid - r * P.nchunk);
   const Tin *row = reinterpret_cast<const Tin *>(P.logits) + r * P.ld;
-
-  float v[16];
+  float v[16], w[16];
   load16<Tin, kVec>(row, P.n, static_cast<int64_t>(c) * kChunk, v);
   float m = kNegInf;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) m = fmaxf(m, v[j]);
   m = block_max(m, redf);
-  float w[16];
   weights16(v, m, P.k2, w);
-
-  if (P.nchunk == 1) {
-    // the whole row lives in this workgroup: Z is the running sum at the row's last element
-    ChunkScan cs;
-    chunk_scan(w, 0.f, cs, redf);
-    const int last = static_cast<int>(P.n - 1);
-    if (static_cast<int>(threadIdx.x) == last / kPerThread) {
-      float z = 0.f;
-#pragma unroll
-      for (int j = 0; j < kPerThread; ++j)
-        if (j == last % kPerThread) z = cs.base + cs.loc[j];
-      bcast[0] = z;
-    }
-    __syncthreads();
-    const float Z = bcast[0];
-    if (threadIdx.x == 0) P.lse[r] = static_cast<double>(m) / P.T + log(static_cast<double>(Z));
-    if (P.probs) {
-      const float inv = 1.f / Z;
-      float *pr = P.probs + r * P.n;
-#pragma unroll
-      for (int j = 0; j < kPerThread; ++j) {
-        const int64_t e = static_cast<int64_t>(threadIdx.x) * kPerThread + j;
-        if (e < P.n) pr[e] = w[j] * inv;
-      }
-    }
-    if (P.u) {
-      const float t = P.u[r] * Z;
-      const int idx = chunk_find(w, cs, t, redi);
-      if (threadIdx.x == 0) P.sampled[r] = idx;
-    }
-    return;
-  }
-
-  // ---- phase 1: publish this chunk's (max, sum)
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) s += w[j];
   s = block_sum(s, redf);
   if (threadIdx.x == 0) P.part[r * P.nchunk + c] = make_float2(m, s);
-  if (!arrive_last(&P.counters[r], static_cast<unsigned int>(P.nchunk), &flag)) return;
+}
 
-  // ---- phase 2 (last workgroup of the row): combine the chunks
+// Pass 2: one workgroup per row combines the chunks into M = max m_c, S_c = s_c exp((m_c - M)/T),
+// the chunk-level running sum P_c and Z = P_last; writes lse = M/T + ln Z in fp64; draws by
+// locating the chunk (first c with u Z <= P_c) and rescanning it.
+template <typename Tin, bool kVec>
+__global__ __launch_bounds__(kBlock) void softmax_combine(SmParams P) {
+  __shared__ float redf[kWavesPerBlock];
+  __shared__ int redi[kWavesPerBlock];
+  __shared__ float bcast;
+  const int64_t r = blockIdx.x;
+  const Tin *row = reinterpret_cast<const Tin *>(P.logits) + r * P.ld;
   const float2 *part = P.part + r * P.nchunk;
   float mm = kNegInf;
   for (int k = threadIdx.x; k < P.nchunk; k += kBlock) mm = fmaxf(mm, part[k].x);
@@ -155,7 +172,7 @@ __global__ __launch_bounds__(kBlock) void softmax_rows(SmParams P) {
     const float2 ps = part[k];
     return (ps.x == kNegInf) ? 0.f : ps.y * exp2_fast((ps.x - M) * P.k2);
   };
-  // chunk-level running sum, in passes of 256 chunks with a carry; Z = its last value
+  // chunk-level running sum in passes of 256 chunks with a carry; Z is its last value
   float carry = 0.f;
   for (int k0 = 0; k0 < P.nchunk; k0 += kBlock) {
     float prev, total;
@@ -169,7 +186,6 @@ __global__ __launch_bounds__(kBlock) void softmax_rows(SmParams P) {
   }
   if (!P.u) return;
 
-  // ---- draw: locate the chunk, then rescan it
   const float t = P.u[r] * Z;
   int cstar = 0x7fffffff;
   float Estar = 0.f;
@@ -181,27 +197,29 @@ __global__ __launch_bounds__(kBlock) void softmax_rows(SmParams P) {
     const bool hit = k < P.nchunk && t <= carry + incl;
     const int first = block_min_int(hit ? k : 0x7fffffff, redi);
     if (first != 0x7fffffff) {
-      if (k == first) bcast[1] = carry + prev;
+      if (k == first) bcast = carry + prev;
       __syncthreads();
       cstar = first;
-      Estar = bcast[1];
+      Estar = bcast;
       break;
     }
     carry = carry + total;
   }
+  bool fallback = false;
   if (cstar == 0x7fffffff) {
-    // u * Z beyond the running sum (only possible for u > 1): last chunk with positive mass
+    // u Z beyond the running sum (only for u > 1 or NaN): last chunk with positive mass
     int lastc = -1;
     for (int k = threadIdx.x; k < P.nchunk; k += kBlock)
       if (chunk_mass(k) > 0.f) lastc = k;
-    cstar = max(block_max_int(lastc, redi), 0);  // never below chunk 0, even for a NaN uniform
-    Estar = kNegInf;  // forces the in-chunk fallback
+    cstar = max(block_max_int(lastc, redi), 0);  // never below chunk 0
+    fallback = true;
   }
+  float v[16], w[16];
   load16<Tin, kVec>(row, P.n, static_cast<int64_t>(cstar) * kChunk, v);
   weights16(v, M, P.k2, w);
   ChunkScan cs;
-  chunk_scan(w, Estar == kNegInf ? 0.f : Estar, cs, redf);
-  const int idx = chunk_find(w, cs, Estar == kNegInf ? __builtin_huge_valf() : t, redi);
+  chunk_scan(w, fallback ? 0.f : Estar, cs, redf);
+  const int idx = chunk_find(w, cs, fallback ? __builtin_huge_valf() : t, redi);
   if (threadIdx.x == 0) P.sampled[r] = cstar * kChunk + idx;
 }
 
@@ -226,29 +244,33 @@ __global__ __launch_bounds__(kBlock) void softmax_probs(SmParams P) {
 }
 
 struct WsLayout {
-  size_t counters, rowstat, part, bytes;
+  size_t rowstat, part, bytes;
 };
 
 WsLayout ws_layout(int64_t rows, int64_t nchunk) {
   WsLayout L{};
   if (nchunk <= 1) return L;
-  L.counters = 0;
-  L.rowstat = align_up(static_cast<size_t>(rows) * sizeof(unsigned int), 256);
-  L.part = L.rowstat + align_up(static_cast<size_t>(rows) * sizeof(float2), 256);
+  L.rowstat = 0;
+  L.part = align_up(static_cast<size_t>(rows) * sizeof(float2), 256);
   L.bytes = L.part + align_up(static_cast<size_t>(rows) * static_cast<size_t>(nchunk) * sizeof(float2), 256);
   return L;
 }
 
-template <typename Tin>
-hipError_t launch_rows(const SmParams &P, bool vec, int64_t grid, hipStream_t stream) {
-  if (vec) return launch(softmax_rows<Tin, true>, dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, stream, P);
-  return launch(softmax_rows<Tin, false>, dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, stream, P);
+template <typename Tin, bool kVec>
+hipError_t launch_all(const SmParams &P, hipStream_t stream) {
+  const unsigned rows = static_cast<unsigned>(P.rows);
+  if (P.nchunk == 1) return launch(softmax_single<Tin, kVec>, dim3(rows), dim3(kBlock), 0, stream, P);
+  const unsigned grid = static_cast<unsigned>(P.rows * P.nchunk);
+  hipError_t e = launch(softmax_partial<Tin, kVec>, dim3(grid), dim3(kBlock), 0, stream, P);
+  if (e != hipSuccess) return e;
+  e = launch(softmax_combine<Tin, kVec>, dim3(rows), dim3(kBlock), 0, stream, P);
+  if (e != hipSuccess || !P.probs) return e;
+  return launch(softmax_probs<Tin, kVec>, dim3(grid), dim3(kBlock), 0, stream, P);
 }
 
 template <typename Tin>
-hipError_t launch_probs(const SmParams &P, bool vec, int64_t grid, hipStream_t stream) {
-  if (vec) return launch(softmax_probs<Tin, true>, dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, stream, P);
-  return launch(softmax_probs<Tin, false>, dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, stream, P);
+hipError_t launch_dtype(const SmParams &P, bool vec, hipStream_t stream) {
+  return vec ? launch_all<Tin, true>(P, stream) : launch_all<Tin, false>(P, stream);
 }
 
 }  // namespace
@@ -289,19 +311,12 @@ extern "C" vt_status_t vt_softmax_temp(const void *logits, vt_dtype_t dtype, int
   P.nchunk = static_cast<int>(nchunk);
   if (L.bytes > 0) {
     char *ws = static_cast<char *>(workspace);
-    P.counters = reinterpret_cast<unsigned int *>(ws + L.counters);
     P.rowstat = reinterpret_cast<float2 *>(ws + L.rowstat);
     P.part = reinterpret_cast<float2 *>(ws + L.part);
   }
   const size_t esize = dtype == VT_F32 ? 4 : 2;
   const int64_t vec_elems = 16 / static_cast<int64_t>(esize);
   const bool vec = aligned16(logits) && ld % vec_elems == 0;
-  const int64_t grid = rows * nchunk;
-  hipError_t e = dtype == VT_F32 ? launch_rows<float>(P, vec, grid, stream) : launch_rows<uint16_t>(P, vec, grid, stream);
-  if (e != hipSuccess) return VT_ERR_HIP;
-  if (probs && nchunk > 1) {
-    e = dtype == VT_F32 ? launch_probs<float>(P, vec, grid, stream) : launch_probs<uint16_t>(P, vec, grid, stream);
-    if (e != hipSuccess) return VT_ERR_HIP;
-  }
-  return VT_OK;
+  const hipError_t e = dtype == VT_F32 ? launch_dtype<float>(P, vec, stream) : launch_dtype<uint16_t>(P, vec, stream);
+  return hip_status(e);
 }

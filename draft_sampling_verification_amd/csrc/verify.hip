@@ -4,14 +4,14 @@
 // balance" and "Extending the rule from one token to a drafted run"; "VocabTrim", Appendix C.1,
 // Algorithm 2 for the map from trimmed ids back to the full vocabulary).
 //
-// One 256-thread workgroup per (sequence b, 4096-id chunk of the full vocabulary).  Every
-// workgroup of a sequence first repeats the sequence's accept scan (gamma <= 64 lanes of wave 0,
-// fp64 ratios, a ballot gives n = first rejection), so all of them agree on which row feeds the
-// final draw without a second launch.  Each then computes, for its chunk of ids x, the weight
-// w(x) = max(0, p_n(x) - q_n(x)) (q_n(x) = 0 off the kept set; w = p_gamma when all drafts were
-// accepted) and publishes the chunk sums of w and of p.  The last workgroup of the sequence to
-// finish forms the chunk-level running sum, falls back to p_n if the residual mass is 0, draws
-// the final token with u_final by rescanning one chunk, and writes the outputs.
+// Pass 1: one 256-thread workgroup per (sequence b, 4096-id chunk of the full vocabulary).  Every
+// workgroup of a sequence repeats the sequence's accept scan (gamma <= 64 lanes of wave 0, fp64
+// ratios, a ballot gives n = first rejection), so all of them know which row feeds the final
+// draw.  Each then computes, for its chunk of ids x, the weight w(x) = max(0, p_n(x) - q_n(x))
+// (q_n(x) = 0 off the kept set; w = p_gamma when all drafts were accepted) and publishes the chunk
+// sums of w and of p.  Pass 2 (next launch, one workgroup per sequence) forms the chunk-level
+// running sum, falls back to p_n if the residual mass is 0, draws the final token with u_final by
+// rescanning one chunk, and writes the outputs.  Vocabularies of one chunk use a single launch.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -36,8 +36,8 @@ struct VfParams {
   const float *ufin;
   int32_t *out_tokens;
   int32_t *out_n;
-  unsigned int *counters;
-  float2 *part;
+  int *nbuf;     // n per sequence, from pass 1 to pass 2
+  float2 *part;  // (sum of final-draw weights, sum of p) per (sequence, chunk)
   int64_t V, Vt, R;
   double Tt, Td;
   float k2t, k2d;  // log2(e) / T
@@ -102,20 +102,12 @@ __device__ __forceinline__ void final_weights(const VfParams &P, int64_t b, int 
   }
 }
 
-template <typename Tin, bool kVec>
-__global__ __launch_bounds__(kBlock) void spec_verify(VfParams P) {
-  __shared__ float redf[kWavesPerBlock];
-  __shared__ int redi[kWavesPerBlock];
-  __shared__ int flag;
-  __shared__ int sh_n;
-  __shared__ float bcast;
-
-  const int64_t bid = blockIdx.x;
-  const int64_t b = bid / P.nchunk;
-  const int c = static_cast<int>(bid - b * P.nchunk);
+// Accept scan of sequence b by wave 0 (lanes 0..gamma-1): n = first rejected draft, gamma if
+// none, -1 if a draft id (or its full id) is out of range.  Broadcast through LDS; all threads
+// of the workgroup must call.
+template <typename Tin>
+__device__ __forceinline__ int accept_scan(const VfParams &P, int64_t b, int *sh_n) {
   const int gamma = P.gamma;
-
-  // ---- accept scan (wave 0): n = first rejected draft, gamma if none, -1 on a bad draft id
   if (wave_id() == 0) {
     const int i = lane_id();
     bool valid = true, accept = true;
@@ -137,44 +129,24 @@ __global__ __launch_bounds__(kBlock) void spec_verify(VfParams P) {
     }
     const unsigned long long bad = __ballot(i < gamma && !valid);
     const unsigned long long rej = __ballot(i < gamma && !accept);
-    if (i == 0) sh_n = bad ? -1 : (rej ? __ffsll(static_cast<long long>(rej)) - 1 : gamma);
+    if (i == 0) *sh_n = bad ? -1 : (rej ? __ffsll(static_cast<long long>(rej)) - 1 : gamma);
   }
   __syncthreads();
-  const int n = sh_n;
+  return *sh_n;
+}
 
-  // ---- phase 1: chunk sums of the residual (or bonus) weights and of p
-  float wv[16], pv[16];
-  float sw = 0.f, sp = 0.f;
-  if (n >= 0) {
-    final_weights<Tin, kVec>(P, b, n, c, false, wv, pv);
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      sw += wv[j];
-      sp += pv[j];
-    }
-  }
-  sw = block_sum(sw, redf);
-  sp = block_sum(sp, redf);
-
-  float2 *part = P.part + b * P.nchunk;
-  if (P.nchunk > 1) {
-    if (threadIdx.x == 0) part[c] = make_float2(sw, sp);
-    if (!arrive_last(&P.counters[b], static_cast<unsigned int>(P.nchunk), &flag)) return;
-  }
-
-  // ---- last workgroup of the sequence: draw the final token, write the outputs
+// Final draw and outputs of sequence b, given n and the chunk sums of the residual (or bonus)
+// weights and of p (mass(k, use_p)); all threads of the workgroup must call.
+template <typename Tin, bool kVec, typename Mass>
+__device__ __forceinline__ void finish_sequence(const VfParams &P, int64_t b, int n, Mass mass, float *redf,
+                                                int *redi, float *bcast) {
+  const int gamma = P.gamma;
   int32_t *tok = P.out_tokens + b * (gamma + 1);
   if (n < 0) {
     for (int i = threadIdx.x; i <= gamma; i += kBlock) tok[i] = -1;
     if (threadIdx.x == 0) P.out_n[b] = -1;
     return;
   }
-  auto mass = [&](int k, bool use_p) -> float {
-    if (k >= P.nchunk) return 0.f;
-    if (P.nchunk == 1) return use_p ? sp : sw;
-    const float2 v = part[k];
-    return use_p ? v.y : v.x;
-  };
   // residual mass; if it rounds to zero, draw from p_n instead
   float carry = 0.f;
   for (int k0 = 0; k0 < P.nchunk; k0 += kBlock) {
@@ -182,7 +154,7 @@ __global__ __launch_bounds__(kBlock) void spec_verify(VfParams P) {
     block_inclusive_scan(mass(k0 + threadIdx.x, false), redf, &prev, &total);
     carry = carry + total;
   }
-  bool use_p = !(carry > 0.f);
+  const bool use_p = !(carry > 0.f);
   float Z = carry;
   if (use_p) {
     carry = 0.f;
@@ -204,10 +176,10 @@ __global__ __launch_bounds__(kBlock) void spec_verify(VfParams P) {
     const bool hit = k < P.nchunk && t <= carry + incl;
     const int first = block_min_int(hit ? k : 0x7fffffff, redi);
     if (first != 0x7fffffff) {
-      if (k == first) bcast = carry + prev;
+      if (k == first) *bcast = carry + prev;
       __syncthreads();
       cstar = first;
-      Estar = bcast;
+      Estar = *bcast;
       break;
     }
     carry = carry + total;
@@ -221,6 +193,7 @@ __global__ __launch_bounds__(kBlock) void spec_verify(VfParams P) {
     fallback = true;
   }
   // rescan chunk c*: running sum inside it, first id reaching t (else last positive id)
+  float wv[16], pv[16];
   final_weights<Tin, kVec>(P, b, n, cstar, use_p, wv, pv);
   float loc[16];
   float acc = 0.f;
@@ -260,23 +233,102 @@ __global__ __launch_bounds__(kBlock) void spec_verify(VfParams P) {
   if (threadIdx.x == 0) P.out_n[b] = n;
 }
 
+// Vocabularies of one chunk (V <= 4096): one workgroup per sequence does everything.
+template <typename Tin, bool kVec>
+__global__ __launch_bounds__(kBlock) void verify_single(VfParams P) {
+  __shared__ float redf[kWavesPerBlock];
+  __shared__ int redi[kWavesPerBlock];
+  __shared__ int sh_n;
+  __shared__ float bcast;
+  const int64_t b = blockIdx.x;
+  const int n = accept_scan<Tin>(P, b, &sh_n);
+  float sw = 0.f, sp = 0.f;
+  if (n >= 0) {
+    float wv[16], pv[16];
+    final_weights<Tin, kVec>(P, b, n, 0, false, wv, pv);
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      sw += wv[j];
+      sp += pv[j];
+    }
+  }
+  sw = block_sum(sw, redf);
+  sp = block_sum(sp, redf);
+  auto mass = [&](int k, bool use_p) -> float { return k == 0 ? (use_p ? sp : sw) : 0.f; };
+  finish_sequence<Tin, kVec>(P, b, n, mass, redf, redi, &bcast);
+}
+
+// Larger vocabularies, pass 1: one workgroup per (sequence, chunk) repeats the sequence's accept
+// scan, then publishes the chunk sums of the residual (or bonus) weights and of p; chunk 0 also
+// records n.  Pass 2 reads them after the kernel boundary.
+template <typename Tin, bool kVec>
+__global__ __launch_bounds__(kBlock) void verify_partial(VfParams P) {
+  __shared__ float redf[kWavesPerBlock];
+  __shared__ int sh_n;
+  const int64_t bid = blockIdx.x;
+  const int64_t b = bid / P.nchunk;
+  const int c = static_cast<int>(bid - b * P.nchunk);
+  const int n = accept_scan<Tin>(P, b, &sh_n);
+  float sw = 0.f, sp = 0.f;
+  if (n >= 0) {
+    float wv[16], pv[16];
+    final_weights<Tin, kVec>(P, b, n, c, false, wv, pv);
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      sw += wv[j];
+      sp += pv[j];
+    }
+  }
+  sw = block_sum(sw, redf);
+  sp = block_sum(sp, redf);
+  if (threadIdx.x == 0) {
+    P.part[b * P.nchunk + c] = make_float2(sw, sp);
+    if (c == 0) P.nbuf[b] = n;
+  }
+}
+
+// Pass 2: one workgroup per sequence draws the final token and writes the outputs.
+template <typename Tin, bool kVec>
+__global__ __launch_bounds__(kBlock) void verify_final(VfParams P) {
+  __shared__ float redf[kWavesPerBlock];
+  __shared__ int redi[kWavesPerBlock];
+  __shared__ float bcast;
+  const int64_t b = blockIdx.x;
+  const int n = P.nbuf[b];
+  const float2 *part = P.part + b * P.nchunk;
+  auto mass = [&](int k, bool use_p) -> float {
+    if (k >= P.nchunk) return 0.f;
+    const float2 v = part[k];
+    return use_p ? v.y : v.x;
+  };
+  finish_sequence<Tin, kVec>(P, b, n, mass, redf, redi, &bcast);
+}
+
 struct WsLayout {
-  size_t counters, part, bytes;
+  size_t nbuf, part, bytes;
 };
 
 WsLayout ws_layout(int64_t B, int64_t nchunk) {
   WsLayout L{};
   if (nchunk <= 1) return L;
-  L.counters = 0;
-  L.part = align_up(static_cast<size_t>(B) * sizeof(unsigned int), 256);
+  L.nbuf = 0;
+  L.part = align_up(static_cast<size_t>(B) * sizeof(int), 256);
   L.bytes = L.part + align_up(static_cast<size_t>(B) * static_cast<size_t>(nchunk) * sizeof(float2), 256);
   return L;
 }
 
+template <typename Tin, bool kVec>
+hipError_t launch_all(const VfParams &P, int64_t B, hipStream_t stream) {
+  if (P.nchunk == 1) return launch(verify_single<Tin, kVec>, dim3(static_cast<unsigned>(B)), dim3(kBlock), 0, stream, P);
+  const hipError_t e = launch(verify_partial<Tin, kVec>, dim3(static_cast<unsigned>(B * P.nchunk)), dim3(kBlock), 0,
+                              stream, P);
+  if (e != hipSuccess) return e;
+  return launch(verify_final<Tin, kVec>, dim3(static_cast<unsigned>(B)), dim3(kBlock), 0, stream, P);
+}
+
 template <typename Tin>
-hipError_t launch_verify(const VfParams &P, bool vec, int64_t grid, hipStream_t stream) {
-  if (vec) return launch(spec_verify<Tin, true>, dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, stream, P);
-  return launch(spec_verify<Tin, false>, dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, stream, P);
+hipError_t launch_verify(const VfParams &P, bool vec, int64_t B, hipStream_t stream) {
+  return vec ? launch_all<Tin, true>(P, B, stream) : launch_all<Tin, false>(P, B, stream);
 }
 
 }  // namespace
@@ -333,14 +385,13 @@ extern "C" vt_status_t vt_spec_verify(int64_t B, int64_t gamma, int64_t V, int64
   P.nchunk = static_cast<int>(nchunk);
   if (L.bytes > 0) {
     char *ws = static_cast<char *>(workspace);
-    P.counters = reinterpret_cast<unsigned int *>(ws + L.counters);
+    P.nbuf = reinterpret_cast<int *>(ws + L.nbuf);
     P.part = reinterpret_cast<float2 *>(ws + L.part);
   }
   const int64_t vec_elems = target_dtype == VT_F32 ? 4 : 8;
   const bool vec = aligned16(target_logits) && V % vec_elems == 0;
-  const int64_t grid = B * nchunk;
-  const hipError_t e = target_dtype == VT_F32 ? launch_verify<float>(P, vec, grid, stream)
-                                              : launch_verify<uint16_t>(P, vec, grid, stream);
+  const hipError_t e = target_dtype == VT_F32 ? launch_verify<float>(P, vec, B, stream)
+                                              : launch_verify<uint16_t>(P, vec, B, stream);
   return hip_status(e);
 }
 

@@ -133,24 +133,6 @@ __device__ __forceinline__ float block_inclusive_scan(float v, float *red, float
   return before + inc;
 }
 
-// Last-workgroup-done protocol: each workgroup of a group (a row, a sequence) publishes its
-// partial result, then bumps the group's counter; the workgroup that brings the counter to
-// `count` combines all partials and resets the counter to zero for the next call.
-__device__ __forceinline__ bool arrive_last(unsigned int *counter, unsigned int count, int *flag_lds) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned int prev = atomicAdd(counter, 1u);
-    const bool last = (prev == count - 1u);
-    if (last) *counter = 0u;
-    *flag_lds = last ? 1 : 0;
-  }
-  __syncthreads();
-  const bool last = *flag_lds != 0;
-  if (last) __threadfence();
-  return last;
-}
-
 // The 16 contiguous elements [base + 16 t, base + 16 t + 16) of a row as fp32; -inf past n.
 template <typename Tin, bool kVec>
 __device__ __forceinline__ void load16(const Tin *__restrict__ row, int64_t n, int64_t base, float (&v)[16]) {

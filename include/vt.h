@@ -29,11 +29,9 @@
  *     inverse of keep_ids (-1 elsewhere); an lse passed in was produced by vt_softmax_temp from
  *     the same logits and temperature.
  *   - Workspaces: a caller-owned device buffer of at least the size the matching
- *     *_workspace_bytes function returns.  It holds per-row partial results and per-row
- *     completion counters.  Before its first use it must be zero-filled (once); every completed
- *     call returns the counters to zero (partials are always written before they are read), so
- *     the buffer can be reused by later calls on the same stream, for any shape it is large
- *     enough for.  Two calls in flight at once must not share a workspace.
+ *     *_workspace_bytes function returns, holding per-chunk partial results between the
+ *     launches of one call.  Its contents need no initialisation and carry nothing between
+ *     calls; two calls in flight at once must not share a workspace.
  */
 #ifndef VT_H_
 #define VT_H_
@@ -93,7 +91,8 @@ vt_status_t vt_lmhead_trimmed(const uint16_t *hidden, const uint16_t *weight, co
  *     order and Z is the last entry of that same running sum, so for u in (0, 1] an index exists
  *     and a zero-weight entry is never returned.  The running sum is formed in fp32 over fixed
  *     4096-element chunks (chunk sums, a prefix over chunks, then a prefix inside the selected
- *     chunk), independent of rows and of the row count.  Where the two levels disagree by a
+ *     chunk), independent of rows and of the row count.  Rows of more than one chunk take two
+ *     launches (chunk partials, then one workgroup per row), plus one for probs.  Where the two levels disagree by a
  *     rounding step at a chunk's end, the last positive-weight entry of that chunk is returned.
  *
  *   logits  fp32 or bf16 (dtype), [rows][ld] with ld >= n
