@@ -12,7 +12,7 @@ Prints ONE JSON line on stdout (progress goes to stderr):
                duration measured live with HIP events on the launch stream, against 8 TB/s
   cpu_baseline the float64 CPU oracle timed on a bounded sample of the same workload
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C] [--no-cpu-baseline] [--graph]
        python bench.py --copy-calibration   (a plain copy of known size, for PMC byte scaling)
 """
 from __future__ import annotations
@@ -48,7 +48,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--serial", action="store_true", help="run all four calls on one stream (no overlap)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay captured HIP graphs (LM head | rest) instead of launching the calls eagerly")
     return ap.parse_args()
 
 
@@ -96,15 +97,16 @@ def measured_traffic(workload_key: str):
 
 
 def copy_calibration():
+    """A plain elementwise copy of 1 GiB (reads 1 GiB, writes 1 GiB per launch), 5 launches."""
     import torch
     n = 1 << 30
     src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(5):
-        dst.copy_(src)
+        torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
-    log(f"copy calibration: 5 copies of {n} bytes (read {n}, write {n} per copy)")
-    print(json.dumps({"copy_bytes": n, "copies": 5}))
+    log(f"copy calibration: 5 launches, each reads {n} and writes {n} bytes")
+    print(json.dumps({"copy_bytes": n, "launches": 5}))
 
 
 def cpu_baseline(cfg, wl_one, budget_s: float):
@@ -179,45 +181,71 @@ def main():
     ws_vf = vt.verify_workspace(B, cfg.V)
     log(f"{n_sets} input sets on device ({bb / 1e6:.1f} MB algorithmic per step)")
 
-    ev_pairs = []
-    # The target's log-normalisers do not depend on the draft: they run on a second stream and
-    # overlap the LM head; verification waits for both.  (Default priority on both streams.)
     main = torch.cuda.current_stream()
-    side = main if args.serial else torch.cuda.Stream()
-    ev_target = torch.cuda.Event()
-    ev_done = torch.cuda.Event()
-    ev_done.record(main)
 
-    def step(s, record):
-        side.wait_event(ev_done)  # the previous step's verify has finished reading tlse
-        with torch.cuda.stream(side):
-            vt.vt_softmax_temp(s["target"].view(B * (g + 1), cfg.V), wl.T, tlse, workspace=ws_sm_t)
-            ev_target.record(side)
-        if record:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(main)
+    def lmhead(s):
         vt.vt_lmhead_trimmed(s["hidden"], s["weight"], keep, logits)
-        if record:
-            e1.record(main)
-            ev_pairs.append((e0, e1))
+
+    def rest(s):
         vt.vt_softmax_temp(logits, wl.T, dlse, None, s["u_draft"], dids, workspace=ws_sm_d)
-        main.wait_event(ev_target)
+        vt.vt_softmax_temp(s["target"].view(B * (g + 1), cfg.V), wl.T, tlse, workspace=ws_sm_t)
         vt.vt_spec_verify(s["target"], tlse, wl.T, logits.view(B, R, cfg.Vt), dlse, wl.T, dids.view(B, R), keep,
                           f2t, s["u_acc"], s["u_fin"], tokens, nacc, workspace=ws_vf)
-        ev_done.record(main)
 
+    outs = (logits, dlse, dids, tlse, tokens, nacc)
+    if not args.graph:
+        runners = [((lambda s=s: lmhead(s)), (lambda s=s: rest(s))) for s in sets]
+    else:
+        # one graph for the LM head and one for the rest of the step, per input set: replaying
+        # them leaves the GPU no host-side gaps; the events between the two replays still time
+        # the LM head on the stream it runs on
+        side = torch.cuda.Stream()
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            for s in sets:
+                lmhead(s)
+                rest(s)
+        main.wait_stream(side)
+        torch.cuda.synchronize()
+        runners = []
+        for s in sets:
+            ga, gb = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(ga):
+                lmhead(s)
+            with torch.cuda.graph(gb):
+                rest(s)
+            runners.append((ga.replay, gb.replay))
+        torch.cuda.synchronize()
+        # the replays must give the eager step's bits
+        lmhead(sets[0]); rest(sets[0]); torch.cuda.synchronize()
+        want = [t.clone() for t in outs]
+        for t in outs:
+            t.fill_(-3)
+        runners[0][0](); runners[0][1](); torch.cuda.synchronize()
+        if not all(torch.equal(a, b) for a, b in zip(want, outs)):
+            raise RuntimeError("graph replay differs from the eager step")
+
+    n_ev = args.steps
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     for i in range(args.warmup):
-        step(sets[i % n_sets], False)
+        a, b = runners[i % n_sets]
+        a()
+        b()
     torch.cuda.synchronize()
     # timed region: K steps between two synchronisations; inside it, every LM-head launch is
     # bracketed by events on the stream it is launched on
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(sets[i % n_sets], True)
+        a, b = runners[i % n_sets]
+        ev_a[i].record(main)
+        a()
+        ev_b[i].record(main)
+        b()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = 1e3 * wall / args.steps
-    lm_ms = sum(a.elapsed_time(b) for a, b in ev_pairs) / len(ev_pairs)
+    lm_ms = sum(x.elapsed_time(y) for x, y in zip(ev_a, ev_b)) / n_ev
 
     value = B * g / (ms_per_step / 1e3)
     lmb = lmhead_bytes(cfg)
@@ -257,7 +285,7 @@ def main():
         "config": {"workload": cfg.name, "batch": B, "gamma": g, "hidden": cfg.H, "vocab": cfg.V,
                    "kept_rows": cfg.Vt, "target_logits": cfg.target_dtype, "temperature": cfg.T,
                    "weights": "bf16", "accumulate": "f32", "input_sets_rotated": n_sets,
-                   "streams": 1 if args.serial else 2,
+                   "launch": "hip graphs (LM head | rest), replayed per step" if args.graph else "eager, one stream",
                    "block_algorithmic_bytes": bb,
                    "block_gbs": round(bb / (ms_per_step / 1e3) / 1e9, 1)},
         "roofline": roof,

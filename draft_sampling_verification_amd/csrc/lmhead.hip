@@ -125,9 +125,15 @@ struct Pow2Ceil<1> {
 #define VT_GEMV_PD 2
 #endif
 constexpr int kGemvPrefetch = VT_GEMV_PD;  // weight rows in flight per wavefront beyond the one in use
+// Row-to-wavefront map: 2 = each workgroup owns one contiguous run of rows and its wavefronts
+// interleave inside it (a workgroup streams a contiguous region of the head, which measured
+// ~10% above the other maps); 1 = each wavefront owns a contiguous run; 0 = grid-stride.
+#ifndef VT_GEMV_MAP
+#define VT_GEMV_MAP 2
+#endif
 
-// Each wavefront walks weight rows j = w, w + W, w + 2W, ... (W = wavefronts in the grid), so at
-// any moment the grid streams one contiguous window of the head.  A ring of PD + 1 register
+// Each workgroup owns a contiguous run of weight rows and its four wavefronts take every fourth
+// row of it, so the workgroup streams one contiguous region of the head.  A ring of PD + 1 register
 // buffers keeps PD rows in flight while one is multiplied.  Every load is unconditional and in
 // bounds (row indices past the wave's last row repeat the last row, pieces past H repeat the
 // last piece and are masked), so the compiler can wait for exactly the oldest row (vmcnt(N))
@@ -156,13 +162,36 @@ __global__ __launch_bounds__(kBlock) void lmhead_gemv(const uint16_t *__restrict
       h[m][it] = live(it) ? v : make_uint4(0, 0, 0, 0);
     }
 
-  const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kWavesPerBlock + wave_id());
+  const int wid = __builtin_amdgcn_readfirstlane(wave_id());
+#if VT_GEMV_MAP == 0
+  // grid-stride: wave w takes rows w, w + W, w + 2W, ...
+  const int wv = static_cast<int>(blockIdx.x) * kWavesPerBlock + wid;
   const int nw = gridDim.x * kWavesPerBlock;
   if (wv >= Vt) return;
   const int nrows = (Vt - 1 - wv) / nw + 1;
+  auto row_of = [&](int t) { return wv + t * nw; };
+#elif VT_GEMV_MAP == 1
+  // wave-contiguous: wave w streams rows [w * per, (w + 1) * per)
+  const int nw = gridDim.x * kWavesPerBlock;
+  const int per = (Vt + nw - 1) / nw;
+  const int wv = (static_cast<int>(blockIdx.x) * kWavesPerBlock + wid) * per;
+  if (wv >= Vt) return;
+  const int nrows = min(per, Vt - wv);
+  auto row_of = [&](int t) { return wv + t; };
+#else
+  // workgroup-contiguous: workgroup k owns rows [k * per, (k + 1) * per); its waves interleave
+  const int per = ((Vt + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x) + kWavesPerBlock - 1) /
+                  kWavesPerBlock * kWavesPerBlock;
+  const int base = static_cast<int>(blockIdx.x) * per;
+  const int wv = base + wid;
+  const int end = min(Vt, base + per);
+  if (wv >= end) return;
+  const int nrows = (end - 1 - wv) / kWavesPerBlock + 1;
+  auto row_of = [&](int t) { return wv + t * kWavesPerBlock; };
+#endif
 
   auto fetch = [&](int t, uint4(&dst)[NIT]) {
-    const int j = wv + min(t, nrows - 1) * nw;  // wave-uniform
+    const int j = row_of(min(t, nrows - 1));  // wave-uniform
     int64_t r = j;
     if constexpr (TRIM) r = keep[j];
     const uint4 *src = reinterpret_cast<const uint4 *>(weight + r * H);
@@ -181,7 +210,7 @@ __global__ __launch_bounds__(kBlock) void lmhead_gemv(const uint16_t *__restrict
     }
     const float sum = transpose_reduce<NP>(acc);
     const int m = lane / kGroup;
-    if ((lane % kGroup) == 0 && m < M) logits[static_cast<int64_t>(m) * Vt + wv + t * nw] = sum;
+    if ((lane % kGroup) == 0 && m < M) logits[static_cast<int64_t>(m) * Vt + row_of(t)] = sum;
   };
 
   uint4 w[PD + 1][NIT];
