@@ -1,7 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the draft-sampling / verification hot path on one MI355X.
 
-One step = one speculative block over the workload's batch: the four library calls
+One step = one speculative block over the workload's batch: by default the fused call
+vt_spec_block (LM head with the draft softmax's first pass in its epilogue, one combine launch
+for draft and target rows, two verify launches); with --calls the four separate calls
   vt_lmhead_trimmed -> vt_softmax_temp (draft, with draws) -> vt_softmax_temp (target) -> vt_spec_verify
 on synthetic inputs already resident in HBM.  Default workload: B=1, gamma=5, hidden 3072, full
 128256-row drafter head, fp32 target logits, T=1 (config 2 of the workload recipe).
@@ -48,6 +50,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--calls", action="store_true",
+                    help="run the step as the four separate calls instead of the fused vt_spec_block")
+    ap.add_argument("--overlap", action="store_true",
+                    help="run the target softmax on a second stream, concurrently with the LM head")
     ap.add_argument("--graph", action="store_true",
                     help="replay captured HIP graphs (LM head | rest) instead of launching the calls eagerly")
     return ap.parse_args()
@@ -183,16 +189,44 @@ def main():
 
     main = torch.cuda.current_stream()
 
+    side = torch.cuda.Stream() if args.overlap else None  # default priority
+    ev_tgt, ev_free = torch.cuda.Event(), torch.cuda.Event()
+    ev_free.record(main)
+
+    def target_lse(s):
+        vt.vt_softmax_temp(s["target"].view(B * (g + 1), cfg.V), wl.T, tlse, workspace=ws_sm_t)
+
     def lmhead(s):
+        if side is not None:
+            # the target's log-normalisers do not depend on the draft: overlap them with the head
+            side.wait_event(ev_free)  # the previous step's verify is done with tlse
+            with torch.cuda.stream(side):
+                target_lse(s)
+                ev_tgt.record(side)
         vt.vt_lmhead_trimmed(s["hidden"], s["weight"], keep, logits)
 
     def rest(s):
         vt.vt_softmax_temp(logits, wl.T, dlse, None, s["u_draft"], dids, workspace=ws_sm_d)
-        vt.vt_softmax_temp(s["target"].view(B * (g + 1), cfg.V), wl.T, tlse, workspace=ws_sm_t)
+        if side is None:
+            target_lse(s)
+        else:
+            main.wait_event(ev_tgt)
         vt.vt_spec_verify(s["target"], tlse, wl.T, logits.view(B, R, cfg.Vt), dlse, wl.T, dids.view(B, R), keep,
                           f2t, s["u_acc"], s["u_fin"], tokens, nacc, workspace=ws_vf)
+        if side is not None:
+            ev_free.record(main)
+
+    ws_blk = vt.block_workspace(B, g, R, cfg.H, cfg.Vt, cfg.V)
+
+    def fused(s, events=None):
+        vt.vt_spec_block(s["hidden"], s["weight"], keep, f2t, s["target"], wl.T, wl.T, s["u_draft"], s["u_acc"],
+                         s["u_fin"], logits, dlse, dids, tlse, tokens, nacc, workspace=ws_blk, lmhead_events=events)
 
     outs = (logits, dlse, dids, tlse, tokens, nacc)
+    if not args.calls and (args.graph or args.overlap):
+        raise SystemExit("--graph and --overlap apply to --calls")
+    if args.graph and args.overlap:
+        raise SystemExit("--graph and --overlap are exclusive")
     if not args.graph:
         runners = [((lambda s=s: lmhead(s)), (lambda s=s: rest(s))) for s in sets]
     else:
@@ -228,21 +262,41 @@ def main():
     n_ev = args.steps
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    if not args.calls:
+        # the fused call must agree with the four separate calls on the LM head and the target
+        # log-normalisers bit for bit (draws may differ only at rounding-level CDF boundaries)
+        runners[0][0](); runners[0][1](); torch.cuda.synchronize()
+        want = [t.clone() for t in outs]
+        fused(sets[0]); torch.cuda.synchronize()
+        if not (torch.equal(want[0], logits) and torch.equal(want[3], tlse)):
+            raise RuntimeError("vt_spec_block differs from the separate calls")
     for i in range(args.warmup):
-        a, b = runners[i % n_sets]
-        a()
-        b()
+        if args.calls:
+            a, b = runners[i % n_sets]
+            a()
+            b()
+        else:
+            fused(sets[i % n_sets])
     torch.cuda.synchronize()
     # timed region: K steps between two synchronisations; inside it, every LM-head launch is
     # bracketed by events on the stream it is launched on
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        a, b = runners[i % n_sets]
-        ev_a[i].record(main)
-        a()
-        ev_b[i].record(main)
-        b()
-    torch.cuda.synchronize()
+    if args.calls:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            a, b = runners[i % n_sets]
+            ev_a[i].record(main)
+            a()
+            ev_b[i].record(main)
+            b()
+        torch.cuda.synchronize()
+    else:
+        for e in ev_a + ev_b:  # materialise the events the library records into
+            e.record(main)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            fused(sets[i % n_sets], (ev_a[i], ev_b[i]))
+        torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = 1e3 * wall / args.steps
     lm_ms = sum(x.elapsed_time(y) for x, y in zip(ev_a, ev_b)) / n_ev
@@ -285,7 +339,10 @@ def main():
         "config": {"workload": cfg.name, "batch": B, "gamma": g, "hidden": cfg.H, "vocab": cfg.V,
                    "kept_rows": cfg.Vt, "target_logits": cfg.target_dtype, "temperature": cfg.T,
                    "weights": "bf16", "accumulate": "f32", "input_sets_rotated": n_sets,
-                   "launch": "hip graphs (LM head | rest), replayed per step" if args.graph else "eager, one stream",
+                   "launch": ("vt_spec_block: one fused call per step (5 kernels)" if not args.calls else
+                              "four calls, hip graphs (LM head | rest) replayed" if args.graph else
+                              "four calls, target softmax on a second stream" if args.overlap else
+                              "four calls, eager, one stream"),
                    "block_algorithmic_bytes": bb,
                    "block_gbs": round(bb / (ms_per_step / 1e3) / 1e9, 1)},
         "roofline": roof,

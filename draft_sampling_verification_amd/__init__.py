@@ -11,7 +11,10 @@ Entry points (same names as the C ABI):
   vt_softmax_temp(logits, temperature, lse, probs=None, u=None, sampled=None, workspace=None, n=None)
   vt_spec_verify(target_logits, target_lse, target_T, draft_logits, draft_lse, draft_T, draft_ids,
                  keep_ids, full_to_trim, u_accept, u_final, out_tokens, out_num_accepted, workspace=None)
-Helpers: softmax_workspace(rows, n), verify_workspace(B, V), lib() (the raw ctypes handle).
+  vt_spec_block(hidden, weight, keep_ids, full_to_trim, target_logits, target_T, draft_T, u_draft, u_accept,
+                u_final, draft_logits, draft_lse, draft_ids, target_lse, out_tokens, out_num_accepted,
+                workspace=None, lmhead_events=None)
+Helpers: softmax_workspace(rows, n), verify_workspace(B, V), block_workspace(...), lib() (the raw ctypes handle).
 """
 from __future__ import annotations
 
@@ -53,6 +56,11 @@ def lib() -> ctypes.CDLL:
         L.vt_spec_verify.restype = I
         L.vt_spec_verify_workspace_bytes.argtypes = [I64, I64]
         L.vt_spec_verify_workspace_bytes.restype = SZ
+        L.vt_spec_block.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I64, P, I, F, F, P, P, P, P, P, P, P, P, P,
+                                    P, P, P, SZ, P]
+        L.vt_spec_block.restype = I
+        L.vt_spec_block_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I64]
+        L.vt_spec_block_workspace_bytes.restype = SZ
         L.vt_status_string.argtypes = [I]
         L.vt_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -60,7 +68,7 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTED = ("vt_lmhead_trimmed", "vt_softmax_temp", "vt_softmax_temp_workspace_bytes", "vt_spec_verify",
-            "vt_spec_verify_workspace_bytes", "vt_status_string")
+            "vt_spec_verify_workspace_bytes", "vt_spec_block", "vt_spec_block_workspace_bytes", "vt_status_string")
 
 
 def _torch():
@@ -186,4 +194,53 @@ def vt_spec_verify(target_logits, target_lse, target_T, draft_logits, draft_lse,
                               _ptr(out_num_accepted, "out_num_accepted", torch.int32, B),
                               _ptr(workspace, "workspace"), wsb, _stream())
     _check("vt_spec_verify", st)
+    return out_tokens, out_num_accepted
+
+
+def block_workspace(B: int, gamma: int, R: int, H: int, Vt: int, V: int, device="cuda"):
+    """A workspace for vt_spec_block (None when the shape needs none)."""
+    nbytes = lib().vt_spec_block_workspace_bytes(B, gamma, R, H, Vt, V)
+    return _torch().empty(nbytes, dtype=_torch().uint8, device=device) if nbytes else None
+
+
+def vt_spec_block(hidden, weight, keep_ids, full_to_trim, target_logits, target_T, draft_T, u_draft, u_accept,
+                  u_final, draft_logits, draft_lse, draft_ids, target_lse, out_tokens, out_num_accepted,
+                  workspace=None, lmhead_events=None):
+    """One whole block.  hidden [B*R, H] bf16, weight [V, H] bf16, target [B, gamma+1, V];
+    outputs draft_logits [B*R, Vt] f32, draft_lse [B*R] f64, draft_ids [B*R] i32, target_lse
+    [B*(gamma+1)] f64, out_tokens [B, gamma+1] i32, out_num_accepted [B] i32.
+    lmhead_events: optional (start, end) torch.cuda.Event pair recorded around the LM-head kernel."""
+    torch = _torch()
+    _bits16(hidden, "hidden")
+    _bits16(weight, "weight")
+    B, g1, V = target_logits.shape
+    gamma = g1 - 1
+    M, H = hidden.shape
+    R = M // B
+    Vt = draft_logits.shape[1]
+    if M != B * R or weight.shape != (V, H) or tuple(draft_logits.shape) != (M, Vt) or \
+            tuple(out_tokens.shape) != (B, g1):
+        raise ValueError("vt_spec_block: shape mismatch")
+    if target_logits.dtype == torch.float32:
+        dt = VT_F32
+    else:
+        _bits16(target_logits, "target_logits")
+        dt = VT_BF16
+    if workspace is None:
+        workspace = block_workspace(B, gamma, R, H, Vt, V, target_logits.device)
+    wsb = workspace.numel() if workspace is not None else 0
+    ev0 = ev1 = None
+    if lmhead_events is not None:
+        ev0, ev1 = (ctypes.c_void_p(e.cuda_event) for e in lmhead_events)
+    st = lib().vt_spec_block(_ptr(hidden, "hidden"), _ptr(weight, "weight"), _ptr(keep_ids, "keep_ids", torch.int32),
+                             _ptr(full_to_trim, "full_to_trim", torch.int32, V), B, gamma, R, H, Vt, V,
+                             _ptr(target_logits, "target_logits"), dt, float(target_T), float(draft_T),
+                             _ptr(u_draft, "u_draft", torch.float32, M), _ptr(u_accept, "u_accept", torch.float32, B * gamma),
+                             _ptr(u_final, "u_final", torch.float32, B), _ptr(draft_logits, "draft_logits", torch.float32),
+                             _ptr(draft_lse, "draft_lse", torch.float64, M), _ptr(draft_ids, "draft_ids", torch.int32, M),
+                             _ptr(target_lse, "target_lse", torch.float64, B * g1),
+                             _ptr(out_tokens, "out_tokens", torch.int32), _ptr(out_num_accepted, "out_num_accepted",
+                                                                                torch.int32, B),
+                             ev0, ev1, _ptr(workspace, "workspace"), wsb, _stream())
+    _check("vt_spec_block", st)
     return out_tokens, out_num_accepted

@@ -1,0 +1,223 @@
+// One whole speculative block per call: trimmed LM head, draft softmax + draws, target softmax,
+// verification -- the operations of vt_lmhead_trimmed, vt_softmax_temp (twice) and vt_spec_verify
+// ("VocabTrim" §3 Eq. 1 and Appendix C.1 Algorithm 2; "Speculative decoding" glossary, "Why a
+// rejection needs a special draw"; "A rejection rule keeps speculative decoding's output exact",
+// "Extending the rule from one token to a drafted run"), launched as few kernels as the
+// dependencies allow:
+//   1. target rows' chunk partials (max, sum of exp)                       [if V > 4096]
+//   2. LM head; on the GEMV path its epilogue also emits the draft rows' partials per row block
+//      (no second pass over the logits); on the MFMA path a partials launch follows
+//   3. one combine launch for the draft rows (lse + draws) and the target rows (lse)
+//   4. verify pass 1 (accept scans, residual chunk sums) and pass 2 (final draws, outputs)
+// Batch-1 decode: 5 launches instead of 7.  Launch order never lets an independent kernel sit
+// between the LM head and its consumers.
+#include "lmhead_impl.hpp"
+#include "softmax_impl.hpp"
+#include "verify_impl.hpp"
+
+namespace vt {
+namespace {
+
+struct BlockPlan {
+  bool fused;       // GEMV with draft partials in its epilogue
+  int64_t M, rows_t;
+  int64_t nchunk_t;  // 4096-chunks of a target row
+  int64_t nchunk_d;  // draft partial chunks per row (GEMV row blocks, or 4096-chunks)
+  int chunk_d;
+  int64_t nchunk_v;
+  size_t off_tpart, off_dpart, off_nbuf, off_vpart, bytes;
+};
+
+BlockPlan plan_block(int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt, int64_t V, bool trim) {
+  BlockPlan p{};
+  p.M = B * R;
+  p.rows_t = B * (gamma + 1);
+  p.fused = pick_gemv<true>(p.M, H, trim) != nullptr;
+  p.nchunk_t = (V + kChunk - 1) / kChunk;
+  if (p.fused) {
+    p.nchunk_d = gemv_blocks(Vt);
+    p.chunk_d = gemv_rows_per_block(Vt);
+  } else {
+    p.nchunk_d = (Vt + kChunk - 1) / kChunk;
+    p.chunk_d = kChunk;
+  }
+  p.nchunk_v = (V + kChunk - 1) / kChunk;
+  size_t off = 0;
+  p.off_tpart = off;
+  if (p.nchunk_t > 1) off += align_up(static_cast<size_t>(p.rows_t * p.nchunk_t) * sizeof(float2), 256);
+  p.off_dpart = off;
+  if (p.fused || p.nchunk_d > 1) off += align_up(static_cast<size_t>(p.M * p.nchunk_d) * sizeof(float2), 256);
+  p.off_nbuf = off;
+  p.off_vpart = off;
+  if (p.nchunk_v > 1) {
+    off += align_up(static_cast<size_t>(B) * sizeof(int), 256);
+    p.off_vpart = off;
+    off += align_up(static_cast<size_t>(B * p.nchunk_v) * sizeof(float2), 256);
+  }
+  p.bytes = off;
+  return p;
+}
+
+template <typename TinT, bool kVecT, bool kVecD>
+hipError_t launch_combine(const SmParams &D, bool d_multi, const SmParams &T, bool t_multi, hipStream_t stream) {
+  if (d_multi && t_multi)
+    return launch(softmax_combine2<float, kVecD, TinT, kVecT>, dim3(static_cast<unsigned>(D.rows + T.rows)),
+                  dim3(kBlock), 0, stream, D, T);
+  if (d_multi)
+    return launch(softmax_combine<float, kVecD>, dim3(static_cast<unsigned>(D.rows)), dim3(kBlock), 0, stream, D);
+  if (t_multi)
+    return launch(softmax_combine<TinT, kVecT>, dim3(static_cast<unsigned>(T.rows)), dim3(kBlock), 0, stream, T);
+  return hipSuccess;
+}
+
+template <typename TinT, bool kVecT, bool kVecD>
+hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, const VfParams &Vp,
+                     const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int64_t H, int64_t Vt,
+                     float *logits, int64_t B, hipEvent_t ev0, hipEvent_t ev1, hipStream_t stream) {
+  hipError_t e = hipSuccess;
+  const bool t_multi = pl.nchunk_t > 1;
+  // 1. target partials (or a whole single-chunk target softmax)
+  if (t_multi)
+    e = launch(softmax_partial<TinT, kVecT>, dim3(static_cast<unsigned>(T.rows * T.nchunk)), dim3(kBlock), 0,
+               stream, T);
+  else
+    e = launch(softmax_single<TinT, kVecT>, dim3(static_cast<unsigned>(T.rows)), dim3(kBlock), 0, stream, T);
+  if (e != hipSuccess) return e;
+  // 2. LM head (+ draft partials), bracketed by the caller's timing events if any
+  if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
+  bool d_multi = true;
+  if (pl.fused) {
+    const GemvFn fn = pick_gemv<true>(pl.M, H, keep != nullptr);
+    e = launch_gemv(fn, hidden, weight, keep, H, Vt, logits, GemvParts{D.part, D.k2}, stream);
+    if (e != hipSuccess) return e;
+    if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
+  } else {
+    e = launch_mfma(hidden, weight, keep, pl.M, H, Vt, logits, stream);
+    if (e != hipSuccess) return e;
+    if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
+    if (pl.nchunk_d > 1) {
+      e = launch(softmax_partial<float, kVecD>, dim3(static_cast<unsigned>(D.rows * D.nchunk)), dim3(kBlock), 0,
+                 stream, D);
+    } else {
+      d_multi = false;
+      e = launch(softmax_single<float, kVecD>, dim3(static_cast<unsigned>(D.rows)), dim3(kBlock), 0, stream, D);
+    }
+    if (e != hipSuccess) return e;
+  }
+  // 3. one combine launch for both row sets
+  e = launch_combine<TinT, kVecT, kVecD>(D, d_multi, T, t_multi, stream);
+  if (e != hipSuccess) return e;
+  // 4. verification
+  return vf_launch_all<TinT, kVecT>(Vp, B, stream);
+}
+
+}  // namespace
+}  // namespace vt
+
+extern "C" size_t vt_spec_block_workspace_bytes(int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt,
+                                                int64_t V) {
+  if (B <= 0 || gamma <= 0 || R < gamma || H <= 0 || Vt <= 0 || V < Vt) return 0;
+  return vt::plan_block(B, gamma, R, H, Vt, V, Vt < V).bytes;
+}
+
+extern "C" vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep_ids,
+                                     const int32_t *full_to_trim, int64_t B, int64_t gamma, int64_t R, int64_t H,
+                                     int64_t Vt, int64_t V, const void *target_logits, vt_dtype_t target_dtype,
+                                     float target_T, float draft_T, const float *u_draft, const float *u_accept,
+                                     const float *u_final, float *draft_logits, double *draft_lse, int32_t *draft_ids,
+                                     double *target_lse, int32_t *out_tokens, int32_t *out_num_accepted,
+                                     hipEvent_t lmhead_begin, hipEvent_t lmhead_end, void *workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  using namespace vt;
+  if (!hidden || !weight || !target_logits || !u_draft || !u_accept || !u_final || !draft_logits || !draft_lse ||
+      !draft_ids || !target_lse || !out_tokens || !out_num_accepted)
+    return VT_ERR_INVALID_ARG;
+  if (target_dtype != VT_F32 && target_dtype != VT_BF16) return VT_ERR_INVALID_ARG;
+  if (B <= 0 || gamma <= 0 || R < gamma || H <= 0 || Vt <= 0 || V <= 0 || Vt > V) return VT_ERR_INVALID_ARG;
+  if (!finite_positive(target_T) || !finite_positive(draft_T)) return VT_ERR_INVALID_ARG;
+  if ((keep_ids == nullptr) != (full_to_trim == nullptr)) return VT_ERR_INVALID_ARG;
+  if (!keep_ids && Vt != V) return VT_ERR_INVALID_ARG;
+  if (gamma > kWave) return VT_ERR_UNSUPPORTED;
+  if (H % 8 != 0 || !aligned16(hidden) || !aligned16(weight)) return VT_ERR_UNSUPPORTED;
+  if (V > INT32_MAX || H > INT32_MAX || B * R > INT32_MAX) return VT_ERR_UNSUPPORTED;
+  const BlockPlan pl = plan_block(B, gamma, R, H, Vt, V, keep_ids != nullptr);
+  if (pl.rows_t * pl.nchunk_t > static_cast<int64_t>(UINT32_MAX) ||
+      pl.M * pl.nchunk_d > static_cast<int64_t>(UINT32_MAX) || B * pl.nchunk_v > static_cast<int64_t>(UINT32_MAX))
+    return VT_ERR_UNSUPPORTED;
+  if (!pl.fused && ((pl.M + kBM - 1) / kBM) * ((Vt + kBN - 1) / kBN) > INT32_MAX) return VT_ERR_UNSUPPORTED;
+  if (pl.bytes > 0 && (!workspace || workspace_bytes < pl.bytes)) return VT_ERR_WORKSPACE;
+  char *ws = static_cast<char *>(workspace);
+
+  const double log2e = 1.4426950408889634;
+  SmParams D{};
+  D.logits = draft_logits;
+  D.rows = pl.M;
+  D.n = Vt;
+  D.ld = Vt;
+  D.T = draft_T;
+  D.k2 = static_cast<float>(log2e / static_cast<double>(draft_T));
+  D.lse = draft_lse;
+  D.u = u_draft;
+  D.sampled = draft_ids;
+  D.nchunk = static_cast<int>(pl.nchunk_d);
+  D.chunk = pl.chunk_d;
+  if (pl.fused || pl.nchunk_d > 1) D.part = reinterpret_cast<float2 *>(ws + pl.off_dpart);
+
+  SmParams T{};
+  T.logits = target_logits;
+  T.rows = pl.rows_t;
+  T.n = V;
+  T.ld = V;
+  T.T = target_T;
+  T.k2 = static_cast<float>(log2e / static_cast<double>(target_T));
+  T.lse = target_lse;
+  T.nchunk = static_cast<int>(pl.nchunk_t);
+  T.chunk = kChunk;
+  if (pl.nchunk_t > 1) T.part = reinterpret_cast<float2 *>(ws + pl.off_tpart);
+
+  VfParams P{};
+  P.target = target_logits;
+  P.tlse = target_lse;
+  P.draft = draft_logits;
+  P.dlse = draft_lse;
+  P.ids = draft_ids;
+  P.keep = keep_ids;
+  P.f2t = full_to_trim;
+  P.uacc = u_accept;
+  P.ufin = u_final;
+  P.out_tokens = out_tokens;
+  P.out_n = out_num_accepted;
+  P.V = V;
+  P.Vt = Vt;
+  P.R = R;
+  P.Tt = target_T;
+  P.Td = draft_T;
+  P.k2t = T.k2;
+  P.k2d = D.k2;
+  P.gamma = static_cast<int>(gamma);
+  P.nchunk = static_cast<int>(pl.nchunk_v);
+  if (pl.nchunk_v > 1) {
+    P.nbuf = reinterpret_cast<int *>(ws + pl.off_nbuf);
+    P.part = reinterpret_cast<float2 *>(ws + pl.off_vpart);
+  }
+
+  const int64_t vec_elems = target_dtype == VT_F32 ? 4 : 8;
+  const bool vt_ = aligned16(target_logits) && V % vec_elems == 0;
+  const bool vd = aligned16(draft_logits) && Vt % 4 == 0 && pl.chunk_d % 4 == 0;
+  auto go = [&](auto run) {
+    return run(pl, D, T, P, hidden, weight, keep_ids, H, Vt, draft_logits, B, lmhead_begin, lmhead_end, stream);
+  };
+  hipError_t e;
+  if (target_dtype == VT_F32) {
+    if (vt_)
+      e = vd ? go(run_block<float, true, true>) : go(run_block<float, true, false>);
+    else
+      e = vd ? go(run_block<float, false, true>) : go(run_block<float, false, false>);
+  } else {
+    if (vt_)
+      e = vd ? go(run_block<uint16_t, true, true>) : go(run_block<uint16_t, true, false>);
+    else
+      e = vd ? go(run_block<uint16_t, false, true>) : go(run_block<uint16_t, false, false>);
+  }
+  return hip_status(e);
+}

@@ -1,0 +1,447 @@
+// Trimmed LM head for gfx950: logits[m][j] = sum_k hidden[m][k] * weight[row(j)][k],
+// row(j) = keep_ids ? keep_ids[j] : j  ("VocabTrim", §3 Eq. 1; Appendix C.1, Algorithm 2).
+//
+// Two kernels, picked by the number of hidden rows M:
+//  * lmhead_gemv  (M small): the batch-1 decode case.  The head is read once from HBM and every
+//    weight row is used M times, so the kernel is bandwidth-bound.  Each wavefront owns whole
+//    weight rows; lane l reads 16-byte pieces l, l+64, ... of a row (coalesced 1 KiB per load
+//    instruction, non-temporal since the head is streamed once), multiplies them with the
+//    matching pieces of the M hidden rows held in its registers using v_dot2 (bf16 pairs,
+//    fp32 accumulate), and the 64 lane partials are combined by a transpose-reduction.
+//  * lmhead_mfma  (M large): a real dense contraction; 128x128 output tiles on bf16 MFMA
+//    (v_mfma_f32_32x32x16_bf16) with LDS double buffering, weight rows gathered through
+//    keep_ids while staging the tile.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "vt_common.hpp"
+
+namespace vt {
+namespace {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float dot8(const uint4 &w, const uint4 &h, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.x), __builtin_bit_cast(bf16x2, h.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.y), __builtin_bit_cast(bf16x2, h.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.z), __builtin_bit_cast(bf16x2, h.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), __builtin_bit_cast(bf16x2, h.w), acc, false);
+  return acc;
+}
+
+__device__ __forceinline__ uint4 load_nt(const uint4 *p) {
+  uint4 r;
+  r.x = __builtin_nontemporal_load(&reinterpret_cast<const unsigned int *>(p)[0]);
+  r.y = __builtin_nontemporal_load(&reinterpret_cast<const unsigned int *>(p)[1]);
+  r.z = __builtin_nontemporal_load(&reinterpret_cast<const unsigned int *>(p)[2]);
+  r.w = __builtin_nontemporal_load(&reinterpret_cast<const unsigned int *>(p)[3]);
+  return r;
+}
+
+// ---- cross-lane exchange on gfx950
+// v_permlane32_swap: lanes 32..63 of the first operand trade places with lanes 0..31 of the
+// second; v_permlane16_swap does the same for the odd 16-lane rows of the first operand and the
+// even rows of the second.  Adding the two results sums each value with its partner at
+// lane ^ 32 (^ 16) while keeping the two values apart -- one instruction per pair, no selects.
+__device__ __forceinline__ void swap32(float &x, float &y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap16(float &x, float &y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+// DPP lane moves inside 16-lane rows: rotate by 8 (partner lane ^ 8), mirror within 8 lanes,
+// and the quad permutations that swap neighbours (lane ^ 1) and pairs (lane ^ 2).
+constexpr int kDppRor8 = 0x128, kDppHalfMirror = 0x141, kDppXor1 = 0xB1, kDppXor2 = 0x4E;
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Transpose-reduction of NP (1, 2, 4 or 8) per-lane partial sums over the 64 lanes.  The steps
+// at lane distance 32, 16 and 8 halve the number of values each lane carries (each lane keeps
+// the half its partner gives up), the remaining steps add within groups of 64/NP lanes.  On
+// return lane l holds the complete sum of value index l / (64 / NP).  About NP + 6 exchanges
+// instead of 6 * NP for NP separate reductions.
+template <int NP>
+__device__ __forceinline__ float transpose_reduce(float (&v)[NP]) {
+  if constexpr (NP >= 2) {
+#pragma unroll
+    for (int k = 0; k < NP / 2; ++k) {
+      float a = v[k], b = v[k + NP / 2];
+      swap32(a, b);
+      v[k] = a + b;
+    }
+  } else {
+    float a = v[0], b = v[0];
+    swap32(a, b);
+    v[0] = a + b;
+  }
+  if constexpr (NP >= 4) {
+#pragma unroll
+    for (int k = 0; k < NP / 4; ++k) {
+      float a = v[k], b = v[k + NP / 4];
+      swap16(a, b);
+      v[k] = a + b;
+    }
+  } else {
+    float a = v[0], b = v[0];
+    swap16(a, b);
+    v[0] = a + b;
+  }
+  if constexpr (NP >= 8) {
+    const bool up = (lane_id() & 8) != 0;
+#pragma unroll
+    for (int k = 0; k < NP / 8; ++k) {
+      const float send = up ? v[k] : v[k + NP / 8];
+      const float keep = up ? v[k + NP / 8] : v[k];
+      v[k] = keep + dpp<kDppRor8>(send);
+    }
+  } else {
+    v[0] += dpp<kDppRor8>(v[0]);
+  }
+  v[0] += dpp<kDppHalfMirror>(v[0]);
+  v[0] += dpp<kDppXor2>(v[0]);
+  v[0] += dpp<kDppXor1>(v[0]);
+  return v[0];
+}
+
+template <int N>
+struct Pow2Ceil {
+  static constexpr int value = N <= 1 ? 1 : 2 * Pow2Ceil<(N + 1) / 2>::value;
+};
+template <>
+struct Pow2Ceil<1> {
+  static constexpr int value = 1;
+};
+
+#ifndef VT_GEMV_PD
+#define VT_GEMV_PD 2
+#endif
+constexpr int kGemvPrefetch = VT_GEMV_PD;  // weight rows in flight per wavefront beyond the one in use
+
+// Rows per workgroup block: the head is cut into contiguous blocks of `per` rows (a multiple of 4,
+// one block per workgroup), sized for one workgroup per CU of a 256-CU device.  The size depends
+// only on Vt, so results never depend on the device or on the batch.
+inline int gemv_rows_per_block(int64_t Vt) {
+  const int64_t per = (Vt + 255) / 256;
+  return static_cast<int>((per + kWavesPerBlock - 1) / kWavesPerBlock * kWavesPerBlock);
+}
+inline int gemv_blocks(int64_t Vt) {
+  const int per = gemv_rows_per_block(Vt);
+  return static_cast<int>((Vt + per - 1) / per);
+}
+
+// Draft softmax partials produced by the GEMV epilogue (optional): for every hidden row m and
+// workgroup block k, (max_j x_mj, sum_j exp((x_mj - max) / T)) over the block's rows j, written
+// to part[m * nblocks + k] (k2 = log2(e) / T).
+struct GemvParts {
+  float2 *part;
+  float k2;
+};
+
+// Workgroup k owns head rows [k * per, (k + 1) * per); its four wavefronts take every fourth row of
+// the block, so the workgroup streams one contiguous region of the head (measured ~10% faster than
+// a grid-stride walk).  A ring of PD + 1 register buffers keeps PD rows in flight while one is
+// multiplied.  Every load is unconditional and in bounds (row indices past the wave's last row
+// repeat the last row, pieces past H repeat the last piece and are masked), so the compiler can
+// wait for exactly the oldest row (vmcnt(N)) instead of draining the queue.  FULL: H is a multiple
+// of 512 (no masking at all).  TRIM: rows are gathered through keep_ids.  PARTS: also produce the
+// draft softmax partials of the block (online max / sum per hidden row, combined over the four
+// wavefronts through LDS), so the softmax never re-reads the logits for its first pass.
+template <int M, int NIT, int PD, bool FULL, bool TRIM, bool PARTS>
+__global__ __launch_bounds__(kBlock) void lmhead_gemv(const uint16_t *__restrict__ hidden,
+                                                      const uint16_t *__restrict__ weight,
+                                                      const int32_t *__restrict__ keep, int H, int Vt, int per,
+                                                      float *__restrict__ logits, GemvParts parts) {
+  constexpr int NP = Pow2Ceil<M>::value;
+  constexpr int kGroup = kWave / NP;
+  const int lane = lane_id();
+  const int pieces = H >> 3;  // 16-byte pieces per row
+  auto piece = [&](int it) -> int {
+    const int p = it * kWave + lane;
+    return (FULL || it < NIT - 1) ? p : min(p, pieces - 1);
+  };
+  auto live = [&](int it) -> bool { return FULL || it < NIT - 1 || it * kWave + lane < pieces; };
+
+  uint4 h[M][NIT];
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const uint4 v = reinterpret_cast<const uint4 *>(hidden + static_cast<int64_t>(m) * H)[piece(it)];
+      h[m][it] = live(it) ? v : make_uint4(0, 0, 0, 0);
+    }
+
+  const int wid = __builtin_amdgcn_readfirstlane(wave_id());
+  const int base = static_cast<int>(blockIdx.x) * per;
+  const int wv = base + wid;
+  const int end = min(Vt, base + per);
+  const int nrows = wv < end ? (end - 1 - wv) / kWavesPerBlock + 1 : 0;
+  auto row_of = [&](int t) { return wv + t * kWavesPerBlock; };
+  const int mrow = lane / kGroup;  // hidden row whose sum this lane holds after the reduction
+  float pmax = kNegInf, psum = 0.f;
+
+  auto fetch = [&](int t, uint4(&dst)[NIT]) {
+    const int j = row_of(min(t, nrows - 1));  // wave-uniform
+    int64_t r = j;
+    if constexpr (TRIM) r = keep[j];
+    const uint4 *src = reinterpret_cast<const uint4 *>(weight + r * H);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) dst[it] = load_nt(src + piece(it));
+  };
+  auto consume = [&](int t, const uint4(&src)[NIT]) {
+    float acc[NP];
+#pragma unroll
+    for (int m = 0; m < NP; ++m) acc[m] = 0.f;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const uint4 wv4 = live(it) ? src[it] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[m] = dot8(wv4, h[m][it], acc[m]);
+    }
+    const float sum = transpose_reduce<NP>(acc);
+    if ((lane % kGroup) == 0 && mrow < M) logits[static_cast<int64_t>(mrow) * Vt + row_of(t)] = sum;
+    if constexpr (PARTS) {
+      const float nm = fmaxf(pmax, sum);
+      psum = psum * __builtin_amdgcn_exp2f((pmax - nm) * parts.k2) + __builtin_amdgcn_exp2f((sum - nm) * parts.k2);
+      pmax = nm;
+    }
+  };
+
+  if (nrows > 0) {
+    uint4 w[PD + 1][NIT];
+#pragma unroll
+    for (int s = 0; s < PD; ++s) fetch(s, w[s]);
+    // whole groups of PD + 1 rows: straight-line code, so each multiply waits only for its own row
+    int t0 = 0;
+    for (; t0 + PD < nrows; t0 += PD + 1) {
+#pragma unroll
+      for (int s = 0; s <= PD; ++s) {
+        fetch(t0 + s + PD, w[(s + PD) % (PD + 1)]);
+        consume(t0 + s, w[s]);
+      }
+    }
+    // the last rows (fewer than PD + 1) are already in flight
+#pragma unroll
+    for (int s = 0; s < PD; ++s)
+      if (t0 + s < nrows) consume(t0 + s, w[s]);
+  }
+
+  if constexpr (PARTS) {
+    __shared__ float2 wpart[kWavesPerBlock][NP];
+    if ((lane % kGroup) == 0) wpart[wid][mrow] = make_float2(pmax, psum);
+    __syncthreads();
+    if (threadIdx.x < M) {
+      const int m = threadIdx.x;
+      float mx = kNegInf;
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) mx = fmaxf(mx, wpart[w][m].x);
+      float sx = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) {
+        const float2 v = wpart[w][m];
+        if (v.x != kNegInf) sx += v.y * __builtin_amdgcn_exp2f((v.x - mx) * parts.k2);
+      }
+      parts.part[static_cast<int64_t>(m) * gridDim.x + blockIdx.x] = make_float2(mx, sx);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------ MFMA path
+constexpr int kBM = 128, kBN = 128, kBK = 32, kLdsPad = 8;
+constexpr int kLdsRow = kBK + kLdsPad;  // bf16 elements per LDS row (80 bytes)
+
+// Workgroups are handed to the 8 XCDs round-robin; remap so that each XCD works on a
+// contiguous range of logical tiles (consecutive tiles share a weight tile in that XCD's L2).
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  constexpr int kXcd = 8;
+  const int per = (nblocks + kXcd - 1) / kXcd;
+  const int tall = nblocks % kXcd == 0 ? kXcd : nblocks % kXcd;
+  const int xcd = bid % kXcd, local = bid / kXcd;
+  return xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
+}
+
+__global__ __launch_bounds__(kBlock) void lmhead_mfma(const uint16_t *__restrict__ hidden,
+                                                      const uint16_t *__restrict__ weight,
+                                                      const int32_t *__restrict__ keep, int M, int H, int Vt,
+                                                      float *__restrict__ logits) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM * kLdsRow];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBN * kLdsRow];
+
+  const int nbm = (M + kBM - 1) / kBM;
+  const int nbn = (Vt + kBN - 1) / kBN;
+  const int tile = xcd_remap(blockIdx.x, nbm * nbn);
+  const int bm = tile % nbm, bn = tile / nbm;
+  const int m0 = bm * kBM, n0 = bn * kBN;
+
+  const int tid = threadIdx.x;
+  // staging: 128 rows x 4 pieces of 8 bf16 per operand = 512 pieces, 2 per thread each
+  int a_row[2], b_row[2], piece[2];
+  const uint16_t *a_src[2];
+  const uint16_t *b_src[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int c = tid + s * kBlock;
+    a_row[s] = c >> 2;
+    b_row[s] = c >> 2;
+    piece[s] = c & 3;
+    const int gm = m0 + a_row[s];
+    a_src[s] = gm < M ? hidden + static_cast<int64_t>(gm) * H : nullptr;
+    const int gn = n0 + b_row[s];
+    if (gn < Vt) {
+      const int64_t r = keep ? static_cast<int64_t>(keep[gn]) : static_cast<int64_t>(gn);
+      b_src[s] = weight + r * H;
+    } else {
+      b_src[s] = nullptr;
+    }
+  }
+  auto fetch = [&](int k0, uint4 (&ra)[2], uint4 (&rb)[2]) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int k = k0 + piece[s] * 8;
+      const bool kin = k < H;
+      ra[s] = (a_src[s] && kin) ? *reinterpret_cast<const uint4 *>(a_src[s] + k) : make_uint4(0, 0, 0, 0);
+      rb[s] = (b_src[s] && kin) ? *reinterpret_cast<const uint4 *>(b_src[s] + k) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto stage = [&](int buf, const uint4 (&ra)[2], const uint4 (&rb)[2]) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      *reinterpret_cast<uint4 *>(&sA[buf][a_row[s] * kLdsRow + piece[s] * 8]) = ra[s];
+      *reinterpret_cast<uint4 *>(&sB[buf][b_row[s] * kLdsRow + piece[s] * 8]) = rb[s];
+    }
+  };
+
+  // 4 waves in a 2x2 arrangement, each owning a 64x64 output block = 2x2 MFMA tiles of 32x32
+  const int w = wave_id();
+  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  const int lane = lane_id();
+  const int lr = lane & 31, lk = (lane >> 5) * 8;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.f;
+
+  uint4 ra[2], rb[2];
+  fetch(0, ra, rb);
+  stage(0, ra, rb);
+  __syncthreads();
+  const int nk = (H + kBK - 1) / kBK;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) fetch((kt + 1) * kBK, ra, rb);
+#pragma unroll
+    for (int kk = 0; kk < kBK; kk += 16) {
+      bf16x8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[i] = *reinterpret_cast<const bf16x8 *>(&sA[cur][(wm + i * 32 + lr) * kLdsRow + kk + lk]);
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        b[jj] = *reinterpret_cast<const bf16x8 *>(&sB[cur][(wn + jj * 32 + lr) * kLdsRow + kk + lk]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[jj], acc[i][jj], 0, 0, 0);
+    }
+    if (kt + 1 < nk) stage(cur ^ 1, ra, rb);
+    __syncthreads();
+  }
+
+  // 32x32 accumulator layout: lane l holds column l % 32; register v holds row
+  // 8 * (v / 4) + 4 * (l / 32) + v % 4.
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int gn = n0 + wn + jj * 32 + lr;
+      if (gn >= Vt) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int gm = m0 + wm + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (gm < M) logits[static_cast<int64_t>(gm) * Vt + gn] = acc[i][jj][v];
+      }
+    }
+}
+
+// ------------------------------------------------------------------------------ dispatch
+using GemvFn = void (*)(const uint16_t *, const uint16_t *, const int32_t *, int, int, int, float *, GemvParts);
+
+constexpr int kGemvMaxM = 8;
+constexpr int kGemvMaxNit = 8;
+constexpr int kGemvMaxRegs = 48;  // M * NIT: the hidden slice lives in 4 * M * NIT VGPRs
+
+template <int M, int NIT, bool PARTS>
+GemvFn gemv_entry(bool full, bool trim) {
+  if constexpr (M * NIT > kGemvMaxRegs) {
+    return nullptr;
+  } else {
+    constexpr int PD = kGemvPrefetch;
+    if (full)
+      return trim ? &lmhead_gemv<M, NIT, PD, true, true, PARTS> : &lmhead_gemv<M, NIT, PD, true, false, PARTS>;
+    return trim ? &lmhead_gemv<M, NIT, PD, false, true, PARTS> : &lmhead_gemv<M, NIT, PD, false, false, PARTS>;
+  }
+}
+
+template <int M, bool PARTS>
+GemvFn gemv_for_nit(int nit, bool full, bool trim) {
+  switch (nit) {
+    case 1: return gemv_entry<M, 1, PARTS>(full, trim);
+    case 2: return gemv_entry<M, 2, PARTS>(full, trim);
+    case 3: return gemv_entry<M, 3, PARTS>(full, trim);
+    case 4: return gemv_entry<M, 4, PARTS>(full, trim);
+    case 5: return gemv_entry<M, 5, PARTS>(full, trim);
+    case 6: return gemv_entry<M, 6, PARTS>(full, trim);
+    case 7: return gemv_entry<M, 7, PARTS>(full, trim);
+    case 8: return gemv_entry<M, 8, PARTS>(full, trim);
+    default: return nullptr;
+  }
+}
+
+// The GEMV kernel for (M, H), or nullptr when the shape needs the MFMA kernel.
+template <bool PARTS>
+GemvFn pick_gemv(int64_t M, int64_t H, bool trim) {
+  const int nit = static_cast<int>((H + 511) / 512);
+  const bool full = H % 512 == 0;
+  if (nit > kGemvMaxNit || M > kGemvMaxM || M * nit > kGemvMaxRegs) return nullptr;
+  switch (M) {
+    case 1: return gemv_for_nit<1, PARTS>(nit, full, trim);
+    case 2: return gemv_for_nit<2, PARTS>(nit, full, trim);
+    case 3: return gemv_for_nit<3, PARTS>(nit, full, trim);
+    case 4: return gemv_for_nit<4, PARTS>(nit, full, trim);
+    case 5: return gemv_for_nit<5, PARTS>(nit, full, trim);
+    case 6: return gemv_for_nit<6, PARTS>(nit, full, trim);
+    case 7: return gemv_for_nit<7, PARTS>(nit, full, trim);
+    case 8: return gemv_for_nit<8, PARTS>(nit, full, trim);
+    default: return nullptr;
+  }
+}
+
+inline hipError_t launch_gemv(GemvFn fn, const uint16_t *hidden, const uint16_t *weight, const int32_t *keep,
+                              int64_t H, int64_t Vt, float *logits, GemvParts parts, hipStream_t stream) {
+  return launch(fn, dim3(static_cast<unsigned>(gemv_blocks(Vt))), dim3(kBlock), 0, stream, hidden, weight, keep,
+                static_cast<int>(H), static_cast<int>(Vt), gemv_rows_per_block(Vt), logits, parts);
+}
+
+inline hipError_t launch_mfma(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int64_t M,
+                              int64_t H, int64_t Vt, float *logits, hipStream_t stream) {
+  const int64_t tiles = ((M + kBM - 1) / kBM) * ((Vt + kBN - 1) / kBN);
+  return launch(lmhead_mfma, dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0, stream, hidden, weight, keep,
+                static_cast<int>(M), static_cast<int>(H), static_cast<int>(Vt), logits);
+}
+
+}  // namespace
+}  // namespace vt
+

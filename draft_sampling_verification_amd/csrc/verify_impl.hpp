@@ -1,0 +1,337 @@
+// Batched modified rejection sampling for gfx950 ("Speculative decoding" glossary, sections
+// "Propose a block, keep a prefix" and "Why a rejection needs a special draw"; "A rejection rule
+// keeps speculative decoding's output exact", sections "What the accept/reject rule has to
+// balance" and "Extending the rule from one token to a drafted run"; "VocabTrim", Appendix C.1,
+// Algorithm 2 for the map from trimmed ids back to the full vocabulary).
+//
+// Pass 1: one 256-thread workgroup per (sequence b, 4096-id chunk of the full vocabulary).  Every
+// workgroup of a sequence repeats the sequence's accept scan (gamma <= 64 lanes of wave 0, fp64
+// ratios, a ballot gives n = first rejection), so all of them know which row feeds the final
+// draw.  Each then computes, for its chunk of ids x, the weight w(x) = max(0, p_n(x) - q_n(x))
+// (q_n(x) = 0 off the kept set; w = p_gamma when all drafts were accepted) and publishes the chunk
+// sums of w and of p.  Pass 2 (next launch, one workgroup per sequence) forms the chunk-level
+// running sum, falls back to p_n if the residual mass is 0, draws the final token with u_final by
+// rescanning one chunk, and writes the outputs.  Vocabularies of one chunk use a single launch.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "vt_common.hpp"
+
+namespace vt {
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634;
+
+struct VfParams {
+  const void *target;
+  const double *tlse;
+  const float *draft;
+  const double *dlse;
+  const int32_t *ids;
+  const int32_t *keep;
+  const int32_t *f2t;
+  const float *uacc;
+  const float *ufin;
+  int32_t *out_tokens;
+  int32_t *out_n;
+  int *nbuf;     // n per sequence, from pass 1 to pass 2
+  float2 *part;  // (sum of final-draw weights, sum of p) per (sequence, chunk)
+  int64_t V, Vt, R;
+  double Tt, Td;
+  float k2t, k2d;  // log2(e) / T
+  int gamma;
+  int nchunk;
+};
+
+// Per-row constants so that exp(x / T - lse) = 2^((x - c0) * k2 - d2) with c0 = lse * T in logit
+// units: the fp32 argument is small for the heavy entries, where accuracy matters.
+struct RowExp {
+  float c0, d2, k2;
+  __device__ __forceinline__ float operator()(float x) const {
+    return x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(fmaf(x - c0, k2, -d2));
+  }
+};
+
+__device__ __forceinline__ RowExp make_row_exp(double lse, double T, float k2) {
+  RowExp e;
+  e.c0 = static_cast<float>(lse * T);
+  e.d2 = static_cast<float>((lse - static_cast<double>(e.c0) / T) * kLog2e);
+  e.k2 = k2;
+  return e;
+}
+
+template <typename Tin>
+__device__ __forceinline__ float load_logit(const Tin *row, int64_t i) {
+  if constexpr (sizeof(Tin) == 4)
+    return reinterpret_cast<const float *>(row)[i];
+  else
+    return bf16_to_f32(reinterpret_cast<const uint16_t *>(row)[i]);
+}
+
+// Weights of the final draw for this thread's 16 ids of chunk c: residual (use_p = false) or
+// p itself; also returns p in pv for the fallback sum.
+template <typename Tin, bool kVec>
+__device__ __forceinline__ void final_weights(const VfParams &P, int64_t b, int n, int c, bool use_p, float (&wv)[16],
+                                              float (&pv)[16]) {
+  const int row = n < P.gamma ? n : P.gamma;
+  const Tin *trow = reinterpret_cast<const Tin *>(P.target) + (b * (P.gamma + 1) + row) * P.V;
+  float lt[16];
+  load16<Tin, kVec>(trow, P.V, static_cast<int64_t>(c) * kChunk, lt);
+  const RowExp pe = make_row_exp(P.tlse[b * (P.gamma + 1) + row], P.Tt, P.k2t);
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) pv[j] = pe(lt[j]);
+  if (n >= P.gamma || use_p) {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) wv[j] = pv[j];
+    return;
+  }
+  const float *drow = P.draft + (b * P.R + n) * P.Vt;
+  const RowExp qe = make_row_exp(P.dlse[b * P.R + n], P.Td, P.k2d);
+  const int64_t x0 = static_cast<int64_t>(c) * kChunk + static_cast<int64_t>(threadIdx.x) * kPerThread;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const int64_t x = x0 + j;
+    float q = 0.f;
+    if (x < P.V) {
+      const int64_t t = P.f2t ? static_cast<int64_t>(P.f2t[x]) : x;
+      if (t >= 0 && t < P.Vt) q = qe(drow[t]);
+    }
+    wv[j] = fmaxf(pv[j] - q, 0.f);
+  }
+}
+
+// Accept scan of sequence b by wave 0 (lanes 0..gamma-1): n = first rejected draft, gamma if
+// none, -1 if a draft id (or its full id) is out of range.  Broadcast through LDS; all threads
+// of the workgroup must call.
+template <typename Tin>
+__device__ __forceinline__ int accept_scan(const VfParams &P, int64_t b, int *sh_n) {
+  const int gamma = P.gamma;
+  if (wave_id() == 0) {
+    const int i = lane_id();
+    bool valid = true, accept = true;
+    if (i < gamma) {
+      const int64_t x = P.ids[b * P.R + i];
+      valid = x >= 0 && x < P.Vt;
+      int64_t y = x;
+      if (valid && P.keep) {
+        y = P.keep[x];
+        valid = y >= 0 && y < P.V;
+      }
+      if (valid) {
+        const Tin *trow = reinterpret_cast<const Tin *>(P.target) + (b * (gamma + 1) + i) * P.V;
+        const double a = static_cast<double>(load_logit(trow, y)) / P.Tt - P.tlse[b * (gamma + 1) + i];
+        const double d = static_cast<double>(P.draft[(b * P.R + i) * P.Vt + x]) / P.Td - P.dlse[b * P.R + i];
+        const double ratio = fmin(1.0, exp(a - d));
+        accept = static_cast<double>(P.uacc[b * gamma + i]) <= ratio;
+      }
+    }
+    const unsigned long long bad = __ballot(i < gamma && !valid);
+    const unsigned long long rej = __ballot(i < gamma && !accept);
+    if (i == 0) *sh_n = bad ? -1 : (rej ? __ffsll(static_cast<long long>(rej)) - 1 : gamma);
+  }
+  __syncthreads();
+  return *sh_n;
+}
+
+// Final draw and outputs of sequence b, given n and the chunk sums of the residual (or bonus)
+// weights and of p (mass(k, use_p)); all threads of the workgroup must call.
+template <typename Tin, bool kVec, typename Mass>
+__device__ __forceinline__ void finish_sequence(const VfParams &P, int64_t b, int n, Mass mass, float *redf,
+                                                int *redi, float *bcast) {
+  const int gamma = P.gamma;
+  int32_t *tok = P.out_tokens + b * (gamma + 1);
+  if (n < 0) {
+    for (int i = threadIdx.x; i <= gamma; i += kBlock) tok[i] = -1;
+    if (threadIdx.x == 0) P.out_n[b] = -1;
+    return;
+  }
+  // residual mass; if it rounds to zero, draw from p_n instead
+  float carry = 0.f;
+  for (int k0 = 0; k0 < P.nchunk; k0 += kBlock) {
+    float prev, total;
+    block_inclusive_scan(mass(k0 + threadIdx.x, false), redf, &prev, &total);
+    carry = carry + total;
+  }
+  const bool use_p = !(carry > 0.f);
+  float Z = carry;
+  if (use_p) {
+    carry = 0.f;
+    for (int k0 = 0; k0 < P.nchunk; k0 += kBlock) {
+      float prev, total;
+      block_inclusive_scan(mass(k0 + threadIdx.x, true), redf, &prev, &total);
+      carry = carry + total;
+    }
+    Z = carry;
+  }
+  const float t = P.ufin[b] * Z;
+  int cstar = 0x7fffffff;
+  float Estar = 0.f;
+  carry = 0.f;
+  for (int k0 = 0; k0 < P.nchunk; k0 += kBlock) {
+    float prev, total;
+    const float incl = block_inclusive_scan(mass(k0 + threadIdx.x, use_p), redf, &prev, &total);
+    const int k = k0 + threadIdx.x;
+    const bool hit = k < P.nchunk && t <= carry + incl;
+    const int first = block_min_int(hit ? k : 0x7fffffff, redi);
+    if (first != 0x7fffffff) {
+      if (k == first) *bcast = carry + prev;
+      __syncthreads();
+      cstar = first;
+      Estar = *bcast;
+      break;
+    }
+    carry = carry + total;
+  }
+  bool fallback = false;
+  if (cstar == 0x7fffffff) {
+    int lastc = -1;
+    for (int k = threadIdx.x; k < P.nchunk; k += kBlock)
+      if (mass(k, use_p) > 0.f) lastc = k;
+    cstar = max(block_max_int(lastc, redi), 0);  // never below chunk 0, even for a NaN uniform
+    fallback = true;
+  }
+  // rescan chunk c*: running sum inside it, first id reaching t (else last positive id)
+  float wv[16], pv[16];
+  final_weights<Tin, kVec>(P, b, n, cstar, use_p, wv, pv);
+  float loc[16];
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    acc += wv[j];
+    loc[j] = acc;
+  }
+  float prev, total;
+  block_inclusive_scan(acc, redf, &prev, &total);
+  const float base = Estar + prev;
+  int found = 0x7fffffff;
+  if (!fallback) {
+#pragma unroll
+    for (int j = kPerThread - 1; j >= 0; --j)
+      if (t <= base + loc[j]) found = static_cast<int>(threadIdx.x) * kPerThread + j;
+  }
+  found = block_min_int(found, redi);
+  if (found == 0x7fffffff) {
+    int last = -1;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j)
+      if (wv[j] > 0.f) last = static_cast<int>(threadIdx.x) * kPerThread + j;
+    found = block_max_int(last, redi);
+  }
+  const int32_t final_id = static_cast<int32_t>(static_cast<int64_t>(cstar) * kChunk + found);
+  for (int i = threadIdx.x; i <= gamma; i += kBlock) {
+    int32_t v = -1;
+    if (i < n) {
+      const int32_t x = P.ids[b * P.R + i];
+      v = P.keep ? P.keep[x] : x;
+    } else if (i == n) {
+      v = final_id;
+    }
+    tok[i] = v;
+  }
+  if (threadIdx.x == 0) P.out_n[b] = n;
+}
+
+// Vocabularies of one chunk (V <= 4096): one workgroup per sequence does everything.
+template <typename Tin, bool kVec>
+__global__ __launch_bounds__(kBlock) void verify_single(VfParams P) {
+  __shared__ float redf[kWavesPerBlock];
+  __shared__ int redi[kWavesPerBlock];
+  __shared__ int sh_n;
+  __shared__ float bcast;
+  const int64_t b = blockIdx.x;
+  const int n = accept_scan<Tin>(P, b, &sh_n);
+  float sw = 0.f, sp = 0.f;
+  if (n >= 0) {
+    float wv[16], pv[16];
+    final_weights<Tin, kVec>(P, b, n, 0, false, wv, pv);
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      sw += wv[j];
+      sp += pv[j];
+    }
+  }
+  sw = block_sum(sw, redf);
+  sp = block_sum(sp, redf);
+  auto mass = [&](int k, bool use_p) -> float { return k == 0 ? (use_p ? sp : sw) : 0.f; };
+  finish_sequence<Tin, kVec>(P, b, n, mass, redf, redi, &bcast);
+}
+
+// Larger vocabularies, pass 1: one workgroup per (sequence, chunk) repeats the sequence's accept
+// scan, then publishes the chunk sums of the residual (or bonus) weights and of p; chunk 0 also
+// records n.  Pass 2 reads them after the kernel boundary.
+template <typename Tin, bool kVec>
+__global__ __launch_bounds__(kBlock) void verify_partial(VfParams P) {
+  __shared__ float redf[kWavesPerBlock];
+  __shared__ int sh_n;
+  const int64_t bid = blockIdx.x;
+  const int64_t b = bid / P.nchunk;
+  const int c = static_cast<int>(bid - b * P.nchunk);
+  const int n = accept_scan<Tin>(P, b, &sh_n);
+  float sw = 0.f, sp = 0.f;
+  if (n >= 0) {
+    float wv[16], pv[16];
+    final_weights<Tin, kVec>(P, b, n, c, false, wv, pv);
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      sw += wv[j];
+      sp += pv[j];
+    }
+  }
+  sw = block_sum(sw, redf);
+  sp = block_sum(sp, redf);
+  if (threadIdx.x == 0) {
+    P.part[b * P.nchunk + c] = make_float2(sw, sp);
+    if (c == 0) P.nbuf[b] = n;
+  }
+}
+
+// Pass 2: one workgroup per sequence draws the final token and writes the outputs.
+template <typename Tin, bool kVec>
+__global__ __launch_bounds__(kBlock) void verify_final(VfParams P) {
+  __shared__ float redf[kWavesPerBlock];
+  __shared__ int redi[kWavesPerBlock];
+  __shared__ float bcast;
+  const int64_t b = blockIdx.x;
+  const int n = P.nbuf[b];
+  const float2 *part = P.part + b * P.nchunk;
+  auto mass = [&](int k, bool use_p) -> float {
+    if (k >= P.nchunk) return 0.f;
+    const float2 v = part[k];
+    return use_p ? v.y : v.x;
+  };
+  finish_sequence<Tin, kVec>(P, b, n, mass, redf, redi, &bcast);
+}
+
+struct VFWsLayout {
+  size_t nbuf, part, bytes;
+};
+
+VFWsLayout vf_ws_layout(int64_t B, int64_t nchunk) {
+  VFWsLayout L{};
+  if (nchunk <= 1) return L;
+  L.nbuf = 0;
+  L.part = align_up(static_cast<size_t>(B) * sizeof(int), 256);
+  L.bytes = L.part + align_up(static_cast<size_t>(B) * static_cast<size_t>(nchunk) * sizeof(float2), 256);
+  return L;
+}
+
+template <typename Tin, bool kVec>
+hipError_t vf_launch_all(const VfParams &P, int64_t B, hipStream_t stream) {
+  if (P.nchunk == 1) return launch(verify_single<Tin, kVec>, dim3(static_cast<unsigned>(B)), dim3(kBlock), 0, stream, P);
+  const hipError_t e = launch(verify_partial<Tin, kVec>, dim3(static_cast<unsigned>(B * P.nchunk)), dim3(kBlock), 0,
+                              stream, P);
+  if (e != hipSuccess) return e;
+  return launch(verify_final<Tin, kVec>, dim3(static_cast<unsigned>(B)), dim3(kBlock), 0, stream, P);
+}
+
+template <typename Tin>
+hipError_t launch_verify(const VfParams &P, bool vec, int64_t B, hipStream_t stream) {
+  return vec ? vf_launch_all<Tin, true>(P, B, stream) : vf_launch_all<Tin, false>(P, B, stream);
+}
+
+}  // namespace
+}  // namespace vt
+

@@ -7,6 +7,7 @@
  *                      optional inverse-CDF draw per row
  *   vt_spec_verify     batched modified rejection sampling: accept scan, residual or bonus draw,
  *                      trimmed-id -> full-id remap
+ * and vt_spec_block runs all of them for one block in a single call, with fused kernels.
  *
  * Pages cited (title, section):
  *   [VT] "VocabTrim: Vocabulary Pruning for Efficient Speculative Decoding in LLMs" (arXiv 2506.22694v2)
@@ -151,6 +152,42 @@ vt_status_t vt_spec_verify(int64_t B, int64_t gamma, int64_t V, int64_t Vt, cons
 
 /* Bytes of workspace vt_spec_verify needs for B sequences over a V-id vocabulary. */
 size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t V);
+
+/*
+ * vt_spec_block -- one whole speculative block in one call: the trimmed LM head, the draft
+ * softmax with draws, the target softmax and the verification, i.e. the four calls above, with
+ * the kernels fused where the dependencies allow (5 launches for decode-sized batches instead
+ * of 7: the LM head also emits the draft softmax's first pass, and one launch finishes both the
+ * draft and the target rows).
+ *   Pages: as for the four calls above.
+ *
+ *   hidden bf16 [B*R][H] (row b*R + i is sequence b's i-th draft position); weight bf16 [V][H]
+ *   (the full head); keep_ids int32 [Vt] and full_to_trim int32 [V] (both NULL iff the head is
+ *   untrimmed, Vt == V); target_logits [B][gamma+1][V] (fp32 or bf16); u_draft fp32 [B*R],
+ *   u_accept fp32 [B][gamma], u_final fp32 [B].
+ *   Outputs: draft_logits fp32 [B*R][Vt], draft_lse fp64 [B*R], draft_ids int32 [B*R] (trimmed
+ *   ids), target_lse fp64 [B*(gamma+1)], out_tokens int32 [B][gamma+1], out_num_accepted int32 [B].
+ *   lmhead_begin / lmhead_end: optional (NULL) events, recorded on `stream` immediately before and
+ *   after the LM-head kernel, for timing it inside the call.
+ *   Results are those of the four calls, except that on the fused path the draft running sums are
+ *   chunked by the LM head's row blocks (ceil(Vt / 256) rounded up to a multiple of 4 rows) instead
+ *   of 4096-element chunks: draws can differ from the separate calls only where a CDF boundary lies
+ *   within rounding of the uniform.
+ *   Errors: INVALID_ARG for NULL required pointers, B, gamma, H, V or Vt <= 0, R < gamma, Vt > V,
+ *   a temperature not finite or <= 0, keep_ids/full_to_trim inconsistent with Vt; UNSUPPORTED for
+ *   gamma > 64, H % 8 != 0 or a hidden/weight base not 16-byte aligned; WORKSPACE if the workspace
+ *   is smaller than vt_spec_block_workspace_bytes.
+ */
+vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep_ids,
+                          const int32_t *full_to_trim, int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt,
+                          int64_t V, const void *target_logits, vt_dtype_t target_dtype, float target_T,
+                          float draft_T, const float *u_draft, const float *u_accept, const float *u_final,
+                          float *draft_logits, double *draft_lse, int32_t *draft_ids, double *target_lse,
+                          int32_t *out_tokens, int32_t *out_num_accepted, hipEvent_t lmhead_begin,
+                          hipEvent_t lmhead_end, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace vt_spec_block needs for this shape. */
+size_t vt_spec_block_workspace_bytes(int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt, int64_t V);
 
 /* Static description of a status code (never NULL). */
 const char *vt_status_string(vt_status_t status);

@@ -139,3 +139,33 @@ def test_missing_library_fails_loudly(tmp_path):
             "try:\n    vt.lib()\nexcept RuntimeError as e:\n    print('raised', 'missing' in str(e))\n")
     out = subprocess.run(["python", "-c", code], capture_output=True, text=True, cwd=ROOT)
     assert out.stdout.strip() == "raised True", out.stderr
+
+
+# ------------------------------------------------------------------ vt_spec_block
+
+def blk(hidden=A, weight=A2, keep=A, f2t=A, B=4, gamma=5, R=6, H=3072, Vt=32768, V=128256, target=A, tdt=F32,
+        Tt=1.0, Td=1.0, ud=A, ua=A, uf=A, dl=A, dlse=A, ids=A, tlse=A, tok=A, nacc=A, ws=A2, wsb=1 << 30):
+    return vt.lib().vt_spec_block(hidden, weight, keep, f2t, B, gamma, R, H, Vt, V, target, tdt, Tt, Td, ud, ua, uf,
+                                  dl, dlse, ids, tlse, tok, nacc, NUL, NUL, ws, wsb, NUL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=NUL), INV), (dict(weight=NUL), INV), (dict(target=NUL), INV), (dict(ud=NUL), INV),
+    (dict(ua=NUL), INV), (dict(uf=NUL), INV), (dict(dl=NUL), INV), (dict(dlse=NUL), INV), (dict(ids=NUL), INV),
+    (dict(tlse=NUL), INV), (dict(tok=NUL), INV), (dict(nacc=NUL), INV), (dict(tdt=2), INV),
+    (dict(B=0), INV), (dict(gamma=0), INV), (dict(R=4), INV), (dict(H=0), INV), (dict(Vt=0), INV),
+    (dict(V=1000), INV), (dict(Tt=0.0), INV), (dict(Td=math.nan), INV),
+    (dict(keep=NUL, f2t=NUL), INV), (dict(keep=NUL), INV), (dict(f2t=NUL), INV),
+    (dict(gamma=65, R=65), UNS), (dict(H=3070), UNS), (dict(hidden=P(0x100004)), UNS),
+    (dict(ws=NUL), WS), (dict(wsb=64), WS),
+])
+def test_block_rejects(kw, status):
+    assert blk(**kw) == status
+
+
+def test_block_workspace_sizes():
+    L = vt.lib()
+    small = L.vt_spec_block_workspace_bytes(1, 5, 6, 3072, 128256, 128256)
+    big = L.vt_spec_block_workspace_bytes(256, 8, 9, 4096, 65536, 128256)
+    assert 0 < small < big
+    assert L.vt_spec_block_workspace_bytes(1, 5, 4, 3072, 100, 100) == 0  # R < gamma
