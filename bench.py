@@ -184,7 +184,7 @@ def main():
     nacc = torch.empty(B, dtype=torch.int32, device="cuda")
     ws_sm_d = vt.softmax_workspace(M, cfg.Vt)
     ws_sm_t = vt.softmax_workspace(B * (g + 1), cfg.V)
-    ws_vf = vt.verify_workspace(B, cfg.V)
+    ws_vf = vt.verify_workspace(B, g, cfg.V)
     log(f"{n_sets} input sets on device ({bb / 1e6:.1f} MB algorithmic per step)")
 
     main = torch.cuda.current_stream()

@@ -54,7 +54,7 @@ def lib() -> ctypes.CDLL:
         L.vt_softmax_temp_workspace_bytes.restype = SZ
         L.vt_spec_verify.argtypes = [I64, I64, I64, I64, P, I, P, F, P, I64, P, F, P, P, P, P, P, P, P, P, SZ, P]
         L.vt_spec_verify.restype = I
-        L.vt_spec_verify_workspace_bytes.argtypes = [I64, I64]
+        L.vt_spec_verify_workspace_bytes.argtypes = [I64, I64, I64]
         L.vt_spec_verify_workspace_bytes.restype = SZ
         L.vt_spec_block.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I64, P, I, F, F, P, P, P, P, P, P, P, P, P,
                                     P, P, P, SZ, P]
@@ -117,9 +117,9 @@ def softmax_workspace(rows: int, n: int, device="cuda"):
     return _torch().empty(nbytes, dtype=_torch().uint8, device=device) if nbytes else None
 
 
-def verify_workspace(B: int, V: int, device="cuda"):
+def verify_workspace(B: int, gamma: int, V: int, device="cuda"):
     """A workspace for vt_spec_verify (None when the shape needs none)."""
-    nbytes = lib().vt_spec_verify_workspace_bytes(B, V)
+    nbytes = lib().vt_spec_verify_workspace_bytes(B, gamma, V)
     return _torch().empty(nbytes, dtype=_torch().uint8, device=device) if nbytes else None
 
 
@@ -167,11 +167,16 @@ def vt_softmax_temp(logits, temperature, lse, probs=None, u=None, sampled=None, 
 
 def vt_spec_verify(target_logits, target_lse, target_T, draft_logits, draft_lse, draft_T, draft_ids, keep_ids,
                    full_to_trim, u_accept, u_final, out_tokens, out_num_accepted, workspace=None):
-    """Modified rejection sampling; shapes: target [B, gamma+1, V], draft [B, R, Vt], ids [B, R]."""
+    """Modified rejection sampling; shapes: target [B, gamma+1, V], draft [B, R, Vt], ids [B, R].
+    target_T = 0: greedy verification (target_lse, draft_logits, draft_lse, u_accept, u_final may be None)."""
     torch = _torch()
     B, g1, V = target_logits.shape
     gamma = g1 - 1
-    Bd, R, Vt = draft_logits.shape
+    if draft_logits is not None:
+        Bd, R, Vt = draft_logits.shape
+    else:  # greedy verification (target_T = 0) reads no draft logits
+        Bd, R = draft_ids.shape
+        Vt = keep_ids.numel() if keep_ids is not None else V
     if Bd != B or tuple(draft_ids.shape) != (B, R) or tuple(out_tokens.shape) != (B, g1):
         raise ValueError("vt_spec_verify: shape mismatch")
     if target_logits.dtype == torch.float32:
@@ -180,12 +185,12 @@ def vt_spec_verify(target_logits, target_lse, target_T, draft_logits, draft_lse,
         _bits16(target_logits, "target_logits")
         dt = VT_BF16
     if workspace is None:
-        workspace = verify_workspace(B, V, target_logits.device)
+        workspace = verify_workspace(B, gamma, V, target_logits.device)
     wsb = workspace.numel() if workspace is not None else 0
     st = lib().vt_spec_verify(B, gamma, V, Vt, _ptr(target_logits, "target_logits"), dt,
                               _ptr(target_lse, "target_lse", torch.float64, B * g1), float(target_T),
                               _ptr(draft_logits, "draft_logits", torch.float32), R,
-                              _ptr(draft_lse, "draft_lse", torch.float64, B * R), float(draft_T),
+                              _ptr(draft_lse, "draft_lse", torch.float64, B * R), float(draft_T or 0.0),
                               _ptr(draft_ids, "draft_ids", torch.int32), _ptr(keep_ids, "keep_ids", torch.int32),
                               _ptr(full_to_trim, "full_to_trim", torch.int32, V),
                               _ptr(u_accept, "u_accept", torch.float32, B * gamma),

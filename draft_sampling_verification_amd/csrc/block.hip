@@ -52,7 +52,7 @@ BlockPlan plan_block(int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt,
   if (p.nchunk_v > 1) {
     off += align_up(static_cast<size_t>(B) * sizeof(int), 256);
     p.off_vpart = off;
-    off += align_up(static_cast<size_t>(B * p.nchunk_v) * sizeof(float2), 256);
+    off += align_up(static_cast<size_t>(B * (gamma + 1) * p.nchunk_v) * sizeof(float2), 256);
   }
   p.bytes = off;
   return p;

@@ -13,8 +13,9 @@ extern "C" vt_status_t vt_softmax_temp(const void *logits, vt_dtype_t dtype, int
   if (!logits || !lse) return VT_ERR_INVALID_ARG;
   if (dtype != VT_F32 && dtype != VT_BF16) return VT_ERR_INVALID_ARG;
   if (rows <= 0 || n <= 0 || ld < n) return VT_ERR_INVALID_ARG;
-  if (!finite_positive(temperature)) return VT_ERR_INVALID_ARG;
-  if ((u == nullptr) != (sampled == nullptr)) return VT_ERR_INVALID_ARG;
+  const bool greedy = temperature == 0.f;
+  if (!greedy && !finite_positive(temperature)) return VT_ERR_INVALID_ARG;
+  if (!greedy && (u == nullptr) != (sampled == nullptr)) return VT_ERR_INVALID_ARG;
   if (n > INT32_MAX) return VT_ERR_UNSUPPORTED;
   const int64_t nchunk = (n + kChunk - 1) / kChunk;
   if (nchunk > INT32_MAX || rows > INT64_MAX / nchunk || rows * nchunk > static_cast<int64_t>(UINT32_MAX))
@@ -27,11 +28,12 @@ extern "C" vt_status_t vt_softmax_temp(const void *logits, vt_dtype_t dtype, int
   P.rows = rows;
   P.n = n;
   P.ld = ld;
-  P.T = static_cast<double>(temperature);
-  P.k2 = static_cast<float>(1.4426950408889634 / static_cast<double>(temperature));
+  P.greedy = greedy;
+  P.T = greedy ? 1.0 : static_cast<double>(temperature);
+  P.k2 = greedy ? 0.f : static_cast<float>(1.4426950408889634 / static_cast<double>(temperature));
   P.lse = lse;
   P.probs = probs;
-  P.u = u;
+  P.u = greedy ? nullptr : u;
   P.sampled = sampled;
   P.nchunk = static_cast<int>(nchunk);
   P.chunk = kChunk;

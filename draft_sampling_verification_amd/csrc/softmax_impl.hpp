@@ -41,7 +41,31 @@ struct SmParams {
   float2 *part;     // (m_c, s_c) per (row, chunk)
   int nchunk;
   int chunk;        // elements per chunk of the partials (<= 4096); 4096 for this file's own partials
+  bool greedy;      // T = 0: argmax (lowest index on ties) instead of softmax; lse = row max
 };
+
+// Argmax of the thread's 16 elements starting at global index e0 (entries at e >= n never win).
+__device__ __forceinline__ void thread_argmax16(const float (&v)[16], int64_t e0, int64_t n, float &bv, int &bi) {
+  bv = kNegInf;
+  bi = kNoIndex;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const int64_t e = e0 + j;
+    if (e < n && argmax_better(v[j], static_cast<int>(e), bv, bi)) {
+      bv = v[j];
+      bi = static_cast<int>(e);
+    }
+  }
+}
+
+// T = 0 (greedy limit) outputs for row r with maximum M at index idx: lse = M, probs one-hot.
+__device__ __forceinline__ void greedy_outputs(const SmParams &P, int64_t r, float M, int idx) {
+  if (threadIdx.x == 0) {
+    P.lse[r] = static_cast<double>(M);
+    if (P.sampled) P.sampled[r] = idx;
+    if (P.rowstat) P.rowstat[r] = make_float2(M, __int_as_float(idx));
+  }
+}
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -97,6 +121,22 @@ __global__ __launch_bounds__(kBlock) void softmax_single(SmParams P) {
   const Tin *row = reinterpret_cast<const Tin *>(P.logits) + r * P.ld;
   float v[16], w[16];
   load16<Tin, kVec>(row, P.n, 0, v);
+  if (P.greedy) {
+    float bv;
+    int bi;
+    thread_argmax16(v, static_cast<int64_t>(threadIdx.x) * kPerThread, P.n, bv, bi);
+    block_argmax(bv, bi, redf, redi);
+    greedy_outputs(P, r, bv, bi);
+    if (P.probs) {
+      float *pr = P.probs + r * P.n;
+#pragma unroll
+      for (int j = 0; j < kPerThread; ++j) {
+        const int64_t e = static_cast<int64_t>(threadIdx.x) * kPerThread + j;
+        if (e < P.n) pr[e] = e == bi ? 1.f : 0.f;
+      }
+    }
+    return;
+  }
   float m = kNegInf;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) m = fmaxf(m, v[j]);
@@ -143,6 +183,16 @@ __global__ __launch_bounds__(kBlock) void softmax_partial(SmParams P) {
   const Tin *row = reinterpret_cast<const Tin *>(P.logits) + r * P.ld;
   float v[16], w[16];
   load16<Tin, kVec>(row, P.n, static_cast<int64_t>(c) * kChunk, v);
+  if (P.greedy) {
+    __shared__ int redi[kWavesPerBlock];
+    float bv;
+    int bi;
+    thread_argmax16(v, static_cast<int64_t>(c) * kChunk + static_cast<int64_t>(threadIdx.x) * kPerThread, P.n, bv,
+                    bi);
+    block_argmax(bv, bi, redf, redi);
+    if (threadIdx.x == 0) P.part[r * P.nchunk + c] = make_float2(bv, __int_as_float(bi));
+    return;
+  }
   float m = kNegInf;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) m = fmaxf(m, v[j]);
@@ -162,6 +212,20 @@ template <typename Tin, bool kVec>
 __device__ __forceinline__ void combine_row(const SmParams &P, int64_t r, float *redf, int *redi, float *bcast) {
   const Tin *row = reinterpret_cast<const Tin *>(P.logits) + r * P.ld;
   const float2 *part = P.part + r * P.nchunk;
+  if (P.greedy) {
+    float bv = kNegInf;
+    int bi = kNoIndex;
+    for (int k = threadIdx.x; k < P.nchunk; k += kBlock) {
+      const float2 pk = part[k];
+      if (argmax_better(pk.x, __float_as_int(pk.y), bv, bi)) {
+        bv = pk.x;
+        bi = __float_as_int(pk.y);
+      }
+    }
+    block_argmax(bv, bi, redf, redi);
+    greedy_outputs(P, r, bv, bi);
+    return;
+  }
   float mm = kNegInf;
   for (int k = threadIdx.x; k < P.nchunk; k += kBlock) mm = fmaxf(mm, part[k].x);
   const float M = block_max(mm, redf);
@@ -253,8 +317,18 @@ __global__ __launch_bounds__(kBlock) void softmax_probs(SmParams P) {
   const int c = static_cast<int>(bid - r * P.nchunk);
   const Tin *row = reinterpret_cast<const Tin *>(P.logits) + r * P.ld;
   float v[16], w[16];
-  load16<Tin, kVec>(row, P.n, static_cast<int64_t>(c) * kChunk, v);
   const float2 mz = P.rowstat[r];
+  if (P.greedy) {
+    const int64_t idx = __float_as_int(mz.y);
+    float *pr = P.probs + r * P.n;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int64_t e = static_cast<int64_t>(c) * kChunk + static_cast<int64_t>(threadIdx.x) * kPerThread + j;
+      if (e < P.n) pr[e] = e == idx ? 1.f : 0.f;
+    }
+    return;
+  }
+  load16<Tin, kVec>(row, P.n, static_cast<int64_t>(c) * kChunk, v);
   weights16(v, mz.x, P.k2, w);
   const float inv = 1.f / mz.y;
   float *pr = P.probs + r * P.n;

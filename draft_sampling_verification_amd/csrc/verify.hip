@@ -1,9 +1,9 @@
 // C entry points of the verifier; the kernels live in verify_impl.hpp.
 #include "verify_impl.hpp"
 
-extern "C" size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t V) {
-  if (B <= 0 || V <= 0) return 0;
-  return vt::vf_ws_layout(B, (V + vt::kChunk - 1) / vt::kChunk).bytes;
+extern "C" size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V) {
+  if (B <= 0 || gamma <= 0 || V <= 0) return 0;
+  return vt::vf_ws_layout(B, gamma, (V + vt::kChunk - 1) / vt::kChunk).bytes;
 }
 
 extern "C" vt_status_t vt_spec_verify(int64_t B, int64_t gamma, int64_t V, int64_t Vt, const void *target_logits,
@@ -14,19 +14,19 @@ extern "C" vt_status_t vt_spec_verify(int64_t B, int64_t gamma, int64_t V, int64
                                       int32_t *out_num_accepted, void *workspace, size_t workspace_bytes,
                                       hipStream_t stream) {
   using namespace vt;
-  if (!target_logits || !target_lse || !draft_logits || !draft_lse || !draft_ids || !u_accept || !u_final ||
-      !out_tokens || !out_num_accepted)
-    return VT_ERR_INVALID_ARG;
+  const bool greedy = target_T == 0.f;
+  if (!target_logits || !draft_ids || !out_tokens || !out_num_accepted) return VT_ERR_INVALID_ARG;
+  if (!greedy && (!target_lse || !draft_logits || !draft_lse || !u_accept || !u_final)) return VT_ERR_INVALID_ARG;
   if (target_dtype != VT_F32 && target_dtype != VT_BF16) return VT_ERR_INVALID_ARG;
   if (B <= 0 || gamma <= 0 || V <= 0 || Vt <= 0 || Vt > V || R < gamma) return VT_ERR_INVALID_ARG;
-  if (!finite_positive(target_T) || !finite_positive(draft_T)) return VT_ERR_INVALID_ARG;
+  if (!greedy && (!finite_positive(target_T) || !finite_positive(draft_T))) return VT_ERR_INVALID_ARG;
   if ((keep_ids == nullptr) != (full_to_trim == nullptr)) return VT_ERR_INVALID_ARG;
   if (!keep_ids && Vt != V) return VT_ERR_INVALID_ARG;
   if (gamma > kWave) return VT_ERR_UNSUPPORTED;
   if (V > INT32_MAX) return VT_ERR_UNSUPPORTED;
   const int64_t nchunk = (V + kChunk - 1) / kChunk;
   if (B > static_cast<int64_t>(UINT32_MAX) / nchunk) return VT_ERR_UNSUPPORTED;
-  const VFWsLayout L = vf_ws_layout(B, nchunk);
+  const VFWsLayout L = vf_ws_layout(B, gamma, nchunk);
   if (L.bytes > 0 && (!workspace || workspace_bytes < L.bytes)) return VT_ERR_WORKSPACE;
 
   VfParams P{};
@@ -44,10 +44,11 @@ extern "C" vt_status_t vt_spec_verify(int64_t B, int64_t gamma, int64_t V, int64
   P.V = V;
   P.Vt = Vt;
   P.R = R;
-  P.Tt = target_T;
-  P.Td = draft_T;
-  P.k2t = static_cast<float>(kLog2e / static_cast<double>(target_T));
-  P.k2d = static_cast<float>(kLog2e / static_cast<double>(draft_T));
+  P.greedy = greedy;
+  P.Tt = greedy ? 1.0 : target_T;
+  P.Td = greedy ? 1.0 : draft_T;
+  P.k2t = greedy ? 0.f : static_cast<float>(kLog2e / static_cast<double>(target_T));
+  P.k2d = greedy ? 0.f : static_cast<float>(kLog2e / static_cast<double>(draft_T));
   P.gamma = static_cast<int>(gamma);
   P.nchunk = static_cast<int>(nchunk);
   if (L.bytes > 0) {

@@ -44,6 +44,7 @@ struct VfParams {
   float k2t, k2d;  // log2(e) / T
   int gamma;
   int nchunk;
+  bool greedy;  // target_T = 0: accept iff the draft equals the target's argmax; final = argmax
 };
 
 // Per-row constants so that exp(x / T - lse) = 2^((x - c0) * k2 - d2) with c0 = lse * T in logit
@@ -234,6 +235,79 @@ __device__ __forceinline__ void finish_sequence(const VfParams &P, int64_t b, in
   if (threadIdx.x == 0) P.out_n[b] = n;
 }
 
+// ---- greedy mode (target temperature 0; "VocabTrim" §4: the target is decoded greedily, so a
+// draft token is kept only if it equals the target's most likely token; Appendix C.1, Algorithm
+// 2: on the first mismatch the target's own token is appended).  a[i] = argmax of target row i
+// (lowest id on ties); n = first i with keep[x_i] != a[i]; final = a[n].
+
+// Argmax of this workgroup's chunk c of target row (b, i).
+template <typename Tin, bool kVec>
+__device__ __forceinline__ void chunk_argmax(const VfParams &P, int64_t b, int i, int c, float &bv, int &bi,
+                                             float *redf, int *redi) {
+  const Tin *trow = reinterpret_cast<const Tin *>(P.target) + (b * (P.gamma + 1) + i) * P.V;
+  float v[16];
+  const int64_t e0 = static_cast<int64_t>(c) * kChunk + static_cast<int64_t>(threadIdx.x) * kPerThread;
+  load16<Tin, kVec>(trow, P.V, static_cast<int64_t>(c) * kChunk, v);
+  bv = kNegInf;
+  bi = kNoIndex;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j)
+    if (e0 + j < P.V && argmax_better(v[j], static_cast<int>(e0 + j), bv, bi)) {
+      bv = v[j];
+      bi = static_cast<int>(e0 + j);
+    }
+  block_argmax(bv, bi, redf, redi);
+}
+
+// Greedy decision and outputs of sequence b given the row argmaxes a[0..gamma] (in LDS).
+__device__ __forceinline__ void greedy_finish(const VfParams &P, int64_t b, const int *a, int *sh_n) {
+  const int gamma = P.gamma;
+  if (wave_id() == 0) {
+    const int i = lane_id();
+    bool valid = true, accept = true;
+    if (i < gamma) {
+      const int64_t x = P.ids[b * P.R + i];
+      valid = x >= 0 && x < P.Vt;
+      int64_t y = x;
+      if (valid && P.keep) {
+        y = P.keep[x];
+        valid = y >= 0 && y < P.V;
+      }
+      accept = valid && y == a[i];
+    }
+    const unsigned long long bad = __ballot(i < gamma && !valid);
+    const unsigned long long rej = __ballot(i < gamma && !accept);
+    if (i == 0) *sh_n = bad ? -1 : (rej ? __ffsll(static_cast<long long>(rej)) - 1 : gamma);
+  }
+  __syncthreads();
+  const int n = *sh_n;
+  int32_t *tok = P.out_tokens + b * (gamma + 1);
+  for (int i = threadIdx.x; i <= gamma; i += kBlock) {
+    int32_t v = -1;
+    if (n >= 0 && i < n) {
+      const int32_t x = P.ids[b * P.R + i];
+      v = P.keep ? P.keep[x] : x;
+    } else if (n >= 0 && i == n) {
+      v = a[n];
+    }
+    tok[i] = v;
+  }
+  if (threadIdx.x == 0) P.out_n[b] = n;
+}
+
+template <typename Tin, bool kVec>
+__device__ __forceinline__ void greedy_single(const VfParams &P, int64_t b, float *redf, int *redi, int *sh_n) {
+  __shared__ int a[kWave + 1];
+  for (int i = 0; i <= P.gamma; ++i) {
+    float bv;
+    int bi;
+    chunk_argmax<Tin, kVec>(P, b, i, 0, bv, bi, redf, redi);
+    if (threadIdx.x == 0) a[i] = bi;
+  }
+  __syncthreads();
+  greedy_finish(P, b, a, sh_n);
+}
+
 // Vocabularies of one chunk (V <= 4096): one workgroup per sequence does everything.
 template <typename Tin, bool kVec>
 __global__ __launch_bounds__(kBlock) void verify_single(VfParams P) {
@@ -242,6 +316,10 @@ __global__ __launch_bounds__(kBlock) void verify_single(VfParams P) {
   __shared__ int sh_n;
   __shared__ float bcast;
   const int64_t b = blockIdx.x;
+  if (P.greedy) {
+    greedy_single<Tin, kVec>(P, b, redf, redi, &sh_n);
+    return;
+  }
   const int n = accept_scan<Tin>(P, b, &sh_n);
   float sw = 0.f, sp = 0.f;
   if (n >= 0) {
@@ -269,6 +347,16 @@ __global__ __launch_bounds__(kBlock) void verify_partial(VfParams P) {
   const int64_t bid = blockIdx.x;
   const int64_t b = bid / P.nchunk;
   const int c = static_cast<int>(bid - b * P.nchunk);
+  if (P.greedy) {
+    __shared__ int redi[kWavesPerBlock];
+    for (int i = 0; i <= P.gamma; ++i) {
+      float bv;
+      int bi;
+      chunk_argmax<Tin, kVec>(P, b, i, c, bv, bi, redf, redi);
+      if (threadIdx.x == 0) P.part[(b * (P.gamma + 1) + i) * P.nchunk + c] = make_float2(bv, __int_as_float(bi));
+    }
+    return;
+  }
   const int n = accept_scan<Tin>(P, b, &sh_n);
   float sw = 0.f, sp = 0.f;
   if (n >= 0) {
@@ -295,6 +383,27 @@ __global__ __launch_bounds__(kBlock) void verify_final(VfParams P) {
   __shared__ int redi[kWavesPerBlock];
   __shared__ float bcast;
   const int64_t b = blockIdx.x;
+  if (P.greedy) {
+    __shared__ int a[kWave + 1];
+    __shared__ int sh_n;
+    for (int i = 0; i <= P.gamma; ++i) {
+      const float2 *pr = P.part + (b * (P.gamma + 1) + i) * P.nchunk;
+      float bv = kNegInf;
+      int bi = kNoIndex;
+      for (int k = threadIdx.x; k < P.nchunk; k += kBlock) {
+        const float2 pk = pr[k];
+        if (argmax_better(pk.x, __float_as_int(pk.y), bv, bi)) {
+          bv = pk.x;
+          bi = __float_as_int(pk.y);
+        }
+      }
+      block_argmax(bv, bi, redf, redi);
+      if (threadIdx.x == 0) a[i] = bi;
+    }
+    __syncthreads();
+    greedy_finish(P, b, a, &sh_n);
+    return;
+  }
   const int n = P.nbuf[b];
   const float2 *part = P.part + b * P.nchunk;
   auto mass = [&](int k, bool use_p) -> float {
@@ -309,12 +418,16 @@ struct VFWsLayout {
   size_t nbuf, part, bytes;
 };
 
-VFWsLayout vf_ws_layout(int64_t B, int64_t nchunk) {
+// pass-1 results: n per sequence, and per (sequence, chunk) sums (sampling) or per (sequence,
+// row, chunk) argmaxes (greedy): sized for the larger of the two.
+VFWsLayout vf_ws_layout(int64_t B, int64_t gamma, int64_t nchunk) {
   VFWsLayout L{};
   if (nchunk <= 1) return L;
   L.nbuf = 0;
   L.part = align_up(static_cast<size_t>(B) * sizeof(int), 256);
-  L.bytes = L.part + align_up(static_cast<size_t>(B) * static_cast<size_t>(nchunk) * sizeof(float2), 256);
+  L.bytes = L.part +
+            align_up(static_cast<size_t>(B) * static_cast<size_t>(gamma + 1) * static_cast<size_t>(nchunk) * sizeof(float2),
+                     256);
   return L;
 }
 

@@ -110,6 +110,43 @@ __device__ __forceinline__ int block_max_int(int v, int *red) {
   return t;
 }
 
+// Argmax with ties to the lowest index (padding carries index INT_MAX, so it never wins a tie).
+constexpr int kNoIndex = 0x7fffffff;
+__device__ __forceinline__ bool argmax_better(float v1, int i1, float v2, int i2) {
+  return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+__device__ __forceinline__ void wave_argmax(float &v, int &i) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const float v2 = __shfl_xor(v, o, kWave);
+    const int i2 = __shfl_xor(i, o, kWave);
+    if (argmax_better(v2, i2, v, i)) {
+      v = v2;
+      i = i2;
+    }
+  }
+}
+
+// Workgroup argmax (all threads call; result broadcast).  redv/redi: LDS scratch of 4 entries.
+__device__ __forceinline__ void block_argmax(float &v, int &i, float *redv, int *redi) {
+  wave_argmax(v, i);
+  __syncthreads();
+  if (lane_id() == 0) {
+    redv[wave_id()] = v;
+    redi[wave_id()] = i;
+  }
+  __syncthreads();
+  v = redv[0];
+  i = redi[0];
+#pragma unroll
+  for (int w = 1; w < kWavesPerBlock; ++w)
+    if (argmax_better(redv[w], redi[w], v, i)) {
+      v = redv[w];
+      i = redi[w];
+    }
+}
+
 // Inclusive prefix over the workgroup's threads in thread order.  Returns this thread's
 // inclusive value; *prev receives the previous thread's inclusive value (0 for thread 0) and
 // *total the last thread's, each formed by the very same floating-point operations as the value

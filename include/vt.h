@@ -101,8 +101,11 @@ vt_status_t vt_lmhead_trimmed(const uint16_t *hidden, const uint16_t *weight, co
  *   probs   optional (NULL), fp32 [rows][n]
  *   u       optional (NULL), fp32 [rows] in (0, 1]; sampled must be non-NULL exactly when u is
  *   workspace / workspace_bytes: see vt_softmax_temp_workspace_bytes
- *   Errors: INVALID_ARG for NULL logits/lse, rows or n <= 0, ld < n, T not finite or <= 0,
- *   exactly one of u/sampled NULL, an unknown dtype; WORKSPACE if the workspace is too small.
+ *   T = 0 is the greedy limit ([VT] §4 decodes the target greedily): sampled[r] (if non-NULL) is
+ *   the index of the row maximum, the lowest such index on ties; lse[r] holds the row maximum
+ *   (the limit of T * logsumexp(x / T)); probs is one-hot at sampled[r]; u is not read.
+ *   Errors: INVALID_ARG for NULL logits/lse, rows or n <= 0, ld < n, T not finite or < 0,
+ *   exactly one of u/sampled NULL (T > 0), an unknown dtype; WORKSPACE if the workspace is too small.
  */
 vt_status_t vt_softmax_temp(const void *logits, vt_dtype_t dtype, int64_t rows, int64_t n, int64_t ld,
                             float temperature, double *lse, float *probs, const float *u, int32_t *sampled,
@@ -127,6 +130,10 @@ size_t vt_softmax_temp_workspace_bytes(int64_t rows, int64_t n);
  *        rule of vt_softmax_temp over full ids, in fixed 4096-id chunks;
  *     3. out_tokens[b] = { y_0 .. y_{n-1}, final, -1 ... } (gamma+1 entries), out_num_accepted[b] = n.
  *   The accept ratio is evaluated in fp64 from the fp32/bf16 logits and the fp64 lse.
+ *   target_T = 0 selects greedy verification ([VT] §4, App. C.1 Algorithm 2 under greedy
+ *   decoding): accept iff y_i == a_i, the lowest id of target row i's maximum; final = a_n (a_gamma
+ *   after full acceptance); target_lse, draft_logits, draft_lse, draft_T, u_accept and u_final
+ *   are not read (may be NULL).
  *   A draft id outside [0, Vt) (or mapping outside [0, V)) among the first gamma makes that
  *   sequence's out_num_accepted -1 and all its tokens -1; this is checked on the device.
  *
@@ -139,8 +146,8 @@ size_t vt_softmax_temp_workspace_bytes(int64_t rows, int64_t n);
  *   u_accept      fp32 [B][gamma];  u_final fp32 [B]
  *   out_tokens    int32 [B][gamma+1];  out_num_accepted int32 [B]
  *   Errors: INVALID_ARG for NULL required pointers, B, gamma, V, Vt <= 0, Vt > V, R < gamma,
- *   a temperature not finite or <= 0, keep_ids/full_to_trim NULL with Vt < V or only one of them
- *   NULL; UNSUPPORTED for gamma > 64; WORKSPACE if the workspace is too small.
+ *   a temperature not finite or <= 0 (target_T > 0), keep_ids/full_to_trim NULL with Vt < V or
+ *   only one of them NULL; UNSUPPORTED for gamma > 64; WORKSPACE if the workspace is too small.
  */
 vt_status_t vt_spec_verify(int64_t B, int64_t gamma, int64_t V, int64_t Vt, const void *target_logits,
                            vt_dtype_t target_dtype, const double *target_lse, float target_T,
@@ -150,8 +157,8 @@ vt_status_t vt_spec_verify(int64_t B, int64_t gamma, int64_t V, int64_t Vt, cons
                            int32_t *out_num_accepted, void *workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
-/* Bytes of workspace vt_spec_verify needs for B sequences over a V-id vocabulary. */
-size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t V);
+/* Bytes of workspace vt_spec_verify needs for B sequences of gamma drafts over a V-id vocabulary. */
+size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
 
 /*
  * vt_spec_block -- one whole speculative block in one call: the trimmed LM head, the draft
@@ -173,6 +180,7 @@ size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t V);
  *   chunked by the LM head's row blocks (ceil(Vt / 256) rounded up to a multiple of 4 rows) instead
  *   of 4096-element chunks: draws can differ from the separate calls only where a CDF boundary lies
  *   within rounding of the uniform.
+ *   Both temperatures must be > 0 (greedy decoding: use the separate calls with T = 0).
  *   Errors: INVALID_ARG for NULL required pointers, B, gamma, H, V or Vt <= 0, R < gamma, Vt > V,
  *   a temperature not finite or <= 0, keep_ids/full_to_trim inconsistent with Vt; UNSUPPORTED for
  *   gamma > 64, H % 8 != 0 or a hidden/weight base not 16-byte aligned; WORKSPACE if the workspace

@@ -241,3 +241,38 @@ def toy_block(target_table, draft_table, T, gamma: int, u_draft, u_acc, u_fin, c
         acc_m.append(m)
     return dict(tokens=tokens, n=n, draft_ids=ids, draft_margins=dmarg, accept_ratios=acc_m,
                 final_margin=fin_m)
+
+
+# ---------------------------------------------------------------- greedy verification
+
+def argmax_lowest(row) -> int:
+    """Index of the largest entry, the lowest such index on ties."""
+    row = np.asarray(row, dtype=np.float64)
+    return int(np.flatnonzero(row == row.max())[0])
+
+
+def greedy_verify(target_logits, draft_ids, keep_ids, gamma: int):
+    """Greedy verification of B sequences ([VT] §4: the target is decoded greedily, so a draft
+    token is accepted only if it equals the target's most likely token; [VT] Appendix C.1,
+    Algorithm 2: on the first mismatch the target's own token is appended and the block ends).
+    READING: ties go to the lowest id; after gamma accepted drafts the target's most likely token
+    at position gamma is appended (the bonus of the sampling rule, in its greedy limit).
+    target_logits [B, gamma+1, V] (any temperature: the argmax does not depend on it);
+    draft_ids [B, R] trimmed ids; keep_ids [Vt] or None.
+    Returns (tokens int64 [B, gamma+1] padded with -1, n int64 [B])."""
+    t = np.asarray(target_logits, dtype=np.float64)
+    B = t.shape[0]
+    tokens = np.full((B, gamma + 1), -1, dtype=np.int64)
+    n = np.empty(B, dtype=np.int64)
+    for b in range(B):
+        k = gamma
+        for i in range(gamma):
+            x = int(draft_ids[b, i])
+            y = x if keep_ids is None else int(keep_ids[x])
+            if y != argmax_lowest(t[b, i]):
+                k = i
+                break
+            tokens[b, i] = y
+        tokens[b, k] = argmax_lowest(t[b, k])
+        n[b] = k
+    return tokens, n

@@ -61,10 +61,11 @@ def test_workspace_sizes():
     assert L.vt_softmax_temp_workspace_bytes(6, 4097) > 0
     big = L.vt_softmax_temp_workspace_bytes(2304, 128256)
     assert big >= 2304 * 32 * 8
-    assert L.vt_spec_verify_workspace_bytes(1, 18) == 0
-    assert L.vt_spec_verify_workspace_bytes(256, 128256) >= 256 * 32 * 8
+    assert L.vt_spec_verify_workspace_bytes(1, 4, 18) == 0
+    assert L.vt_spec_verify_workspace_bytes(256, 8, 128256) >= 256 * 9 * 32 * 8  # greedy: per target row
+    assert L.vt_spec_verify_workspace_bytes(4, 0, 128256) == 0
     assert L.vt_softmax_temp_workspace_bytes(0, 10) == 0
-    assert L.vt_spec_verify_workspace_bytes(-1, 10) == 0
+    assert L.vt_spec_verify_workspace_bytes(-1, 3, 10) == 0
 
 
 # ------------------------------------------------------------------ vt_lmhead_trimmed
@@ -96,7 +97,7 @@ def sm(logits=A, dtype=F32, rows=6, n=128256, ld=None, T=1.0, lse=A, probs=NUL, 
 @pytest.mark.parametrize("kw,status", [
     (dict(logits=NUL), INV), (dict(lse=NUL), INV), (dict(dtype=7), INV),
     (dict(rows=0), INV), (dict(n=0), INV), (dict(n=10, ld=9), INV),
-    (dict(T=0.0), INV), (dict(T=-1.0), INV), (dict(T=math.nan), INV), (dict(T=math.inf), INV),
+    (dict(T=-1.0), INV), (dict(T=math.nan), INV), (dict(T=math.inf), INV), (dict(T=-0.0 - 1e-30), INV),
     (dict(u=A), INV), (dict(sampled=A), INV),            # u and sampled come together
     (dict(ws=NUL), WS), (dict(wsb=16), WS),
 ])
@@ -123,7 +124,8 @@ def vf(B=4, gamma=5, V=128256, Vt=32768, target=A, tdt=F32, tlse=A, Tt=1.0, draf
     (dict(tdt=3), INV), (dict(B=0), INV), (dict(gamma=0), INV), (dict(V=0), INV), (dict(Vt=0), INV),
     (dict(Vt=200000), INV),                              # more kept ids than the vocabulary
     (dict(R=4), INV),                                    # fewer draft rows than drafts
-    (dict(Tt=0.0), INV), (dict(Td=-0.5), INV), (dict(Tt=math.nan), INV), (dict(Td=math.inf), INV),
+    (dict(Tt=-1.0), INV), (dict(Td=-0.5), INV), (dict(Tt=math.nan), INV), (dict(Td=math.inf), INV),
+    (dict(Tt=0.0, ids=NUL), INV),                        # greedy still needs the draft ids
     (dict(keep=NUL, f2t=NUL), INV),                      # trimmed head without the id maps
     (dict(keep=NUL), INV), (dict(f2t=NUL), INV),         # only one of the two maps
     (dict(gamma=65, R=66), UNS),

@@ -261,7 +261,7 @@ def test_determinism_and_batch_independence():
 
 def test_workspace_reuse_across_calls():
     # a workspace carries nothing between calls: reuse one buffer for differently shaped calls
-    wsz = vt.verify_workspace(64, 20000)
+    wsz = vt.verify_workspace(64, 7, 20000)
     cfg = SCALED["c3-trimmed"]
     for B in (3, 1, 5):
         wl = make_workload(cfg.scaled(B=B), aligned=True)
