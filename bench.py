@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--traffic-record", nargs=4, metavar="CSV",
+                    help="bench FETCH_SIZE, bench WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE counter csv "
+                         "files from rocprofv3 --pmc: write the LM-head traffic record for --config")
     ap.add_argument("--calls", action="store_true",
                     help="run the step as the four separate calls instead of the fused vt_spec_block")
     ap.add_argument("--overlap", action="store_true",
@@ -83,10 +86,17 @@ def block_bytes(cfg) -> int:
     return lm + draft_sm + target_sm + verify
 
 
+LMHEAD_SOURCES = ("lmhead_impl.hpp", "vt_common.hpp", "block.hip")
+
+
 def kernel_source_hash() -> str:
-    path = os.path.join(ROOT, "draft_sampling_verification_amd", "csrc", "lmhead.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """Hash of every source the timed LM-head kernel is compiled from (a traffic record taken on
+    other code does not describe this one)."""
+    h = hashlib.sha256()
+    for name in LMHEAD_SOURCES:
+        with open(os.path.join(ROOT, "draft_sampling_verification_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload_key: str):
@@ -100,6 +110,71 @@ def measured_traffic(workload_key: str):
     if rec.get("lmhead_source_sha256") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _pmc_rows(csv_path, counter):
+    import csv
+    with open(csv_path, newline="") as f:
+        return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in csv.DictReader(f)
+                if r["Counter_Name"] == counter]
+
+
+def write_traffic_record(config: int, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv) -> str:
+    """Turn two `rocprofv3 --pmc` passes over this bench (FETCH_SIZE, then WRITE_SIZE) and the same
+    two over --copy-calibration into profiles/lmhead_traffic_config<C>.json: HBM bytes per launch of
+    the LM-head kernel the timed loop runs (the most frequent lmhead_* kernel), each counter scaled
+    by what it reads for a copy of known size."""
+    from collections import Counter
+
+    from workloads import CONFIGS
+
+    def lm_avg(path, counter):
+        rows = [(k, v) for k, v in _pmc_rows(path, counter) if "lmhead_" in k]
+        name = Counter(k for k, _ in rows).most_common(1)[0][0]
+        vals = [v for k, v in rows if k == name]
+        return name, sum(vals) / len(vals), len(vals)
+
+    def copy_avg(path, counter):
+        vals = [v for k, v in _pmc_rows(path, counter) if "AUnaryFunctor" in k]
+        return sum(vals) / len(vals)
+
+    cfg = CONFIGS[config]
+    kname, fetch_kib, nf = lm_avg(fetch_csv, "FETCH_SIZE")
+    kname_w, write_kib, nw = lm_avg(write_csv, "WRITE_SIZE")
+    assert kname == kname_w, (kname, kname_w)
+    n = 1 << 30
+    cf, cw = copy_avg(copy_fetch_csv, "FETCH_SIZE"), copy_avg(copy_write_csv, "WRITE_SIZE")
+    fs, wsc = n / (cf * 1024), n / (cw * 1024)
+    M = cfg.B * cfg.R
+    alg_w = M * cfg.Vt * 4
+    rec = {
+        "kernel": kname.replace("void vt::(anonymous namespace)::", "").strip('"')[:160],
+        "workload": cfg.name,
+        "lmhead_source_sha256": kernel_source_hash(),
+        "fetch_size_kib_per_launch_raw": fetch_kib, "write_size_kib_per_launch_raw": write_kib,
+        "launches_sampled": [nf, nw],
+        "copy_calibration": {"bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                             "fetch_size_kib_raw": cf, "write_size_kib_raw": cw,
+                             "fetch_scale": fs, "write_scale": wsc},
+        "hbm_fetch_bytes_per_launch": round(fetch_kib * 1024 * fs),
+        "hbm_write_bytes_per_launch": round(write_kib * 1024 * wsc),
+        "algorithmic_read_bytes": lmhead_bytes(cfg) - alg_w, "algorithmic_write_bytes": alg_w,
+        "commands": [
+            f"rocprofv3 --pmc FETCH_SIZE -f csv -d <out> -o bench -- python3 bench.py --config {config} "
+            "--no-cpu-baseline --steps 10 --warmup 3",
+            f"rocprofv3 --pmc WRITE_SIZE -f csv -d <out> -o bench -- python3 bench.py --config {config} "
+            "--no-cpu-baseline --steps 10 --warmup 3",
+            "rocprofv3 --pmc FETCH_SIZE -f csv -d <out> -o copy -- python3 bench.py --copy-calibration",
+            "rocprofv3 --pmc WRITE_SIZE -f csv -d <out> -o copy -- python3 bench.py --copy-calibration",
+            f"python3 bench.py --config {config} --traffic-record <4 csv files>"],
+    }
+    rec["hbm_bytes_per_launch"] = rec["hbm_fetch_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
+    rec["traffic_over_algorithmic"] = round(rec["hbm_bytes_per_launch"] / lmhead_bytes(cfg), 4)
+    out = os.path.join(ROOT, "profiles", f"lmhead_traffic_config{config}.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return out
 
 
 def copy_calibration():
@@ -146,6 +221,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.traffic_record:
+        print(write_traffic_record(args.config, *args.traffic_record))
         return
 
     import torch

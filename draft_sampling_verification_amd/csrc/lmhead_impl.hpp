@@ -259,16 +259,6 @@ __global__ __launch_bounds__(kBlock) void lmhead_gemv(const uint16_t *__restrict
 constexpr int kBM = 128, kBN = 128, kBK = 32, kLdsPad = 8;
 constexpr int kLdsRow = kBK + kLdsPad;  // bf16 elements per LDS row (80 bytes)
 
-// Workgroups are handed to the 8 XCDs round-robin; remap so that each XCD works on a
-// contiguous range of logical tiles (consecutive tiles share a weight tile in that XCD's L2).
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-  constexpr int kXcd = 8;
-  const int per = (nblocks + kXcd - 1) / kXcd;
-  const int tall = nblocks % kXcd == 0 ? kXcd : nblocks % kXcd;
-  const int xcd = bid % kXcd, local = bid / kXcd;
-  return xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
-}
-
 __global__ __launch_bounds__(kBlock) void lmhead_mfma(const uint16_t *__restrict__ hidden,
                                                       const uint16_t *__restrict__ weight,
                                                       const int32_t *__restrict__ keep, int M, int H, int Vt,
@@ -278,7 +268,7 @@ __global__ __launch_bounds__(kBlock) void lmhead_mfma(const uint16_t *__restrict
 
   const int nbm = (M + kBM - 1) / kBM;
   const int nbn = (Vt + kBN - 1) / kBN;
-  const int tile = xcd_remap(blockIdx.x, nbm * nbn);
+  const int tile = static_cast<int>(xcd_remap(blockIdx.x, static_cast<int64_t>(nbm) * nbn));
   const int bm = tile % nbm, bn = tile / nbm;
   const int m0 = bm * kBM, n0 = bn * kBN;
 

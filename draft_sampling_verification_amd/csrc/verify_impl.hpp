@@ -344,7 +344,9 @@ template <typename Tin, bool kVec>
 __global__ __launch_bounds__(kBlock) void verify_partial(VfParams P) {
   __shared__ float redf[kWavesPerBlock];
   __shared__ int sh_n;
-  const int64_t bid = blockIdx.x;
+  // all chunks of a sequence on one XCD: its draft row (gathered through full_to_trim) stays in
+  // that XCD's L2 instead of being fetched from the last-level cache for every random read
+  const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t b = bid / P.nchunk;
   const int c = static_cast<int>(bid - b * P.nchunk);
   if (P.greedy) {

@@ -110,6 +110,18 @@ __device__ __forceinline__ int block_max_int(int v, int *red) {
   return t;
 }
 
+// Workgroups are handed to the 8 XCDs of the device round-robin (workgroup i runs on XCD i % 8).
+// xcd_remap returns a logical index such that each XCD works through one contiguous range of
+// logical indices, so workgroups that share data (a weight tile, a sequence's rows) can be given
+// neighbouring logical indices and meet in one XCD's L2.
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblocks) {
+  constexpr int64_t kXcd = 8;
+  const int64_t per = (nblocks + kXcd - 1) / kXcd;
+  const int64_t tall = nblocks % kXcd == 0 ? kXcd : nblocks % kXcd;
+  const int64_t xcd = bid % kXcd, local = bid / kXcd;
+  return xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
+}
+
 // Argmax with ties to the lowest index (padding carries index INT_MAX, so it never wins a tie).
 constexpr int kNoIndex = 0x7fffffff;
 __device__ __forceinline__ bool argmax_better(float v1, int i1, float v2, int i2) {
