@@ -13,6 +13,7 @@ from .gen import (  # noqa: F401
     bf16_round,
     counter_uniforms,
     make_workload,
+    token_stream,
     toy_tables,
     zipf_ranking,
 )

@@ -11,6 +11,7 @@ Streams (numpy SeedSequence entropy = [key..., stream]):
   3  target-logit noise ~ N(0, 2)                  (keyed by model id, per sequence)
   4  u_draft, 5 u_accept, 6 u_final                (counter-based, keyed by config id)
   7  toy target table, 8 toy context-free unigram  (keyed by config id)
+  9  calibration token stream (Zipf ranks)          (keyed by V and a stream seed)
 
 Per-sequence streams make sequence b's inputs independent of the batch size B.
 
@@ -156,6 +157,28 @@ def target_logits(cfg: Config, b0: int, B: int) -> np.ndarray:
     return out
 
 
+@functools.lru_cache(maxsize=2)
+def _zipf_rank_cdf(V: int, s: float) -> np.ndarray:
+    w = np.arange(1, V + 1, dtype=np.float64) ** -s
+    c = np.cumsum(w)
+    return c / c[-1]
+
+
+def token_stream(V: int, n: int, seed: int = 0, s: float = 1.1, chunk: int = 1 << 22) -> np.ndarray:
+    """int32 [n] token ids of a synthetic calibration corpus: ranks drawn from a Zipf(s) law over
+    1..V (P(rank r) proportional to r**-s), mapped to ids through the same seeded permutation
+    that ranks the target logits, so frequent ids here are the ids the target favours."""
+    perm, _ = zipf_ranking(V)
+    cdf = _zipf_rank_cdf(V, s)
+    rng = _rng(V, 9, seed)
+    out = np.empty(n, dtype=np.int32)
+    for i in range(0, n, chunk):
+        u = rng.random(min(chunk, n - i))
+        r = np.minimum(np.searchsorted(cdf, u, side="right"), V - 1)
+        out[i:i + len(u)] = perm[r]
+    return out
+
+
 @dataclasses.dataclass
 class ToyTables:
     """Order-1 toy: rows are contexts (row 0 = start-of-sequence, never emitted), columns tokens."""
@@ -192,7 +215,7 @@ class Workload:
     T: np.float32
     hidden: Optional[np.ndarray] = None  # bf16 bits [B*R, H]
     weight: Optional[np.ndarray] = None  # bf16 bits [V, H], the full head
-    keep_ids: Optional[np.ndarray] = None  # int32 [Vt], rank order; None for the full head
+    keep_ids: Optional[np.ndarray] = None  # int32 [Vt]; None for the full head
     full_to_trim: Optional[np.ndarray] = None  # int32 [V], -1 off the kept set
     target: Optional[np.ndarray] = None  # [B, gamma+1, V] f32 or bf16 bits
     draft_logits: Optional[np.ndarray] = None  # f32 [B*R, Vt]; only for the aligned variant
@@ -202,22 +225,32 @@ class Workload:
     u_fin: Optional[np.ndarray] = None  # f32 [B]
 
 
-def keep_set(cfg: Config):
-    """keep_ids = the Vt best-ranked ids, in rank order, and the inverse map (or None, None)."""
+def keep_set(cfg: Config, order: str = "id"):
+    """keep_ids = the Vt best-ranked ids and the inverse map (or None, None).
+
+    order "id": the kept ids in ascending id order (the storage order of a trimmed head built
+    by a sorted row gather); "rank": in rank order, best first.
+    """
     if not cfg.trimmed:
         return None, None
     perm, _ = zipf_ranking(cfg.V)
     keep = np.ascontiguousarray(perm[: cfg.Vt], dtype=np.int32)
+    if order == "id":
+        keep = np.sort(keep)
+    elif order != "rank":
+        raise ValueError(order)
     inv = np.full(cfg.V, -1, dtype=np.int32)
     inv[keep] = np.arange(cfg.Vt, dtype=np.int32)
     return keep, inv
 
 
-def make_workload(cfg: Config, B: Optional[int] = None, b0: int = 0, aligned: bool = False) -> Workload:
+def make_workload(cfg: Config, B: Optional[int] = None, b0: int = 0, aligned: bool = False,
+                  keep_order: str = "id") -> Workload:
     """Inputs for sequences b0 .. b0+B-1 of a config.
 
     aligned=True replaces the LM head by draft logits equal to the target logits gathered at
     keep_ids (same temperature): q is then p restricted to the kept set and renormalised.
+    keep_order: storage order of the kept ids ("id" ascending, or "rank").
     """
     B = cfg.B if B is None else B
     wl = Workload(cfg=cfg, b0=b0, B=B, T=np.float32(cfg.T))
@@ -227,7 +260,7 @@ def make_workload(cfg: Config, B: Optional[int] = None, b0: int = 0, aligned: bo
     if cfg.H == 0:
         wl.toy = toy_tables(cfg)
         return wl
-    wl.keep_ids, wl.full_to_trim = keep_set(cfg)
+    wl.keep_ids, wl.full_to_trim = keep_set(cfg, keep_order)
     wl.target = target_logits(cfg, b0, B)
     if aligned:
         t32 = wl.target if cfg.target_dtype == "f32" else bf16_bits_to_f32(wl.target)
