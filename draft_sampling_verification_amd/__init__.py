@@ -14,6 +14,10 @@ Entry points (same names as the C ABI):
   vt_spec_block(hidden, weight, keep_ids, full_to_trim, target_logits, target_T, draft_T, u_draft, u_accept,
                 u_final, draft_logits, draft_lse, draft_ids, target_lse, out_tokens, out_num_accepted,
                 workspace=None, lmhead_events=None)
+Keep-set construction (include/vt_keepset.h):
+  vt_token_histogram(tokens, V, counts, accumulate=False, workspace=None)
+  vt_keep_select(counts, rule, keep_ids, full_to_trim, num_kept, k=0, p=0.0, min_count=0)
+  vt_trim_head(weight, keep_ids, trimmed)
 Helpers: softmax_workspace(rows, n), verify_workspace(B, V), block_workspace(...), lib() (the raw ctypes handle).
 """
 from __future__ import annotations
@@ -61,6 +65,14 @@ def lib() -> ctypes.CDLL:
         L.vt_spec_block.restype = I
         L.vt_spec_block_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I64]
         L.vt_spec_block_workspace_bytes.restype = SZ
+        L.vt_token_histogram.argtypes = [P, I64, I64, I, P, P, SZ, P]
+        L.vt_token_histogram.restype = I
+        L.vt_token_histogram_workspace_bytes.argtypes = [I64, I64]
+        L.vt_token_histogram_workspace_bytes.restype = SZ
+        L.vt_keep_select.argtypes = [P, I64, I, I64, ctypes.c_double, ctypes.c_uint32, P, P, P, P]
+        L.vt_keep_select.restype = I
+        L.vt_trim_head.argtypes = [P, I64, I64, P, I64, P, P]
+        L.vt_trim_head.restype = I
         L.vt_status_string.argtypes = [I]
         L.vt_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -68,7 +80,10 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTED = ("vt_lmhead_trimmed", "vt_softmax_temp", "vt_softmax_temp_workspace_bytes", "vt_spec_verify",
-            "vt_spec_verify_workspace_bytes", "vt_spec_block", "vt_spec_block_workspace_bytes", "vt_status_string")
+            "vt_spec_verify_workspace_bytes", "vt_spec_block", "vt_spec_block_workspace_bytes", "vt_status_string",
+            "vt_token_histogram", "vt_token_histogram_workspace_bytes", "vt_keep_select", "vt_trim_head")
+
+VT_SELECT_TOP_K, VT_SELECT_TOP_P, VT_SELECT_MIN_FREQ = range(3)
 
 
 def _torch():
@@ -249,3 +264,57 @@ def vt_spec_block(hidden, weight, keep_ids, full_to_trim, target_logits, target_
                              ev0, ev1, _ptr(workspace, "workspace"), wsb, _stream())
     _check("vt_spec_block", st)
     return out_tokens, out_num_accepted
+
+
+# ---------------------------------------------------------------- keep-set construction
+
+def histogram_workspace(n: int, V: int, device="cuda"):
+    """A workspace for vt_token_histogram (None when the shape needs none)."""
+    nbytes = lib().vt_token_histogram_workspace_bytes(n, V)
+    return _torch().empty(nbytes, dtype=_torch().uint8, device=device) if nbytes else None
+
+
+def vt_token_histogram(tokens, V: int, counts, accumulate: bool = False, workspace=None):
+    """counts[V] (uint32 storage: int32 or uint32 tensor) = (counts +) occurrences of each id in tokens."""
+    torch = _torch()
+    n = tokens.numel()
+    if workspace is None:
+        workspace = histogram_workspace(n, V, tokens.device)
+    if counts.numel() != V or counts.dtype not in (torch.int32, torch.uint32):
+        raise ValueError("vt_token_histogram: counts must hold V 32-bit entries")
+    ws = _ptr(workspace, "workspace") if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().vt_token_histogram(_ptr(tokens, "tokens", torch.int32) if n else None, n, V, 1 if accumulate else 0,
+                                  _ptr(counts, "counts"), ws, wsb, _stream())
+    _check("vt_token_histogram", st)
+    return counts
+
+
+def vt_keep_select(counts, rule: int, keep_ids, full_to_trim, num_kept, k: int = 0, p: float = 0.0,
+                   min_count: int = 0):
+    """Kept ids (ascending) into keep_ids[:K], the inverse map into full_to_trim, K into num_kept[0]."""
+    torch = _torch()
+    V = counts.numel()
+    if counts.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("vt_keep_select: counts must be 32-bit")
+    st = lib().vt_keep_select(_ptr(counts, "counts"), V, rule, k, p, min_count,
+                              _ptr(keep_ids, "keep_ids", torch.int32, V),
+                              _ptr(full_to_trim, "full_to_trim", torch.int32, V),
+                              _ptr(num_kept, "num_kept", torch.int32, 1), _stream())
+    _check("vt_keep_select", st)
+    return num_kept
+
+
+def vt_trim_head(weight, keep_ids, trimmed):
+    """trimmed[k, H] = weight[keep_ids] (bf16 rows)."""
+    torch = _torch()
+    _bits16(weight, "weight")
+    _bits16(trimmed, "trimmed")
+    V_rows, H = weight.shape
+    k = keep_ids.numel()
+    if tuple(trimmed.shape) != (k, H):
+        raise ValueError("vt_trim_head: shape mismatch")
+    st = lib().vt_trim_head(_ptr(weight, "weight"), V_rows, H, _ptr(keep_ids, "keep_ids", torch.int32), k,
+                            _ptr(trimmed, "trimmed"), _stream())
+    _check("vt_trim_head", st)
+    return trimmed

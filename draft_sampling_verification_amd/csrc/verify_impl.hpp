@@ -73,10 +73,15 @@ __device__ __forceinline__ float load_logit(const Tin *row, int64_t i) {
 }
 
 // Weights of the final draw for this thread's 16 ids of chunk c: residual (use_p = false) or
-// p itself; also returns p in pv for the fallback sum.
+// p itself; also returns p in pv for the fallback sum.  p comes from 16-byte loads of the
+// thread's own ids.  q_n is fetched lane-contiguously (consecutive lanes read consecutive
+// full_to_trim entries and, for an ascending keep set, consecutive draft entries) into LDS and
+// read back in the thread's order: a per-thread loop over its 16 ids would make every load
+// instruction touch 64 different cache lines.  All threads of the workgroup must call.
 template <typename Tin, bool kVec>
 __device__ __forceinline__ void final_weights(const VfParams &P, int64_t b, int n, int c, bool use_p, float (&wv)[16],
                                               float (&pv)[16]) {
+  __shared__ __align__(16) float sq[kChunk];
   const int row = n < P.gamma ? n : P.gamma;
   const Tin *trow = reinterpret_cast<const Tin *>(P.target) + (b * (P.gamma + 1) + row) * P.V;
   float lt[16];
@@ -91,16 +96,31 @@ __device__ __forceinline__ void final_weights(const VfParams &P, int64_t b, int 
   }
   const float *drow = P.draft + (b * P.R + n) * P.Vt;
   const RowExp qe = make_row_exp(P.dlse[b * P.R + n], P.Td, P.k2d);
-  const int64_t x0 = static_cast<int64_t>(c) * kChunk + static_cast<int64_t>(threadIdx.x) * kPerThread;
+  const int64_t base = static_cast<int64_t>(c) * kChunk;
+  __syncthreads();  // a previous call's readers are done with sq
+  int32_t tv[kPerThread];
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    const int64_t x = x0 + j;
-    float q = 0.f;
-    if (x < P.V) {
-      const int64_t t = P.f2t ? static_cast<int64_t>(P.f2t[x]) : x;
-      if (t >= 0 && t < P.Vt) q = qe(drow[t]);
-    }
-    wv[j] = fmaxf(pv[j] - q, 0.f);
+  for (int r = 0; r < kPerThread; ++r) {
+    const int64_t x = base + r * kBlock + threadIdx.x;
+    tv[r] = x < P.V ? (P.f2t ? P.f2t[x] : static_cast<int32_t>(x)) : -1;
+  }
+  float dv[kPerThread];
+#pragma unroll
+  for (int r = 0; r < kPerThread; ++r) {
+    const int32_t t = tv[r];
+    dv[r] = (t >= 0 && t < P.Vt) ? drow[t] : kNegInf;
+  }
+#pragma unroll
+  for (int r = 0; r < kPerThread; ++r) sq[r * kBlock + threadIdx.x] = qe(dv[r]);
+  __syncthreads();
+  const float4 *q4 = reinterpret_cast<const float4 *>(sq + threadIdx.x * kPerThread);
+#pragma unroll
+  for (int k = 0; k < kPerThread / 4; ++k) {
+    const float4 q = q4[k];
+    wv[4 * k + 0] = fmaxf(pv[4 * k + 0] - q.x, 0.f);
+    wv[4 * k + 1] = fmaxf(pv[4 * k + 1] - q.y, 0.f);
+    wv[4 * k + 2] = fmaxf(pv[4 * k + 2] - q.z, 0.f);
+    wv[4 * k + 3] = fmaxf(pv[4 * k + 3] - q.w, 0.f);
   }
 }
 

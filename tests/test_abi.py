@@ -12,7 +12,8 @@ import pytest
 import draft_sampling_verification_amd as vt
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "vt.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(vt.LIB_PATH), reason="libvt.so not built")
 
@@ -25,13 +26,14 @@ NUL = None
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(vt_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_three_operations():
     names = declared_functions()
-    for fn in ("vt_lmhead_trimmed", "vt_softmax_temp", "vt_spec_verify"):
+    for fn in ("vt_lmhead_trimmed", "vt_softmax_temp", "vt_spec_verify", "vt_token_histogram", "vt_keep_select",
+               "vt_trim_head"):
         assert fn in names
     assert set(names) == set(vt.EXPORTED)
 
@@ -171,3 +173,52 @@ def test_block_workspace_sizes():
     big = L.vt_spec_block_workspace_bytes(256, 8, 9, 4096, 65536, 128256)
     assert 0 < small < big
     assert L.vt_spec_block_workspace_bytes(1, 5, 4, 3072, 100, 100) == 0  # R < gamma
+
+
+# ------------------------------------------------------------------ keep-set construction
+
+def hist(tokens=A, n=1000, V=128256, acc=0, counts=A2, ws=NUL, wsb=0):
+    return vt.lib().vt_token_histogram(tokens, n, V, acc, counts, ws, wsb, NUL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(counts=NUL), INV), (dict(tokens=NUL), INV), (dict(n=-1), INV), (dict(V=0), INV),
+    (dict(V=1 << 31), UNS), (dict(tokens=P(0x100002)), UNS),
+    (dict(n=1 << 24), WS), (dict(n=1 << 24, ws=A, wsb=1024), WS),
+])
+def test_histogram_rejects(kw, status):
+    assert hist(**kw) == status
+
+
+def test_histogram_workspace_sizes():
+    L = vt.lib()
+    assert L.vt_token_histogram_workspace_bytes(1000, 128256) == 0      # one group writes counts directly
+    assert L.vt_token_histogram_workspace_bytes(1 << 26, 128256) == 64 * 128256 * 4
+    assert L.vt_token_histogram_workspace_bytes(1 << 26, 1000) == 256 * 1000 * 4
+    assert L.vt_token_histogram_workspace_bytes(-1, 10) == 0
+
+
+def sel(counts=A, V=128256, rule=0, k=100, p=0.5, f=1, keep=A2, f2t=A2, nk=A):
+    return vt.lib().vt_keep_select(counts, V, rule, k, p, f, keep, f2t, nk, NUL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(counts=NUL), INV), (dict(keep=NUL), INV), (dict(f2t=NUL), INV), (dict(nk=NUL), INV), (dict(V=0), INV),
+    (dict(rule=3), INV), (dict(k=0), INV), (dict(k=128257), INV),
+    (dict(rule=1, p=0.0), INV), (dict(rule=1, p=1.5), INV), (dict(rule=1, p=math.nan), INV),
+    (dict(V=1 << 31), UNS),
+])
+def test_keep_select_rejects(kw, status):
+    assert sel(**kw) == status
+
+
+def trim(w=A, V=128256, H=3072, keep=A2, k=10, out=A):
+    return vt.lib().vt_trim_head(w, V, H, keep, k, out, NUL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=NUL), INV), (dict(keep=NUL), INV), (dict(out=NUL), INV), (dict(V=0), INV), (dict(H=0), INV),
+    (dict(k=0), INV), (dict(H=3070), UNS), (dict(w=P(0x100008)), UNS), (dict(out=P(0x100004)), UNS),
+])
+def test_trim_head_rejects(kw, status):
+    assert trim(**kw) == status

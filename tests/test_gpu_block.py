@@ -40,6 +40,13 @@ def test_fused_block_parity_scaled(name):
     _check(make_workload(SCALED[name]))
 
 
+@pytest.mark.parametrize("name", ["c3-trimmed", "c3-ragged", "c5-mfma"])
+def test_fused_block_rank_ordered_keep_set(name):
+    # kept ids stored best-ranked first instead of ascending: the gathers are no longer monotone
+    say(f"fused block parity {name}, keep set in rank order")
+    _check(make_workload(SCALED[name], keep_order="rank"))
+
+
 @pytest.mark.parametrize("name", ["c3-trimmed", "c4-batched-mfma"])
 def test_fused_matches_separate_calls(name):
     wl = make_workload(SCALED[name])
@@ -52,11 +59,11 @@ def test_fused_matches_separate_calls(name):
     assert same.mean() >= 0.95, same.mean()
 
 
-@pytest.mark.parametrize("c", [2, 3, 5])
-def test_fused_block_full_size(c):
+@pytest.mark.parametrize("c,order", [(2, "id"), (3, "id"), (5, "id"), (3, "rank")])
+def test_fused_block_full_size(c, order):
     cfg = CONFIGS[c]
-    say(f"fused block full size config {c}")
-    wl = make_workload(cfg)
+    say(f"fused block full size config {c}, keep order {order}")
+    wl = make_workload(cfg, keep_order=order)
     ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     for e in ev:
         e.record()  # materialise the events
@@ -66,7 +73,7 @@ def test_fused_block_full_size(c):
     assert ev[0].elapsed_time(ev[1]) > 0
     R = cfg.R
     for s in ([0] if cfg.B == 1 else [0, cfg.B - 1]):
-        one = make_workload(cfg, B=1, b0=s)
+        one = make_workload(cfg, B=1, b0=s, keep_order=order)
         orc = oracle_block(one)
         sub = dict(draft_ids=gpu["draft_ids"][s:s + 1], n=gpu["n"][s:s + 1], tokens=gpu["tokens"][s:s + 1])
         st = compare_tokens(sub, orc, one)
