@@ -20,4 +20,4 @@ Pages cited (by title and section):
 Every function is pinned by tests under tests/ (test_oracle_*.py); none is "parity unpinned"
 except the synthetic input recipe itself, which both sides read as identical arrays.
 """
-from . import exact, keepset, ref  # noqa: F401
+from . import exact, keepset, ref, stats  # noqa: F401

@@ -243,6 +243,60 @@ def toy_block(target_table, draft_table, T, gamma: int, u_draft, u_acc, u_fin, c
                 final_margin=fin_m)
 
 
+def toy_generate(target_table, draft_table, target_T: float, draft_T: float, gamma: int, n_tokens: int, u,
+                 band: float = 0.0):
+    """Chained blocks of the order-1 toy until each sequence has n_tokens tokens.
+
+    [RR] "Extending the rule from one token to a drafted run", the generation loop: every block
+    starts from the last token emitted so far (the start context for the first block), drafts
+    gamma tokens autoregressively from q, verifies them against p at the gamma+1 positions along
+    the draft, and appends the accepted drafts plus the corrected or bonus token; [VT] Appendix
+    C.1, Algorithm 2 has the same loop around the trimmed drafter.  Table row r is the context
+    "previous token = r-1" (row 0: start).  A trimmed draft is a draft table with -inf logits off
+    the kept set.
+    u: float32 [B, n_tokens, 2*gamma+1]; block j of sequence b reads u[b, j]: slots 0..gamma-1 for
+    the drafts, gamma..2*gamma-1 for the accept tests, 2*gamma for the final draw (a block emits at
+    least one token, so n_tokens blocks always suffice).
+    Returns dict: tokens int64 [B, n_tokens]; per sequence blocks, tests (accept tests performed:
+    n+1 after a rejection at n, gamma when all pass), accepted (sum of n), emitted (tokens of all
+    blocks, including any past n_tokens in the last one); tie_block: index of the first block
+    holding a decision within `band` of its uniform (n_tokens if none) and tie_token: the number
+    of tokens emitted before that block.
+    """
+    _, P = softmax_temp(np.asarray(target_table, dtype=np.float64), target_T)
+    _, Q = softmax_temp(np.asarray(draft_table, dtype=np.float64), draft_T)
+    u = np.asarray(u, dtype=np.float32)
+    B = u.shape[0]
+    tokens = np.full((B, n_tokens), -1, dtype=np.int64)
+    stats = {k: np.zeros(B, dtype=np.int64) for k in ("blocks", "tests", "accepted", "emitted")}
+    tie_block = np.full(B, n_tokens, dtype=np.int64)
+    tie_token = np.full(B, n_tokens, dtype=np.int64)
+    for b in range(B):
+        out, ctx, j = [], 0, 0
+        while len(out) < n_tokens:
+            ub = u[b, j]
+            rows, ids, near = [ctx], [], False
+            for i in range(gamma):
+                x, m = draw(Q[rows[-1]], float(ub[i]))
+                near |= m < band
+                ids.append(x)
+                rows.append(x + 1)
+            toks, n, ratios, fm = verify_sequence(P[rows], Q[rows[:gamma]], ids, None, ub[gamma:2 * gamma],
+                                                  ub[2 * gamma], gamma)
+            near |= fm < band or any(abs(float(ub[gamma + i]) - r) < band for i, r in enumerate(ratios))
+            if near and tie_block[b] == n_tokens:
+                tie_block[b], tie_token[b] = j, len(out)
+            out.extend(int(t) for t in toks[: n + 1])
+            stats["tests"][b] += n + 1 if n < gamma else gamma
+            stats["accepted"][b] += n
+            stats["emitted"][b] += n + 1
+            ctx = int(toks[n]) + 1
+            j += 1
+        stats["blocks"][b] = j
+        tokens[b] = out[:n_tokens]
+    return dict(tokens=tokens, tie_block=tie_block, tie_token=tie_token, **stats)
+
+
 # ---------------------------------------------------------------- greedy verification
 
 def argmax_lowest(row) -> int:
