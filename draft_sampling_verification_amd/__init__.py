@@ -18,6 +18,8 @@ Keep-set construction (include/vt_keepset.h):
   vt_token_histogram(tokens, V, counts, accumulate=False, workspace=None)
   vt_keep_select(counts, rule, keep_ids, full_to_trim, num_kept, k=0, p=0.0, min_count=0)
   vt_trim_head(weight, keep_ids, trimmed)
+Generation loop for table models (include/vt_generate.h):
+  vt_spec_generate_markov(target_table, draft_table, target_T, draft_T, gamma, u, out_tokens, out_stats=None)
 Helpers: softmax_workspace(rows, n), verify_workspace(B, V), block_workspace(...), lib() (the raw ctypes handle).
 """
 from __future__ import annotations
@@ -73,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.vt_keep_select.restype = I
         L.vt_trim_head.argtypes = [P, I64, I64, P, I64, P, P]
         L.vt_trim_head.restype = I
+        L.vt_spec_generate_markov.argtypes = [P, P, I64, F, F, I64, I64, I64, P, P, P, P]
+        L.vt_spec_generate_markov.restype = I
         L.vt_status_string.argtypes = [I]
         L.vt_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -81,7 +85,8 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("vt_lmhead_trimmed", "vt_softmax_temp", "vt_softmax_temp_workspace_bytes", "vt_spec_verify",
             "vt_spec_verify_workspace_bytes", "vt_spec_block", "vt_spec_block_workspace_bytes", "vt_status_string",
-            "vt_token_histogram", "vt_token_histogram_workspace_bytes", "vt_keep_select", "vt_trim_head")
+            "vt_token_histogram", "vt_token_histogram_workspace_bytes", "vt_keep_select", "vt_trim_head",
+            "vt_spec_generate_markov")
 
 VT_SELECT_TOP_K, VT_SELECT_TOP_P, VT_SELECT_MIN_FREQ = range(3)
 
@@ -318,3 +323,26 @@ def vt_trim_head(weight, keep_ids, trimmed):
                             _ptr(trimmed, "trimmed"), _stream())
     _check("vt_trim_head", st)
     return trimmed
+
+
+# ---------------------------------------------------------------- generation loop
+
+def vt_spec_generate_markov(target_table, draft_table, target_T: float, draft_T: float, gamma: int, u, out_tokens,
+                            out_stats=None):
+    """Chained speculative blocks for B sequences of order-1 table models (tables fp32 [V+1, V],
+    u fp32 [B, n_tokens, 2*gamma+1]) -> out_tokens int32 [B, n_tokens], out_stats int32 [B, 4]."""
+    torch = _torch()
+    rows, V = target_table.shape
+    B, L = out_tokens.shape
+    if rows != V + 1 or tuple(draft_table.shape) != (V + 1, V):
+        raise ValueError("vt_spec_generate_markov: tables must be [V+1, V]")
+    if tuple(u.shape) != (B, L, 2 * gamma + 1):
+        raise ValueError("vt_spec_generate_markov: u must be [B, n_tokens, 2*gamma+1]")
+    if out_stats is not None and tuple(out_stats.shape) != (B, 4):
+        raise ValueError("vt_spec_generate_markov: out_stats must be [B, 4]")
+    st = lib().vt_spec_generate_markov(_ptr(target_table, "target_table", torch.float32),
+                                       _ptr(draft_table, "draft_table", torch.float32), V, target_T, draft_T, gamma,
+                                       B, L, _ptr(u, "u", torch.float32), _ptr(out_tokens, "out_tokens", torch.int32),
+                                       _ptr(out_stats, "out_stats", torch.int32), _stream())
+    _check("vt_spec_generate_markov", st)
+    return out_tokens

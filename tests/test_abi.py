@@ -33,7 +33,7 @@ def declared_functions():
 def test_header_declares_the_three_operations():
     names = declared_functions()
     for fn in ("vt_lmhead_trimmed", "vt_softmax_temp", "vt_spec_verify", "vt_token_histogram", "vt_keep_select",
-               "vt_trim_head"):
+               "vt_trim_head", "vt_spec_generate_markov"):
         assert fn in names
     assert set(names) == set(vt.EXPORTED)
 
@@ -222,3 +222,19 @@ def trim(w=A, V=128256, H=3072, keep=A2, k=10, out=A):
 ])
 def test_trim_head_rejects(kw, status):
     assert trim(**kw) == status
+
+
+# ------------------------------------------------------------------ generation loop
+
+def gen(tt=A, dt=A2, V=18, Tt=1.0, Td=1.0, g=4, B=10, L=20, u=A, tok=A2, st=NUL):
+    return vt.lib().vt_spec_generate_markov(tt, dt, V, Tt, Td, g, B, L, u, tok, st, NUL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(tt=NUL), INV), (dict(dt=NUL), INV), (dict(u=NUL), INV), (dict(tok=NUL), INV),
+    (dict(V=0), INV), (dict(g=0), INV), (dict(B=0), INV), (dict(L=0), INV),
+    (dict(Tt=0.0), INV), (dict(Td=-1.0), INV), (dict(Tt=math.inf), INV), (dict(Td=math.nan), INV),
+    (dict(V=65), UNS), (dict(g=65), UNS), (dict(L=1 << 31), UNS),
+])
+def test_generate_rejects(kw, status):
+    assert gen(**kw) == status
