@@ -47,9 +47,15 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--workload", default="block", choices=["block", "keepset", "generate"],
+                    help="block: one speculative block per step (the default); keepset: token counter -> "
+                         "Top-K -> trimmed head over a Zipf calibration stream; generate: the chained "
+                         "generation loop on the order-1 toy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--valu-record", metavar="CSV",
+                    help="SQ_INSTS_VALU counter csv of --workload generate: write the generation kernel's record")
     ap.add_argument("--traffic-record", nargs=4, metavar="CSV",
                     help="bench FETCH_SIZE, bench WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE counter csv "
                          "files from rocprofv3 --pmc: write the LM-head traffic record for --config")
@@ -213,6 +219,211 @@ def cpu_baseline(cfg, wl_one, budget_s: float):
                       f"{el:.1f} s total, {per_block:.2f} s per block"}
 
 
+# ---------------------------------------------------------------- keep-set construction
+
+KS_TOKENS, KS_V, KS_K, KS_H = 1 << 26, 128256, 32768, 3072
+
+
+def bench_keepset(args):
+    """One step = vt_token_histogram over a 64M-token Zipf(1.1) stream (V = 128256) ->
+    vt_keep_select Top-K 32768 -> vt_trim_head of the 3072-wide bf16 head.  Each launch is
+    bracketed by HIP events on the stream it runs on."""
+    import torch
+
+    import draft_sampling_verification_amd as vt
+    from workloads import token_stream
+    from workloads.gen import lm_head_weights
+
+    t0 = time.perf_counter()
+    toks_h = token_stream(KS_V, KS_TOKENS, seed=1)
+    W_h = lm_head_weights(KS_V, KS_H)
+    log(f"keep-set inputs generated in {time.perf_counter() - t0:.1f} s")
+    toks = torch.from_numpy(toks_h).cuda()
+    W = torch.from_numpy(W_h.view(np.int16)).cuda().view(torch.bfloat16)
+    counts = torch.empty(KS_V, dtype=torch.int32, device="cuda")
+    keep = torch.empty(KS_V, dtype=torch.int32, device="cuda")
+    f2t = torch.empty(KS_V, dtype=torch.int32, device="cuda")
+    nk = torch.empty(1, dtype=torch.int32, device="cuda")
+    trimmed = torch.empty(KS_K, KS_H, dtype=torch.bfloat16, device="cuda")
+    ws = vt.histogram_workspace(KS_TOKENS, KS_V)
+    keep_k = keep[:KS_K]
+    main = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e: e[0].record(main)
+        vt.vt_token_histogram(toks, KS_V, counts, workspace=ws)
+        if e: e[1].record(main)
+        vt.vt_keep_select(counts, vt.VT_SELECT_TOP_K, keep, f2t, nk, k=KS_K)
+        if e: e[2].record(main)
+        vt.vt_trim_head(W, keep_k, trimmed)
+        if e: e[3].record(main)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = 1e3 * wall / args.steps
+    hist_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    sel_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    trim_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
+    hist_bytes = KS_TOKENS * 4 + KS_V * 4
+    trim_bytes = 2 * KS_K * KS_H * 2 + KS_K * 4
+    kern = {"vt_token_histogram": (hist_ms, hist_bytes), "vt_trim_head": (trim_ms, trim_bytes)}
+    dom = max(kern, key=lambda k: kern[k][0])
+    d_ms, d_bytes = kern[dom]
+    ach = d_bytes / (d_ms / 1e3) / 1e9
+    log(f"step {ms:.4f} ms: histogram {hist_ms:.4f} ms ({hist_bytes / hist_ms / 1e6:.0f} GB/s), select "
+        f"{sel_ms:.4f} ms, trim {trim_ms:.4f} ms ({trim_bytes / trim_ms / 1e6:.0f} GB/s)")
+    cpu = None
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info, threadpool_limits
+
+        from oracle import keepset
+        threadpool_limits(limits=len(os.sched_getaffinity(0)))
+        used = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        sample = toks_h[: 1 << 24]
+        runs, t0 = 0, time.perf_counter()
+        while True:
+            c = keepset.count_tokens(sample, KS_V)
+            kp, _ = keepset.top_k(c, KS_K)
+            keepset.trim_head(W_h, kp)
+            runs += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or runs >= 50:
+                break
+        cpu = {"value": round(runs * len(sample) / el, 1), "unit": "calibration tokens/s", "cores": int(used),
+               "kind": "oracle",
+               "sample": f"{runs} pass(es) of count + Top-K + head slice over the first {len(sample)} tokens "
+                         f"of the same stream, {el:.1f} s"}
+    out = {
+        "metric": "calibration tokens/s through token counting, Top-K selection and head trimming, 1 GPU",
+        "value": round(KS_TOKENS / (ms / 1e3), 1), "unit": "calibration tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u32", "data": "synthetic",
+        "config": {"workload": f"keep-set construction: {KS_TOKENS} Zipf(1.1) tokens, V={KS_V}, Top-K {KS_K}, "
+                               f"head {KS_V}x{KS_H} bf16",
+                   "kernel_ms": {"histogram": round(hist_ms, 5), "select": round(sel_ms, 5),
+                                 "trim_head": round(trim_ms, 5)}},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                     "algorithmic_bytes_per_launch": d_bytes, "avg_launch_ms": round(d_ms, 5)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+# ---------------------------------------------------------------- generation loop
+
+GEN_B, GEN_L, GEN_GAMMA, GEN_W = 16384, 256, 4, 0.5
+VALU_PEAK_LANE_OPS = 256 * 2.4e9 * 64 / 1e12  # T lane-ops/s: one wave64 VALU instruction per CU per clock
+
+
+def bench_generate(args):
+    """One step = vt_spec_generate_markov: 16384 sequences x 256 tokens of the order-1 toy
+    (V = 18, gamma = 4, draft = 0.5 target + 0.5 unigram)."""
+    import torch
+
+    import draft_sampling_verification_amd as vt
+    from workloads import CONFIGS, counter_uniforms, toy_tables
+
+    t = toy_tables(CONFIGS[1], GEN_W)
+    g, B, L = GEN_GAMMA, GEN_B, GEN_L
+    u_h = counter_uniforms(1, 70, B, L * (2 * g + 1)).reshape(B, L, 2 * g + 1)
+    tt = torch.from_numpy(t.target_logits).cuda()
+    dt = torch.from_numpy(t.draft_logits).cuda()
+    u = torch.from_numpy(u_h).cuda()
+    tok = torch.empty(B, L, dtype=torch.int32, device="cuda")
+    st = torch.empty(B, 4, dtype=torch.int32, device="cuda")
+    main = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        vt.vt_spec_generate_markov(tt, dt, 1.0, 1.0, g, u, tok, st)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(main)
+        vt.vt_spec_generate_markov(tt, dt, 1.0, 1.0, g, u, tok, st)
+        ev[i][1].record(main)
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    k_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    s = st.cpu().numpy().astype(np.int64)
+    a_hat = s[:, 2].sum() / s[:, 1].sum()
+    tau = s[:, 3].sum() / s[:, 0].sum()
+    log(f"step {ms:.4f} ms, kernel {k_ms:.4f} ms; measured acceptance {a_hat:.5f}, tokens/block {tau:.4f}")
+    rec = valu_record()
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import ref
+        n_seq, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds and n_seq < B:
+            ref.toy_generate(t.target_logits, t.draft_logits, 1.0, 1.0, g, L, u_h[n_seq:n_seq + 8])
+            n_seq += 8
+        el = time.perf_counter() - t0
+        cpu = {"value": round(n_seq * L / el, 1), "unit": "generated tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"the first {n_seq} sequences of the same workload ({n_seq * L} tokens), {el:.1f} s"}
+    roof = {"bound": "alu", "achieved": None, "peak": VALU_PEAK_LANE_OPS, "unit": "T lane-ops/s", "frac": None,
+            "traffic": None, "kernel": "markov_generate", "avg_launch_ms": round(k_ms, 5)}
+    if rec is not None:
+        lane_ops = rec["valu_insts_per_launch"] * 64
+        roof["achieved"] = round(lane_ops / (k_ms / 1e3) / 1e12, 3)
+        roof["frac"] = round(roof["achieved"] / VALU_PEAK_LANE_OPS, 4)
+        roof["valu_insts_per_launch"] = rec["valu_insts_per_launch"]
+    out = {
+        "metric": "generated tokens/s, chained speculative blocks on the order-1 toy, 1 GPU",
+        "value": round(B * L / (ms / 1e3), 1), "unit": "generated tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"toy generation loop: B={B} sequences x {L} tokens, V=18, gamma={g}, w={GEN_W}",
+                   "measured_acceptance": round(float(a_hat), 5), "tokens_per_block": round(float(tau), 5)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def generate_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("generate.hip", "verify_impl.hpp", "vt_common.hpp"):
+        with open(os.path.join(ROOT, "draft_sampling_verification_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def write_valu_record(csv_path) -> str:
+    """profiles/generate_valu_toy.json from a `rocprofv3 --pmc SQ_INSTS_VALU` pass over
+    `bench.py --workload generate`: VALU instructions (per wavefront, summed over the device)
+    per launch of the generation kernel."""
+    vals = [v for k, v in _pmc_rows(csv_path, "SQ_INSTS_VALU") if "markov_generate" in k]
+    rec = {"kernel": "markov_generate", "workload": f"toy generation loop B={GEN_B} L={GEN_L} gamma={GEN_GAMMA}",
+           "source_sha256": generate_source_hash(), "launches_sampled": len(vals),
+           "valu_insts_per_launch": sum(vals) / len(vals),
+           "commands": ["rocprofv3 --pmc SQ_INSTS_VALU -f csv -d <out> -o gen -- python3 bench.py --workload generate "
+                        "--no-cpu-baseline --steps 10 --warmup 2",
+                        "python3 bench.py --valu-record <counter csv>"]}
+    out = os.path.join(ROOT, "profiles", "generate_valu_toy.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return out
+
+
+def valu_record():
+    """VALU instructions per launch of the generation kernel from a committed PMC record."""
+    path = os.path.join(ROOT, "profiles", "generate_valu_toy.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return rec if rec.get("source_sha256") == generate_source_hash() else None
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -224,6 +435,15 @@ def main():
         return
     if args.traffic_record:
         print(write_traffic_record(args.config, *args.traffic_record))
+        return
+    if args.valu_record:
+        print(write_valu_record(args.valu_record))
+        return
+    if args.workload == "keepset":
+        bench_keepset(args)
+        return
+    if args.workload == "generate":
+        bench_generate(args)
         return
 
     import torch

@@ -39,13 +39,51 @@ size_t hist_ws_bytes(const HistPlan &p, int64_t V) {
   return p.groups > 1 ? static_cast<size_t>(p.groups) * static_cast<size_t>(V) * sizeof(uint32_t) : 0;
 }
 
+// The slab bin holding the most counts so far (lowest index on ties); all threads call.
+__device__ __forceinline__ int hottest_bin(const uint32_t *bins, int len, uint32_t *redc, int *redi) {
+  uint32_t bc = 0;
+  int bi = 0;
+  for (int i = threadIdx.x; i < len; i += kHistThreads)
+    if (bins[i] > bc) {
+      bc = bins[i];
+      bi = i;
+    }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const uint32_t c2 = __shfl_xor(bc, o, kWave);
+    const int i2 = __shfl_xor(bi, o, kWave);
+    if (c2 > bc || (c2 == bc && i2 < bi)) {
+      bc = c2;
+      bi = i2;
+    }
+  }
+  if (lane_id() == 0) {
+    redc[wave_id()] = bc;
+    redi[wave_id()] = bi;
+  }
+  __syncthreads();
+  bc = redc[0];
+  bi = redi[0];
+  for (int w = 1; w < kHistThreads / kWave; ++w)
+    if (redc[w] > bc || (redc[w] == bc && redi[w] < bi)) {
+      bc = redc[w];
+      bi = redi[w];
+    }
+  return bi;
+}
+
 // Counts tokens [g*seg, min(n, (g+1)*seg)) that fall in slab s.  With one group the slab is
 // written (or added) to counts directly; otherwise to part[g][.] for hist_sum.
+// Token frequencies are heavy-tailed, and lanes of one LDS atomic that hit the same bin are
+// serialised; so after the first 64K tokens of the segment the slab's most frequent bin so far
+// is counted in a register per lane instead, and folded in once at the end.
 template <bool kVec>
 __global__ __launch_bounds__(kHistThreads) void hist_slab(const int32_t *__restrict__ tokens, int64_t n, int64_t seg,
                                                           int V, int slabs, int accumulate, uint32_t *__restrict__ counts,
                                                           uint32_t *__restrict__ part) {
   __shared__ uint32_t bins[kSlabBins];
+  __shared__ uint32_t redc[kHistThreads / kWave];
+  __shared__ int redi[kHistThreads / kWave];
   const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t g = L / slabs;
   const int s = static_cast<int>(L - g * slabs);
@@ -56,17 +94,17 @@ __global__ __launch_bounds__(kHistThreads) void hist_slab(const int32_t *__restr
 
   const int64_t b0 = g * seg;
   const int64_t b1 = min(n, b0 + seg);
+  uint32_t hot = 0, hot_n = 0;
+  bool use_hot = false;
   auto add = [&](int32_t t) {
     const uint32_t u = static_cast<uint32_t>(t - lo);  // negative ids and ids past the slab fail
-    if (u < static_cast<uint32_t>(len)) atomicAdd(&bins[u], 1u);
+    if (use_hot && u == hot)
+      ++hot_n;
+    else if (u < static_cast<uint32_t>(len))
+      atomicAdd(&bins[u], 1u);
   };
-  int64_t tail = b0;
-  if (kVec && b1 > b0) {
-    // b0 is a multiple of 4 and tokens is 16-byte aligned: whole int4 groups up to b1 & ~3
-    const int4 *t4 = reinterpret_cast<const int4 *>(tokens);
-    const int64_t q0 = b0 / 4, q1 = b1 / 4;
-    constexpr int kU = 4;
-    int64_t q = q0 + threadIdx.x;
+  constexpr int kU = 4;
+  auto run = [&](const int4 *t4, int64_t q, int64_t q1) {
     for (; q + (kU - 1) * kHistThreads < q1; q += kU * kHistThreads) {
       int4 v[kU];
 #pragma unroll
@@ -86,9 +124,28 @@ __global__ __launch_bounds__(kHistThreads) void hist_slab(const int32_t *__restr
       add(v.z);
       add(v.w);
     }
+  };
+  int64_t tail = b0;
+  if (kVec && b1 > b0) {
+    // b0 is a multiple of 4 and tokens is 16-byte aligned: whole int4 groups up to b1 & ~3
+    const int4 *t4 = reinterpret_cast<const int4 *>(tokens);
+    const int64_t q0 = b0 / 4, q1 = b1 / 4;
+    const int64_t qa = min(q1, q0 + 16 * kHistThreads);
+    run(t4, q0 + threadIdx.x, qa);
+    if (qa < q1) {
+      __syncthreads();
+      hot = static_cast<uint32_t>(hottest_bin(bins, len, redc, redi));
+      use_hot = true;
+      run(t4, qa + threadIdx.x, q1);
+    }
     tail = q1 * 4;
   }
   for (int64_t i = tail + threadIdx.x; i < b1; i += kHistThreads) add(tokens[i]);
+  if (use_hot) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) hot_n += __shfl_xor(hot_n, o, kWave);
+    if (lane_id() == 0 && hot_n) atomicAdd(&bins[hot], hot_n);
+  }
   __syncthreads();
 
   if (part == nullptr) {
@@ -110,9 +167,15 @@ __global__ __launch_bounds__(kBlock) void hist_sum(const uint32_t *__restrict__ 
 }
 
 // ---------------------------------------------------------------- selection (one workgroup)
+//
+// The counts (513 KB at V = 128256) are walked in tiles of 16384: thread t owns the 16 contiguous
+// ids [tile + 16 t, tile + 16 t + 16), fetched with 16-byte loads, so every pass is a handful of
+// wide loads per thread rather than a latency-bound loop.
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kSelPer = 16;
+constexpr int kSelTile = kSelThreads * kSelPer;
 constexpr int kDigitBits = 11;
 constexpr int kDigits = 1 << kDigitBits;   // 2048 buckets, two per thread
 
@@ -124,6 +187,13 @@ __device__ __forceinline__ T wave_incl_scan_t(T v) {
     const T y = __shfl_up(v, d, kWave);
     if (lane >= d) v += y;
   }
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum_t(T v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
 }
 
@@ -157,13 +227,39 @@ struct SelParams {
   int32_t *num_kept;
 };
 
+// This thread's 16 counts of the tile starting at id `tile`; returns how many are in range.
+template <bool kVec>
+__device__ __forceinline__ int load_tile(const SelParams &P, int tile, uint32_t (&c)[kSelPer]) {
+  const int e0 = tile + static_cast<int>(threadIdx.x) * kSelPer;
+  const int nv = max(0, min(kSelPer, P.V - e0));
+  if (kVec && nv == kSelPer) {
+    const uint4 *p4 = reinterpret_cast<const uint4 *>(P.counts + e0);
+#pragma unroll
+    for (int q = 0; q < kSelPer / 4; ++q) {
+      const uint4 v = p4[q];
+      c[4 * q] = v.x;
+      c[4 * q + 1] = v.y;
+      c[4 * q + 2] = v.z;
+      c[4 * q + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kSelPer; ++j) c[j] = j < nv ? P.counts[e0 + j] : 0u;
+  }
+  return nv;
+}
+
 // Radix descent for the threshold count.  by_mass = false: `want` counts ids (the k-th largest
 // count); by_mass = true: `want` is a summed count.  Returns the threshold c* and leaves in *rest
-// what the ids with count == c* must still contribute (ids or count).
+// what the ids with count == c* must still contribute (ids or count).  Each thread folds runs of
+// equal digits among its 16 ids before touching LDS, and each wavefront merges the bucket of its
+// first contributing lane into a single atomic: heavy-tailed counts put most ids in one bucket.
+template <bool kVec>
 __device__ uint32_t radix_threshold(const SelParams &P, bool by_mass, uint64_t want, uint64_t *hist, uint64_t *red,
                                     uint64_t *rest) {
   __shared__ uint32_t sh_digit;
   __shared__ uint64_t sh_above;
+  const int lane = lane_id();
   uint32_t prefix = 0, mask = 0;
   const int shifts[3] = {21, 10, 0};
   const uint32_t dmasks[3] = {2047u, 2047u, 1023u};
@@ -172,10 +268,34 @@ __device__ uint32_t radix_threshold(const SelParams &P, bool by_mass, uint64_t w
     const uint32_t dm = dmasks[pass];
     for (int i = threadIdx.x; i < kDigits; i += kSelThreads) hist[i] = 0;
     __syncthreads();
-    for (int i = threadIdx.x; i < P.V; i += kSelThreads) {
-      const uint32_t c = P.counts[i];
-      if ((c & mask) == prefix) atomicAdd(reinterpret_cast<unsigned long long *>(&hist[(c >> sh) & dm]),
-                                          static_cast<unsigned long long>(by_mass ? c : 1u));
+    for (int tile = 0; tile < P.V; tile += kSelTile) {
+      uint32_t c[kSelPer];
+      const int nv = load_tile<kVec>(P, tile, c);
+      int cur = -1;
+      uint64_t acc = 0;
+#pragma unroll
+      for (int j = 0; j < kSelPer; ++j) {
+        if (j < nv && (c[j] & mask) == prefix) {
+          const int d = static_cast<int>((c[j] >> sh) & dm);
+          const uint64_t v = by_mass ? c[j] : 1u;
+          if (d == cur) {
+            acc += v;
+          } else {
+            if (cur >= 0) atomicAdd(reinterpret_cast<unsigned long long *>(&hist[cur]), acc);
+            cur = d;
+            acc = v;
+          }
+        }
+      }
+      const unsigned long long has = __ballot(cur >= 0);
+      if (has) {
+        const int leader = __ffsll(static_cast<long long>(has)) - 1;
+        const int d0 = __shfl(cur, leader, kWave);
+        const bool same = cur >= 0 && cur == d0;
+        const uint64_t tot = wave_sum_t<uint64_t>(same ? acc : 0);
+        if (lane == leader) atomicAdd(reinterpret_cast<unsigned long long *>(&hist[d0]), tot);
+        if (cur >= 0 && !same) atomicAdd(reinterpret_cast<unsigned long long *>(&hist[cur]), acc);
+      }
     }
     __syncthreads();
     // thread t owns digits hi = 2047 - 2t and hi - 1, so thread order is descending digit order
@@ -202,11 +322,11 @@ __device__ uint32_t radix_threshold(const SelParams &P, bool by_mass, uint64_t w
   return prefix;
 }
 
+template <bool kVec>
 __global__ __launch_bounds__(kSelThreads) void keep_select(SelParams P) {
   __shared__ uint64_t hist[kDigits];
   __shared__ uint64_t red64[kSelWaves];
   __shared__ int red32[kSelWaves];
-  __shared__ uint64_t sh_total;
 
   // threshold count and how many ids at exactly that count are kept (lowest ids first)
   uint32_t thr = 0;
@@ -219,54 +339,72 @@ __global__ __launch_bounds__(kSelThreads) void keep_select(SelParams P) {
     bool by_mass = false;
     if (P.rule == VT_SELECT_TOP_P) {
       uint64_t s = 0;
-      for (int i = threadIdx.x; i < P.V; i += kSelThreads) s += P.counts[i];
-      uint64_t tot;
-      (void)sel_exclusive_scan<uint64_t>(s, red64, &tot);
-      if (threadIdx.x == 0) sh_total = tot;
-      __syncthreads();
-      const double target = ceil(P.p * static_cast<double>(sh_total));
-      want = static_cast<uint64_t>(target);
+      for (int tile = 0; tile < P.V; tile += kSelTile) {
+        uint32_t c[kSelPer];
+        load_tile<kVec>(P, tile, c);
+#pragma unroll
+        for (int j = 0; j < kSelPer; ++j) s += c[j];
+      }
+      uint64_t total;
+      (void)sel_exclusive_scan<uint64_t>(s, red64, &total);
+      want = static_cast<uint64_t>(ceil(P.p * static_cast<double>(total)));
       by_mass = want > 0;
       if (!by_mass) want = 1;  // nothing counted: keep one id
     }
     uint64_t rest;
-    thr = radix_threshold(P, by_mass, want, hist, red64, &rest);
+    thr = radix_threshold<kVec>(P, by_mass, want, hist, red64, &rest);
     // by mass, ties are taken until their count covers the rest: ceil(rest / thr) of them
     need = by_mass ? static_cast<int64_t>((rest + thr - 1) / thr) : static_cast<int64_t>(rest);
   }
 
-  // ordered compaction: thread t owns ids [t*run, (t+1)*run)
-  const int run = (P.V + kSelThreads - 1) / kSelThreads;
-  const int i0 = min(P.V, static_cast<int>(threadIdx.x) * run), i1 = min(P.V, i0 + run);
-  int above = 0, ties = 0;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t c = P.counts[i];
-    above += c > thr;
-    ties += c == thr;
-  }
-  int tot;
-  const int tie_base = sel_exclusive_scan<int>(ties, red32, &tot);
-  const int64_t take = min<int64_t>(ties, max<int64_t>(0, need - tie_base));
-  const int mine = above + static_cast<int>(take);
-  int kept_total;
-  const int base = sel_exclusive_scan<int>(mine, red32, &kept_total);
-  int pos = base, tie_rank = tie_base;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t c = P.counts[i];
-    bool kept = c > thr;
-    if (c == thr) {
-      kept = tie_rank < need;
-      ++tie_rank;
+  // ordered compaction, tile by tile, carrying the tie and kept counts across tiles.  full_to_trim
+  // goes out as 16-byte stores of each thread's 16 ids; the tile's kept ids are staged in LDS and
+  // written contiguously by consecutive lanes.
+  __shared__ int32_t kbuf[kSelTile];
+  int tie_carry = 0, keep_carry = 0;
+  for (int tile = 0; tile < P.V; tile += kSelTile) {
+    uint32_t c[kSelPer];
+    const int nv = load_tile<kVec>(P, tile, c);
+    int above = 0, ties = 0;
+#pragma unroll
+    for (int j = 0; j < kSelPer; ++j) {
+      above += j < nv && c[j] > thr;
+      ties += j < nv && c[j] == thr;
     }
-    if (kept) {
-      P.keep[pos] = i;
-      P.f2t[i] = pos;
-      ++pos;
+    int tie_total;
+    const int tie_base = tie_carry + sel_exclusive_scan<int>(ties, red32, &tie_total);
+    const int take = static_cast<int>(min<int64_t>(ties, max<int64_t>(0, need - tie_base)));
+    int kept_total;
+    const int local = sel_exclusive_scan<int>(above + take, red32, &kept_total);
+    const int e0 = tile + static_cast<int>(threadIdx.x) * kSelPer;
+    int pos = local, tie_rank = tie_base;
+    int32_t f[kSelPer];
+#pragma unroll
+    for (int j = 0; j < kSelPer; ++j) {
+      bool kept = j < nv && c[j] > thr;
+      if (j < nv && c[j] == thr) {
+        kept = tie_rank < need;
+        ++tie_rank;
+      }
+      f[j] = kept ? keep_carry + pos : -1;
+      if (kept) kbuf[pos++] = e0 + j;
+    }
+    if (kVec && nv == kSelPer) {
+      int4 *f4 = reinterpret_cast<int4 *>(P.f2t + e0);
+#pragma unroll
+      for (int q = 0; q < kSelPer / 4; ++q) f4[q] = make_int4(f[4 * q], f[4 * q + 1], f[4 * q + 2], f[4 * q + 3]);
     } else {
-      P.f2t[i] = -1;
+#pragma unroll
+      for (int j = 0; j < kSelPer; ++j)
+        if (j < nv) P.f2t[e0 + j] = f[j];
     }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kept_total; i += kSelThreads) P.keep[keep_carry + i] = kbuf[i];
+    __syncthreads();
+    tie_carry += tie_total;
+    keep_carry += kept_total;
   }
-  if (threadIdx.x == 0) *P.num_kept = kept_total;
+  if (threadIdx.x == 0) *P.num_kept = keep_carry;
 }
 
 // ---------------------------------------------------------------- trimmed head
@@ -331,7 +469,9 @@ extern "C" vt_status_t vt_keep_select(const uint32_t *counts, int64_t V, vt_sele
   if (V > INT32_MAX) return VT_ERR_UNSUPPORTED;
   const SelParams P{counts, static_cast<int>(V), static_cast<int>(rule), k, p, min_count, keep_ids, full_to_trim,
                     num_kept};
-  return hip_status(launch(keep_select, dim3(1), dim3(kSelThreads), 0, stream, P));
+  return hip_status(aligned16(counts) && aligned16(full_to_trim)
+                        ? launch(keep_select<true>, dim3(1), dim3(kSelThreads), 0, stream, P)
+                                      : launch(keep_select<false>, dim3(1), dim3(kSelThreads), 0, stream, P));
 }
 
 extern "C" vt_status_t vt_trim_head(const uint16_t *weight, int64_t V_rows, int64_t H, const int32_t *keep_ids,
