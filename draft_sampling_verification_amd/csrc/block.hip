@@ -5,8 +5,9 @@
 // "Extending the rule from one token to a drafted run"), launched as few kernels as the
 // dependencies allow:
 //   1. target rows' chunk partials (max, sum of exp)                       [if V > 4096]
-//   2. LM head; on the GEMV path its epilogue also emits the draft rows' partials per row block
-//      (no second pass over the logits); on the MFMA path a partials launch follows
+//   2. LM head; on the GEMV path and on the large-batch MFMA path its epilogue also emits the
+//      draft rows' partials per row block or column tile (no second pass over the logits); on
+//      the small MFMA path a partials launch follows
 //   3. one combine launch for the draft rows (lse + draws) and the target rows (lse)
 //   4. verify pass 1 (accept scans, residual chunk sums) and pass 2 (final draws, outputs)
 // Batch-1 decode: 5 launches instead of 7.  Launch order never lets an independent kernel sit
@@ -20,6 +21,7 @@ namespace {
 
 struct BlockPlan {
   bool fused;       // GEMV with draft partials in its epilogue
+  bool fused_mfma;  // large-batch MFMA tiles with draft partials in their epilogue
   int64_t M, rows_t;
   int64_t nchunk_t;  // 4096-chunks of a target row
   int64_t nchunk_d;  // draft partial chunks per row (GEMV row blocks, or 4096-chunks)
@@ -34,9 +36,13 @@ BlockPlan plan_block(int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt,
   p.rows_t = B * (gamma + 1);
   p.fused = pick_gemv<true>(p.M, H, trim) != nullptr;
   p.nchunk_t = (V + kChunk - 1) / kChunk;
+  p.fused_mfma = !p.fused && p.M >= kBigMinM;
   if (p.fused) {
     p.nchunk_d = gemv_blocks(Vt);
     p.chunk_d = gemv_rows_per_block(Vt);
+  } else if (p.fused_mfma) {
+    p.nchunk_d = mfma_big_tiles_n(Vt);
+    p.chunk_d = kBigBN;
   } else {
     p.nchunk_d = (Vt + kChunk - 1) / kChunk;
     p.chunk_d = kChunk;
@@ -46,7 +52,8 @@ BlockPlan plan_block(int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt,
   p.off_tpart = off;
   if (p.nchunk_t > 1) off += align_up(static_cast<size_t>(p.rows_t * p.nchunk_t) * sizeof(float2), 256);
   p.off_dpart = off;
-  if (p.fused || p.nchunk_d > 1) off += align_up(static_cast<size_t>(p.M * p.nchunk_d) * sizeof(float2), 256);
+  if (p.fused || p.fused_mfma || p.nchunk_d > 1)
+    off += align_up(static_cast<size_t>(p.M * p.nchunk_d) * sizeof(float2), 256);
   p.off_nbuf = off;
   p.off_vpart = off;
   if (p.nchunk_v > 1) {
@@ -89,6 +96,10 @@ hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, 
   if (pl.fused) {
     const GemvFn fn = pick_gemv<true>(pl.M, H, keep != nullptr);
     e = launch_gemv(fn, hidden, weight, keep, H, Vt, logits, GemvParts{D.part, D.k2}, stream);
+    if (e != hipSuccess) return e;
+    if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
+  } else if (pl.fused_mfma) {
+    e = launch_mfma_big<true>(hidden, weight, keep, pl.M, H, Vt, logits, GemvParts{D.part, D.k2}, stream);
     if (e != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   } else {
@@ -161,7 +172,7 @@ extern "C" vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *wei
   D.sampled = draft_ids;
   D.nchunk = static_cast<int>(pl.nchunk_d);
   D.chunk = pl.chunk_d;
-  if (pl.fused || pl.nchunk_d > 1) D.part = reinterpret_cast<float2 *>(ws + pl.off_dpart);
+  if (pl.fused || pl.fused_mfma || pl.nchunk_d > 1) D.part = reinterpret_cast<float2 *>(ws + pl.off_dpart);
 
   SmParams T{};
   T.logits = target_logits;

@@ -419,6 +419,205 @@ GemvFn pick_gemv(int64_t M, int64_t H, bool trim) {
   }
 }
 
+// ---------------------------------------------------------------- large batches (M >= 256)
+//
+// 256 x 256 output tiles (hidden rows x head rows), K in steps of 64, one workgroup of four waves
+// per CU (the double-buffered tiles take 144 KB of LDS).  Each wave owns a 128 x 128 quarter as
+// 4 x 4 v_mfma_f32_32x32x16_bf16 accumulators, so every 16-deep slice reads 4 + 4 fragments from
+// LDS for 16 MFMAs (half the LDS traffic per MFMA of a 64 x 64 wave tile).  The next K step is
+// fetched into registers while the current one is multiplied.  Loads are unconditional: rows past
+// M or Vt repeat the last row (their outputs are never stored) and pieces past H are zeroed.
+// PARTS: the epilogue also emits the draft softmax partials of the tile's 256 columns per hidden
+// row (max and sum of 2^((x - max) k2)), combined across the two waves that share rows.
+constexpr int kBigBM = 256, kBigBN = 256, kBigBK = 64, kBigPad = 8;
+constexpr int kBigRow = kBigBK + kBigPad;  // bf16 per LDS row: 144 bytes
+constexpr int kBigMinM = 256;
+
+template <bool TRIM, bool PARTS, bool KFULL>
+__global__ __launch_bounds__(kBlock, 1) void lmhead_mfma_big(const uint16_t *__restrict__ hidden,
+                                                             const uint16_t *__restrict__ weight,
+                                                             const int32_t *__restrict__ keep, int M, int H, int Vt,
+                                                             float *__restrict__ logits, GemvParts parts) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2][(kBigBM + kBigBN) * kBigRow];
+  const int nbm = (M + kBigBM - 1) / kBigBM;
+  const int nbn = (Vt + kBigBN - 1) / kBigBN;
+  const int tile = static_cast<int>(xcd_remap(blockIdx.x, static_cast<int64_t>(nbm) * nbn));
+  const int bm = tile % nbm, bn = tile / nbm;
+  const int m0 = bm * kBigBM, n0 = bn * kBigBN;
+  const int tid = threadIdx.x;
+
+  // staging: thread t moves 16-byte piece (t & 7) of rows (t >> 3) + 32 i, i < 8, of both operands
+  const int piece = tid & 7, r0 = tid >> 3;
+  int arow[8], brow[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    arow[i] = min(m0 + r0 + 32 * i, M - 1);
+    const int n = min(n0 + r0 + 32 * i, Vt - 1);
+    brow[i] = TRIM ? keep[n] : n;
+  }
+  uint4 ra[8], rb[8];
+  uint32_t keepk = 0xffffffffu;  // all ones while the fetched pieces lie inside H; pieces past H are zeroed
+  auto fetch = [&](int k0) {
+    const int k = k0 + piece * 8;
+    const bool kin = KFULL || k < H;
+    const int kc = kin ? k : 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ra[i] = *reinterpret_cast<const uint4 *>(hidden + static_cast<int64_t>(arow[i]) * H + kc);
+      rb[i] = *reinterpret_cast<const uint4 *>(weight + static_cast<int64_t>(brow[i]) * H + kc);
+    }
+    if (!KFULL) keepk = kin ? 0xffffffffu : 0u;
+  };
+  // the masking happens here, when the data are written to LDS, so that nothing waits for the
+  // global loads before then
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint4 x = ra[i], y = rb[i];
+      if (!KFULL) {
+        x = make_uint4(x.x & keepk, x.y & keepk, x.z & keepk, x.w & keepk);
+        y = make_uint4(y.x & keepk, y.y & keepk, y.z & keepk, y.w & keepk);
+      }
+      *reinterpret_cast<uint4 *>(&smem[buf][(r0 + 32 * i) * kBigRow + piece * 8]) = x;
+      *reinterpret_cast<uint4 *>(&smem[buf][(kBigBM + r0 + 32 * i) * kBigRow + piece * 8]) = y;
+    }
+  };
+
+  const int w = wave_id();
+  const int wm = (w >> 1) * 128, wn = (w & 1) * 128;
+  const int lane = lane_id();
+  const int lr = lane & 31, lk = (lane >> 5) * 8;
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  fetch(0);
+  stage(0);
+  __syncthreads();
+  const int nk = (H + kBigBK - 1) / kBigBK;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const uint16_t *sa = smem[cur] + (wm + lr) * kBigRow + lk;
+    const uint16_t *sb = smem[cur] + (kBigBM + wn + lr) * kBigRow + lk;
+    // fragments double-buffered in registers: the slice kk + 16 is read from LDS while the 16
+    // MFMAs of slice kk run.  The next K step is fetched unconditionally (the last step re-reads
+    // itself) so the whole iteration is one scheduling region.
+    bf16x8 a[2][4], b[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[0][i] = *reinterpret_cast<const bf16x8 *>(sa + i * 32 * kBigRow);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[0][j] = *reinterpret_cast<const bf16x8 *>(sb + j * 32 * kBigRow);
+    fetch(min(kt + 1, nk - 1) * kBigBK);
+#pragma unroll
+    for (int s4 = 0; s4 < kBigBK / 16; ++s4) {
+      const int c = s4 & 1;
+      if (s4 + 1 < kBigBK / 16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          a[c ^ 1][i] = *reinterpret_cast<const bf16x8 *>(sa + i * 32 * kBigRow + (s4 + 1) * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          b[c ^ 1][j] = *reinterpret_cast<const bf16x8 *>(sb + j * 32 * kBigRow + (s4 + 1) * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
+    }
+    stage(cur ^ 1);
+    // issue order for the iteration: the first fragments and the next step's global loads, then
+    // each slice's MFMAs interleaved with the LDS reads of the following slice, and the last
+    // slice's MFMAs interleaved with the LDS writes of the next step
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);
+#pragma unroll
+    for (int q = 0; q < kBigBK / 16 - 1; ++q) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    }
+    __syncthreads();
+  }
+
+  // 32x32 accumulator layout: lane l holds column l % 32; register v holds row
+  // 8 * (v / 4) + 4 * (l / 32) + v % 4.
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int gm = m0 + wm + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (gm < M) {
+        float *dst = logits + static_cast<int64_t>(gm) * Vt;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int gn = n0 + wn + j * 32 + lr;
+          if (gn < Vt) dst[gn] = acc[i][j][v];
+        }
+      }
+    }
+  if constexpr (PARTS) {
+    // per hidden row: max and sum of exp2((x - max) k2) over this wave's 128 columns (32 lanes
+    // of a half-wave x 4 subtiles), then merged with the other wave covering the same rows
+    __shared__ float2 wpart[2][kBigBM];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float x[4];
+        float mx = kNegInf;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[j] = (n0 + wn + j * 32 + lr < Vt) ? acc[i][j][v] : kNegInf;
+          mx = fmaxf(mx, x[j]);
+        }
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+        float sm = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sm += x[j] == kNegInf ? 0.f : __builtin_amdgcn_exp2f((x[j] - mx) * parts.k2);
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) sm += __shfl_xor(sm, o, kWave);
+        if (lr == 0) wpart[w & 1][wm + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)] = make_float2(mx, sm);
+      }
+    __syncthreads();
+    const int r = tid;  // 256 threads, one per row of the tile
+    const int gm = m0 + r;
+    if (gm < M) {
+      const float2 p0 = wpart[0][r], p1 = wpart[1][r];
+      const float mx = fmaxf(p0.x, p1.x);
+      float sm = 0.f;
+      if (p0.x != kNegInf) sm += p0.y * __builtin_amdgcn_exp2f((p0.x - mx) * parts.k2);
+      if (p1.x != kNegInf) sm += p1.y * __builtin_amdgcn_exp2f((p1.x - mx) * parts.k2);
+      parts.part[static_cast<int64_t>(gm) * nbn + bn] = make_float2(mx, sm);
+    }
+  }
+}
+
+inline int64_t mfma_big_tiles_n(int64_t Vt) { return (Vt + kBigBN - 1) / kBigBN; }
+
+template <bool PARTS>
+inline hipError_t launch_mfma_big(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int64_t M,
+                                  int64_t H, int64_t Vt, float *logits, GemvParts parts, hipStream_t stream) {
+  const int64_t tiles = ((M + kBigBM - 1) / kBigBM) * mfma_big_tiles_n(Vt);
+  auto fn = H % kBigBK == 0 ? (keep ? &lmhead_mfma_big<true, PARTS, true> : &lmhead_mfma_big<false, PARTS, true>)
+                            : (keep ? &lmhead_mfma_big<true, PARTS, false> : &lmhead_mfma_big<false, PARTS, false>);
+  return launch(fn, dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0, stream, hidden, weight, keep,
+                static_cast<int>(M), static_cast<int>(H), static_cast<int>(Vt), logits, parts);
+}
+
 inline hipError_t launch_gemv(GemvFn fn, const uint16_t *hidden, const uint16_t *weight, const int32_t *keep,
                               int64_t H, int64_t Vt, float *logits, GemvParts parts, hipStream_t stream) {
   return launch(fn, dim3(static_cast<unsigned>(gemv_blocks(Vt))), dim3(kBlock), 0, stream, hidden, weight, keep,
@@ -427,6 +626,7 @@ inline hipError_t launch_gemv(GemvFn fn, const uint16_t *hidden, const uint16_t 
 
 inline hipError_t launch_mfma(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int64_t M,
                               int64_t H, int64_t Vt, float *logits, hipStream_t stream) {
+  if (M >= kBigMinM) return launch_mfma_big<false>(hidden, weight, keep, M, H, Vt, logits, GemvParts{}, stream);
   const int64_t tiles = ((M + kBM - 1) / kBM) * ((Vt + kBN - 1) / kBN);
   return launch(lmhead_mfma, dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0, stream, hidden, weight, keep,
                 static_cast<int>(M), static_cast<int>(H), static_cast<int>(Vt), logits);

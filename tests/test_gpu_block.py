@@ -17,6 +17,8 @@ SCALED = {
     "c3-ragged": CONFIGS[3].scaled(V=9001, Vt=1234, H=520),
     "c4-batched-mfma": CONFIGS[4].scaled(B=24, V=20000, Vt=5000, H=256),
     "c5-mfma": CONFIGS[5].scaled(B=16, V=13000, Vt=6000, H=256),
+    "c4-big-tiles": CONFIGS[4].scaled(B=40, V=20000, Vt=5000, H=520),  # M = 320: fused 256x256 tiles
+    "c5-big-tiles": CONFIGS[5].scaled(B=32, V=13000, Vt=6001, H=256),  # M = 288, ragged Vt
     "c3-one-chunk-target": CONFIGS[3].scaled(V=4000, Vt=1500, H=256),
 }
 
@@ -47,7 +49,7 @@ def test_fused_block_rank_ordered_keep_set(name):
     _check(make_workload(SCALED[name], keep_order="rank"))
 
 
-@pytest.mark.parametrize("name", ["c3-trimmed", "c4-batched-mfma"])
+@pytest.mark.parametrize("name", ["c3-trimmed", "c4-batched-mfma", "c4-big-tiles"])
 def test_fused_matches_separate_calls(name):
     wl = make_workload(SCALED[name])
     a = gpu_block(wl)
@@ -59,7 +61,7 @@ def test_fused_matches_separate_calls(name):
     assert same.mean() >= 0.95, same.mean()
 
 
-@pytest.mark.parametrize("c,order", [(2, "id"), (3, "id"), (5, "id"), (3, "rank")])
+@pytest.mark.parametrize("c,order", [(2, "id"), (3, "id"), (4, "id"), (5, "id"), (3, "rank")])
 def test_fused_block_full_size(c, order):
     cfg = CONFIGS[c]
     say(f"fused block full size config {c}, keep order {order}")

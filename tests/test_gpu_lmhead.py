@@ -42,6 +42,9 @@ CASES = [
     (512, 3072, 2000, 1000, True),  # MFMA at config 4's M and H
     (7, 8192, 700, 700, False),     # M * ceil(H/512) too large for registers: MFMA
     (2304, 512, 300, 257, True),    # MFMA at config 5's M
+    (256, 520, 900, 512, True),     # 256 x 256 tiles: one row tile, K tail inside a 64-wide step
+    (300, 1024, 700, 700, False),   # 256 x 256 tiles, ragged rows and columns, untrimmed
+    (512, 3072, 40000, 32768, True),  # config 4's shape on the 256 x 256 tiles
 ]
 
 
@@ -57,7 +60,7 @@ def test_lmhead_parity(M, H, V, Vt, trim):
     assert np.all(err <= bound)
 
 
-@pytest.mark.parametrize("M,H", [(6, 3072), (200, 1024)])
+@pytest.mark.parametrize("M,H", [(6, 3072), (200, 1024), (260, 520)])
 def test_trimmed_equals_full_gathered_bitwise(M, H):
     # trimmed logits are the untrimmed logits at the kept ids, bit for bit (row-independent order)
     say(f"trimmed == full[:, keep] M={M} H={H}")
