@@ -8,6 +8,8 @@
  *   vt_spec_verify     batched modified rejection sampling: accept scan, residual or bonus draw,
  *                      trimmed-id -> full-id remap
  * and vt_spec_block runs all of them for one block in a single call, with fused kernels.
+ * vt_keepset.h builds the kept vocabulary and the trimmed head; vt_generate.h chains blocks into
+ * a generation loop for table models.
  *
  * Pages cited (title, section):
  *   [VT] "VocabTrim: Vocabulary Pruning for Efficient Speculative Decoding in LLMs" (arXiv 2506.22694v2)
@@ -176,10 +178,11 @@ size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
  *   ids), target_lse fp64 [B*(gamma+1)], out_tokens int32 [B][gamma+1], out_num_accepted int32 [B].
  *   lmhead_begin / lmhead_end: optional (NULL) events, recorded on `stream` immediately before and
  *   after the LM-head kernel, for timing it inside the call.
- *   Results are those of the four calls, except that on the fused path the draft running sums are
- *   chunked by the LM head's row blocks (ceil(Vt / 256) rounded up to a multiple of 4 rows) instead
- *   of 4096-element chunks: draws can differ from the separate calls only where a CDF boundary lies
- *   within rounding of the uniform.
+ *   Results are those of the four calls (the logits and target_lse bit for bit), except that on
+ *   the fused paths the draft running sums are chunked by the LM head's own blocks of head rows
+ *   instead of 4096-element chunks: ceil(Vt / 256) rounded up to a multiple of 4 rows when B*R <= 8,
+ *   256 rows when B*R >= 256.  Draws can then differ from the separate calls only where a CDF
+ *   boundary lies within rounding of the uniform.
  *   Both temperatures must be > 0 (greedy decoding: use the separate calls with T = 0).
  *   Errors: INVALID_ARG for NULL required pointers, B, gamma, H, V or Vt <= 0, R < gamma, Vt > V,
  *   a temperature not finite or <= 0, keep_ids/full_to_trim inconsistent with Vt; UNSUPPORTED for
