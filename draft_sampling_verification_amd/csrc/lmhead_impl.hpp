@@ -433,6 +433,69 @@ constexpr int kBigBM = 256, kBigBN = 256, kBigBK = 64, kBigPad = 8;
 constexpr int kBigRow = kBigBK + kBigPad;  // bf16 per LDS row: 144 bytes
 constexpr int kBigMinM = 256;
 
+// Epilogue of a 256 x 256 tile held by four waves as 4 x 4 accumulators each: the logits, and
+// with PARTS the draft softmax partials of the tile's 256 columns per hidden row.  All threads of
+// the workgroup must call.
+template <bool PARTS>
+__device__ __forceinline__ void big_tile_store(const f32x16 (&acc)[4][4], int M, int Vt, int m0, int n0, int wm,
+                                               int wn, int nbn, int bn, float *__restrict__ logits,
+                                               const GemvParts &parts) {
+  const int tid = threadIdx.x, w = wave_id(), lane = lane_id(), lr = lane & 31;
+  // 32x32 accumulator layout: lane l holds column l % 32; register v holds row
+  // 8 * (v / 4) + 4 * (l / 32) + v % 4.
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int gm = m0 + wm + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (gm < M) {
+        float *dst = logits + static_cast<int64_t>(gm) * Vt;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int gn = n0 + wn + j * 32 + lr;
+          if (gn < Vt) dst[gn] = acc[i][j][v];
+        }
+      }
+    }
+  if constexpr (PARTS) {
+    // per hidden row: max and sum of exp2((x - max) k2) over this wave's 128 columns (32 lanes
+    // of a half-wave x 4 subtiles), then merged with the other wave covering the same rows
+    __shared__ float2 wpart[2][kBigBM];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float x[4];
+        float mx = kNegInf;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[j] = (n0 + wn + j * 32 + lr < Vt) ? acc[i][j][v] : kNegInf;
+          mx = fmaxf(mx, x[j]);
+        }
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+        float sm = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sm += x[j] == kNegInf ? 0.f : __builtin_amdgcn_exp2f((x[j] - mx) * parts.k2);
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) sm += __shfl_xor(sm, o, kWave);
+        if (lr == 0) wpart[w & 1][wm + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)] = make_float2(mx, sm);
+      }
+    __syncthreads();
+    const int r = tid;  // 256 threads, one per row of the tile
+    const int gm = m0 + r;
+    if (gm < M) {
+      const float2 p0 = wpart[0][r], p1 = wpart[1][r];
+      const float mx = fmaxf(p0.x, p1.x);
+      float sm = 0.f;
+      if (p0.x != kNegInf) sm += p0.y * __builtin_amdgcn_exp2f((p0.x - mx) * parts.k2);
+      if (p1.x != kNegInf) sm += p1.y * __builtin_amdgcn_exp2f((p1.x - mx) * parts.k2);
+      parts.part[static_cast<int64_t>(gm) * nbn + bn] = make_float2(mx, sm);
+    }
+  }
+}
+
+
 template <bool TRIM, bool PARTS, bool KFULL>
 __global__ __launch_bounds__(kBlock, 1) void lmhead_mfma_big(const uint16_t *__restrict__ hidden,
                                                              const uint16_t *__restrict__ weight,
@@ -552,58 +615,141 @@ __global__ __launch_bounds__(kBlock, 1) void lmhead_mfma_big(const uint16_t *__r
     __syncthreads();
   }
 
-  // 32x32 accumulator layout: lane l holds column l % 32; register v holds row
-  // 8 * (v / 4) + 4 * (l / 32) + v % 4.
+  big_tile_store<PARTS>(acc, M, Vt, m0, n0, wm, wn, nbn, bn, logits, parts);
+}
+
+// The same 256 x 256 tiles with the operands brought into LDS by the load units themselves
+// (global_load_lds_dwordx4: each lane's 16 bytes land at LDS base + 16 * lane), through a ring of
+// four K steps of 32, so a load has three steps of MFMA work to arrive and no register staging or
+// LDS write instructions are needed.  A wave's 64 pieces fill 16 rows x 64 bytes contiguously, so
+// rows cannot be padded; instead piece p of tile row r is stored at slot p ^ f(r),
+// f(r) = ((r >> 1) ^ (r >> 3)) & 3, which spreads the 16 rows of a fragment read over all banks.
+// The waits are explicit: before the barrier of step k a thread waits until at most the loads of
+// steps k + 1 and k + 2 are outstanding (vmcnt(16)); the barrier then makes every thread's pieces
+// of step k visible and frees the slot of step k - 1 for step k + 3.  Steps past the last re-fetch
+// the last step into the free slot (never read), so every step issues the same 8 loads per thread.
+// Needs H % 32 == 0 (a piece past H cannot be zeroed on the way into LDS).
+constexpr int kDmaBK = 32;
+constexpr int kDmaStages = 4;
+constexpr int kDmaRowBytes = kDmaBK * 2;                          // 64
+constexpr int kDmaOperandBytes = kBigBM * kDmaRowBytes;           // 16 KB per operand per step
+constexpr int kDmaStageBytes = 2 * kDmaOperandBytes;              // 32 KB
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int dma_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding: vmcnt[3:0],
+// expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in bits [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <bool TRIM, bool PARTS>
+__global__ __launch_bounds__(kBlock, 1) void lmhead_mfma_dma(const uint16_t *__restrict__ hidden,
+                                                             const uint16_t *__restrict__ weight,
+                                                             const int32_t *__restrict__ keep, int M, int H, int Vt,
+                                                             float *__restrict__ logits, GemvParts parts) {
+  __shared__ __attribute__((aligned(1024))) char smem[kDmaStages * kDmaStageBytes];
+  const int nbm = (M + kBigBM - 1) / kBigBM;
+  const int nbn = (Vt + kBigBN - 1) / kBigBN;
+  const int tile = static_cast<int>(xcd_remap(blockIdx.x, static_cast<int64_t>(nbm) * nbn));
+  const int bm = tile % nbm, bn = tile / nbm;
+  const int m0 = bm * kBigBM, n0 = bn * kBigBN;
+  const int w = wave_id(), lane = lane_id();
+
+  // loads: wave w fills 1 KB chunks q = 4 w + j (j < 4) of each operand, i.e. tile rows
+  // 16 q .. 16 q + 15; lane L writes row 16 q + L / 4, slot L % 4, and fetches piece slot ^ f(row)
+  const uint16_t *asrc[4], *bsrc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 16 * (4 * w + j) + (lane >> 2);
+    const int piece = (lane & 3) ^ dma_swz(r);
+    const int am = min(m0 + r, M - 1);
+    const int n = min(n0 + r, Vt - 1);
+    const int64_t brow = TRIM ? static_cast<int64_t>(keep[n]) : static_cast<int64_t>(n);
+    asrc[j] = hidden + static_cast<int64_t>(am) * H + piece * 8;
+    bsrc[j] = weight + brow * H + piece * 8;
+  }
+  const int nk = H / kDmaBK;
+  auto issue = [&](int kstep, int slot) {
+    const int k0 = min(kstep, nk - 1) * kDmaBK;
+    char *base = smem + slot * kDmaStageBytes;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_global_load_lds(asrc[j] + k0, (lds_void *)(base + (4 * w + j) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_global_load_lds(bsrc[j] + k0, (lds_void *)(base + kDmaOperandBytes + (4 * w + j) * 1024),
+                                       16, 0, 0);
+  };
+
+  const int wm = (w >> 1) * 128, wn = (w & 1) * 128;
+  const int lr = lane & 31;
+  // fragment reads: tile row wm + 32 i + lr (f depends on lr only), pieces 2 s + lane / 32 of
+  // the step's 4, for the two 16-deep slices s
+  const int sw = dma_swz(lr);
+  const int off0 = lr * kDmaRowBytes + (((lane >> 5) ^ sw) << 4);
+  const int off1 = lr * kDmaRowBytes + (((2 + (lane >> 5)) ^ sw) << 4);
+  f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int gm = m0 + wm + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (gm < M) {
-        float *dst = logits + static_cast<int64_t>(gm) * Vt;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int gn = n0 + wn + j * 32 + lr;
-          if (gn < Vt) dst[gn] = acc[i][j][v];
-        }
-      }
-    }
-  if constexpr (PARTS) {
-    // per hidden row: max and sum of exp2((x - max) k2) over this wave's 128 columns (32 lanes
-    // of a half-wave x 4 subtiles), then merged with the other wave covering the same rows
-    __shared__ float2 wpart[2][kBigBM];
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  auto frags = [&](int slot, int off, bf16x8(&a)[4], bf16x8(&b)[4]) {
+    const char *sa = smem + slot * kDmaStageBytes + wm * kDmaRowBytes + off;
+    const char *sb = smem + slot * kDmaStageBytes + kDmaOperandBytes + wn * kDmaRowBytes + off;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(sa + i * 32 * kDmaRowBytes);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(sb + j * 32 * kDmaRowBytes);
+  };
+  auto mfmas = [&](const bf16x8(&a)[4], const bf16x8(&b)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float x[4];
-        float mx = kNegInf;
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  };
+  auto interleave = [&]() {  // 8 LDS reads spread over the first 8 of 16 MFMAs
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          x[j] = (n0 + wn + j * 32 + lr < Vt) ? acc[i][j][v] : kNegInf;
-          mx = fmaxf(mx, x[j]);
-        }
-#pragma unroll
-        for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
-        float sm = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sm += x[j] == kNegInf ? 0.f : __builtin_amdgcn_exp2f((x[j] - mx) * parts.k2);
-#pragma unroll
-        for (int o = 16; o > 0; o >>= 1) sm += __shfl_xor(sm, o, kWave);
-        if (lr == 0) wpart[w & 1][wm + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)] = make_float2(mx, sm);
-      }
-    __syncthreads();
-    const int r = tid;  // 256 threads, one per row of the tile
-    const int gm = m0 + r;
-    if (gm < M) {
-      const float2 p0 = wpart[0][r], p1 = wpart[1][r];
-      const float mx = fmaxf(p0.x, p1.x);
-      float sm = 0.f;
-      if (p0.x != kNegInf) sm += p0.y * __builtin_amdgcn_exp2f((p0.x - mx) * parts.k2);
-      if (p1.x != kNegInf) sm += p1.y * __builtin_amdgcn_exp2f((p1.x - mx) * parts.k2);
-      parts.part[static_cast<int64_t>(gm) * nbn + bn] = make_float2(mx, sm);
+    for (int r = 0; r < 8; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  };
+
+  // Each step k: the MFMAs of its first 16-deep slice run while the second slice's fragments are
+  // read; then (wait + barrier) step k + 1 is complete in LDS and the slot of step k - 1 is free,
+  // the loads of step k + 3 go into it, and the second slice's MFMAs run while the first slice of
+  // step k + 1 is read.  LDS reads never wait on an idle MFMA pipe; loads have two steps to land.
+  bf16x8 a0[4], b0[4], a1[4], b1[4];
+  issue(0, 0);
+  issue(1, 1);
+  issue(2, 2);
+  wait_vmcnt<16>();
+  __builtin_amdgcn_s_barrier();
+  frags(0, off0, a0, b0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int slot = kt & (kDmaStages - 1);
+    frags(slot, off1, a1, b1);
+    mfmas(a0, b0);
+    interleave();
+    wait_vmcnt<8>();
+    __builtin_amdgcn_s_barrier();
+    issue(kt + 3, (kt + 3) & (kDmaStages - 1));
+    frags((kt + 1) & (kDmaStages - 1), off0, a0, b0);  // past the last step: unused reads of a re-fetch
+    mfmas(a1, b1);
+    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);
+    interleave();
   }
+  wait_vmcnt<0>();  // the re-fetches past the last step land in a free slot: drain them
+  __syncthreads();
+  big_tile_store<PARTS>(acc, M, Vt, m0, n0, wm, wn, nbn, bn, logits, parts);
 }
 
 inline int64_t mfma_big_tiles_n(int64_t Vt) { return (Vt + kBigBN - 1) / kBigBN; }
@@ -612,6 +758,11 @@ template <bool PARTS>
 inline hipError_t launch_mfma_big(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int64_t M,
                                   int64_t H, int64_t Vt, float *logits, GemvParts parts, hipStream_t stream) {
   const int64_t tiles = ((M + kBigBM - 1) / kBigBM) * mfma_big_tiles_n(Vt);
+  if (H % kDmaBK == 0) {
+    auto fd = keep ? &lmhead_mfma_dma<true, PARTS> : &lmhead_mfma_dma<false, PARTS>;
+    return launch(fd, dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0, stream, hidden, weight, keep,
+                  static_cast<int>(M), static_cast<int>(H), static_cast<int>(Vt), logits, parts);
+  }
   auto fn = H % kBigBK == 0 ? (keep ? &lmhead_mfma_big<true, PARTS, true> : &lmhead_mfma_big<false, PARTS, true>)
                             : (keep ? &lmhead_mfma_big<true, PARTS, false> : &lmhead_mfma_big<false, PARTS, false>);
   return launch(fn, dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0, stream, hidden, weight, keep,
