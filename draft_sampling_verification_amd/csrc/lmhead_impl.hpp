@@ -436,10 +436,13 @@ constexpr int kBigMinM = 256;
 // Epilogue of a 256 x 256 tile held by four waves as 4 x 4 accumulators each: the logits, and
 // with PARTS the draft softmax partials of the tile's 256 columns per hidden row.  All threads of
 // the workgroup must call.
+// wpart: LDS scratch of 2 x 256 float2 that the caller no longer needs (its operand tiles), so
+// that the kernel keeps a single LDS object (a second one makes the compiler wait for every
+// outstanding direct-to-LDS load before any LDS read in the main loop).
 template <bool PARTS>
 __device__ __forceinline__ void big_tile_store(const f32x16 (&acc)[4][4], int M, int Vt, int m0, int n0, int wm,
                                                int wn, int nbn, int bn, float *__restrict__ logits,
-                                               const GemvParts &parts) {
+                                               const GemvParts &parts, float2 (*wpart)[kBigBM]) {
   const int tid = threadIdx.x, w = wave_id(), lane = lane_id(), lr = lane & 31;
   // 32x32 accumulator layout: lane l holds column l % 32; register v holds row
   // 8 * (v / 4) + 4 * (l / 32) + v % 4.
@@ -453,14 +456,13 @@ __device__ __forceinline__ void big_tile_store(const f32x16 (&acc)[4][4], int M,
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int gn = n0 + wn + j * 32 + lr;
-          if (gn < Vt) dst[gn] = acc[i][j][v];
+          if (gn < Vt) __builtin_nontemporal_store(acc[i][j][v], dst + gn);  // streamed out, not re-read here
         }
       }
     }
   if constexpr (PARTS) {
     // per hidden row: max and sum of exp2((x - max) k2) over this wave's 128 columns (32 lanes
     // of a half-wave x 4 subtiles), then merged with the other wave covering the same rows
-    __shared__ float2 wpart[2][kBigBM];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -615,7 +617,8 @@ __global__ __launch_bounds__(kBlock, 1) void lmhead_mfma_big(const uint16_t *__r
     __syncthreads();
   }
 
-  big_tile_store<PARTS>(acc, M, Vt, m0, n0, wm, wn, nbn, bn, logits, parts);
+  big_tile_store<PARTS>(acc, M, Vt, m0, n0, wm, wn, nbn, bn, logits, parts,
+                        reinterpret_cast<float2(*)[kBigBM]>(&smem[0][0]));
 }
 
 // The same 256 x 256 tiles with the operands brought into LDS by the load units themselves
@@ -749,7 +752,8 @@ __global__ __launch_bounds__(kBlock, 1) void lmhead_mfma_dma(const uint16_t *__r
   }
   wait_vmcnt<0>();  // the re-fetches past the last step land in a free slot: drain them
   __syncthreads();
-  big_tile_store<PARTS>(acc, M, Vt, m0, n0, wm, wn, nbn, bn, logits, parts);
+  big_tile_store<PARTS>(acc, M, Vt, m0, n0, wm, wn, nbn, bn, logits, parts,
+                        reinterpret_cast<float2(*)[kBigBM]>(smem));
 }
 
 inline int64_t mfma_big_tiles_n(int64_t Vt) { return (Vt + kBigBN - 1) / kBigBN; }
