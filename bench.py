@@ -14,7 +14,7 @@ Prints ONE JSON line on stdout (progress goes to stderr):
                duration measured live with HIP events on the launch stream, against 8 TB/s
   cpu_baseline the float64 CPU oracle timed on a bounded sample of the same workload
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C] [--no-cpu-baseline] [--graph]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C] [--greedy] [--no-cpu-baseline] [--calls] [--graph]
        python bench.py --copy-calibration   (a plain copy of known size, for PMC byte scaling)
 """
 from __future__ import annotations
@@ -63,6 +63,8 @@ def parse():
                     help="run the step as the four separate calls instead of the fused vt_spec_block")
     ap.add_argument("--overlap", action="store_true",
                     help="run the target softmax on a second stream, concurrently with the LM head")
+    ap.add_argument("--greedy", action="store_true",
+                    help="temperature 0 for target and draft: argmax drafts and greedy verification")
     ap.add_argument("--graph", action="store_true",
                     help="replay captured HIP graphs (LM head | rest) instead of launching the calls eagerly")
     return ap.parse_args()
@@ -81,11 +83,13 @@ def lmhead_flops(cfg) -> float:
     return 2.0 * cfg.B * cfg.R * cfg.H * cfg.Vt
 
 
-def block_bytes(cfg) -> int:
+def block_bytes(cfg, greedy: bool = False) -> int:
     """Algorithmic bytes of the whole block (each kernel's distinct inputs and outputs once)."""
     M, B, g, V, Vt = cfg.B * cfg.R, cfg.B, cfg.gamma, cfg.V, cfg.Vt
     s_t = 4 if cfg.target_dtype == "f32" else 2
     lm = lmhead_bytes(cfg)
+    if greedy:  # argmax of the draft rows, argmax of every target row, outputs
+        return lm + M * Vt * 4 + M * 12 + B * (g + 1) * V * s_t + B * ((g + 2) * 4 + g * 4)
     draft_sm = M * Vt * 4 + M * (8 + 4 + 4)  # read logits; write lse, ids; read u
     target_sm = B * (g + 1) * V * s_t + B * (g + 1) * 8
     verify = B * (V * s_t + Vt * 4 + (V * 4 if cfg.trimmed else 0) + (g + 2) * 4 + g * 4 + 4)
@@ -465,7 +469,7 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
     # enough copies of the inputs that the 256 MB MALL cannot serve a step from cache
-    bb = block_bytes(cfg)
+    bb = block_bytes(cfg, args.greedy)
     n_sets = max(2, math.ceil(3 * MALL_BYTES / bb))
     base = dict(weight=bf16(wl.weight), hidden=bf16(wl.hidden),
                 target=f(wl.target) if cfg.target_dtype == "f32" else bf16(wl.target),
@@ -491,8 +495,11 @@ def main():
     ev_tgt, ev_free = torch.cuda.Event(), torch.cuda.Event()
     ev_free.record(main)
 
+    T = 0.0 if args.greedy else float(wl.T)
+
     def target_lse(s):
-        vt.vt_softmax_temp(s["target"].view(B * (g + 1), cfg.V), wl.T, tlse, workspace=ws_sm_t)
+        if not args.greedy:  # greedy verification reads no log-normalisers
+            vt.vt_softmax_temp(s["target"].view(B * (g + 1), cfg.V), T, tlse, workspace=ws_sm_t)
 
     def lmhead(s):
         if side is not None:
@@ -504,12 +511,12 @@ def main():
         vt.vt_lmhead_trimmed(s["hidden"], s["weight"], keep, logits)
 
     def rest(s):
-        vt.vt_softmax_temp(logits, wl.T, dlse, None, s["u_draft"], dids, workspace=ws_sm_d)
+        vt.vt_softmax_temp(logits, T, dlse, None, None if args.greedy else s["u_draft"], dids, workspace=ws_sm_d)
         if side is None:
             target_lse(s)
         else:
             main.wait_event(ev_tgt)
-        vt.vt_spec_verify(s["target"], tlse, wl.T, logits.view(B, R, cfg.Vt), dlse, wl.T, dids.view(B, R), keep,
+        vt.vt_spec_verify(s["target"], tlse, T, logits.view(B, R, cfg.Vt), dlse, T, dids.view(B, R), keep,
                           f2t, s["u_acc"], s["u_fin"], tokens, nacc, workspace=ws_vf)
         if side is not None:
             ev_free.record(main)
@@ -517,7 +524,7 @@ def main():
     ws_blk = vt.block_workspace(B, g, R, cfg.H, cfg.Vt, cfg.V)
 
     def fused(s, events=None):
-        vt.vt_spec_block(s["hidden"], s["weight"], keep, f2t, s["target"], wl.T, wl.T, s["u_draft"], s["u_acc"],
+        vt.vt_spec_block(s["hidden"], s["weight"], keep, f2t, s["target"], T, T, s["u_draft"], s["u_acc"],
                          s["u_fin"], logits, dlse, dids, tlse, tokens, nacc, workspace=ws_blk, lmhead_events=events)
 
     outs = (logits, dlse, dids, tlse, tokens, nacc)
@@ -566,7 +573,10 @@ def main():
         runners[0][0](); runners[0][1](); torch.cuda.synchronize()
         want = [t.clone() for t in outs]
         fused(sets[0]); torch.cuda.synchronize()
-        if not (torch.equal(want[0], logits) and torch.equal(want[3], tlse)):
+        same = torch.equal(want[0], logits) and (args.greedy or torch.equal(want[3], tlse))
+        if args.greedy:  # argmax decisions on the same logits: every output agrees
+            same = same and all(torch.equal(a, b) for a, b in zip(want[1:3] + want[4:], (dlse, dids, tokens, nacc)))
+        if not same:
             raise RuntimeError("vt_spec_block differs from the separate calls")
     for i in range(args.warmup):
         if args.calls:
@@ -635,9 +645,10 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": cfg.name, "batch": B, "gamma": g, "hidden": cfg.H, "vocab": cfg.V,
-                   "kept_rows": cfg.Vt, "target_logits": cfg.target_dtype, "temperature": cfg.T,
+                   "kept_rows": cfg.Vt, "target_logits": cfg.target_dtype, "temperature": 0.0 if args.greedy else cfg.T,
                    "weights": "bf16", "accumulate": "f32", "input_sets_rotated": n_sets,
-                   "launch": ("vt_spec_block: one fused call per step (5 kernels)" if not args.calls else
+                   "verification": "greedy (temperature 0)" if args.greedy else "sampling",
+                   "launch": ("vt_spec_block: one fused call per step" if not args.calls else
                               "four calls, hip graphs (LM head | rest) replayed" if args.graph else
                               "four calls, target softmax on a second stream" if args.overlap else
                               "four calls, eager, one stream"),

@@ -234,7 +234,9 @@ def vt_spec_block(hidden, weight, keep_ids, full_to_trim, target_logits, target_
     """One whole block.  hidden [B*R, H] bf16, weight [V, H] bf16, target [B, gamma+1, V];
     outputs draft_logits [B*R, Vt] f32, draft_lse [B*R] f64, draft_ids [B*R] i32, target_lse
     [B*(gamma+1)] f64, out_tokens [B, gamma+1] i32, out_num_accepted [B] i32.
-    lmhead_events: optional (start, end) torch.cuda.Event pair recorded around the LM-head kernel."""
+    lmhead_events: optional (start, end) torch.cuda.Event pair recorded around the LM-head kernel.
+    target_T = 0: greedy verification (target_lse, u_accept, u_final may be None); draft_T = 0 (with
+    target_T = 0): argmax drafts (u_draft may be None)."""
     torch = _torch()
     _bits16(hidden, "hidden")
     _bits16(weight, "weight")

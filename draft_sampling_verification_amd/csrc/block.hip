@@ -12,6 +12,8 @@
 //   4. verify pass 1 (accept scans, residual chunk sums) and pass 2 (final draws, outputs)
 // Batch-1 decode: 5 launches instead of 7.  Launch order never lets an independent kernel sit
 // between the LM head and its consumers.
+#include <algorithm>
+
 #include "lmhead_impl.hpp"
 #include "softmax_impl.hpp"
 #include "verify_impl.hpp"
@@ -30,13 +32,16 @@ struct BlockPlan {
   size_t off_tpart, off_dpart, off_nbuf, off_vpart, bytes;
 };
 
-BlockPlan plan_block(int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt, int64_t V, bool trim) {
+// greedy_t: the target is decoded greedily (no target softmax; verification compares argmaxes).
+// greedy_d: the drafts are the draft rows' argmaxes (the LM head runs without softmax partials).
+BlockPlan plan_block(int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt, int64_t V, bool trim,
+                     bool greedy_t = false, bool greedy_d = false) {
   BlockPlan p{};
   p.M = B * R;
   p.rows_t = B * (gamma + 1);
-  p.fused = pick_gemv<true>(p.M, H, trim) != nullptr;
-  p.nchunk_t = (V + kChunk - 1) / kChunk;
-  p.fused_mfma = !p.fused && p.M >= kBigMinM;
+  p.fused = !greedy_d && pick_gemv<true>(p.M, H, trim) != nullptr;
+  p.nchunk_t = greedy_t ? 1 : (V + kChunk - 1) / kChunk;
+  p.fused_mfma = !greedy_d && !p.fused && p.M >= kBigMinM;
   if (p.fused) {
     p.nchunk_d = gemv_blocks(Vt);
     p.chunk_d = gemv_rows_per_block(Vt);
@@ -82,12 +87,13 @@ hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, 
                      const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int64_t H, int64_t Vt,
                      float *logits, int64_t B, hipEvent_t ev0, hipEvent_t ev1, hipStream_t stream) {
   hipError_t e = hipSuccess;
-  const bool t_multi = pl.nchunk_t > 1;
-  // 1. target partials (or a whole single-chunk target softmax)
+  const bool greedy_t = Vp.greedy;
+  const bool t_multi = !greedy_t && pl.nchunk_t > 1;
+  // 1. target partials (or a whole single-chunk target softmax); greedy verification needs none
   if (t_multi)
     e = launch(softmax_partial<TinT, kVecT>, dim3(static_cast<unsigned>(T.rows * T.nchunk)), dim3(kBlock), 0,
                stream, T);
-  else
+  else if (!greedy_t)
     e = launch(softmax_single<TinT, kVecT>, dim3(static_cast<unsigned>(T.rows)), dim3(kBlock), 0, stream, T);
   if (e != hipSuccess) return e;
   // 2. LM head (+ draft partials), bracketed by the caller's timing events if any
@@ -103,7 +109,9 @@ hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, 
     if (e != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   } else {
-    e = launch_mfma(hidden, weight, keep, pl.M, H, Vt, logits, stream);
+    const GemvFn plain = pick_gemv<false>(pl.M, H, keep != nullptr);
+    e = plain ? launch_gemv(plain, hidden, weight, keep, H, Vt, logits, GemvParts{}, stream)
+              : launch_mfma(hidden, weight, keep, pl.M, H, Vt, logits, stream);
     if (e != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
     if (pl.nchunk_d > 1) {
@@ -128,7 +136,11 @@ hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, 
 extern "C" size_t vt_spec_block_workspace_bytes(int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt,
                                                 int64_t V) {
   if (B <= 0 || gamma <= 0 || R < gamma || H <= 0 || Vt <= 0 || V < Vt) return 0;
-  return vt::plan_block(B, gamma, R, H, Vt, V, Vt < V).bytes;
+  // enough for every temperature mode
+  size_t bytes = 0;
+  for (int mode = 0; mode < 3; ++mode)
+    bytes = std::max(bytes, vt::plan_block(B, gamma, R, H, Vt, V, Vt < V, mode >= 1, mode == 2).bytes);
+  return bytes;
 }
 
 extern "C" vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep_ids,
@@ -140,18 +152,23 @@ extern "C" vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *wei
                                      hipEvent_t lmhead_begin, hipEvent_t lmhead_end, void *workspace,
                                      size_t workspace_bytes, hipStream_t stream) {
   using namespace vt;
-  if (!hidden || !weight || !target_logits || !u_draft || !u_accept || !u_final || !draft_logits || !draft_lse ||
-      !draft_ids || !target_lse || !out_tokens || !out_num_accepted)
+  const bool greedy_t = target_T == 0.f, greedy_d = draft_T == 0.f;
+  if (!hidden || !weight || !target_logits || !draft_logits || !draft_lse || !draft_ids || !out_tokens ||
+      !out_num_accepted)
     return VT_ERR_INVALID_ARG;
+  if (!greedy_d && !u_draft) return VT_ERR_INVALID_ARG;
+  if (!greedy_t && (!u_accept || !u_final || !target_lse)) return VT_ERR_INVALID_ARG;
   if (target_dtype != VT_F32 && target_dtype != VT_BF16) return VT_ERR_INVALID_ARG;
   if (B <= 0 || gamma <= 0 || R < gamma || H <= 0 || Vt <= 0 || V <= 0 || Vt > V) return VT_ERR_INVALID_ARG;
-  if (!finite_positive(target_T) || !finite_positive(draft_T)) return VT_ERR_INVALID_ARG;
+  if (!greedy_t && !finite_positive(target_T)) return VT_ERR_INVALID_ARG;
+  if (!greedy_d && !finite_positive(draft_T)) return VT_ERR_INVALID_ARG;
+  if (greedy_d && !greedy_t) return VT_ERR_INVALID_ARG;  // sampling verification needs a draft distribution
   if ((keep_ids == nullptr) != (full_to_trim == nullptr)) return VT_ERR_INVALID_ARG;
   if (!keep_ids && Vt != V) return VT_ERR_INVALID_ARG;
   if (gamma > kWave) return VT_ERR_UNSUPPORTED;
   if (H % 8 != 0 || !aligned16(hidden) || !aligned16(weight)) return VT_ERR_UNSUPPORTED;
   if (V > INT32_MAX || H > INT32_MAX || B * R > INT32_MAX) return VT_ERR_UNSUPPORTED;
-  const BlockPlan pl = plan_block(B, gamma, R, H, Vt, V, keep_ids != nullptr);
+  const BlockPlan pl = plan_block(B, gamma, R, H, Vt, V, keep_ids != nullptr, greedy_t, greedy_d);
   if (pl.rows_t * pl.nchunk_t > static_cast<int64_t>(UINT32_MAX) ||
       pl.M * pl.nchunk_d > static_cast<int64_t>(UINT32_MAX) || B * pl.nchunk_v > static_cast<int64_t>(UINT32_MAX))
     return VT_ERR_UNSUPPORTED;
@@ -165,10 +182,11 @@ extern "C" vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *wei
   D.rows = pl.M;
   D.n = Vt;
   D.ld = Vt;
-  D.T = draft_T;
-  D.k2 = static_cast<float>(log2e / static_cast<double>(draft_T));
+  D.greedy = greedy_d;
+  D.T = greedy_d ? 1.0 : draft_T;
+  D.k2 = greedy_d ? 0.f : static_cast<float>(log2e / static_cast<double>(draft_T));
   D.lse = draft_lse;
-  D.u = u_draft;
+  D.u = greedy_d ? nullptr : u_draft;
   D.sampled = draft_ids;
   D.nchunk = static_cast<int>(pl.nchunk_d);
   D.chunk = pl.chunk_d;
@@ -179,12 +197,12 @@ extern "C" vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *wei
   T.rows = pl.rows_t;
   T.n = V;
   T.ld = V;
-  T.T = target_T;
-  T.k2 = static_cast<float>(log2e / static_cast<double>(target_T));
+  T.T = greedy_t ? 1.0 : target_T;
+  T.k2 = greedy_t ? 0.f : static_cast<float>(log2e / static_cast<double>(target_T));
   T.lse = target_lse;
   T.nchunk = static_cast<int>(pl.nchunk_t);
   T.chunk = kChunk;
-  if (pl.nchunk_t > 1) T.part = reinterpret_cast<float2 *>(ws + pl.off_tpart);
+  if (!greedy_t && pl.nchunk_t > 1) T.part = reinterpret_cast<float2 *>(ws + pl.off_tpart);
 
   VfParams P{};
   P.target = target_logits;
@@ -201,8 +219,9 @@ extern "C" vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *wei
   P.V = V;
   P.Vt = Vt;
   P.R = R;
-  P.Tt = target_T;
-  P.Td = draft_T;
+  P.greedy = greedy_t;
+  P.Tt = greedy_t ? 1.0 : target_T;
+  P.Td = greedy_d ? 1.0 : draft_T;
   P.k2t = T.k2;
   P.k2d = D.k2;
   P.gamma = static_cast<int>(gamma);

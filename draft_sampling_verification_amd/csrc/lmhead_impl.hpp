@@ -58,11 +58,25 @@ __device__ __forceinline__ void swap16(float &x, float &y) {
   y = __uint_as_float(r[1]);
 }
 // DPP lane moves inside 16-lane rows: rotate by 8 (partner lane ^ 8), mirror within 8 lanes,
-// and the quad permutations that swap neighbours (lane ^ 1) and pairs (lane ^ 2).
-constexpr int kDppRor8 = 0x128, kDppHalfMirror = 0x141, kDppXor1 = 0xB1, kDppXor2 = 0x4E;
+// mirror within 16 lanes, and the quad permutations that swap neighbours (lane ^ 1) and pairs (lane ^ 2).
+constexpr int kDppRor8 = 0x128, kDppHalfMirror = 0x141, kDppMirror = 0x140, kDppXor1 = 0xB1, kDppXor2 = 0x4E;
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Reduction over each half-wave (lanes 0..31 and 32..63), the result in every lane of the half:
+// quad steps (lane ^ 1, ^ 2), then the mirrors within 8 and 16 lanes (after each step a lane's
+// partner holds the other half of its group), then lane ^ 16 -- all DPP / permlane moves, no LDS.
+template <typename Op>
+__device__ __forceinline__ float half_wave_reduce(float v, Op op) {
+  v = op(v, dpp<kDppXor1>(v));
+  v = op(v, dpp<kDppXor2>(v));
+  v = op(v, dpp<kDppHalfMirror>(v));
+  v = op(v, dpp<kDppMirror>(v));
+  float a = v, b = v;
+  swap16(a, b);
+  return op(a, b);
 }
 
 // Transpose-reduction of NP (1, 2, 4 or 8) per-lane partial sums over the 64 lanes.  The steps
@@ -474,13 +488,11 @@ __device__ __forceinline__ void big_tile_store(const f32x16 (&acc)[4][4], int M,
           x[j] = (n0 + wn + j * 32 + lr < Vt) ? acc[i][j][v] : kNegInf;
           mx = fmaxf(mx, x[j]);
         }
-#pragma unroll
-        for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+        mx = half_wave_reduce(mx, [](float a, float b) { return fmaxf(a, b); });
         float sm = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) sm += x[j] == kNegInf ? 0.f : __builtin_amdgcn_exp2f((x[j] - mx) * parts.k2);
-#pragma unroll
-        for (int o = 16; o > 0; o >>= 1) sm += __shfl_xor(sm, o, kWave);
+        sm = half_wave_reduce(sm, [](float a, float b) { return a + b; });
         if (lr == 0) wpart[w & 1][wm + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)] = make_float2(mx, sm);
       }
     __syncthreads();

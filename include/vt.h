@@ -183,9 +183,14 @@ size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
  *   instead of 4096-element chunks: ceil(Vt / 256) rounded up to a multiple of 4 rows when B*R <= 8,
  *   256 rows when B*R >= 256.  Draws can then differ from the separate calls only where a CDF
  *   boundary lies within rounding of the uniform.
- *   Both temperatures must be > 0 (greedy decoding: use the separate calls with T = 0).
+ *   target_T = 0 selects greedy verification as in vt_spec_verify ([VT] §4): no target softmax
+ *   runs, target_lse is not written, u_accept and u_final are not read (all three may be NULL).
+ *   draft_T = 0 (allowed only with target_T = 0) makes each draft the lowest id of its row's
+ *   maximum, draft_lse the row maximum, and u_draft is not read (may be NULL); the LM head then
+ *   runs without the fused softmax partials.
  *   Errors: INVALID_ARG for NULL required pointers, B, gamma, H, V or Vt <= 0, R < gamma, Vt > V,
- *   a temperature not finite or <= 0, keep_ids/full_to_trim inconsistent with Vt; UNSUPPORTED for
+ *   a temperature not finite or < 0, draft_T = 0 with target_T > 0, keep_ids/full_to_trim
+ *   inconsistent with Vt; UNSUPPORTED for
  *   gamma > 64, H % 8 != 0 or a hidden/weight base not 16-byte aligned; WORKSPACE if the workspace
  *   is smaller than vt_spec_block_workspace_bytes.
  */

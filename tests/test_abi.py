@@ -158,7 +158,10 @@ def blk(hidden=A, weight=A2, keep=A, f2t=A, B=4, gamma=5, R=6, H=3072, Vt=32768,
     (dict(ua=NUL), INV), (dict(uf=NUL), INV), (dict(dl=NUL), INV), (dict(dlse=NUL), INV), (dict(ids=NUL), INV),
     (dict(tlse=NUL), INV), (dict(tok=NUL), INV), (dict(nacc=NUL), INV), (dict(tdt=2), INV),
     (dict(B=0), INV), (dict(gamma=0), INV), (dict(R=4), INV), (dict(H=0), INV), (dict(Vt=0), INV),
-    (dict(V=1000), INV), (dict(Tt=0.0), INV), (dict(Td=math.nan), INV),
+    (dict(V=1000), INV), (dict(Tt=-1.0), INV), (dict(Td=math.nan), INV),
+    (dict(Td=0.0), INV),                                  # argmax drafts need greedy verification
+    (dict(Tt=0.0, Td=0.0, ud=NUL, ua=NUL, uf=NUL, tlse=NUL, ids=NUL), INV),  # greedy still writes ids
+    (dict(Tt=0.0, ua=NUL, uf=NUL, tlse=NUL, ud=NUL), INV),  # sampled drafts still need u_draft
     (dict(keep=NUL, f2t=NUL), INV), (dict(keep=NUL), INV), (dict(f2t=NUL), INV),
     (dict(gamma=65, R=65), UNS), (dict(H=3070), UNS), (dict(hidden=P(0x100004)), UNS),
     (dict(ws=NUL), WS), (dict(wsb=64), WS),

@@ -97,3 +97,49 @@ def test_greedy_flags_bad_ids():
     ids[1, 2] = 5000
     tok, n = _greedy_gpu(target, "f32", ids, None, None)
     assert n[1] == -1 and (tok[1] == -1).all() and n[0] >= 0 and n[2] >= 0
+
+
+def _block_greedy(wl, draft_T):
+    cfg = wl.cfg
+    B, R, g = wl.B, cfg.R, cfg.gamma
+    keep = dev(wl.keep_ids) if wl.keep_ids is not None else None
+    f2t = dev(wl.full_to_trim) if wl.full_to_trim is not None else None
+    target = dev(wl.target) if cfg.target_dtype == "f32" else dev_bf16(wl.target)
+    logits = torch.empty(B * R, cfg.Vt, dtype=torch.float32, device="cuda")
+    dlse = torch.empty(B * R, dtype=torch.float64, device="cuda")
+    dids = torch.empty(B * R, dtype=torch.int32, device="cuda")
+    tok = torch.full((B, g + 1), -9, dtype=torch.int32, device="cuda")
+    nacc = torch.empty(B, dtype=torch.int32, device="cuda")
+    ud = dev(wl.u_draft.reshape(-1)) if draft_T > 0 else None
+    vt.vt_spec_block(dev_bf16(wl.hidden), dev_bf16(wl.weight), keep, f2t, target, 0.0, draft_T, ud, None, None,
+                     logits, dlse, dids, None, tok, nacc)
+    torch.cuda.synchronize()
+    return (logits.cpu().numpy(), dlse.cpu().numpy(), dids.cpu().numpy().reshape(B, R), tok.cpu().numpy(),
+            nacc.cpu().numpy())
+
+
+@pytest.mark.parametrize("name,cfg,draft_T", [
+    ("c3-scaled argmax drafts", CONFIGS[3].scaled(B=4, V=20000, Vt=5000, H=512), 0.0),
+    ("c3-scaled sampled drafts", CONFIGS[3].scaled(B=4, V=20000, Vt=5000, H=512), 1.0),
+    ("c4-scaled argmax drafts", CONFIGS[4].scaled(B=24, V=9001, Vt=3000, H=256), 0.0),
+    ("c4 big tiles argmax drafts", CONFIGS[4].scaled(B=40, V=20000, Vt=5000, H=256), 0.0),
+    ("c5-scaled sampled drafts", CONFIGS[5].scaled(B=32, V=13000, Vt=6001, H=256), 0.8),
+    ("c2 full size argmax drafts", CONFIGS[2], 0.0),
+])
+def test_block_greedy(name, cfg, draft_T):
+    """vt_spec_block with target_T = 0: argmax drafts (draft_T = 0) decided on the call's own fp32
+    logits, or sampled drafts; the greedy verification is then exact against the oracle."""
+    say(f"fused block, greedy target: {name}")
+    wl = make_workload(cfg)
+    logits, dlse, ids, tok, n = _block_greedy(wl, draft_T)
+    B, R, g = wl.B, cfg.R, cfg.gamma
+    if draft_T == 0.0:
+        want_ids = np.array([ref.argmax_lowest(row) for row in logits]).reshape(B, R)
+        assert np.array_equal(ids, want_ids)
+        assert np.array_equal(dlse, logits.max(axis=1).astype(np.float64))
+    else:
+        assert np.all((ids >= 0) & (ids < cfg.Vt))
+    t64 = ref.as_f64(wl.target, cfg.target_dtype)
+    want_tok, want_n = ref.greedy_verify(t64, ids, wl.keep_ids, g)
+    say(f"  mean accepted {want_n.mean():.2f}")
+    assert np.array_equal(n, want_n) and np.array_equal(tok, want_tok)
