@@ -29,15 +29,11 @@ struct GenParams {
 };
 
 __device__ __forceinline__ double wave_max_d(double v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, kWave));
-  return v;
+  return wave_reduce(v, [](double a, double b) { return fmax(a, b); });
 }
 
 __device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_reduce(v, [](double a, double b) { return a + b; });
 }
 
 // Inverse-CDF draw over lanes 0..V-1 (token order) from weights w (0 on lanes >= V): the first
@@ -46,7 +42,7 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 __device__ __forceinline__ int wave_draw(float w, float u, int V) {
   const int lane = lane_id();
   const float C = wave_inclusive_scan(w);
-  const float Z = __shfl(C, V - 1, kWave);
+  const float Z = lane_value(C, V - 1);
   const float t = u * Z;
   const unsigned long long hit = __ballot(lane < V && t <= C);
   if (hit) return __ffsll(static_cast<long long>(hit)) - 1;
@@ -107,7 +103,7 @@ __global__ __launch_bounds__(kBlock) void markov_generate(GenParams P) {
       const unsigned long long rej = __ballot(lane < g && !ok);
       const int n = rej ? __ffsll(static_cast<long long>(rej)) - 1 : g;
       // final token: residual max(0, p_n - q_n) after a rejection, p_gamma after g acceptances
-      const int rn = n < g ? __shfl(myrow, n, kWave) : cur;
+      const int rn = n < g ? lane_value(myrow, n) : cur;
       const RowExp pe = make_row_exp(tlse[rn], P.Tt, P.k2t);
       const float p = on ? pe(tl[rn * V + lane]) : 0.f;
       float w = p;
@@ -115,7 +111,7 @@ __global__ __launch_bounds__(kBlock) void markov_generate(GenParams P) {
         const RowExp qe = make_row_exp(dlse[rn], P.Td, P.k2d);
         const float q = on ? qe(dl[rn * V + lane]) : 0.f;
         w = fmaxf(p - q, 0.f);
-        const float z = __shfl(wave_inclusive_scan(w), V - 1, kWave);
+        const float z = lane_value(wave_inclusive_scan(w), V - 1);
         if (!(z > 0.f)) w = p;
       }
       const int fin = wave_draw(w, ub[2 * g], V);

@@ -48,15 +48,11 @@ __device__ __forceinline__ int hottest_bin(const uint32_t *bins, int len, uint32
       bc = bins[i];
       bi = i;
     }
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    const uint32_t c2 = __shfl_xor(bc, o, kWave);
-    const int i2 = __shfl_xor(bi, o, kWave);
-    if (c2 > bc || (c2 == bc && i2 < bi)) {
-      bc = c2;
-      bi = i2;
-    }
-  }
+  // (count, -index) ordered as one 64-bit key: the wave maximum is the hottest, lowest bin
+  const uint64_t key = wave_reduce((static_cast<uint64_t>(bc) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(bi)),
+                                   [](uint64_t a, uint64_t b) { return a > b ? a : b; });
+  bc = static_cast<uint32_t>(key >> 32);
+  bi = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
   if (lane_id() == 0) {
     redc[wave_id()] = bc;
     redi[wave_id()] = bi;
@@ -142,8 +138,7 @@ __global__ __launch_bounds__(kHistThreads) void hist_slab(const int32_t *__restr
   }
   for (int64_t i = tail + threadIdx.x; i < b1; i += kHistThreads) add(tokens[i]);
   if (use_hot) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) hot_n += __shfl_xor(hot_n, o, kWave);
+    hot_n = wave_reduce(hot_n, [](uint32_t a, uint32_t b) { return a + b; });
     if (lane_id() == 0 && hot_n) atomicAdd(&bins[hot], hot_n);
   }
   __syncthreads();
@@ -180,28 +175,15 @@ constexpr int kDigitBits = 11;
 constexpr int kDigits = 1 << kDigitBits;   // 2048 buckets, two per thread
 
 template <typename T>
-__device__ __forceinline__ T wave_incl_scan_t(T v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const T y = __shfl_up(v, d, kWave);
-    if (lane >= d) v += y;
-  }
-  return v;
-}
-
-template <typename T>
 __device__ __forceinline__ T wave_sum_t(T v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_reduce(v, [](T a, T b) { return a + b; });
 }
 
 // Exclusive prefix over the 1024 threads in thread order; *total gets the sum of all.
 template <typename T>
 __device__ __forceinline__ T sel_exclusive_scan(T v, T *red, T *total) {
   const int lane = lane_id(), w = wave_id();
-  const T inc = wave_incl_scan_t(v);
+  const T inc = wave_scan_incl(v);
   __syncthreads();
   if (lane == kWave - 1) red[w] = inc;
   __syncthreads();
@@ -290,7 +272,7 @@ __device__ uint32_t radix_threshold(const SelParams &P, bool by_mass, uint64_t w
       const unsigned long long has = __ballot(cur >= 0);
       if (has) {
         const int leader = __ffsll(static_cast<long long>(has)) - 1;
-        const int d0 = __shfl(cur, leader, kWave);
+        const int d0 = lane_value(cur, leader);
         const bool same = cur >= 0 && cur == d0;
         const uint64_t tot = wave_sum_t<uint64_t>(same ? acc : 0);
         if (lane == leader) atomicAdd(reinterpret_cast<unsigned long long *>(&hist[d0]), tot);

@@ -42,29 +42,6 @@ __device__ __forceinline__ uint4 load_nt(const uint4 *p) {
   return r;
 }
 
-// ---- cross-lane exchange on gfx950
-// v_permlane32_swap: lanes 32..63 of the first operand trade places with lanes 0..31 of the
-// second; v_permlane16_swap does the same for the odd 16-lane rows of the first operand and the
-// even rows of the second.  Adding the two results sums each value with its partner at
-// lane ^ 32 (^ 16) while keeping the two values apart -- one instruction per pair, no selects.
-__device__ __forceinline__ void swap32(float &x, float &y) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-  x = __uint_as_float(r[0]);
-  y = __uint_as_float(r[1]);
-}
-__device__ __forceinline__ void swap16(float &x, float &y) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-  x = __uint_as_float(r[0]);
-  y = __uint_as_float(r[1]);
-}
-// DPP lane moves inside 16-lane rows: rotate by 8 (partner lane ^ 8), mirror within 8 lanes,
-// mirror within 16 lanes, and the quad permutations that swap neighbours (lane ^ 1) and pairs (lane ^ 2).
-constexpr int kDppRor8 = 0x128, kDppHalfMirror = 0x141, kDppMirror = 0x140, kDppXor1 = 0xB1, kDppXor2 = 0x4E;
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
 // Reduction over each half-wave (lanes 0..31 and 32..63), the result in every lane of the half:
 // quad steps (lane ^ 1, ^ 2), then the mirrors within 8 and 16 lanes (after each step a lane's
 // partner holds the other half of its group), then lane ^ 16 -- all DPP / permlane moves, no LDS.

@@ -29,39 +29,125 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 __device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return static_cast<int>(threadIdx.x) / kWave; }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
+// ---- cross-lane moves without LDS: DPP within 16-lane rows, v_permlane16/32_swap across rows.
+// (Shuffles with a computed lane index compile to ds_bpermute, an LDS round trip with a wait;
+// these are plain VALU operations.)
+// DPP controls: quad permutations that swap neighbours (lane ^ 1) and pairs (lane ^ 2), mirror
+// within 8 and 16 lanes, rotate a row by 8, shift a row right by 1, 2, 4, 8, broadcast lane 15 of
+// each row to the next row and lane 31 to the upper half, and shift the whole wave right by 1.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140, kDppRor8 = 0x128;
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143, kDppWaveShr1 = 0x138;
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-
-__device__ __forceinline__ int wave_min_int(int v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-
-__device__ __forceinline__ int wave_max_int(int v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-
-// Inclusive prefix sum across the 64 lanes of a wavefront (Hillis-Steele).
-__device__ __forceinline__ float wave_inclusive_scan(float v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    float y = __shfl_up(v, d, kWave);
-    if (lane >= d) v += y;
+// x from the DPP source lane; lanes without one (or in rows outside ROWMASK) get `old`.
+template <int CTRL, int ROWMASK = 0xF, typename T>
+__device__ __forceinline__ T lane_move(T x, T old) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(
+        T, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, x), CTRL, ROWMASK, 0xF,
+                                       false));
+  } else {
+    const int2 xv = __builtin_bit_cast(int2, x), ov = __builtin_bit_cast(int2, old);
+    int2 r;
+    r.x = __builtin_amdgcn_update_dpp(ov.x, xv.x, CTRL, ROWMASK, 0xF, false);
+    r.y = __builtin_amdgcn_update_dpp(ov.y, xv.y, CTRL, ROWMASK, 0xF, false);
+    return __builtin_bit_cast(T, r);
   }
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return lane_move<CTRL>(x, x);
+}
+
+// v_permlane32_swap: lanes 32..63 of the first operand trade places with lanes 0..31 of the
+// second; v_permlane16_swap does the same for the odd 16-lane rows of the first operand and the
+// even rows of the second.  With both operands equal, each lane then holds its own value and its
+// partner's at lane ^ 32 (^ 16), one in each result.
+__device__ __forceinline__ void swap32(float &x, float &y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap16(float &x, float &y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+template <bool k32, typename T>
+__device__ __forceinline__ void swap_rows(T &x, T &y) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  constexpr int W = sizeof(T) / 4;
+  uint32_t xa[W], ya[W];
+  __builtin_memcpy(xa, &x, sizeof(T));
+  __builtin_memcpy(ya, &y, sizeof(T));
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    const auto r = k32 ? __builtin_amdgcn_permlane32_swap(xa[w], ya[w], false, false)
+                       : __builtin_amdgcn_permlane16_swap(xa[w], ya[w], false, false);
+    xa[w] = r[0];
+    ya[w] = r[1];
+  }
+  __builtin_memcpy(&x, xa, sizeof(T));
+  __builtin_memcpy(&y, ya, sizeof(T));
+}
+
+// Reduction of a commutative, associative op over the 64 lanes, the result in every lane: quad
+// steps, the mirrors within 8 and 16 lanes (after each step a lane's partner holds the other
+// half of its group), then lane ^ 16 and lane ^ 32.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  v = op(v, lane_move<kDppXor1>(v, v));
+  v = op(v, lane_move<kDppXor2>(v, v));
+  v = op(v, lane_move<kDppHalfMirror>(v, v));
+  v = op(v, lane_move<kDppMirror>(v, v));
+  T a = v, b = v;
+  swap_rows<false>(a, b);
+  v = op(a, b);
+  a = v;
+  b = v;
+  swap_rows<true>(a, b);
+  return op(a, b);
+}
+
+__device__ __forceinline__ float wave_sum(float v) { return wave_reduce(v, [](float a, float b) { return a + b; }); }
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); }); }
+__device__ __forceinline__ int wave_min_int(int v) { return wave_reduce(v, [](int a, int b) { return min(a, b); }); }
+__device__ __forceinline__ int wave_max_int(int v) { return wave_reduce(v, [](int a, int b) { return max(a, b); }); }
+
+// Inclusive prefix sum across the 64 lanes: shifts by 1, 2, 4, 8 inside each 16-lane row, then
+// the last lane of each row is added to the next row and lane 31 to the upper half.
+template <typename T>
+__device__ __forceinline__ T wave_scan_incl(T v) {
+  const T z = T(0);
+  v = v + lane_move<kDppRowShr1>(v, z);
+  v = v + lane_move<kDppRowShr2>(v, z);
+  v = v + lane_move<kDppRowShr4>(v, z);
+  v = v + lane_move<kDppRowShr8>(v, z);
+  v = v + lane_move<kDppRowBcast15, 0xA>(v, z);
+  v = v + lane_move<kDppRowBcast31, 0xC>(v, z);
   return v;
+}
+__device__ __forceinline__ float wave_inclusive_scan(float v) { return wave_scan_incl(v); }
+
+// The previous lane's value (`first` in lane 0).
+template <typename T>
+__device__ __forceinline__ T wave_prev(T v, T first) {
+  return lane_move<kDppWaveShr1>(v, first);
+}
+
+// Lane k's value in every lane (k uniform across the wave).
+template <typename T>
+__device__ __forceinline__ T lane_value(T v, int k) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), k));
+  } else {
+    int2 x = __builtin_bit_cast(int2, v);
+    x.x = __builtin_amdgcn_readlane(x.x, k);
+    x.y = __builtin_amdgcn_readlane(x.y, k);
+    return __builtin_bit_cast(T, x);
+  }
 }
 
 // Workgroup-wide reductions (all kBlock threads must call; result broadcast to every thread).
@@ -128,16 +214,18 @@ __device__ __forceinline__ bool argmax_better(float v1, int i1, float v2, int i2
   return v1 > v2 || (v1 == v2 && i1 < i2);
 }
 
+struct ValIdx {
+  float v;
+  int i;
+};
 __device__ __forceinline__ void wave_argmax(float &v, int &i) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    const float v2 = __shfl_xor(v, o, kWave);
-    const int i2 = __shfl_xor(i, o, kWave);
-    if (argmax_better(v2, i2, v, i)) {
-      v = v2;
-      i = i2;
-    }
-  }
+  const uint64_t best = wave_reduce(__builtin_bit_cast(uint64_t, ValIdx{v, i}), [](uint64_t a, uint64_t b) {
+    const ValIdx x = __builtin_bit_cast(ValIdx, a), y = __builtin_bit_cast(ValIdx, b);
+    return argmax_better(y.v, y.i, x.v, x.i) ? b : a;
+  });
+  const ValIdx r = __builtin_bit_cast(ValIdx, best);
+  v = r.v;
+  i = r.i;
 }
 
 // Workgroup argmax (all threads call; result broadcast).  redv/redi: LDS scratch of 4 entries.
@@ -166,7 +254,7 @@ __device__ __forceinline__ void block_argmax(float &v, int &i, float *redv, int 
 __device__ __forceinline__ float block_inclusive_scan(float v, float *red, float *prev, float *total) {
   const int lane = lane_id(), w = wave_id();
   const float inc = wave_inclusive_scan(v);
-  const float up = __shfl_up(inc, 1, kWave);
+  const float up = wave_prev(inc, 0.f);
   __syncthreads();
   if (lane == kWave - 1) red[w] = inc;
   __syncthreads();
