@@ -79,6 +79,21 @@ def lmhead_bytes(cfg) -> int:
     return b
 
 
+def small_batch_block(cfg, greedy: bool = False) -> bool:
+    """Batch-1-sized blocks (at most 8 draft rows, both sides sampled): the GEMV head launch also
+    runs the target rows' first softmax pass in extra workgroups."""
+    return cfg.B * cfg.R <= 8 and not greedy
+
+
+def lmhead_launch_bytes(cfg, greedy: bool = False, calls: bool = False) -> int:
+    """Algorithmic bytes of the timed head launch: the LM head's, plus the target logits when the
+    fused call's GEMV launch also takes the target partials."""
+    b = lmhead_bytes(cfg)
+    if small_batch_block(cfg, greedy) and not calls:
+        b += cfg.B * (cfg.gamma + 1) * cfg.V * (4 if cfg.target_dtype == "f32" else 2)
+    return b
+
+
 def lmhead_flops(cfg) -> float:
     return 2.0 * cfg.B * cfg.R * cfg.H * cfg.Vt
 
@@ -96,7 +111,7 @@ def block_bytes(cfg, greedy: bool = False) -> int:
     return lm + draft_sm + target_sm + verify
 
 
-LMHEAD_SOURCES = ("lmhead_impl.hpp", "vt_common.hpp", "block.hip")
+LMHEAD_SOURCES = ("lmhead_impl.hpp", "softmax_impl.hpp", "vt_common.hpp", "block.hip")
 
 
 def kernel_source_hash() -> str:
@@ -168,7 +183,7 @@ def write_traffic_record(config: int, fetch_csv, write_csv, copy_fetch_csv, copy
                              "fetch_scale": fs, "write_scale": wsc},
         "hbm_fetch_bytes_per_launch": round(fetch_kib * 1024 * fs),
         "hbm_write_bytes_per_launch": round(write_kib * 1024 * wsc),
-        "algorithmic_read_bytes": lmhead_bytes(cfg) - alg_w, "algorithmic_write_bytes": alg_w,
+        "algorithmic_read_bytes": lmhead_launch_bytes(cfg) - alg_w, "algorithmic_write_bytes": alg_w,
         "commands": [
             f"rocprofv3 --pmc FETCH_SIZE -f csv -d <out> -o bench -- python3 bench.py --config {config} "
             "--no-cpu-baseline --steps 10 --warmup 3",
@@ -179,7 +194,7 @@ def write_traffic_record(config: int, fetch_csv, write_csv, copy_fetch_csv, copy
             f"python3 bench.py --config {config} --traffic-record <4 csv files>"],
     }
     rec["hbm_bytes_per_launch"] = rec["hbm_fetch_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
-    rec["traffic_over_algorithmic"] = round(rec["hbm_bytes_per_launch"] / lmhead_bytes(cfg), 4)
+    rec["traffic_over_algorithmic"] = round(rec["hbm_bytes_per_launch"] / lmhead_launch_bytes(cfg), 4)
     out = os.path.join(ROOT, "profiles", f"lmhead_traffic_config{config}.json")
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)
@@ -610,13 +625,14 @@ def main():
     lm_ms = sum(x.elapsed_time(y) for x, y in zip(ev_a, ev_b)) / n_ev
 
     value = B * g / (ms_per_step / 1e3)
-    lmb = lmhead_bytes(cfg)
+    lmb = lmhead_launch_bytes(cfg, args.greedy, args.calls)
     achieved = lmb / (lm_ms / 1e3) / 1e9
     wl_key = f"config{args.config}"
     traffic = measured_traffic(wl_key)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "lmhead_gemv" if B * R <= 8 else "lmhead_mfma",
+            "kernel": ("lmhead_gemv" if B * R <= 8 else "lmhead_mfma")
+                      + (" + target softmax partials" if small_batch_block(cfg, args.greedy) and not args.calls else ""),
             "algorithmic_bytes_per_launch": lmb, "avg_launch_ms": round(lm_ms, 5)}
     if B * R > 8:
         tf = lmhead_flops(cfg) / (lm_ms / 1e3) / 1e12

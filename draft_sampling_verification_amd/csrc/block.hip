@@ -10,12 +10,15 @@
 //      the small MFMA path a partials launch follows
 //   3. one combine launch for the draft rows (lse + draws) and the target rows (lse)
 //   4. verify pass 1 (accept scans, residual chunk sums) and pass 2 (final draws, outputs)
-// Batch-1 decode: 5 launches instead of 7.  Launch order never lets an independent kernel sit
-// between the LM head and its consumers.
+// Launch order never lets an independent kernel sit between the LM head and its consumers.
+// Small batches (the GEMV head, both sides sampled) take 3 launches instead: the target
+// partials ride in extra workgroups of the GEMV launch, and one chunk pass forms every
+// log-normaliser, draft draw, accept scan and residual chunk sum, followed by the final draw.
 #include <algorithm>
 
 #include "lmhead_impl.hpp"
 #include "softmax_impl.hpp"
+#include "verify_fused.hpp"
 #include "verify_impl.hpp"
 
 namespace vt {
@@ -24,6 +27,8 @@ namespace {
 struct BlockPlan {
   bool fused;       // GEMV with draft partials in its epilogue
   bool fused_mfma;  // large-batch MFMA tiles with draft partials in their epilogue
+  bool fv;          // small batch, sampling both sides: target partials ride in the GEMV launch,
+                    // then one chunk pass and one final pass (verify_fused_chunk / _final)
   int64_t M, rows_t;
   int64_t nchunk_t;  // 4096-chunks of a target row
   int64_t nchunk_d;  // draft partial chunks per row (GEMV row blocks, or 4096-chunks)
@@ -52,16 +57,17 @@ BlockPlan plan_block(int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt,
     p.nchunk_d = (Vt + kChunk - 1) / kChunk;
     p.chunk_d = kChunk;
   }
-  p.nchunk_v = (V + kChunk - 1) / kChunk;
+  p.fv = p.fused && !greedy_t && R <= kFvMaxR && p.nchunk_d <= kFvMaxParts;
+  p.nchunk_v = (V + (p.fv ? kFvIds : kChunk) - 1) / (p.fv ? kFvIds : kChunk);
   size_t off = 0;
   p.off_tpart = off;
-  if (p.nchunk_t > 1) off += align_up(static_cast<size_t>(p.rows_t * p.nchunk_t) * sizeof(float2), 256);
+  if (p.nchunk_t > 1 || p.fv) off += align_up(static_cast<size_t>(p.rows_t * p.nchunk_t) * sizeof(float2), 256);
   p.off_dpart = off;
   if (p.fused || p.fused_mfma || p.nchunk_d > 1)
     off += align_up(static_cast<size_t>(p.M * p.nchunk_d) * sizeof(float2), 256);
   p.off_nbuf = off;
   p.off_vpart = off;
-  if (p.nchunk_v > 1) {
+  if (p.nchunk_v > 1 || p.fv) {
     off += align_up(static_cast<size_t>(B) * sizeof(int), 256);
     p.off_vpart = off;
     off += align_up(static_cast<size_t>(B * (gamma + 1) * p.nchunk_v) * sizeof(float2), 256);
@@ -82,10 +88,48 @@ hipError_t launch_combine(const SmParams &D, bool d_multi, const SmParams &T, bo
   return hipSuccess;
 }
 
+// Small batch, sampling both sides: 3 launches.  The GEMV launch carries the target rows'
+// chunk partials in extra workgroups; the chunk pass forms every log-normaliser and draft draw
+// itself from the partials; the final pass draws the last token.
+template <typename TinT, bool kVecT>
+hipError_t run_block_small(const BlockPlan &pl, const SmParams &D, const SmParams &T, const VfParams &Vp,
+                           const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int64_t H,
+                           int64_t Vt, float *logits, const float *u_draft, int64_t B, hipEvent_t ev0,
+                           hipEvent_t ev1, hipStream_t stream) {
+  hipError_t e = hipSuccess;
+  GemvParts gp{};
+  gp.part = D.part;
+  gp.k2 = D.k2;
+  gp.tgt = T;
+  gp.tsel = sizeof(TinT) == 4 ? (kVecT ? 1 : 2) : (kVecT ? 3 : 4);
+  if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
+  e = launch_gemv(pick_gemv<true>(pl.M, H, keep != nullptr), hidden, weight, keep, H, Vt, logits, gp, stream,
+                  T.rows * T.nchunk);
+  if (e != hipSuccess) return e;
+  if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
+  FvParams F{};
+  F.v = Vp;
+  F.dpart = D.part;
+  F.nd = static_cast<int>(pl.nchunk_d);
+  F.dper = pl.chunk_d;
+  F.udraft = u_draft;
+  F.tpart = T.part;
+  F.nt = T.nchunk;
+  F.dlse_out = D.lse;
+  F.dids_out = D.sampled;
+  F.tlse_out = T.lse;
+  e = launch(verify_fused_chunk<TinT, kVecT>, dim3(static_cast<unsigned>(B * Vp.nchunk)), dim3(kFvBlock), 0, stream,
+             F);
+  if (e != hipSuccess) return e;
+  return launch(verify_fused_final<TinT, kVecT>, dim3(static_cast<unsigned>(B)), dim3(kBlock), 0, stream, Vp);
+}
+
 template <typename TinT, bool kVecT, bool kVecD>
 hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, const VfParams &Vp,
                      const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int64_t H, int64_t Vt,
                      float *logits, int64_t B, hipEvent_t ev0, hipEvent_t ev1, hipStream_t stream) {
+  if (pl.fv) return run_block_small<TinT, kVecT>(pl, D, T, Vp, hidden, weight, keep, H, Vt, logits, D.u, B, ev0, ev1,
+                                                 stream);
   hipError_t e = hipSuccess;
   const bool greedy_t = Vp.greedy;
   const bool t_multi = !greedy_t && pl.nchunk_t > 1;
@@ -202,7 +246,7 @@ extern "C" vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *wei
   T.lse = target_lse;
   T.nchunk = static_cast<int>(pl.nchunk_t);
   T.chunk = kChunk;
-  if (!greedy_t && pl.nchunk_t > 1) T.part = reinterpret_cast<float2 *>(ws + pl.off_tpart);
+  if (!greedy_t && (pl.nchunk_t > 1 || pl.fv)) T.part = reinterpret_cast<float2 *>(ws + pl.off_tpart);
 
   VfParams P{};
   P.target = target_logits;
@@ -226,7 +270,7 @@ extern "C" vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *wei
   P.k2d = D.k2;
   P.gamma = static_cast<int>(gamma);
   P.nchunk = static_cast<int>(pl.nchunk_v);
-  if (pl.nchunk_v > 1) {
+  if (pl.nchunk_v > 1 || pl.fv) {
     P.nbuf = reinterpret_cast<int *>(ws + pl.off_nbuf);
     P.part = reinterpret_cast<float2 *>(ws + pl.off_vpart);
   }

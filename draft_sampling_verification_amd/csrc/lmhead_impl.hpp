@@ -16,6 +16,7 @@
 
 #include <cstdint>
 
+#include "softmax_impl.hpp"
 #include "vt_common.hpp"
 
 namespace vt {
@@ -133,10 +134,26 @@ inline int gemv_blocks(int64_t Vt) {
 // Draft softmax partials produced by the GEMV epilogue (optional): for every hidden row m and
 // workgroup block k, (max_j x_mj, sum_j exp((x_mj - max) / T)) over the block's rows j, written
 // to part[m * nblocks + k] (k2 = log2(e) / T).
+// The batch-1 block also hands the GEMV launch the target rows' first softmax pass: workgroups
+// past the head's row blocks each take one (row, 4096-chunk) of the target logits (tsel: 0 none,
+// 1 fp32 16-byte loads, 2 fp32 element loads, 3 bf16 16-byte loads, 4 bf16 element loads), so
+// that pass overlaps the head instead of preceding it.
 struct GemvParts {
   float2 *part;
   float k2;
+  SmParams tgt;
+  int tsel;
 };
+
+__device__ __forceinline__ void target_partial_chunk(const GemvParts &parts, int64_t t) {
+  switch (parts.tsel) {
+    case 1: partial_chunk<float, true>(parts.tgt, t); break;
+    case 2: partial_chunk<float, false>(parts.tgt, t); break;
+    case 3: partial_chunk<uint16_t, true>(parts.tgt, t); break;
+    case 4: partial_chunk<uint16_t, false>(parts.tgt, t); break;
+    default: break;
+  }
+}
 
 // Workgroup k owns head rows [k * per, (k + 1) * per); its four wavefronts take every fourth row of
 // the block, so the workgroup streams one contiguous region of the head (measured ~10% faster than
@@ -154,6 +171,13 @@ __global__ __launch_bounds__(kBlock) void lmhead_gemv(const uint16_t *__restrict
                                                       float *__restrict__ logits, GemvParts parts) {
   constexpr int NP = Pow2Ceil<M>::value;
   constexpr int kGroup = kWave / NP;
+  const int nblk = (Vt + per - 1) / per;
+  if constexpr (PARTS) {
+    if (static_cast<int>(blockIdx.x) >= nblk) {
+      target_partial_chunk(parts, static_cast<int64_t>(blockIdx.x) - nblk);
+      return;
+    }
+  }
   const int lane = lane_id();
   const int pieces = H >> 3;  // 16-byte pieces per row
   auto piece = [&](int it) -> int {
@@ -241,7 +265,7 @@ __global__ __launch_bounds__(kBlock) void lmhead_gemv(const uint16_t *__restrict
         const float2 v = wpart[w][m];
         if (v.x != kNegInf) sx += v.y * __builtin_amdgcn_exp2f((v.x - mx) * parts.k2);
       }
-      parts.part[static_cast<int64_t>(m) * gridDim.x + blockIdx.x] = make_float2(mx, sx);
+      parts.part[static_cast<int64_t>(m) * nblk + blockIdx.x] = make_float2(mx, sx);
     }
   }
 }
@@ -762,9 +786,11 @@ inline hipError_t launch_mfma_big(const uint16_t *hidden, const uint16_t *weight
                 static_cast<int>(M), static_cast<int>(H), static_cast<int>(Vt), logits, parts);
 }
 
+// extra: workgroups past the head's row blocks (target partial chunks; PARTS kernels only).
 inline hipError_t launch_gemv(GemvFn fn, const uint16_t *hidden, const uint16_t *weight, const int32_t *keep,
-                              int64_t H, int64_t Vt, float *logits, GemvParts parts, hipStream_t stream) {
-  return launch(fn, dim3(static_cast<unsigned>(gemv_blocks(Vt))), dim3(kBlock), 0, stream, hidden, weight, keep,
+                              int64_t H, int64_t Vt, float *logits, GemvParts parts, hipStream_t stream,
+                              int64_t extra = 0) {
+  return launch(fn, dim3(static_cast<unsigned>(gemv_blocks(Vt) + extra)), dim3(kBlock), 0, stream, hidden, weight, keep,
                 static_cast<int>(H), static_cast<int>(Vt), gemv_rows_per_block(Vt), logits, parts);
 }
 

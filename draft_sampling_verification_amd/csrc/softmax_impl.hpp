@@ -174,10 +174,11 @@ __global__ __launch_bounds__(kBlock) void softmax_single(SmParams P) {
 // Rows of several chunks, pass 1: one workgroup per (row, chunk) publishes the chunk's
 // (max m_c, sum s_c of exp((x - m_c)/T)).  The next launch reads them (kernel boundaries order
 // the two passes; no device-wide fences are needed).
+// Workgroup `bid` of the pass: row bid / nchunk, chunk bid % nchunk.  Also run by extra
+// workgroups of the batch-1 LM-head launch, so it takes its index as an argument.
 template <typename Tin, bool kVec>
-__global__ __launch_bounds__(kBlock) void softmax_partial(SmParams P) {
+__device__ __forceinline__ void partial_chunk(const SmParams &P, int64_t bid) {
   __shared__ float redf[kWavesPerBlock];
-  const int64_t bid = blockIdx.x;
   const int64_t r = bid / P.nchunk;
   const int c = static_cast<int>(bid - r * P.nchunk);
   const Tin *row = reinterpret_cast<const Tin *>(P.logits) + r * P.ld;
@@ -203,6 +204,11 @@ __global__ __launch_bounds__(kBlock) void softmax_partial(SmParams P) {
   for (int j = 0; j < kPerThread; ++j) s += w[j];
   s = block_sum(s, redf);
   if (threadIdx.x == 0) P.part[r * P.nchunk + c] = make_float2(m, s);
+}
+
+template <typename Tin, bool kVec>
+__global__ __launch_bounds__(kBlock) void softmax_partial(SmParams P) {
+  partial_chunk<Tin, kVec>(P, blockIdx.x);
 }
 
 // Pass 2 for one row r: combine the chunks into M = max m_c, S_c = s_c exp((m_c - M)/T), the

@@ -78,44 +78,47 @@ __device__ __forceinline__ float load_logit(const Tin *row, int64_t i) {
 // full_to_trim entries and, for an ascending keep set, consecutive draft entries) into LDS and
 // read back in the thread's order: a per-thread loop over its 16 ids would make every load
 // instruction touch 64 different cache lines.  All threads of the workgroup must call.
-template <typename Tin, bool kVec>
-__device__ __forceinline__ void final_weights(const VfParams &P, int64_t b, int n, int c, bool use_p, float (&wv)[16],
-                                              float (&pv)[16]) {
-  __shared__ __align__(16) float sq[kChunk];
+// PER ids per thread: chunks of PER * 256 ids (16: the 4096-id chunks of the separate verify
+// call; 4: the 1024-id chunks of the batch-1 block).
+template <typename Tin, bool kVec, int PER = kPerThread>
+__device__ __forceinline__ void final_weights(const VfParams &P, int64_t b, int n, int c, bool use_p, float (&wv)[PER],
+                                              float (&pv)[PER]) {
+  constexpr int kIds = PER * kBlock;
+  __shared__ __align__(16) float sq[kIds];
   const int row = n < P.gamma ? n : P.gamma;
   const Tin *trow = reinterpret_cast<const Tin *>(P.target) + (b * (P.gamma + 1) + row) * P.V;
-  float lt[16];
-  load16<Tin, kVec>(trow, P.V, static_cast<int64_t>(c) * kChunk, lt);
+  float lt[PER];
+  load_run<Tin, kVec, PER>(trow, P.V, static_cast<int64_t>(c) * kIds, lt);
   const RowExp pe = make_row_exp(P.tlse[b * (P.gamma + 1) + row], P.Tt, P.k2t);
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) pv[j] = pe(lt[j]);
+  for (int j = 0; j < PER; ++j) pv[j] = pe(lt[j]);
   if (n >= P.gamma || use_p) {
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) wv[j] = pv[j];
+    for (int j = 0; j < PER; ++j) wv[j] = pv[j];
     return;
   }
   const float *drow = P.draft + (b * P.R + n) * P.Vt;
   const RowExp qe = make_row_exp(P.dlse[b * P.R + n], P.Td, P.k2d);
-  const int64_t base = static_cast<int64_t>(c) * kChunk;
+  const int64_t base = static_cast<int64_t>(c) * kIds;
   __syncthreads();  // a previous call's readers are done with sq
-  int32_t tv[kPerThread];
+  int32_t tv[PER];
 #pragma unroll
-  for (int r = 0; r < kPerThread; ++r) {
+  for (int r = 0; r < PER; ++r) {
     const int64_t x = base + r * kBlock + threadIdx.x;
     tv[r] = x < P.V ? (P.f2t ? P.f2t[x] : static_cast<int32_t>(x)) : -1;
   }
-  float dv[kPerThread];
+  float dv[PER];
 #pragma unroll
-  for (int r = 0; r < kPerThread; ++r) {
+  for (int r = 0; r < PER; ++r) {
     const int32_t t = tv[r];
     dv[r] = (t >= 0 && t < P.Vt) ? drow[t] : kNegInf;
   }
 #pragma unroll
-  for (int r = 0; r < kPerThread; ++r) sq[r * kBlock + threadIdx.x] = qe(dv[r]);
+  for (int r = 0; r < PER; ++r) sq[r * kBlock + threadIdx.x] = qe(dv[r]);
   __syncthreads();
-  const float4 *q4 = reinterpret_cast<const float4 *>(sq + threadIdx.x * kPerThread);
+  const float4 *q4 = reinterpret_cast<const float4 *>(sq + threadIdx.x * PER);
 #pragma unroll
-  for (int k = 0; k < kPerThread / 4; ++k) {
+  for (int k = 0; k < PER / 4; ++k) {
     const float4 q = q4[k];
     wv[4 * k + 0] = fmaxf(pv[4 * k + 0] - q.x, 0.f);
     wv[4 * k + 1] = fmaxf(pv[4 * k + 1] - q.y, 0.f);
@@ -159,7 +162,7 @@ __device__ __forceinline__ int accept_scan(const VfParams &P, int64_t b, int *sh
 
 // Final draw and outputs of sequence b, given n and the chunk sums of the residual (or bonus)
 // weights and of p (mass(k, use_p)); all threads of the workgroup must call.
-template <typename Tin, bool kVec, typename Mass>
+template <typename Tin, bool kVec, typename Mass, int PER = kPerThread>
 __device__ __forceinline__ void finish_sequence(const VfParams &P, int64_t b, int n, Mass mass, float *redf,
                                                 int *redi, float *bcast) {
   const int gamma = P.gamma;
@@ -215,12 +218,12 @@ __device__ __forceinline__ void finish_sequence(const VfParams &P, int64_t b, in
     fallback = true;
   }
   // rescan chunk c*: running sum inside it, first id reaching t (else last positive id)
-  float wv[16], pv[16];
-  final_weights<Tin, kVec>(P, b, n, cstar, use_p, wv, pv);
-  float loc[16];
+  float wv[PER], pv[PER];
+  final_weights<Tin, kVec, PER>(P, b, n, cstar, use_p, wv, pv);
+  float loc[PER];
   float acc = 0.f;
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
+  for (int j = 0; j < PER; ++j) {
     acc += wv[j];
     loc[j] = acc;
   }
@@ -230,18 +233,18 @@ __device__ __forceinline__ void finish_sequence(const VfParams &P, int64_t b, in
   int found = 0x7fffffff;
   if (!fallback) {
 #pragma unroll
-    for (int j = kPerThread - 1; j >= 0; --j)
-      if (t <= base + loc[j]) found = static_cast<int>(threadIdx.x) * kPerThread + j;
+    for (int j = PER - 1; j >= 0; --j)
+      if (t <= base + loc[j]) found = static_cast<int>(threadIdx.x) * PER + j;
   }
   found = block_min_int(found, redi);
   if (found == 0x7fffffff) {
     int last = -1;
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j)
-      if (wv[j] > 0.f) last = static_cast<int>(threadIdx.x) * kPerThread + j;
+    for (int j = 0; j < PER; ++j)
+      if (wv[j] > 0.f) last = static_cast<int>(threadIdx.x) * PER + j;
     found = block_max_int(last, redi);
   }
-  const int32_t final_id = static_cast<int32_t>(static_cast<int64_t>(cstar) * kChunk + found);
+  const int32_t final_id = static_cast<int32_t>(static_cast<int64_t>(cstar) * (PER * kBlock) + found);
   for (int i = threadIdx.x; i <= gamma; i += kBlock) {
     int32_t v = -1;
     if (i < n) {

@@ -270,25 +270,27 @@ __device__ __forceinline__ float block_inclusive_scan(float v, float *red, float
   return before + inc;
 }
 
-// The 16 contiguous elements [base + 16 t, base + 16 t + 16) of a row as fp32; -inf past n.
-template <typename Tin, bool kVec>
-__device__ __forceinline__ void load16(const Tin *__restrict__ row, int64_t n, int64_t base, float (&v)[16]) {
-  const int64_t e0 = base + static_cast<int64_t>(threadIdx.x) * kPerThread;
-  if (kVec && e0 + kPerThread <= n) {
+// The N contiguous elements [base + N t, base + N t + N) of a row as fp32 (t = thread index);
+// -inf past n.  kVec: the row start is 16-byte aligned and n a multiple of 8 (bf16) or 4 (fp32).
+template <typename Tin, bool kVec, int N>
+__device__ __forceinline__ void load_run(const Tin *__restrict__ row, int64_t n, int64_t base, float (&v)[N]) {
+  static_assert(N % 4 == 0, "whole 4-element pieces");
+  const int64_t e0 = base + static_cast<int64_t>(threadIdx.x) * N;
+  if (kVec && e0 + N <= n) {
     if constexpr (sizeof(Tin) == 4) {
       const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(row) + e0);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < N / 4; ++q) {
         const float4 f = p[q];
         v[4 * q + 0] = f.x;
         v[4 * q + 1] = f.y;
         v[4 * q + 2] = f.z;
         v[4 * q + 3] = f.w;
       }
-    } else {
+    } else if constexpr (N % 8 == 0) {
       const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(row) + e0);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+      for (int q = 0; q < N / 8; ++q) {
         const uint4 b = p[q];
         const unsigned int wds[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
@@ -297,10 +299,20 @@ __device__ __forceinline__ void load16(const Tin *__restrict__ row, int64_t n, i
           v[8 * q + 2 * k + 1] = __uint_as_float(wds[k] & 0xffff0000u);
         }
       }
+    } else {
+      const uint2 *p = reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(row) + e0);
+#pragma unroll
+      for (int q = 0; q < N / 4; ++q) {
+        const uint2 b = p[q];
+        v[4 * q + 0] = __uint_as_float(b.x << 16);
+        v[4 * q + 1] = __uint_as_float(b.x & 0xffff0000u);
+        v[4 * q + 2] = __uint_as_float(b.y << 16);
+        v[4 * q + 3] = __uint_as_float(b.y & 0xffff0000u);
+      }
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
+    for (int j = 0; j < N; ++j) {
       const int64_t e = e0 + j;
       if (e < n) {
         if constexpr (sizeof(Tin) == 4)
@@ -312,6 +324,11 @@ __device__ __forceinline__ void load16(const Tin *__restrict__ row, int64_t n, i
       }
     }
   }
+}
+
+template <typename Tin, bool kVec>
+__device__ __forceinline__ void load16(const Tin *__restrict__ row, int64_t n, int64_t base, float (&v)[16]) {
+  load_run<Tin, kVec, kPerThread>(row, n, base, v);
 }
 
 // Launch with an explicit status: arguments are converted to the kernel's parameter types and
