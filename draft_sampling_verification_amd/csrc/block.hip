@@ -228,6 +228,7 @@ extern "C" vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *wei
   D.ld = Vt;
   D.greedy = greedy_d;
   D.T = greedy_d ? 1.0 : draft_T;
+  D.invT = 1.0 / D.T;
   D.k2 = greedy_d ? 0.f : static_cast<float>(log2e / static_cast<double>(draft_T));
   D.lse = draft_lse;
   D.u = greedy_d ? nullptr : u_draft;
@@ -242,6 +243,7 @@ extern "C" vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *wei
   T.n = V;
   T.ld = V;
   T.T = greedy_t ? 1.0 : target_T;
+  T.invT = 1.0 / T.T;
   T.k2 = greedy_t ? 0.f : static_cast<float>(log2e / static_cast<double>(target_T));
   T.lse = target_lse;
   T.nchunk = static_cast<int>(pl.nchunk_t);
@@ -266,6 +268,8 @@ extern "C" vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *wei
   P.greedy = greedy_t;
   P.Tt = greedy_t ? 1.0 : target_T;
   P.Td = greedy_d ? 1.0 : draft_T;
+  P.invTt = 1.0 / P.Tt;
+  P.invTd = 1.0 / P.Td;
   P.k2t = T.k2;
   P.k2d = D.k2;
   P.gamma = static_cast<int>(gamma);

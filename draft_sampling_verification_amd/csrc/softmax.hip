@@ -30,6 +30,7 @@ extern "C" vt_status_t vt_softmax_temp(const void *logits, vt_dtype_t dtype, int
   P.ld = ld;
   P.greedy = greedy;
   P.T = greedy ? 1.0 : static_cast<double>(temperature);
+  P.invT = 1.0 / P.T;
   P.k2 = greedy ? 0.f : static_cast<float>(1.4426950408889634 / static_cast<double>(temperature));
   P.lse = lse;
   P.probs = probs;

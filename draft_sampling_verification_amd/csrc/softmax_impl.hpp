@@ -33,6 +33,7 @@ struct SmParams {
   int64_t rows, n, ld;
   float k2;   // log2(e) / T
   double T;
+  double invT;  // 1 / T, rounded once on the host: log-normalisers take M * invT
   double *lse;
   float *probs;
   const float *u;
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(kBlock) void softmax_single(SmParams P) {
   }
   __syncthreads();
   const float Z = bcast;
-  if (threadIdx.x == 0) P.lse[r] = static_cast<double>(m) / P.T + log(static_cast<double>(Z));
+  if (threadIdx.x == 0) P.lse[r] = static_cast<double>(m) * P.invT + log(static_cast<double>(Z));
   if (P.probs) {
     const float inv = 1.f / Z;
     float *pr = P.probs + r * P.n;
@@ -249,7 +250,7 @@ __device__ __forceinline__ void combine_row(const SmParams &P, int64_t r, float 
   }
   const float Z = carry;
   if (threadIdx.x == 0) {
-    P.lse[r] = static_cast<double>(M) / P.T + log(static_cast<double>(Z));
+    P.lse[r] = static_cast<double>(M) * P.invT + log(static_cast<double>(Z));
     if (P.rowstat) P.rowstat[r] = make_float2(M, Z);
   }
   if (!P.u) return;

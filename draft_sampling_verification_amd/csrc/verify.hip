@@ -47,6 +47,8 @@ extern "C" vt_status_t vt_spec_verify(int64_t B, int64_t gamma, int64_t V, int64
   P.greedy = greedy;
   P.Tt = greedy ? 1.0 : target_T;
   P.Td = greedy ? 1.0 : draft_T;
+  P.invTt = 1.0 / P.Tt;
+  P.invTd = 1.0 / P.Td;
   P.k2t = greedy ? 0.f : static_cast<float>(kLog2e / static_cast<double>(target_T));
   P.k2d = greedy ? 0.f : static_cast<float>(kLog2e / static_cast<double>(draft_T));
   P.gamma = static_cast<int>(gamma);

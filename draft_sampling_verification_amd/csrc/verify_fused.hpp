@@ -13,10 +13,11 @@
 //      launch left behind (per head row block for the draft rows, per 4096-chunk for the target
 //      rows).
 //   1. Wave w draws draft row w (log-normaliser from the partials, the block whose running mass
-//      reaches u Z, then a scan of that block's logits) and forms the log-normaliser of target
-//      rows w and w + 8.  Every workgroup of the sequence repeats this small amount of work, so
-//      no workgroup waits for another; the first chunk's workgroup writes the outputs.
-//   2. Wave 0 runs the accept scan (fp64 ratios, a ballot gives n = first rejection).
+//      reaches u Z, then a scan of that block's logits and keep ids), forms the log-normaliser
+//      of target rows w and w + 8, and runs the accept test of draft w (fp64 ratio).  Every
+//      workgroup of the sequence repeats this small amount of work, so no workgroup waits for
+//      another; the first chunk's workgroup writes the outputs.
+//   2. After one barrier every thread reads the verdicts: n = first rejection.
 //   3. From the registers loaded in step 0: the chunk sums of w(x) = max(0, p_n(x) - q_n(x))
 //      (p_gamma when every draft was kept) and of p_n(x).
 // Final pass: one workgroup per sequence locates the 1024-id chunk where the running residual
@@ -27,6 +28,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "softmax_impl.hpp"
 #include "verify_impl.hpp"
@@ -58,72 +60,102 @@ struct FvParams {
   double *tlse_out;      // [B * (gamma + 1)]
 };
 
-// Two consecutive elements [e0, e0 + 2) of a row as fp32; -inf past n.  kVec: the row start is
-// 16-byte aligned and n even, so the pair is one aligned load.
+// Raw bits of two consecutive elements [e0, e0 + 2) of a row (even e0), loaded unconditionally
+// at an index clamped into the row.  Nothing here looks at the loaded values: a select on them
+// would make the compiler wait for each load on the spot, so the caller masks entries past the
+// row end where it uses them.  kVec: the row start is 16-byte aligned and n a multiple of 4, so
+// the pair is one aligned load.
+template <typename Tin>
+struct RawPair {
+  typename std::conditional<sizeof(Tin) == 4, float2, uint32_t>::type v;
+};
+
 template <typename Tin, bool kVec>
-__device__ __forceinline__ void load_pair(const Tin *__restrict__ row, int64_t n, int64_t e0, float (&v)[2]) {
-  if (kVec && e0 + 2 <= n) {
-    if constexpr (sizeof(Tin) == 4) {
-      const float2 f = *reinterpret_cast<const float2 *>(reinterpret_cast<const float *>(row) + e0);
-      v[0] = f.x;
-      v[1] = f.y;
+__device__ __forceinline__ RawPair<Tin> load_pair_raw(const Tin *__restrict__ row, int64_t n, int64_t e0) {
+  RawPair<Tin> r;
+  if constexpr (sizeof(Tin) == 4) {
+    if constexpr (kVec) {
+      r.v = *reinterpret_cast<const float2 *>(reinterpret_cast<const float *>(row) + (e0 < n ? e0 : n - 2));
     } else {
-      const uint32_t u = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(row) + e0);
-      v[0] = __uint_as_float(u << 16);
-      v[1] = __uint_as_float(u & 0xffff0000u);
+      const float *f = reinterpret_cast<const float *>(row);
+      r.v.x = f[e0 < n ? e0 : n - 1];
+      r.v.y = f[e0 + 1 < n ? e0 + 1 : n - 1];
     }
   } else {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t e = e0 + j;
-      v[j] = e < n ? load_logit(row, e) : kNegInf;
+    if constexpr (kVec) {
+      r.v = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(row) + (e0 < n ? e0 : n - 2));
+    } else {
+      const uint16_t *h = reinterpret_cast<const uint16_t *>(row);
+      r.v = static_cast<uint32_t>(h[e0 < n ? e0 : n - 1]) | (static_cast<uint32_t>(h[e0 + 1 < n ? e0 + 1 : n - 1]) << 16);
     }
   }
+  return r;
+}
+
+template <typename Tin>
+__device__ __forceinline__ float pair_elem(const RawPair<Tin> &r, int j) {
+  if constexpr (sizeof(Tin) == 4)
+    return j ? r.v.y : r.v.x;
+  else
+    return __uint_as_float(j ? (r.v & 0xffff0000u) : (r.v << 16));
 }
 
 // Draft row m, one wavefront: lse = M / T + ln Z from the head's per-block partials; the draw
 // t = u Z walks the block-level running sum to the first block reaching t, then that block's
-// logits.  pv: the row's partials (entry k = 64 j + lane), loaded by the caller.  Returns the
-// drawn index (-1 if nothing carries weight) and its logit.
-__device__ __forceinline__ void fv_draft_row(const FvParams &F, int64_t m, const float2 (&pv)[4], float u,
-                                             double &lse, int &x, float &xl) {
+// logits.  Lane l holds blocks 4l .. 4l+3 (pv, loaded by the caller) and, in the rescan, logits
+// 8l .. 8l+7 of each 512-logit batch: a lane-local running sum plus one wavefront scan per level.
+// Returns the drawn trimmed index x (-1 if nothing carries weight), its logit and its full id
+// keep[x] (x itself without a keep set).
+struct DraftDraw {
+  double lse;
+  int x;
+  int64_t y;
+  float xl;
+};
+
+__device__ __forceinline__ DraftDraw fv_draft_row(const FvParams &F, int64_t m, const float2 (&pv)[4], float u) {
   const int lane = lane_id();
   const float k2 = F.v.k2d;
-  float mx = kNegInf;
+  float px[4];  // block maxima, -inf past the last block
 #pragma unroll
-  for (int j = 0; j < 4; ++j) mx = fmaxf(mx, pv[j].x);
+  for (int j = 0; j < 4; ++j) px[j] = 4 * lane + j < F.nd ? pv[j].x : kNegInf;
+  float mx = fmaxf(fmaxf(px[0], px[1]), fmaxf(px[2], px[3]));
   const float M = wave_max(mx);
-  float mass[4], inc[4], before[4];
-  float carry = 0.f;
+  float mass[4], lp[4];  // this lane's block masses and their running sum
+  float acc = 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    mass[j] = pv[j].x == kNegInf ? 0.f : pv[j].y * exp2_fast((pv[j].x - M) * k2);
-    inc[j] = wave_scan_incl(mass[j]);
-    before[j] = carry;
-    carry = carry + lane_value(inc[j], kWave - 1);
+    mass[j] = px[j] == kNegInf ? 0.f : pv[j].y * exp2_fast((px[j] - M) * k2);
+    acc += mass[j];
+    lp[j] = acc;
   }
-  const float Z = carry;
-  lse = static_cast<double>(M) / F.v.Td + log(static_cast<double>(Z));
+  const float inc = wave_scan_incl(acc);
+  const float excl = wave_prev(inc, 0.f);
+  const float Z = lane_value(inc, kWave - 1);
   const float t = u * Z;
-  int ks = -1;
-  float E = 0.f;
+  // first block k = 4 lane + j with t <= excl + lp[j]
+  int jf = 4;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const unsigned long long hit = __ballot(kWave * j + lane < F.nd && t <= before[j] + inc[j]);
-    const float prev = wave_prev(inc[j], 0.f);
-    if (ks < 0 && hit) {
-      const int l = __ffsll(static_cast<long long>(hit)) - 1;
-      ks = kWave * j + l;
-      E = before[j] + lane_value(prev, l);
-    }
-  }
+  for (int j = 3; j >= 0; --j)
+    if (4 * lane + j < F.nd && t <= excl + lp[j]) jf = j;
+  const unsigned long long hit = __ballot(jf < 4);
+  int ks;
+  float E = 0.f;
   bool fallback = false;
-  if (ks < 0) {
+  if (hit) {
+    const int l = __ffsll(static_cast<long long>(hit)) - 1;
+    float before = excl;
+#pragma unroll
+    for (int j = 1; j < 4; ++j)
+      if (jf == j) before = excl + lp[j - 1];
+    ks = 4 * l + lane_value(jf, l);
+    E = lane_value(before, l);
+  } else {
     // t beyond the running sum (u >= 1 or NaN): the last block with positive mass
     int last = -1;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (kWave * j + lane < F.nd && mass[j] > 0.f) last = kWave * j + lane;
+      if (4 * lane + j < F.nd && mass[j] > 0.f) last = 4 * lane + j;
     ks = max(wave_max_int(last), 0);
     fallback = true;
   }
@@ -133,72 +165,104 @@ __device__ __forceinline__ void fv_draft_row(const FvParams &F, int64_t m, const
   const int64_t r1 = r0 + F.dper < F.v.Vt ? r0 + F.dper : F.v.Vt;
   const float te = fallback ? __builtin_huge_valf() : t;
   float run = fallback ? 0.f : E;
-  int found = -1, lastpos = -1;
-  float fl = kNegInf;
-  for (int64_t g0 = r0; g0 < r1 && found < 0; g0 += kWave * kFvScanBatch) {
+  DraftDraw d{};
+  d.lse = static_cast<double>(M) * F.v.invTd + log(static_cast<double>(Z));
+  d.x = -1;
+  d.xl = kNegInf;
+  int lastpos = -1;
+  for (int64_t g0 = r0; g0 < r1 && d.x < 0; g0 += kWave * kFvScanBatch) {
+    const int64_t e0 = g0 + kFvScanBatch * lane;
     float vals[kFvScanBatch];
+    int32_t ids[kFvScanBatch];
 #pragma unroll
     for (int q = 0; q < kFvScanBatch; ++q) {
-      const int64_t e = g0 + kWave * q + lane;
-      vals[q] = e < r1 ? row[e] : kNegInf;
+      const int64_t e = e0 + q < r1 ? e0 + q : r1 - 1;  // clamped: unconditional loads
+      vals[q] = row[e];
+      ids[q] = F.v.keep ? F.v.keep[e] : static_cast<int32_t>(e);
+      if (e0 + q >= r1) vals[q] = kNegInf;
     }
+    float loc[kFvScanBatch];
+    float a = 0.f;
 #pragma unroll
     for (int q = 0; q < kFvScanBatch; ++q) {
-      const int64_t e = g0 + kWave * q + lane;
       const float wgt = M == kNegInf ? 0.f : exp2_fast((vals[q] - M) * k2);
-      const float G = run + wave_scan_incl(wgt);
-      if (e < r1 && wgt > 0.f) lastpos = static_cast<int>(e);
-      const unsigned long long hit = __ballot(e < r1 && te <= G);
-      if (found < 0 && hit) {
-        const int l = __ffsll(static_cast<long long>(hit)) - 1;
-        found = static_cast<int>(g0 + kWave * q + l);
-        fl = lane_value(vals[q], l);
-      }
-      run = lane_value(G, kWave - 1);
+      if (e0 + q < r1 && wgt > 0.f) lastpos = static_cast<int>(e0 + q);
+      a += wgt;
+      loc[q] = a;
+    }
+    const float binc = wave_scan_incl(a);
+    const float base = run + wave_prev(binc, 0.f);
+    int qf = kFvScanBatch;
+#pragma unroll
+    for (int q = kFvScanBatch - 1; q >= 0; --q)
+      if (e0 + q < r1 && te <= base + loc[q]) qf = q;
+    const unsigned long long bh = __ballot(qf < kFvScanBatch);
+    if (bh) {
+      const int l = __ffsll(static_cast<long long>(bh)) - 1;
+      float v = vals[0];
+      int32_t id = ids[0];
+#pragma unroll
+      for (int q = 1; q < kFvScanBatch; ++q)
+        if (qf == q) {
+          v = vals[q];
+          id = ids[q];
+        }
+      const int ql = lane_value(qf, l);
+      d.x = static_cast<int>(g0 + kFvScanBatch * l + ql);
+      d.xl = lane_value(v, l);
+      d.y = lane_value(id, l);
+    }
+    run = run + lane_value(binc, kWave - 1);
+  }
+  if (d.x < 0) {
+    d.x = wave_max_int(lastpos);
+    if (d.x >= 0) {
+      d.xl = row[d.x];
+      d.y = F.v.keep ? F.v.keep[d.x] : d.x;
     }
   }
-  if (found < 0) {
-    found = wave_max_int(lastpos);
-    if (found >= 0) fl = row[found];
-  }
-  x = found;
-  xl = fl;
+  return d;
 }
 
 // Log-normaliser of target row r from its 4096-chunk partials, one wavefront, with exactly the
 // operations (and so the bits) of the combine pass of the separate softmax call: chunk masses
-// scanned 64 at a time, four scans to a 256-chunk pass added in order, passes carried.  p0: the
-// row's first 64 partials, loaded by the caller.
+// scanned 64 at a time, four scans to a 256-chunk pass added in order, passes carried (a group
+// past the last chunk adds +0 there, so it is skipped here).  p0: the row's first 64 partials,
+// loaded by the caller (lanes past the last chunk hold a repeated entry and are masked here).
 __device__ __forceinline__ double fv_target_lse(const FvParams &F, int64_t r, float2 p0) {
   const int lane = lane_id();
   const float2 *pp = F.tpart + r * F.nt;
+  if (lane >= F.nt) p0 = make_float2(kNegInf, 0.f);
   float mx = p0.x;
-  for (int k = kWave + lane; k < F.nt; k += kWave) mx = fmaxf(mx, pp[k].x);
+  for (int k0 = kWave; k0 < F.nt; k0 += kWave) {
+    const int k = k0 + lane;
+    const float2 ps = pp[k < F.nt ? k : F.nt - 1];
+    if (k < F.nt) mx = fmaxf(mx, ps.x);
+  }
   const float M = wave_max(mx);
+  auto mass = [&](float2 ps, int k) -> float {
+    return (k < F.nt && ps.x != kNegInf) ? ps.y * exp2_fast((ps.x - M) * F.v.k2t) : 0.f;
+  };
+  // first 64 chunks from p0 (no load on this path: a load here would wait for every load in flight)
+  float total = 0.f;
+  total += lane_value(wave_scan_incl(mass(p0, lane)), kWave - 1);
   float carry = 0.f;
   for (int k0 = 0; k0 < F.nt; k0 += kBlock) {
-    float total = 0.f;
-#pragma unroll
-    for (int q = 0; q < kWavesPerBlock; ++q) {
+    if (k0 > 0) total = 0.f;
+    for (int q = k0 == 0 ? 1 : 0; q < kWavesPerBlock; ++q) {
+      if (k0 + kWave * q >= F.nt) break;
       const int k = k0 + kWave * q + lane;
-      float s = 0.f;
-      if (k < F.nt) {
-        const float2 ps = k < kWave ? p0 : pp[k];
-        s = ps.x == kNegInf ? 0.f : ps.y * exp2_fast((ps.x - M) * F.v.k2t);
-      }
-      total += lane_value(wave_scan_incl(s), kWave - 1);
+      total += lane_value(wave_scan_incl(mass(pp[k < F.nt ? k : F.nt - 1], k)), kWave - 1);
     }
     carry = carry + total;
   }
-  return static_cast<double>(M) / F.v.Tt + log(static_cast<double>(carry));
+  return static_cast<double>(M) * F.v.invTt + log(static_cast<double>(carry));
 }
 
 template <typename Tin, bool kVec>
 __global__ __launch_bounds__(kFvBlock) void verify_fused_chunk(FvParams F) {
   __shared__ double s_tlse[kFvMaxT], s_dlse[kFvMaxR];
-  __shared__ float s_dlog[kFvMaxR];
-  __shared__ int s_x[kFvMaxR];
-  __shared__ int s_n;
+  __shared__ int s_acc[kFvMaxR];  // accept test of draft i: 1 kept, 0 rejected, -1 invalid id
   __shared__ float2 s_red[kFvWaves];
   const VfParams &P = F.v;
   // all chunks of a sequence on one XCD: the gathered draft rows meet in that XCD's L2
@@ -208,123 +272,129 @@ __global__ __launch_bounds__(kFvBlock) void verify_fused_chunk(FvParams F) {
   const int lane = lane_id(), w = static_cast<int>(threadIdx.x) / kWave;
   const int g = P.gamma, R = static_cast<int>(P.R);
 
-  // 0. loads that need nothing computed first
+  // 0. loads that need nothing computed first, all at clamped in-range indices and none of them
+  //    inspected until its use (see load_pair_raw)
   const int64_t x0 = static_cast<int64_t>(c) * kFvIds + kFvPer * static_cast<int64_t>(threadIdx.x);
   int32_t ti[kFvPer];
 #pragma unroll
   for (int j = 0; j < kFvPer; ++j) {
     const int64_t x = x0 + j;
-    ti[j] = x < P.V ? (P.f2t ? P.f2t[x] : static_cast<int32_t>(x)) : -1;
+    ti[j] = P.f2t ? P.f2t[x < P.V ? x : P.V - 1] : static_cast<int32_t>(x);
   }
   const bool my_draft = w < R && (w < g || c == 0);  // rows past gamma only feed the outputs
   const int64_t m = b * R + w;
   float2 pv[4];
   float ud = 0.f;
+  if (my_draft) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int k = kWave * j + lane;
-    pv[j] = (my_draft && k < F.nd) ? F.dpart[m * F.nd + k] : make_float2(kNegInf, 0.f);
+    for (int j = 0; j < 4; ++j) {
+      const int k = 4 * lane + j;
+      pv[j] = F.dpart[m * F.nd + (k < F.nd ? k : F.nd - 1)];
+    }
+    ud = F.udraft[m];
   }
-  if (my_draft) ud = F.udraft[m];
+  const float ua = w < g ? P.uacc[b * g + w] : 0.f;
   float2 tp[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int i = w + kFvWaves * s;
-    tp[s] = (i <= g && lane < F.nt) ? F.tpart[(b * (g + 1) + i) * F.nt + lane] : make_float2(kNegInf, 0.f);
+    tp[s] = make_float2(kNegInf, 0.f);
+    if (i <= g) tp[s] = F.tpart[(b * (g + 1) + i) * F.nt + (lane < F.nt ? lane : F.nt - 1)];
   }
-  float tg[kFvMaxT][kFvPer];
+  RawPair<Tin> tg[kFvMaxT];
 #pragma unroll
   for (int i = 0; i < kFvMaxT; ++i) {
-    if (i <= g) {
-      load_pair<Tin, kVec>(reinterpret_cast<const Tin *>(P.target) + (b * (g + 1) + i) * P.V, P.V, x0, tg[i]);
-    } else {
-      tg[i][0] = tg[i][1] = kNegInf;
-    }
+    const int ri = i <= g ? i : g;  // rows past gamma repeat row gamma (never selected)
+    tg[i] = load_pair_raw<Tin, kVec>(reinterpret_cast<const Tin *>(P.target) + (b * (g + 1) + ri) * P.V, P.V, x0);
   }
+  bool on[kFvPer];  // id inside the vocabulary and kept
+#pragma unroll
+  for (int j = 0; j < kFvPer; ++j) on[j] = x0 + j < P.V && ti[j] >= 0 && ti[j] < P.Vt;
   float dg[kFvMaxR][kFvPer];
 #pragma unroll
   for (int i = 0; i < kFvMaxR; ++i) {
-    const float *drow = P.draft + (b * R + i) * P.Vt;
+    const int ri = i < g ? i : g - 1;  // rows past gamma - 1 repeat row gamma - 1 (never selected)
+    const float *drow = P.draft + (b * R + ri) * P.Vt;
 #pragma unroll
-    for (int j = 0; j < kFvPer; ++j) dg[i][j] = (i < g && ti[j] >= 0 && ti[j] < P.Vt) ? drow[ti[j]] : kNegInf;
+    for (int j = 0; j < kFvPer; ++j) dg[i][j] = drow[on[j] ? ti[j] : 0];
   }
 
-  // 1. draft row w: log-normaliser and draw; target rows w, w + 8: log-normalisers
+  // 1. wave w: draw of draft row w; log-normalisers of target rows w and w + 8; accept test of
+  //    draft w (fp64 ratio exp(a - d), a and d the two log-probabilities of the drafted token)
+  DraftDraw dd{};
+  bool valid = false;
+  float tl = 0.f;
   if (my_draft) {
-    double lse;
-    int x;
-    float xl;
-    fv_draft_row(F, m, pv, ud, lse, x, xl);
+    dd = fv_draft_row(F, m, pv, ud);
+    valid = dd.x >= 0 && dd.x < P.Vt && dd.y >= 0 && dd.y < P.V;
+    if (w < g && valid)  // the target logit of the drafted token, in flight during the target lse
+      tl = load_logit(reinterpret_cast<const Tin *>(P.target) + (b * (g + 1) + w) * P.V, dd.y);
     if (lane == 0) {
-      s_dlse[w] = lse;
-      s_x[w] = x;
-      s_dlog[w] = xl;
+      s_dlse[w] = dd.lse;
       if (c == 0) {
-        F.dlse_out[m] = lse;
-        F.dids_out[m] = x;
+        F.dlse_out[m] = dd.lse;
+        F.dids_out[m] = dd.x;
       }
     }
   }
+  double tl_w = 0.0;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int i = w + kFvWaves * s;
     if (i <= g) {
       const double l = fv_target_lse(F, b * (g + 1) + i, tp[s]);
+      if (s == 0) tl_w = l;
       if (lane == 0) {
         s_tlse[i] = l;
         if (c == 0) F.tlse_out[b * (g + 1) + i] = l;
       }
     }
   }
-  __syncthreads();
-
-  // 2. accept scan: lanes 0..gamma-1 of wave 0; n = first rejection, gamma if none, -1 if a
-  //    draft id (or its full id) is out of range
-  if (w == 0) {
-    bool valid = true, accept = true;
-    if (lane < g) {
-      const int x = s_x[lane];
-      valid = x >= 0 && x < P.Vt;
-      int64_t y = x;
-      if (valid && P.keep) {
-        y = P.keep[x];
-        valid = y >= 0 && y < P.V;
-      }
-      if (valid) {
-        const Tin *trow = reinterpret_cast<const Tin *>(P.target) + (b * (g + 1) + lane) * P.V;
-        const double a = static_cast<double>(load_logit(trow, y)) / P.Tt - s_tlse[lane];
-        const double d = static_cast<double>(s_dlog[lane]) / P.Td - s_dlse[lane];
-        accept = static_cast<double>(P.uacc[b * g + lane]) <= fmin(1.0, exp(a - d));
-      }
+  if (w < g && lane == 0) {
+    int verdict = -1;
+    if (valid) {
+      const double a = static_cast<double>(tl) * P.invTt - tl_w;
+      const double d = static_cast<double>(dd.xl) * P.invTd - dd.lse;
+      verdict = accept_ratio(ua, a - d) ? 1 : 0;
     }
-    const unsigned long long bad = __ballot(lane < g && !valid);
-    const unsigned long long rej = __ballot(lane < g && !accept);
-    if (lane == 0) s_n = bad ? -1 : (rej ? __ffsll(static_cast<long long>(rej)) - 1 : g);
+    s_acc[w] = verdict;
   }
   __syncthreads();
 
+  // 2. n = first rejected draft, gamma if none, -1 if any draft id is out of range
+  int n = g;
+  bool bad = false;
+  for (int i = 0; i < g; ++i) {
+    const int a = s_acc[i];
+    bad = bad || a < 0;
+    if (a == 0 && n == g) n = i;
+  }
+  if (bad) n = -1;
+
   // 3. chunk sums of the final-draw weights of row n and of p_n
-  const int n = s_n;
   float sw = 0.f, sp = 0.f;
   if (n >= 0) {
-    float t2[kFvPer], d2[kFvPer];
+    RawPair<Tin> tn = tg[0];
+    float d2[kFvPer];
 #pragma unroll
-    for (int j = 0; j < kFvPer; ++j) {
-      t2[j] = tg[0][j];
-      d2[j] = dg[0][j];
-    }
+    for (int j = 0; j < kFvPer; ++j) d2[j] = dg[0][j];
 #pragma unroll
     for (int i = 1; i < kFvMaxT; ++i)
       if (i == n) {
+        tn = tg[i];
 #pragma unroll
-        for (int j = 0; j < kFvPer; ++j) {
-          t2[j] = tg[i][j];
+        for (int j = 0; j < kFvPer; ++j)
           if (i < kFvMaxR) d2[j] = dg[i][j];
-        }
       }
-    const RowExp pe = make_row_exp(s_tlse[n], P.Tt, P.k2t);
+    float t2[kFvPer];
+#pragma unroll
+    for (int j = 0; j < kFvPer; ++j) {
+      t2[j] = x0 + j < P.V ? pair_elem(tn, j) : kNegInf;
+      if (!on[j]) d2[j] = kNegInf;
+    }
+    const RowExp pe = make_row_exp_inv(s_tlse[n], P.Tt, P.invTt, P.k2t);
     if (n < g) {
-      const RowExp qe = make_row_exp(s_dlse[n], P.Td, P.k2d);
+      const RowExp qe = make_row_exp_inv(s_dlse[n], P.Td, P.invTd, P.k2d);
 #pragma unroll
       for (int j = 0; j < kFvPer; ++j) {
         const float p = pe(t2[j]);

@@ -41,6 +41,7 @@ struct VfParams {
   float2 *part;  // (sum of final-draw weights, sum of p) per (sequence, chunk)
   int64_t V, Vt, R;
   double Tt, Td;
+  double invTt, invTd;  // 1 / T, rounded once on the host
   float k2t, k2d;  // log2(e) / T
   int gamma;
   int nchunk;
@@ -62,6 +63,29 @@ __device__ __forceinline__ RowExp make_row_exp(double lse, double T, float k2) {
   e.d2 = static_cast<float>((lse - static_cast<double>(e.c0) / T) * kLog2e);
   e.k2 = k2;
   return e;
+}
+
+// The same with a host-rounded 1 / T in place of the division.
+__device__ __forceinline__ RowExp make_row_exp_inv(double lse, double T, double invT, float k2) {
+  RowExp e;
+  e.c0 = static_cast<float>(lse * T);
+  e.d2 = static_cast<float>((lse - static_cast<double>(e.c0) * invT) * kLog2e);
+  e.k2 = k2;
+  return e;
+}
+
+// u <= min(1, exp(x)), the accept test with fp64 log-ratio x, decided exactly as in fp64: a
+// single-precision 2^(x log2 e) settles it whenever u lies outside a 1e-5 relative band around
+// it (its error is below 2^-24 |x| from the exponent's rounding plus one ulp, under 1e-5 for
+// every result above 1e-30); otherwise, and for tiny ratios, the fp64 exp decides.
+__device__ __forceinline__ bool accept_ratio(float u, double x) {
+  if (!(x < 0.0)) return u <= 1.f;  // ratio 1 (a NaN ratio also reads as 1 under fmin)
+  const float r = __builtin_amdgcn_exp2f(static_cast<float>(x * kLog2e));
+  if (r >= 1e-30f) {
+    const float du = u - r;
+    if (fabsf(du) > 1e-5f * r) return du < 0.f;
+  }
+  return static_cast<double>(u) <= exp(x);
 }
 
 template <typename Tin>

@@ -55,9 +55,24 @@ __device__ __forceinline__ T lane_move(T x, T old) {
     return __builtin_bit_cast(T, r);
   }
 }
+// x from the DPP source lane for patterns in which every lane has one (quad permutations,
+// mirrors, rotations).  Written with bound_ctrl and no old value, so the compiler can fold the
+// move into the consuming VALU operation (one v_*_dpp instead of a copy, a wait state and a move).
+template <int CTRL, typename T>
+__device__ __forceinline__ T lane_swap(T x) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+  } else {
+    int2 v = __builtin_bit_cast(int2, x);
+    v.x = __builtin_amdgcn_mov_dpp(v.x, CTRL, 0xF, 0xF, true);
+    v.y = __builtin_amdgcn_mov_dpp(v.y, CTRL, 0xF, 0xF, true);
+    return __builtin_bit_cast(T, v);
+  }
+}
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return lane_move<CTRL>(x, x);
+  return lane_swap<CTRL>(x);
 }
 
 // v_permlane32_swap: lanes 32..63 of the first operand trade places with lanes 0..31 of the
@@ -97,10 +112,10 @@ __device__ __forceinline__ void swap_rows(T &x, T &y) {
 // half of its group), then lane ^ 16 and lane ^ 32.
 template <typename T, typename Op>
 __device__ __forceinline__ T wave_reduce(T v, Op op) {
-  v = op(v, lane_move<kDppXor1>(v, v));
-  v = op(v, lane_move<kDppXor2>(v, v));
-  v = op(v, lane_move<kDppHalfMirror>(v, v));
-  v = op(v, lane_move<kDppMirror>(v, v));
+  v = op(v, lane_swap<kDppXor1>(v));
+  v = op(v, lane_swap<kDppXor2>(v));
+  v = op(v, lane_swap<kDppHalfMirror>(v));
+  v = op(v, lane_swap<kDppMirror>(v));
   T a = v, b = v;
   swap_rows<false>(a, b);
   v = op(a, b);
@@ -120,10 +135,11 @@ __device__ __forceinline__ int wave_max_int(int v) { return wave_reduce(v, [](in
 template <typename T>
 __device__ __forceinline__ T wave_scan_incl(T v) {
   const T z = T(0);
-  v = v + lane_move<kDppRowShr1>(v, z);
-  v = v + lane_move<kDppRowShr2>(v, z);
-  v = v + lane_move<kDppRowShr4>(v, z);
-  v = v + lane_move<kDppRowShr8>(v, z);
+  // row shifts: bound_ctrl gives 0 to the lanes without a source
+  v = v + lane_swap<kDppRowShr1>(v);
+  v = v + lane_swap<kDppRowShr2>(v);
+  v = v + lane_swap<kDppRowShr4>(v);
+  v = v + lane_swap<kDppRowShr8>(v);
   v = v + lane_move<kDppRowBcast15, 0xA>(v, z);
   v = v + lane_move<kDppRowBcast31, 0xC>(v, z);
   return v;
