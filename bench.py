@@ -2,8 +2,10 @@
 """Benchmark of the draft-sampling / verification hot path on one MI355X.
 
 One step = one speculative block over the workload's batch: by default the fused call
-vt_spec_block (LM head with the draft softmax's first pass in its epilogue, one combine launch
-for draft and target rows, two verify launches); with --calls the four separate calls
+vt_spec_block (at batch 1: the LM head launch with the draft and target softmax partials, one
+chunk pass that draws, accepts and sums the residual, one final draw; larger batches: LM head
+with the draft partials, target partials, one combine launch, two verify launches); with
+--calls the four separate calls
   vt_lmhead_trimmed -> vt_softmax_temp (draft, with draws) -> vt_softmax_temp (target) -> vt_spec_verify
 on synthetic inputs already resident in HBM.  Default workload: B=1, gamma=5, hidden 3072, full
 128256-row drafter head, fp32 target logits, T=1 (config 2 of the workload recipe).

@@ -165,9 +165,12 @@ size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
 /*
  * vt_spec_block -- one whole speculative block in one call: the trimmed LM head, the draft
  * softmax with draws, the target softmax and the verification, i.e. the four calls above, with
- * the kernels fused where the dependencies allow (5 launches for decode-sized batches instead
- * of 7: the LM head also emits the draft softmax's first pass, and one launch finishes both the
- * draft and the target rows).
+ * the kernels fused where the dependencies allow.  Decode-sized batches (B*R <= 8, both sides
+ * sampled) take 3 launches instead of 7: the LM head launch also emits the draft softmax's
+ * first pass and, in extra workgroups, the target rows' first pass; one chunk pass over the
+ * full vocabulary forms the log-normalisers, draft draws, accept tests and residual chunk sums;
+ * one final pass draws the last token.  Larger batches take 5 (LM head with the draft partials,
+ * target partials, one combine launch for both row sets, two verify passes).
  *   Pages: as for the four calls above.
  *
  *   hidden bf16 [B*R][H] (row b*R + i is sequence b's i-th draft position); weight bf16 [V][H]
