@@ -23,6 +23,21 @@ SCALED = {
 }
 
 
+# Decode-sized blocks (B*R <= 8, both sides sampled) run the three-launch path: each case reaches
+# a branch of it the configs above do not.
+SMALL = {
+    "b1-wide-vocab": CONFIGS[3].scaled(V=300000, Vt=20000, H=256),        # > 64 target chunks
+    "b1-gamma8": CONFIGS[3].scaled(gamma=8, R=8, V=20000, Vt=5000, H=256),  # target row 8 on wave 0
+    "b1-bf16-target": CONFIGS[4].scaled(B=1, gamma=5, R=6, V=20000, Vt=5000, H=256),
+    "b1-bf16-ragged": CONFIGS[4].scaled(B=1, gamma=4, R=5, V=9001, Vt=1234, H=520),  # element loads
+    "b2-r4": CONFIGS[3].scaled(B=2, gamma=3, R=4, V=20000, Vt=5000, H=256),
+    "b1-rows-past-gamma": CONFIGS[3].scaled(gamma=3, R=6, V=20000, Vt=5000, H=256),
+    "b1-cold": CONFIGS[3].scaled(T=0.3, V=20000, Vt=5000, H=256),
+    "b1-tiny-head": CONFIGS[3].scaled(V=3000, Vt=64, H=256),  # 4-row head blocks, one chunk
+    "b1-full-head": CONFIGS[2].scaled(V=20000, Vt=20000, H=512),  # untrimmed: no full_to_trim
+}
+
+
 def _check(wl):
     gpu = gpu_block_fused(wl)
     orc = oracle_block(wl)
@@ -40,6 +55,44 @@ def _check(wl):
 def test_fused_block_parity_scaled(name):
     say(f"fused block parity {name}")
     _check(make_workload(SCALED[name]))
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_fused_block_parity_small_batch(name):
+    say(f"fused block parity {name} (three-launch path)")
+    _check(make_workload(SMALL[name]))
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_fused_block_small_batch_long_runs(name):
+    # a drafter that follows the target: accepted runs of every length, rejections at every
+    # position and full acceptance (the bonus draw from p_gamma) over six seeds
+    say(f"fused block parity {name}, following drafter")
+    seen = set()
+    for b0 in range(6):
+        _, orc = _check(make_workload(SMALL[name], b0=b0, follow=0.5))
+        seen.update(int(x) for x in orc["n"])
+    say(f"  accepted counts seen: {sorted(seen)}")
+    assert len(seen) >= 2 and max(seen) > 0
+
+
+@pytest.mark.parametrize("name", ["c4-batched-mfma", "c4-big-tiles", "c5-mfma", "c5-big-tiles"])
+def test_fused_block_following_drafter(name):
+    say(f"fused block parity {name}, following drafter")
+    _, orc = _check(make_workload(SCALED[name], follow=0.5))
+    say(f"  accepted counts: {np.bincount(orc['n'], minlength=SCALED[name].gamma + 1).tolist()}")
+    assert orc["n"].max() > 0
+
+
+@pytest.mark.parametrize("name", ["b1-wide-vocab", "b1-bf16-target", "b1-bf16-ragged"])
+def test_small_batch_matches_separate_calls(name):
+    wl = make_workload(SMALL[name])
+    a = gpu_block(wl)
+    b = gpu_block_fused(wl)
+    assert np.array_equal(a["draft_logits"], b["draft_logits"])
+    assert np.array_equal(a["target_lse"], b["target_lse"])  # same operations, same bits
+    assert np.abs(a["draft_lse"] - b["draft_lse"]).max() < 1e-6
+    assert (a["tokens"] == b["tokens"]).all() and (a["n"] == b["n"]).all()
 
 
 @pytest.mark.parametrize("name", ["c3-trimmed", "c3-ragged", "c5-mfma"])
@@ -61,11 +114,12 @@ def test_fused_matches_separate_calls(name):
     assert same.mean() >= 0.95, same.mean()
 
 
-@pytest.mark.parametrize("c,order", [(2, "id"), (3, "id"), (4, "id"), (5, "id"), (3, "rank")])
-def test_fused_block_full_size(c, order):
+@pytest.mark.parametrize("c,order,follow", [(2, "id", 0.0), (3, "id", 0.0), (4, "id", 0.0), (5, "id", 0.0),
+                                            (3, "rank", 0.0), (3, "id", 0.5)])
+def test_fused_block_full_size(c, order, follow):
     cfg = CONFIGS[c]
-    say(f"fused block full size config {c}, keep order {order}")
-    wl = make_workload(cfg, keep_order=order)
+    say(f"fused block full size config {c}, keep order {order}, following drafter {follow}")
+    wl = make_workload(cfg, keep_order=order, follow=follow)
     ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     for e in ev:
         e.record()  # materialise the events
@@ -75,7 +129,7 @@ def test_fused_block_full_size(c, order):
     assert ev[0].elapsed_time(ev[1]) > 0
     R = cfg.R
     for s in ([0] if cfg.B == 1 else [0, cfg.B - 1]):
-        one = make_workload(cfg, B=1, b0=s, keep_order=order)
+        one = make_workload(cfg, B=1, b0=s, keep_order=order, follow=follow)
         orc = oracle_block(one)
         sub = dict(draft_ids=gpu["draft_ids"][s:s + 1], n=gpu["n"][s:s + 1], tokens=gpu["tokens"][s:s + 1])
         st = compare_tokens(sub, orc, one)

@@ -244,13 +244,51 @@ def keep_set(cfg: Config, order: str = "id"):
     return keep, inv
 
 
+def following_head(cfg: Config, b0: int, B: int, noise: float):
+    """A drafter that follows the target, for parity cases that reach long accepted runs.
+
+    Hidden row (b, i) is 16 e_0 + 32 e_j with a seeded column j = j(b, i) >= 1, and column 0 of
+    the head holds bf16(z(x) / 16), z(x) = -1.1 ln rank(x) the Zipf bias of the target recipe;
+    the other columns are the usual N(0, 0.02) head.  The LM head then gives exactly (up to one
+    fp32 rounding) 16 W[x, 0] + 32 W[x, j], and target row (b, i) is that value over all V ids
+    plus N(0, noise) (row gamma takes a fresh column when there is no draft row gamma).  No
+    product is formed here beyond the two scalings that define the rows.
+    Returns (hidden bf16 bits [B*R, H], weight bf16 bits [V, H], target [B, gamma+1, V]).
+    """
+    V, H, R, g = cfg.V, cfg.H, cfg.R, cfg.gamma
+    w = lm_head_weights(V, H).copy()
+    _, rank = zipf_ranking(V)
+    w[:, 0] = bf16_round((-1.1 * np.log(rank.astype(np.float64)) / 16.0).astype(np.float32))
+    w0 = bf16_bits_to_f32(w[:, 0]).astype(np.float64)
+    hidden = np.zeros((B * R, H), dtype=np.uint16)
+    one = bf16_round(np.array([16.0, 32.0], dtype=np.float32))
+    if cfg.target_dtype == "f32":
+        target = np.empty((B, g + 1, V), dtype=np.float32)
+    else:
+        target = np.empty((B, g + 1, V), dtype=np.uint16)
+    for k in range(B):
+        rng = _rng(cfg.model_id, 7, b0 + k)
+        cols = rng.integers(1, H, size=max(R, g + 1) + 1)
+        hidden[k * R:(k + 1) * R, 0] = one[0]
+        for i in range(R):
+            hidden[k * R + i, cols[i]] = one[1]
+        for i in range(g + 1):
+            col = cols[i] if i < R else cols[-1]
+            v = 16.0 * w0 + 32.0 * bf16_bits_to_f32(w[:, col]).astype(np.float64)
+            v = (v + noise * rng.standard_normal(V)).astype(np.float32)
+            target[k, i] = v if cfg.target_dtype == "f32" else bf16_round(v)
+    w.setflags(write=False)
+    return hidden, w, target
+
+
 def make_workload(cfg: Config, B: Optional[int] = None, b0: int = 0, aligned: bool = False,
-                  keep_order: str = "id") -> Workload:
+                  keep_order: str = "id", follow: float = 0.0) -> Workload:
     """Inputs for sequences b0 .. b0+B-1 of a config.
 
     aligned=True replaces the LM head by draft logits equal to the target logits gathered at
     keep_ids (same temperature): q is then p restricted to the kept set and renormalised.
     keep_order: storage order of the kept ids ("id" ascending, or "rank").
+    follow > 0: the drafter follows the target (following_head, target noise N(0, follow)).
     """
     B = cfg.B if B is None else B
     wl = Workload(cfg=cfg, b0=b0, B=B, T=np.float32(cfg.T))
@@ -261,6 +299,9 @@ def make_workload(cfg: Config, B: Optional[int] = None, b0: int = 0, aligned: bo
         wl.toy = toy_tables(cfg)
         return wl
     wl.keep_ids, wl.full_to_trim = keep_set(cfg, keep_order)
+    if follow > 0:
+        wl.hidden, wl.weight, wl.target = following_head(cfg, b0, B, follow)
+        return wl
     wl.target = target_logits(cfg, b0, B)
     if aligned:
         t32 = wl.target if cfg.target_dtype == "f32" else bf16_bits_to_f32(wl.target)
