@@ -125,12 +125,16 @@ def _block_greedy(wl, draft_T):
     ("c4 big tiles argmax drafts", CONFIGS[4].scaled(B=40, V=20000, Vt=5000, H=256), 0.0),
     ("c5-scaled sampled drafts", CONFIGS[5].scaled(B=32, V=13000, Vt=6001, H=256), 0.8),
     ("c2 full size argmax drafts", CONFIGS[2], 0.0),
+    ("c3-scaled argmax drafts, following drafter", CONFIGS[3].scaled(B=4, V=20000, Vt=5000, H=512), 0.0),
+    ("c4-scaled argmax drafts, following drafter", CONFIGS[4].scaled(B=24, V=9001, Vt=3000, H=256), 0.0),
+    ("c5-scaled sampled drafts, following drafter", CONFIGS[5].scaled(B=32, V=13000, Vt=6001, H=256), 0.8),
 ])
 def test_block_greedy(name, cfg, draft_T):
     """vt_spec_block with target_T = 0: argmax drafts (draft_T = 0) decided on the call's own fp32
-    logits, or sampled drafts; the greedy verification is then exact against the oracle."""
+    logits, or sampled drafts; the greedy verification is then exact against the oracle.  The
+    following drafter (draft argmax mostly the target's) reaches long accepted runs."""
     say(f"fused block, greedy target: {name}")
-    wl = make_workload(cfg)
+    wl = make_workload(cfg, follow=0.5 if "following" in name else 0.0)
     logits, dlse, ids, tok, n = _block_greedy(wl, draft_T)
     B, R, g = wl.B, cfg.R, cfg.gamma
     if draft_T == 0.0:
@@ -143,3 +147,5 @@ def test_block_greedy(name, cfg, draft_T):
     want_tok, want_n = ref.greedy_verify(t64, ids, wl.keep_ids, g)
     say(f"  mean accepted {want_n.mean():.2f}")
     assert np.array_equal(n, want_n) and np.array_equal(tok, want_tok)
+    if "following" in name:
+        assert want_n.max() > 0
