@@ -454,11 +454,13 @@ constexpr int kBigMinM = 256;
 // wpart: LDS scratch of 2 x 256 float2 that the caller no longer needs (its operand tiles), so
 // that the kernel keeps a single LDS object (a second one makes the compiler wait for every
 // outstanding direct-to-LDS load before any LDS read in the main loop).
-template <bool PARTS>
-__device__ __forceinline__ void big_tile_store(const f32x16 (&acc)[4][4], int M, int Vt, int m0, int n0, int wm,
+template <bool PARTS, int NJ = 4>
+__device__ __forceinline__ void big_tile_store(const f32x16 (&acc)[4][NJ], int M, int Vt, int m0, int n0, int wm,
                                                int wn, int nbn, int bn, float *__restrict__ logits,
                                                const GemvParts &parts, float2 (*wpart)[kBigBM]) {
-  const int tid = threadIdx.x, w = wave_id(), lane = lane_id(), lr = lane & 31;
+  constexpr int kSlots = kBigBN / (32 * NJ);  // waves covering the same tile rows
+  const int tid = threadIdx.x, lane = lane_id(), lr = lane & 31;
+  const int slot = wn / (32 * NJ);
   // 32x32 accumulator layout: lane l holds column l % 32; register v holds row
   // 8 * (v / 4) + 4 * (l / 32) + v % 4.
 #pragma unroll
@@ -469,42 +471,46 @@ __device__ __forceinline__ void big_tile_store(const f32x16 (&acc)[4][4], int M,
       if (gm < M) {
         float *dst = logits + static_cast<int64_t>(gm) * Vt;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           const int gn = n0 + wn + j * 32 + lr;
           if (gn < Vt) __builtin_nontemporal_store(acc[i][j][v], dst + gn);  // streamed out, not re-read here
         }
       }
     }
   if constexpr (PARTS) {
-    // per hidden row: max and sum of exp2((x - max) k2) over this wave's 128 columns (32 lanes
-    // of a half-wave x 4 subtiles), then merged with the other wave covering the same rows
+    // per hidden row: max and sum of exp2((x - max) k2) over this wave's 32 NJ columns (32 lanes
+    // of a half-wave x NJ subtiles), then merged with the other waves covering the same rows
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        float x[4];
+        float x[NJ];
         float mx = kNegInf;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           x[j] = (n0 + wn + j * 32 + lr < Vt) ? acc[i][j][v] : kNegInf;
           mx = fmaxf(mx, x[j]);
         }
         mx = half_wave_reduce(mx, [](float a, float b) { return fmaxf(a, b); });
         float sm = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sm += x[j] == kNegInf ? 0.f : __builtin_amdgcn_exp2f((x[j] - mx) * parts.k2);
+        for (int j = 0; j < NJ; ++j) sm += x[j] == kNegInf ? 0.f : __builtin_amdgcn_exp2f((x[j] - mx) * parts.k2);
         sm = half_wave_reduce(sm, [](float a, float b) { return a + b; });
-        if (lr == 0) wpart[w & 1][wm + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)] = make_float2(mx, sm);
+        if (lr == 0) wpart[slot][wm + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)] = make_float2(mx, sm);
       }
     __syncthreads();
-    const int r = tid;  // 256 threads, one per row of the tile
+    const int r = tid;  // one thread per row of the tile
     const int gm = m0 + r;
-    if (gm < M) {
-      const float2 p0 = wpart[0][r], p1 = wpart[1][r];
-      const float mx = fmaxf(p0.x, p1.x);
+    if (r < kBigBM && gm < M) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int k = 0; k < kSlots; ++k) mx = fmaxf(mx, wpart[k][r].x);
       float sm = 0.f;
-      if (p0.x != kNegInf) sm += p0.y * __builtin_amdgcn_exp2f((p0.x - mx) * parts.k2);
-      if (p1.x != kNegInf) sm += p1.y * __builtin_amdgcn_exp2f((p1.x - mx) * parts.k2);
+#pragma unroll
+      for (int k = 0; k < kSlots; ++k) {
+        const float2 p = wpart[k][r];
+        if (p.x != kNegInf) sm += p.y * __builtin_amdgcn_exp2f((p.x - mx) * parts.k2);
+      }
       parts.part[static_cast<int64_t>(gm) * nbn + bn] = make_float2(mx, sm);
     }
   }
@@ -646,7 +652,13 @@ __global__ __launch_bounds__(kBlock, 1) void lmhead_mfma_big(const uint16_t *__r
 // the last step into the free slot (never read), so every step issues the same 8 loads per thread.
 // Needs H % 32 == 0 (a piece past H cannot be zeroed on the way into LDS).
 constexpr int kDmaBK = 32;
-constexpr int kDmaStages = 4;
+#ifndef VT_DMA_STAGES
+#define VT_DMA_STAGES 4
+#endif
+constexpr int kDmaStages = VT_DMA_STAGES;
+#ifndef VT_MFMA_WAVES
+#define VT_MFMA_WAVES 8  // waves per 256 x 256 tile in the direct-to-LDS kernel: 4 or 8
+#endif  // ring depth: loads get kDmaStages - 2 steps to land
 constexpr int kDmaRowBytes = kDmaBK * 2;                          // 64
 constexpr int kDmaOperandBytes = kBigBM * kDmaRowBytes;           // 16 KB per operand per step
 constexpr int kDmaStageBytes = 2 * kDmaOperandBytes;              // 32 KB
@@ -744,21 +756,21 @@ __global__ __launch_bounds__(kBlock, 1) void lmhead_mfma_dma(const uint16_t *__r
   // the loads of step k + 3 go into it, and the second slice's MFMAs run while the first slice of
   // step k + 1 is read.  LDS reads never wait on an idle MFMA pipe; loads have two steps to land.
   bf16x8 a0[4], b0[4], a1[4], b1[4];
-  issue(0, 0);
-  issue(1, 1);
-  issue(2, 2);
-  wait_vmcnt<16>();
+  constexpr int kAhead = kDmaStages - 1;  // steps in flight after each issue
+#pragma unroll
+  for (int s = 0; s < kAhead; ++s) issue(s, s);
+  wait_vmcnt<8 * (kAhead - 1)>();  // step 0 has landed (8 loads per step and wave)
   __builtin_amdgcn_s_barrier();
   frags(0, off0, a0, b0);
   for (int kt = 0; kt < nk; ++kt) {
-    const int slot = kt & (kDmaStages - 1);
+    const int slot = kt % kDmaStages;
     frags(slot, off1, a1, b1);
     mfmas(a0, b0);
     interleave();
-    wait_vmcnt<8>();
+    wait_vmcnt<8 * (kAhead - 2)>();  // step kt + 1 has landed
     __builtin_amdgcn_s_barrier();
-    issue(kt + 3, (kt + 3) & (kDmaStages - 1));
-    frags((kt + 1) & (kDmaStages - 1), off0, a0, b0);  // past the last step: unused reads of a re-fetch
+    issue(kt + kAhead, (kt + kAhead) % kDmaStages);
+    frags((kt + 1) % kDmaStages, off0, a0, b0);  // past the last step: unused reads of a re-fetch
     mfmas(a1, b1);
     __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);
     interleave();
@@ -769,6 +781,115 @@ __global__ __launch_bounds__(kBlock, 1) void lmhead_mfma_dma(const uint16_t *__r
                         reinterpret_cast<float2(*)[kBigBM]>(smem));
 }
 
+// The same 256 x 256 tile and LDS ring with eight waves (two per SIMD): wave w computes rows
+// 128 (w / 4) .. +127 and columns 64 (w % 4) .. +63 of the tile, 4 x 2 accumulator blocks (128
+// AGPRs), so each SIMD holds two waves and one issues MFMAs while the other waits on LDS or the
+// barrier.  Each wave loads two 1 KB chunks of each operand per K step.
+constexpr int kDma8Block = 512;
+
+template <bool TRIM, bool PARTS>
+__global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_dma8(const uint16_t *__restrict__ hidden,
+                                                                  const uint16_t *__restrict__ weight,
+                                                                  const int32_t *__restrict__ keep, int M, int H,
+                                                                  int Vt, float *__restrict__ logits,
+                                                                  GemvParts parts) {
+  __shared__ __attribute__((aligned(1024))) char smem[kDmaStages * kDmaStageBytes];
+  const int nbm = (M + kBigBM - 1) / kBigBM;
+  const int nbn = (Vt + kBigBN - 1) / kBigBN;
+  const int tile = static_cast<int>(xcd_remap(blockIdx.x, static_cast<int64_t>(nbm) * nbn));
+  const int bm = tile % nbm, bn = tile / nbm;
+  const int m0 = bm * kBigBM, n0 = bn * kBigBN;
+  const int w = wave_id(), lane = lane_id();
+
+  // loads: wave w fills 1 KB chunks q = 2 w + j (j < 2) of each operand, i.e. tile rows
+  // 16 q .. 16 q + 15; lane L writes row 16 q + L / 4, slot L % 4, and fetches piece slot ^ f(row)
+  const uint16_t *asrc[2], *bsrc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 16 * (2 * w + j) + (lane >> 2);
+    const int piece = (lane & 3) ^ dma_swz(r);
+    const int am = min(m0 + r, M - 1);
+    const int n = min(n0 + r, Vt - 1);
+    const int64_t brow = TRIM ? static_cast<int64_t>(keep[n]) : static_cast<int64_t>(n);
+    asrc[j] = hidden + static_cast<int64_t>(am) * H + piece * 8;
+    bsrc[j] = weight + brow * H + piece * 8;
+  }
+  const int nk = H / kDmaBK;
+  auto issue = [&](int kstep, int slot) {
+    const int k0 = min(kstep, nk - 1) * kDmaBK;
+    char *base = smem + slot * kDmaStageBytes;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_global_load_lds(asrc[j] + k0, (lds_void *)(base + (2 * w + j) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_global_load_lds(bsrc[j] + k0, (lds_void *)(base + kDmaOperandBytes + (2 * w + j) * 1024),
+                                       16, 0, 0);
+  };
+
+  const int wm = (w >> 2) * 128, wn = (w & 3) * 64;
+  const int lr = lane & 31;
+  const int sw = dma_swz(lr);
+  const int off0 = lr * kDmaRowBytes + (((lane >> 5) ^ sw) << 4);
+  const int off1 = lr * kDmaRowBytes + (((2 + (lane >> 5)) ^ sw) << 4);
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  auto frags = [&](int slot, int off, bf16x8(&a)[4], bf16x8(&b)[2]) {
+    const char *sa = smem + slot * kDmaStageBytes + wm * kDmaRowBytes + off;
+    const char *sb = smem + slot * kDmaStageBytes + kDmaOperandBytes + wn * kDmaRowBytes + off;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(sa + i * 32 * kDmaRowBytes);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(sb + j * 32 * kDmaRowBytes);
+  };
+  auto mfmas = [&](const bf16x8(&a)[4], const bf16x8(&b)[2]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  };
+  auto interleave = [&]() {  // 6 LDS reads spread over the first 6 of 8 MFMAs
+#pragma unroll
+    for (int r = 0; r < 6; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  };
+
+  // the step schedule of lmhead_mfma_dma, with 4 loads per step and wave
+  bf16x8 a0[4], b0[2], a1[4], b1[2];
+  constexpr int kAhead = kDmaStages - 1;
+#pragma unroll
+  for (int s = 0; s < kAhead; ++s) issue(s, s);
+  wait_vmcnt<4 * (kAhead - 1)>();
+  __builtin_amdgcn_s_barrier();
+  frags(0, off0, a0, b0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int slot = kt % kDmaStages;
+    frags(slot, off1, a1, b1);
+    mfmas(a0, b0);
+    interleave();
+    wait_vmcnt<4 * (kAhead - 2)>();
+    __builtin_amdgcn_s_barrier();
+    issue(kt + kAhead, (kt + kAhead) % kDmaStages);
+    frags((kt + 1) % kDmaStages, off0, a0, b0);  // past the last step: unused reads of a re-fetch
+    mfmas(a1, b1);
+    __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
+    interleave();
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  big_tile_store<PARTS, 2>(acc, M, Vt, m0, n0, wm, wn, nbn, bn, logits, parts,
+                           reinterpret_cast<float2(*)[kBigBM]>(smem));
+}
+
 inline int64_t mfma_big_tiles_n(int64_t Vt) { return (Vt + kBigBN - 1) / kBigBN; }
 
 template <bool PARTS>
@@ -776,9 +897,15 @@ inline hipError_t launch_mfma_big(const uint16_t *hidden, const uint16_t *weight
                                   int64_t H, int64_t Vt, float *logits, GemvParts parts, hipStream_t stream) {
   const int64_t tiles = ((M + kBigBM - 1) / kBigBM) * mfma_big_tiles_n(Vt);
   if (H % kDmaBK == 0) {
+#if VT_MFMA_WAVES == 8
+    auto fd = keep ? &lmhead_mfma_dma8<true, PARTS> : &lmhead_mfma_dma8<false, PARTS>;
+    return launch(fd, dim3(static_cast<unsigned>(tiles)), dim3(kDma8Block), 0, stream, hidden, weight, keep,
+                  static_cast<int>(M), static_cast<int>(H), static_cast<int>(Vt), logits, parts);
+#else
     auto fd = keep ? &lmhead_mfma_dma<true, PARTS> : &lmhead_mfma_dma<false, PARTS>;
     return launch(fd, dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0, stream, hidden, weight, keep,
                   static_cast<int>(M), static_cast<int>(H), static_cast<int>(Vt), logits, parts);
+#endif
   }
   auto fn = H % kBigBK == 0 ? (keep ? &lmhead_mfma_big<true, PARTS, true> : &lmhead_mfma_big<false, PARTS, true>)
                             : (keep ? &lmhead_mfma_big<true, PARTS, false> : &lmhead_mfma_big<false, PARTS, false>);
