@@ -65,6 +65,9 @@ def parse():
                     help="run the step as the four separate calls instead of the fused vt_spec_block")
     ap.add_argument("--overlap", action="store_true",
                     help="run the target softmax on a second stream, concurrently with the LM head")
+    ap.add_argument("--follow", type=float, default=0.0, metavar="SIGMA",
+                    help="a drafter that follows the target (target = the head's own two columns + N(0, SIGMA)): "
+                         "drafts get accepted; the default is the recipe's unrelated random head")
     ap.add_argument("--greedy", action="store_true",
                     help="temperature 0 for target and draft: argmax drafts and greedy verification")
     ap.add_argument("--graph", action="store_true",
@@ -476,7 +479,7 @@ def main():
     B, g, R = cfg.B, cfg.gamma, cfg.R
     log(f"workload: {cfg.name}")
     t0 = time.perf_counter()
-    wl = make_workload(cfg)
+    wl = make_workload(cfg, follow=args.follow)
     log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
 
     def bf16(bits):
@@ -645,7 +648,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        wl_one = make_workload(cfg, B=1)
+        wl_one = make_workload(cfg, B=1, follow=args.follow)
         log("timing the CPU oracle ...")
         cpu = cpu_baseline(cfg, wl_one, args.cpu_seconds)
 
@@ -671,7 +674,11 @@ def main():
                               "four calls, target softmax on a second stream" if args.overlap else
                               "four calls, eager, one stream"),
                    "block_algorithmic_bytes": bb,
-                   "block_gbs": round(bb / (ms_per_step / 1e3) / 1e9, 1)},
+                   "block_gbs": round(bb / (ms_per_step / 1e3) / 1e9, 1),
+                   "drafter": f"follows the target, noise sd {args.follow}" if args.follow > 0 else
+                              "unrelated random head (the recipe)",
+                   "mean_accepted": round(float(nacc.double().mean()), 4),
+                   "tokens_per_block": round(float(nacc.double().mean()) + 1.0, 4)},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
