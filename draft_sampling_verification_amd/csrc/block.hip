@@ -29,6 +29,8 @@ struct BlockPlan {
   bool fused_mfma;  // large-batch MFMA tiles with draft partials in their epilogue
   bool fv;          // small batch, sampling both sides: target partials ride in the GEMV launch,
                     // then one chunk pass and one final pass (verify_fused_chunk / _final)
+  bool fg;          // small batch, greedy both sides: argmax partials in the GEMV launch (head
+                    // blocks and, in extra workgroups, target chunks), then verify_greedy_small
   int64_t M, rows_t;
   int64_t nchunk_t;  // 4096-chunks of a target row
   int64_t nchunk_d;  // draft partial chunks per row (GEMV row blocks, or 4096-chunks)
@@ -44,10 +46,11 @@ BlockPlan plan_block(int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt,
   BlockPlan p{};
   p.M = B * R;
   p.rows_t = B * (gamma + 1);
-  p.fused = !greedy_d && pick_gemv<true>(p.M, H, trim) != nullptr;
-  p.nchunk_t = greedy_t ? 1 : (V + kChunk - 1) / kChunk;
+  p.fused = !greedy_d && pick_gemv<kPartsSoftmax>(p.M, H, trim) != nullptr;
+  p.fg = greedy_t && greedy_d && R <= kFvMaxR && pick_gemv<kPartsArgmax>(p.M, H, trim) != nullptr;
+  p.nchunk_t = greedy_t && !p.fg ? 1 : (V + kChunk - 1) / kChunk;
   p.fused_mfma = !greedy_d && !p.fused && p.M >= kBigMinM;
-  if (p.fused) {
+  if (p.fused || p.fg) {
     p.nchunk_d = gemv_blocks(Vt);
     p.chunk_d = gemv_rows_per_block(Vt);
   } else if (p.fused_mfma) {
@@ -61,9 +64,10 @@ BlockPlan plan_block(int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt,
   p.nchunk_v = (V + (p.fv ? kFvIds : kChunk) - 1) / (p.fv ? kFvIds : kChunk);
   size_t off = 0;
   p.off_tpart = off;
-  if (p.nchunk_t > 1 || p.fv) off += align_up(static_cast<size_t>(p.rows_t * p.nchunk_t) * sizeof(float2), 256);
+  if (p.nchunk_t > 1 || p.fv || p.fg)
+    off += align_up(static_cast<size_t>(p.rows_t * p.nchunk_t) * sizeof(float2), 256);
   p.off_dpart = off;
-  if (p.fused || p.fused_mfma || p.nchunk_d > 1)
+  if (p.fused || p.fused_mfma || p.fg || p.nchunk_d > 1)
     off += align_up(static_cast<size_t>(p.M * p.nchunk_d) * sizeof(float2), 256);
   p.off_nbuf = off;
   p.off_vpart = off;
@@ -103,7 +107,7 @@ hipError_t run_block_small(const BlockPlan &pl, const SmParams &D, const SmParam
   gp.tgt = T;
   gp.tsel = sizeof(TinT) == 4 ? (kVecT ? 1 : 2) : (kVecT ? 3 : 4);
   if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-  e = launch_gemv(pick_gemv<true>(pl.M, H, keep != nullptr), hidden, weight, keep, H, Vt, logits, gp, stream,
+  e = launch_gemv(pick_gemv<kPartsSoftmax>(pl.M, H, keep != nullptr), hidden, weight, keep, H, Vt, logits, gp, stream,
                   T.rows * T.nchunk);
   if (e != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
@@ -124,12 +128,44 @@ hipError_t run_block_small(const BlockPlan &pl, const SmParams &D, const SmParam
   return launch(verify_fused_final<TinT, kVecT>, dim3(static_cast<unsigned>(B)), dim3(kBlock), 0, stream, Vp);
 }
 
+// Small batch, greedy both sides: 2 launches.  The GEMV launch leaves per-block argmax partials
+// of the draft rows and, in extra workgroups, per-chunk argmaxes of the target rows; one
+// workgroup per sequence reduces, compares and writes the outputs.
+template <typename TinT, bool kVecT>
+hipError_t run_block_greedy_small(const BlockPlan &pl, const SmParams &D, const SmParams &T, const VfParams &Vp,
+                                  const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int64_t H,
+                                  int64_t Vt, float *logits, int64_t B, hipEvent_t ev0, hipEvent_t ev1,
+                                  hipStream_t stream) {
+  hipError_t e = hipSuccess;
+  GemvParts gp{};
+  gp.part = D.part;
+  gp.tgt = T;
+  gp.tsel = sizeof(TinT) == 4 ? (kVecT ? 1 : 2) : (kVecT ? 3 : 4);
+  if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
+  e = launch_gemv(pick_gemv<kPartsArgmax>(pl.M, H, keep != nullptr), hidden, weight, keep, H, Vt, logits, gp, stream,
+                  T.rows * T.nchunk);
+  if (e != hipSuccess) return e;
+  if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
+  FvParams F{};
+  F.v = Vp;
+  F.dpart = D.part;
+  F.nd = static_cast<int>(pl.nchunk_d);
+  F.dper = pl.chunk_d;
+  F.tpart = T.part;
+  F.nt = T.nchunk;
+  F.dlse_out = D.lse;
+  F.dids_out = D.sampled;
+  return launch(verify_greedy_small, dim3(static_cast<unsigned>(B)), dim3(kFvBlock), 0, stream, F);
+}
+
 template <typename TinT, bool kVecT, bool kVecD>
 hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, const VfParams &Vp,
                      const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int64_t H, int64_t Vt,
                      float *logits, int64_t B, hipEvent_t ev0, hipEvent_t ev1, hipStream_t stream) {
   if (pl.fv) return run_block_small<TinT, kVecT>(pl, D, T, Vp, hidden, weight, keep, H, Vt, logits, D.u, B, ev0, ev1,
                                                  stream);
+  if (pl.fg)
+    return run_block_greedy_small<TinT, kVecT>(pl, D, T, Vp, hidden, weight, keep, H, Vt, logits, B, ev0, ev1, stream);
   hipError_t e = hipSuccess;
   const bool greedy_t = Vp.greedy;
   const bool t_multi = !greedy_t && pl.nchunk_t > 1;
@@ -144,7 +180,7 @@ hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, 
   if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
   bool d_multi = true;
   if (pl.fused) {
-    const GemvFn fn = pick_gemv<true>(pl.M, H, keep != nullptr);
+    const GemvFn fn = pick_gemv<kPartsSoftmax>(pl.M, H, keep != nullptr);
     e = launch_gemv(fn, hidden, weight, keep, H, Vt, logits, GemvParts{D.part, D.k2}, stream);
     if (e != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
@@ -153,7 +189,7 @@ hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, 
     if (e != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   } else {
-    const GemvFn plain = pick_gemv<false>(pl.M, H, keep != nullptr);
+    const GemvFn plain = pick_gemv<kPartsNone>(pl.M, H, keep != nullptr);
     e = plain ? launch_gemv(plain, hidden, weight, keep, H, Vt, logits, GemvParts{}, stream)
               : launch_mfma(hidden, weight, keep, pl.M, H, Vt, logits, stream);
     if (e != hipSuccess) return e;
@@ -235,7 +271,7 @@ extern "C" vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *wei
   D.sampled = draft_ids;
   D.nchunk = static_cast<int>(pl.nchunk_d);
   D.chunk = pl.chunk_d;
-  if (pl.fused || pl.fused_mfma || pl.nchunk_d > 1) D.part = reinterpret_cast<float2 *>(ws + pl.off_dpart);
+  if (pl.fused || pl.fused_mfma || pl.fg || pl.nchunk_d > 1) D.part = reinterpret_cast<float2 *>(ws + pl.off_dpart);
 
   SmParams T{};
   T.logits = target_logits;
@@ -248,7 +284,8 @@ extern "C" vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *wei
   T.lse = target_lse;
   T.nchunk = static_cast<int>(pl.nchunk_t);
   T.chunk = kChunk;
-  if (!greedy_t && (pl.nchunk_t > 1 || pl.fv)) T.part = reinterpret_cast<float2 *>(ws + pl.off_tpart);
+  if ((!greedy_t && (pl.nchunk_t > 1 || pl.fv)) || pl.fg) T.part = reinterpret_cast<float2 *>(ws + pl.off_tpart);
+  T.greedy = greedy_t;
 
   VfParams P{};
   P.target = target_logits;

@@ -11,7 +11,7 @@ extern "C" vt_status_t vt_lmhead_trimmed(const uint16_t *hidden, const uint16_t 
   if (M > INT32_MAX || H > INT32_MAX || Vt > INT32_MAX) return VT_ERR_UNSUPPORTED;
   if (H % 8 != 0 || !aligned16(hidden) || !aligned16(weight)) return VT_ERR_UNSUPPORTED;
 
-  const GemvFn gemv = pick_gemv<false>(M, H, keep_ids != nullptr);
+  const GemvFn gemv = pick_gemv<kPartsNone>(M, H, keep_ids != nullptr);
   if (gemv) return hip_status(launch_gemv(gemv, hidden, weight, keep_ids, H, Vt, logits, GemvParts{}, stream));
   const int64_t tiles = ((M + kBM - 1) / kBM) * ((Vt + kBN - 1) / kBN);
   if (tiles > INT32_MAX) return VT_ERR_UNSUPPORTED;

@@ -161,10 +161,14 @@ __device__ __forceinline__ void target_partial_chunk(const GemvParts &parts, int
 // multiplied.  Every load is unconditional and in bounds (row indices past the wave's last row
 // repeat the last row, pieces past H repeat the last piece and are masked), so the compiler can
 // wait for exactly the oldest row (vmcnt(N)) instead of draining the queue.  FULL: H is a multiple
-// of 512 (no masking at all).  TRIM: rows are gathered through keep_ids.  PARTS: also produce the
-// draft softmax partials of the block (online max / sum per hidden row, combined over the four
-// wavefronts through LDS), so the softmax never re-reads the logits for its first pass.
-template <int M, int NIT, int PD, bool FULL, bool TRIM, bool PARTS>
+// of 512 (no masking at all).  TRIM: rows are gathered through keep_ids.  PARTS = kPartsSoftmax:
+// also produce the draft softmax partials of the block (online max / sum per hidden row, combined
+// over the four wavefronts through LDS), so the softmax never re-reads the logits for its first
+// pass; kPartsArgmax: the block's (max, lowest index of the max) per hidden row instead, for
+// argmax drafts.
+constexpr int kPartsNone = 0, kPartsSoftmax = 1, kPartsArgmax = 2;
+
+template <int M, int NIT, int PD, bool FULL, bool TRIM, int PARTS>
 __global__ __launch_bounds__(kBlock) void lmhead_gemv(const uint16_t *__restrict__ hidden,
                                                       const uint16_t *__restrict__ weight,
                                                       const int32_t *__restrict__ keep, int H, int Vt, int per,
@@ -172,7 +176,7 @@ __global__ __launch_bounds__(kBlock) void lmhead_gemv(const uint16_t *__restrict
   constexpr int NP = Pow2Ceil<M>::value;
   constexpr int kGroup = kWave / NP;
   const int nblk = (Vt + per - 1) / per;
-  if constexpr (PARTS) {
+  if constexpr (PARTS != kPartsNone) {
     if (static_cast<int>(blockIdx.x) >= nblk) {
       target_partial_chunk(parts, static_cast<int64_t>(blockIdx.x) - nblk);
       return;
@@ -203,6 +207,7 @@ __global__ __launch_bounds__(kBlock) void lmhead_gemv(const uint16_t *__restrict
   auto row_of = [&](int t) { return wv + t * kWavesPerBlock; };
   const int mrow = lane / kGroup;  // hidden row whose sum this lane holds after the reduction
   float pmax = kNegInf, psum = 0.f;
+  int pidx = kNoIndex;
 
   auto fetch = [&](int t, uint4(&dst)[NIT]) {
     const int j = row_of(min(t, nrows - 1));  // wave-uniform
@@ -224,10 +229,15 @@ __global__ __launch_bounds__(kBlock) void lmhead_gemv(const uint16_t *__restrict
     }
     const float sum = transpose_reduce<NP>(acc);
     if ((lane % kGroup) == 0 && mrow < M) logits[static_cast<int64_t>(mrow) * Vt + row_of(t)] = sum;
-    if constexpr (PARTS) {
+    if constexpr (PARTS == kPartsSoftmax) {
       const float nm = fmaxf(pmax, sum);
       psum = psum * __builtin_amdgcn_exp2f((pmax - nm) * parts.k2) + __builtin_amdgcn_exp2f((sum - nm) * parts.k2);
       pmax = nm;
+    } else if constexpr (PARTS == kPartsArgmax) {
+      if (argmax_better(sum, row_of(t), pmax, pidx)) {
+        pmax = sum;
+        pidx = row_of(t);
+      }
     }
   };
 
@@ -250,7 +260,26 @@ __global__ __launch_bounds__(kBlock) void lmhead_gemv(const uint16_t *__restrict
       if (t0 + s < nrows) consume(t0 + s, w[s]);
   }
 
-  if constexpr (PARTS) {
+  if constexpr (PARTS == kPartsArgmax) {
+    __shared__ float2 wbest[kWavesPerBlock][NP];
+    if ((lane % kGroup) == 0) wbest[wid][mrow] = make_float2(pmax, __int_as_float(pidx));
+    __syncthreads();
+    if (threadIdx.x < M) {
+      const int m = threadIdx.x;
+      float bv = kNegInf;
+      int bi = kNoIndex;
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) {
+        const float2 v = wbest[w][m];
+        if (argmax_better(v.x, __float_as_int(v.y), bv, bi)) {
+          bv = v.x;
+          bi = __float_as_int(v.y);
+        }
+      }
+      parts.part[static_cast<int64_t>(m) * nblk + blockIdx.x] = make_float2(bv, __int_as_float(bi));
+    }
+  }
+  if constexpr (PARTS == kPartsSoftmax) {
     __shared__ float2 wpart[kWavesPerBlock][NP];
     if ((lane % kGroup) == 0) wpart[wid][mrow] = make_float2(pmax, psum);
     __syncthreads();
@@ -388,7 +417,7 @@ constexpr int kGemvMaxM = 8;
 constexpr int kGemvMaxNit = 8;
 constexpr int kGemvMaxRegs = 48;  // M * NIT: the hidden slice lives in 4 * M * NIT VGPRs
 
-template <int M, int NIT, bool PARTS>
+template <int M, int NIT, int PARTS>
 GemvFn gemv_entry(bool full, bool trim) {
   if constexpr (M * NIT > kGemvMaxRegs) {
     return nullptr;
@@ -400,7 +429,7 @@ GemvFn gemv_entry(bool full, bool trim) {
   }
 }
 
-template <int M, bool PARTS>
+template <int M, int PARTS>
 GemvFn gemv_for_nit(int nit, bool full, bool trim) {
   switch (nit) {
     case 1: return gemv_entry<M, 1, PARTS>(full, trim);
@@ -416,7 +445,7 @@ GemvFn gemv_for_nit(int nit, bool full, bool trim) {
 }
 
 // The GEMV kernel for (M, H), or nullptr when the shape needs the MFMA kernel.
-template <bool PARTS>
+template <int PARTS>
 GemvFn pick_gemv(int64_t M, int64_t H, bool trim) {
   const int nit = static_cast<int>((H + 511) / 512);
   const bool full = H % 512 == 0;

@@ -426,6 +426,77 @@ __global__ __launch_bounds__(kFvBlock) void verify_fused_chunk(FvParams F) {
   }
 }
 
+// Greedy blocks at decode sizes (both temperatures 0; "VocabTrim" §4 and Appendix C.1,
+// Algorithm 2: a draft is kept only while it equals the target's most likely token, and the
+// target's own token follows the first mismatch).  The head launch leaves per-block (max, lowest
+// index of the max) of every draft row and per-4096-chunk argmaxes of every target row; one
+// 512-thread workgroup per sequence reduces them (wave w: draft row w, target rows w and w + 8),
+// compares, and writes every output.  No logits are read here.
+__device__ __forceinline__ void partial_argmax(const float2 *p, int n, float &bv, int &bi) {
+  bv = kNegInf;
+  bi = kNoIndex;
+  for (int k = lane_id(); k < n; k += kWave) {
+    const float2 v = p[k];
+    if (argmax_better(v.x, __float_as_int(v.y), bv, bi)) {
+      bv = v.x;
+      bi = __float_as_int(v.y);
+    }
+  }
+  wave_argmax(bv, bi);
+}
+
+__global__ __launch_bounds__(kFvBlock) void verify_greedy_small(FvParams F) {
+  __shared__ int s_x[kFvMaxR];
+  __shared__ int s_a[kFvMaxT];
+  const VfParams &P = F.v;
+  const int64_t b = blockIdx.x;
+  const int lane = lane_id(), w = static_cast<int>(threadIdx.x) / kWave;
+  const int g = P.gamma, R = static_cast<int>(P.R);
+  if (w < R) {
+    const int64_t m = b * R + w;
+    float bv;
+    int bi;
+    partial_argmax(F.dpart + m * F.nd, F.nd, bv, bi);
+    if (lane == 0) {
+      s_x[w] = bi;
+      F.dlse_out[m] = static_cast<double>(bv);  // the greedy limit of the log-normaliser: the row max
+      F.dids_out[m] = bi;
+    }
+  }
+  for (int i = w; i <= g; i += kFvWaves) {
+    float bv;
+    int bi;
+    partial_argmax(F.tpart + (b * (g + 1) + i) * F.nt, F.nt, bv, bi);
+    if (lane == 0) s_a[i] = bi;
+  }
+  __syncthreads();
+  if (w != 0) return;
+  // n = first draft whose full id differs from the target's argmax, gamma if none, -1 if an id
+  // is out of range; tokens = the kept drafts, then the target's argmax at n, then -1
+  bool valid = true, accept = true;
+  int32_t y = -1;
+  if (lane < g) {
+    const int x = s_x[lane];
+    valid = x >= 0 && x < P.Vt;
+    if (valid) {
+      y = P.keep ? P.keep[x] : x;
+      valid = y >= 0 && y < P.V;
+    }
+    accept = valid && y == s_a[lane];
+  }
+  const unsigned long long bad = __ballot(lane < g && !valid);
+  const unsigned long long rej = __ballot(lane < g && !accept);
+  const int n = bad ? -1 : (rej ? __ffsll(static_cast<long long>(rej)) - 1 : g);
+  int32_t *tok = P.out_tokens + b * (g + 1);
+  for (int i = lane; i <= g; i += kWave) {
+    int32_t v = -1;
+    if (n >= 0 && i < n) v = y;  // lane i holds draft i's full id
+    else if (n >= 0 && i == n) v = s_a[n];
+    tok[i] = v;
+  }
+  if (lane == 0) P.out_n[b] = n;
+}
+
 // Final pass: one 256-thread workgroup per sequence draws the final token from the chunk sums
 // and writes the outputs (the log-normalisers and draft ids were written by the chunk pass).
 template <typename Tin, bool kVec>

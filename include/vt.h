@@ -190,7 +190,9 @@ size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
  *   runs, target_lse is not written, u_accept and u_final are not read (all three may be NULL).
  *   draft_T = 0 (allowed only with target_T = 0) makes each draft the lowest id of its row's
  *   maximum, draft_lse the row maximum, and u_draft is not read (may be NULL); the LM head then
- *   runs without the fused softmax partials.
+ *   runs without the fused softmax partials, except at decode sizes (B*R <= 8), where it emits
+ *   per-block argmax partials of the draft rows and, in extra workgroups, per-chunk argmaxes of
+ *   the target rows, and one more launch finishes the block (2 launches).
  *   Errors: INVALID_ARG for NULL required pointers, B, gamma, H, V or Vt <= 0, R < gamma, Vt > V,
  *   a temperature not finite or < 0, draft_T = 0 with target_T > 0, keep_ids/full_to_trim
  *   inconsistent with Vt; UNSUPPORTED for

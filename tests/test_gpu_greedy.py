@@ -149,3 +149,30 @@ def test_block_greedy(name, cfg, draft_T):
     assert np.array_equal(n, want_n) and np.array_equal(tok, want_tok)
     if "following" in name:
         assert want_n.max() > 0
+
+
+# Decode-sized greedy blocks (B*R <= 8, both temperatures 0) take the two-launch path: argmax
+# partials from the GEMV head launch, then one reduce-and-compare workgroup per sequence.
+@pytest.mark.parametrize("name,cfg,b0,follow", [
+    ("c3 batch 1, random head", CONFIGS[3].scaled(B=1, V=20000, Vt=5000, H=512), 0, 0.0),
+    ("c3 batch 1, following drafter", CONFIGS[3].scaled(B=1, V=20000, Vt=5000, H=512), 1, 0.5),
+    ("c4 bf16 batch 1, 8 draft rows, following drafter", CONFIGS[4].scaled(B=1, gamma=7, R=8, V=9001, Vt=3000, H=256),
+     2, 0.5),
+    ("two sequences, 300000-id vocabulary, following drafter",
+     CONFIGS[3].scaled(B=2, gamma=3, R=4, V=300000, Vt=20000, H=256), 0, 0.5),
+    ("c2 full size, following drafter", CONFIGS[2], 0, 0.5),
+])
+def test_block_greedy_small(name, cfg, b0, follow):
+    say(f"fused block, greedy, decode-sized: {name}")
+    wl = make_workload(cfg, b0=b0, follow=follow)
+    logits, dlse, ids, tok, n = _block_greedy(wl, 0.0)
+    B, R, g = wl.B, cfg.R, cfg.gamma
+    want_ids = np.array([ref.argmax_lowest(row) for row in logits]).reshape(B, R)
+    assert np.array_equal(ids, want_ids)
+    assert np.array_equal(dlse, logits.max(axis=1).astype(np.float64))
+    t64 = ref.as_f64(wl.target, cfg.target_dtype)
+    want_tok, want_n = ref.greedy_verify(t64, ids, wl.keep_ids, g)
+    say(f"  accepted {want_n.tolist()}")
+    assert np.array_equal(n, want_n) and np.array_equal(tok, want_tok)
+    if follow > 0:
+        assert want_n.max() > 0
