@@ -23,6 +23,8 @@
 // Final pass: one workgroup per sequence locates the 1024-id chunk where the running residual
 // mass reaches u_final times its total and rescans it (the shared final-draw code of the verify
 // call, at 4 ids per thread).
+// Greedy blocks (both temperatures 0) need no chunk pass: verify_greedy_small reduces the argmax
+// partials of the head launch and compares.
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -50,10 +52,10 @@ static_assert(kFvWaves == kFvMaxR, "one wavefront per draft row");
 
 struct FvParams {
   VfParams v;            // verification view: target, draft logits, keep set, uniforms, outputs
-  const float2 *dpart;   // [B * R][nd]: (max, sum of exp) per head row block
+  const float2 *dpart;   // [B * R][nd] per head row block: (max, sum of exp), or (max, argmax) if greedy
   int nd, dper;          // row blocks per draft row, head rows per block
   const float *udraft;   // [B * R]
-  const float2 *tpart;   // [B * (gamma + 1)][nt]: (max, sum of exp) per 4096-chunk
+  const float2 *tpart;   // [B * (gamma + 1)][nt] per 4096-chunk: (max, sum of exp), or (max, argmax)
   int nt;
   double *dlse_out;      // [B * R]
   int32_t *dids_out;     // [B * R]
