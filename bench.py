@@ -48,7 +48,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--batch", type=int, default=1,
+                    help="sequences per step for the toy (--config 1); the other configs fix their batch")
     ap.add_argument("--workload", default="block", choices=["block", "keepset", "generate"],
                     help="block: one speculative block per step (the default); keepset: token counter -> "
                          "Top-K -> trimmed head over a Zipf calibration stream; generate: the chained "
@@ -241,6 +243,105 @@ def cpu_baseline(cfg, wl_one, budget_s: float):
             "cores": int(used), "kind": "oracle",
             "sample": f"{blocks} whole block(s) of {wl_one.B} sequence(s) of this workload, float64 numpy, "
                       f"{el:.1f} s total, {per_block:.2f} s per block"}
+
+
+# ---------------------------------------------------------------- config 1: the order-1 toy
+
+def bench_toy(args):
+    """One step = one speculative block of the order-1 toy (V = 18, gamma = 4) for --batch
+    sequences, through the separate calls: gamma draft rows looked up from the draft table by the
+    previous token (the toy's "model", a torch gather) and drawn with vt_softmax_temp, the gamma+1
+    target rows looked up the same way, vt_softmax_temp for their log-normalisers, vt_spec_verify.
+    At batch 1 this is launch latency; the verify kernel is timed with HIP events for the
+    roofline line."""
+    import torch
+
+    import draft_sampling_verification_amd as vt
+    from workloads import CONFIGS, make_workload
+
+    cfg = CONFIGS[1]
+    B, g, V = args.batch, cfg.gamma, cfg.V
+    wl = make_workload(cfg, B=B)
+
+    def f(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    Q, P = f(wl.toy.draft_logits), f(wl.toy.target_logits)
+    ud_cols = [f(wl.u_draft[:, k]) for k in range(g)]
+    ua, uf = f(wl.u_acc), f(wl.u_fin)
+    lse_k = [torch.empty(B, dtype=torch.float64, device="cuda") for _ in range(g)]
+    ids_k = [torch.empty(B, dtype=torch.int32, device="cuda") for _ in range(g)]
+    tlse = torch.empty(B * (g + 1), dtype=torch.float64, device="cuda")
+    tok = torch.empty(B, g + 1, dtype=torch.int32, device="cuda")
+    nacc = torch.empty(B, dtype=torch.int32, device="cuda")
+    ctx0 = torch.zeros(B, dtype=torch.long, device="cuda")
+    ws_d = vt.softmax_workspace(B, V)
+    ws_t = vt.softmax_workspace(B * (g + 1), V)
+    ws_v = vt.verify_workspace(B, g, V)
+    main_s = torch.cuda.current_stream()
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+
+    def step(i=None):
+        ctx = ctx0
+        rows, tcols = [], [P[ctx]]
+        for k in range(g):
+            r = Q[ctx]
+            vt.vt_softmax_temp(r, wl.T, lse_k[k], None, ud_cols[k], ids_k[k], workspace=ws_d)
+            rows.append(r)
+            ctx = ids_k[k].long() + 1
+            tcols.append(P[ctx])
+        target = torch.stack(tcols, 1)
+        vt.vt_softmax_temp(target.view(-1, V), wl.T, tlse, workspace=ws_t)
+        draft, dl, di = torch.stack(rows, 1), torch.stack(lse_k, 1), torch.stack(ids_k, 1)
+        if i is not None:
+            ev_a[i].record(main_s)
+        vt.vt_spec_verify(target, tlse, wl.T, draft, dl, wl.T, di, None, None, ua, uf, tok, nacc, workspace=ws_v)
+        if i is not None:
+            ev_b[i].record(main_s)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = 1e3 * wall / args.steps
+    v_ms = sum(a.elapsed_time(b) for a, b in zip(ev_a, ev_b)) / args.steps
+    # verify kernel: target rows + draft rows + lse + ids + uniforms in, tokens + n out
+    vb = B * ((g + 1) * V * 4 + g * V * 4 + (g + 1) * 8 + g * 8 + g * 4 + (g + 1) * 4 + (g + 2) * 4)
+    log(f"step {ms:.4f} ms ({1e3 * ms:.1f} us), verify call {v_ms * 1e3:.1f} us; "
+        f"mean accepted {float(nacc.double().mean()):.3f}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import ref
+        one = make_workload(cfg, B=min(B, 1000))
+        n, t1 = 0, time.perf_counter()
+        while time.perf_counter() - t1 < min(args.cpu_seconds, 5.0):
+            ref.toy_block(one.toy.target_logits, one.toy.draft_logits, one.T, g, one.u_draft, one.u_acc, one.u_fin)
+            n += 1
+        el = time.perf_counter() - t1
+        cpu = {"value": one.B * g * n / el, "unit": "verified draft positions/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n} toy block(s) of {one.B} sequence(s), float64 numpy, {el:.1f} s"}
+    out = {
+        "metric": "verified draft positions/sec (order-1 toy, launch-latency bound at batch 1), 1 GPU",
+        "value": round(B * g / (ms / 1e3), 1),
+        "unit": "verified draft positions/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}; batch {B}", "batch": B, "gamma": g, "vocab": V,
+                   "launch": "gamma draft draws + target softmax + verify, separate calls (toy rows gathered by torch)",
+                   "us_per_step": round(1e3 * ms, 2),
+                   "mean_accepted": round(float(nacc.double().mean()), 4)},
+        "roofline": {"bound": "hbm", "achieved": round(vb / (v_ms / 1e3) / 1e9, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(vb / (v_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 5), "traffic": None,
+                     "kernel": "verify_single (vt_spec_verify)", "algorithmic_bytes_per_launch": vb,
+                     "avg_launch_ms": round(v_ms, 5)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
 
 
 # ---------------------------------------------------------------- keep-set construction
@@ -468,6 +569,9 @@ def main():
         return
     if args.workload == "generate":
         bench_generate(args)
+        return
+    if args.config == 1:
+        bench_toy(args)
         return
 
     import torch
