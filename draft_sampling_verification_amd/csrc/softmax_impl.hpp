@@ -172,6 +172,55 @@ __global__ __launch_bounds__(kBlock) void softmax_single(SmParams P) {
   }
 }
 
+// Rows of at most 64 elements (the toy vocabularies): one wavefront per row, four rows per
+// workgroup, lane j holding element j; the same definitions as softmax_single (Z is the running
+// sum at the row's last element; the draw takes the first element reaching u Z, else the last
+// one with positive weight), with the row's sums as wave scans instead of workgroup scans.
+template <typename Tin>
+__global__ __launch_bounds__(kBlock) void softmax_wave(SmParams P) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_id();
+  if (r >= P.rows) return;  // the whole wavefront
+  const int lane = lane_id();
+  const bool in = lane < P.n;
+  const Tin *row = reinterpret_cast<const Tin *>(P.logits) + r * P.ld;
+  float x;
+  if constexpr (sizeof(Tin) == 4)
+    x = reinterpret_cast<const float *>(row)[in ? lane : 0];
+  else
+    x = bf16_to_f32(reinterpret_cast<const uint16_t *>(row)[in ? lane : 0]);
+  const float v = in ? x : kNegInf;
+  if (P.greedy) {
+    float bv = v;
+    int bi = in ? lane : kNoIndex;
+    wave_argmax(bv, bi);
+    if (lane == 0) {
+      P.lse[r] = static_cast<double>(bv);
+      if (P.sampled) P.sampled[r] = bi;
+      if (P.rowstat) P.rowstat[r] = make_float2(bv, __int_as_float(bi));
+    }
+    if (P.probs && in) P.probs[r * P.n + lane] = lane == bi ? 1.f : 0.f;
+    return;
+  }
+  const float M = wave_max(v);
+  const float w = M == kNegInf ? 0.f : exp2_fast((v - M) * P.k2);
+  const float C = wave_scan_incl(w);
+  const float Z = lane_value(C, static_cast<int>(P.n) - 1);
+  if (lane == 0) P.lse[r] = static_cast<double>(M) * P.invT + log(static_cast<double>(Z));
+  if (P.probs && in) P.probs[r * P.n + lane] = w * (1.f / Z);
+  if (P.u) {
+    const float t = P.u[r] * Z;
+    const unsigned long long hit = __ballot(in && t <= C);
+    int idx;
+    if (hit) {
+      idx = __ffsll(static_cast<long long>(hit)) - 1;
+    } else {
+      const unsigned long long pos = __ballot(in && w > 0.f);
+      idx = pos ? 63 - __clzll(static_cast<long long>(pos)) : -1;
+    }
+    if (lane == 0) P.sampled[r] = idx;
+  }
+}
+
 // Rows of several chunks, pass 1: one workgroup per (row, chunk) publishes the chunk's
 // (max m_c, sum s_c of exp((x - m_c)/T)).  The next launch reads them (kernel boundaries order
 // the two passes; no device-wide fences are needed).
@@ -362,6 +411,9 @@ SMWsLayout sm_ws_layout(int64_t rows, int64_t nchunk) {
 template <typename Tin, bool kVec>
 hipError_t sm_launch_all(const SmParams &P, hipStream_t stream) {
   const unsigned rows = static_cast<unsigned>(P.rows);
+  if (P.nchunk == 1 && P.n <= kWave)
+    return launch(softmax_wave<Tin>, dim3(static_cast<unsigned>((P.rows + kWavesPerBlock - 1) / kWavesPerBlock)),
+                  dim3(kBlock), 0, stream, P);
   if (P.nchunk == 1) return launch(softmax_single<Tin, kVec>, dim3(rows), dim3(kBlock), 0, stream, P);
   const unsigned grid = static_cast<unsigned>(P.rows * P.nchunk);
   hipError_t e = launch(softmax_partial<Tin, kVec>, dim3(grid), dim3(kBlock), 0, stream, P);

@@ -355,6 +355,90 @@ __device__ __forceinline__ void greedy_single(const VfParams &P, int64_t b, floa
   greedy_finish(P, b, a, sh_n);
 }
 
+// Vocabularies of at most 64 ids (the toy): one wavefront per sequence, four per workgroup, lane x
+// holding id x; the same decisions as verify_single (fp64 accept ratios, n = first rejection,
+// residual max(0, p_n - q_n) or p_gamma, p_n when the residual sums to zero, the first id whose
+// running sum reaches u Z, else the last one with positive weight), with wave scans and ballots
+// instead of workgroup barriers.
+template <typename Tin>
+__global__ __launch_bounds__(kBlock) void verify_wave(VfParams P, int64_t B) {
+  const int64_t b = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_id();
+  if (b >= B) return;  // the whole wavefront
+  const int lane = lane_id(), g = P.gamma;
+  const bool in = lane < P.V;
+  const int xs = in ? lane : 0;
+  auto tlogit = [&](int i, int64_t y) {
+    return load_logit(reinterpret_cast<const Tin *>(P.target) + (b * (g + 1) + i) * P.V, y);
+  };
+  int32_t *tok = P.out_tokens + b * (g + 1);
+  // draft i on lane i: its trimmed id, full id, validity
+  int32_t x = -1, y = -1;
+  bool valid = true;
+  if (lane < g) {
+    x = P.ids[b * P.R + lane];
+    valid = x >= 0 && x < P.Vt;
+    if (valid) {
+      y = P.keep ? P.keep[x] : x;
+      valid = y >= 0 && y < P.V;
+    }
+  }
+  const unsigned long long bad = __ballot(lane < g && !valid);
+  int n, fin;
+  if (P.greedy) {
+    // argmax of every target row (lowest id on ties), one row at a time over the lanes
+    int am = -1;  // lane i keeps row i's argmax
+    for (int i = 0; i <= g; ++i) {
+      float bv = in ? tlogit(i, xs) : kNegInf;
+      int bi = in ? lane : kNoIndex;
+      wave_argmax(bv, bi);
+      if (lane == i) am = bi;
+    }
+    const unsigned long long rej = __ballot(lane < g && !(valid && y == am));
+    n = bad ? -1 : (rej ? __ffsll(static_cast<long long>(rej)) - 1 : g);
+    fin = n >= 0 ? lane_value(am, n) : -1;
+  } else {
+    bool accept = true;
+    if (lane < g && valid) {
+      const double a = static_cast<double>(tlogit(lane, y)) / P.Tt - P.tlse[b * (g + 1) + lane];
+      const double d = static_cast<double>(P.draft[(b * P.R + lane) * P.Vt + x]) / P.Td - P.dlse[b * P.R + lane];
+      accept = static_cast<double>(P.uacc[b * g + lane]) <= fmin(1.0, exp(a - d));
+    }
+    const unsigned long long rej = __ballot(lane < g && !accept);
+    n = bad ? -1 : (rej ? __ffsll(static_cast<long long>(rej)) - 1 : g);
+    fin = -1;
+    if (n >= 0) {
+      const int row = n < g ? n : g;
+      const RowExp pe = make_row_exp(P.tlse[b * (g + 1) + row], P.Tt, P.k2t);
+      const float p = in ? pe(tlogit(row, xs)) : 0.f;
+      float w = p;
+      if (n < g) {
+        const RowExp qe = make_row_exp(P.dlse[b * P.R + n], P.Td, P.k2d);
+        const int32_t t = in ? (P.f2t ? P.f2t[xs] : xs) : -1;
+        const bool kept = t >= 0 && t < P.Vt;
+        const float q = kept ? qe(P.draft[(b * P.R + n) * P.Vt + (kept ? t : 0)]) : 0.f;
+        w = fmaxf(p - q, 0.f);
+        if (!(lane_value(wave_scan_incl(w), kWave - 1) > 0.f)) w = p;  // residual rounds to zero
+      }
+      const float C = wave_scan_incl(w);
+      const float tt = P.ufin[b] * lane_value(C, kWave - 1);
+      const unsigned long long hit = __ballot(in && tt <= C);
+      if (hit) {
+        fin = __ffsll(static_cast<long long>(hit)) - 1;
+      } else {
+        const unsigned long long pos = __ballot(in && w > 0.f);
+        fin = pos ? 63 - __clzll(static_cast<long long>(pos)) : -1;
+      }
+    }
+  }
+  for (int i = lane; i <= g; i += kWave) {
+    int32_t v = -1;
+    if (n >= 0 && i < n) v = y;  // lane i holds draft i's full id (g <= 64)
+    else if (n >= 0 && i == n) v = fin;
+    tok[i] = v;
+  }
+  if (lane == 0) P.out_n[b] = n;
+}
+
 // Vocabularies of one chunk (V <= 4096): one workgroup per sequence does everything.
 template <typename Tin, bool kVec>
 __global__ __launch_bounds__(kBlock) void verify_single(VfParams P) {
@@ -482,6 +566,9 @@ VFWsLayout vf_ws_layout(int64_t B, int64_t gamma, int64_t nchunk) {
 
 template <typename Tin, bool kVec>
 hipError_t vf_launch_all(const VfParams &P, int64_t B, hipStream_t stream) {
+  if (P.nchunk == 1 && P.V <= kWave)
+    return launch(verify_wave<Tin>, dim3(static_cast<unsigned>((B + kWavesPerBlock - 1) / kWavesPerBlock)),
+                  dim3(kBlock), 0, stream, P, B);
   if (P.nchunk == 1) return launch(verify_single<Tin, kVec>, dim3(static_cast<unsigned>(B)), dim3(kBlock), 0, stream, P);
   const hipError_t e = launch(verify_partial<Tin, kVec>, dim3(static_cast<unsigned>(B * P.nchunk)), dim3(kBlock), 0,
                               stream, P);
