@@ -209,16 +209,21 @@ struct SelParams {
   int32_t *num_kept;
 };
 
-// This thread's 16 counts of the tile starting at id `tile`; returns how many are in range.
+// This thread's 16 counts of the tile starting at id `tile`, loaded without a branch, at
+// indices clamped into [0, V) (kVec is chosen only when V is a multiple of 4, so V >= 4 and each
+// 16-byte piece lies wholly inside or wholly past the end); entries past
+// V hold repeats and must be masked by the caller (tile_valid).  Loading the next tile this way
+// while the current one is processed keeps the loads in flight: a branch around them would make
+// the compiler wait for them at the join.
 template <bool kVec>
-__device__ __forceinline__ int load_tile(const SelParams &P, int tile, uint32_t (&c)[kSelPer]) {
+__device__ __forceinline__ void load_tile_raw(const SelParams &P, int tile, uint32_t (&c)[kSelPer]) {
   const int e0 = tile + static_cast<int>(threadIdx.x) * kSelPer;
-  const int nv = max(0, min(kSelPer, P.V - e0));
-  if (kVec && nv == kSelPer) {
-    const uint4 *p4 = reinterpret_cast<const uint4 *>(P.counts + e0);
+  if constexpr (kVec) {
+    const uint4 *p4 = reinterpret_cast<const uint4 *>(P.counts);
+    const int last = P.V / 4 - 1;
 #pragma unroll
     for (int q = 0; q < kSelPer / 4; ++q) {
-      const uint4 v = p4[q];
+      const uint4 v = p4[min(e0 / 4 + q, last)];
       c[4 * q] = v.x;
       c[4 * q + 1] = v.y;
       c[4 * q + 2] = v.z;
@@ -226,9 +231,12 @@ __device__ __forceinline__ int load_tile(const SelParams &P, int tile, uint32_t 
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < kSelPer; ++j) c[j] = j < nv ? P.counts[e0 + j] : 0u;
+    for (int j = 0; j < kSelPer; ++j) c[j] = P.counts[min(e0 + j, P.V - 1)];
   }
-  return nv;
+}
+
+__device__ __forceinline__ int tile_valid(const SelParams &P, int tile) {
+  return max(0, min(kSelPer, P.V - tile - static_cast<int>(threadIdx.x) * kSelPer));
 }
 
 // Radix descent for the threshold count.  by_mass = false: `want` counts ids (the k-th largest
@@ -250,9 +258,11 @@ __device__ uint32_t radix_threshold(const SelParams &P, bool by_mass, uint64_t w
     const uint32_t dm = dmasks[pass];
     for (int i = threadIdx.x; i < kDigits; i += kSelThreads) hist[i] = 0;
     __syncthreads();
+    uint32_t c[kSelPer], cn[kSelPer];
+    load_tile_raw<kVec>(P, 0, c);
     for (int tile = 0; tile < P.V; tile += kSelTile) {
-      uint32_t c[kSelPer];
-      const int nv = load_tile<kVec>(P, tile, c);
+      load_tile_raw<kVec>(P, tile + kSelTile, cn);  // the next tile (clamped, unused past the end)
+      const int nv = tile_valid(P, tile);
       int cur = -1;
       uint64_t acc = 0;
 #pragma unroll
@@ -278,6 +288,8 @@ __device__ uint32_t radix_threshold(const SelParams &P, bool by_mass, uint64_t w
         if (lane == leader) atomicAdd(reinterpret_cast<unsigned long long *>(&hist[d0]), tot);
         if (cur >= 0 && !same) atomicAdd(reinterpret_cast<unsigned long long *>(&hist[cur]), acc);
       }
+#pragma unroll
+      for (int j = 0; j < kSelPer; ++j) c[j] = cn[j];
     }
     __syncthreads();
     // thread t owns digits hi = 2047 - 2t and hi - 1, so thread order is descending digit order
@@ -321,11 +333,16 @@ __global__ __launch_bounds__(kSelThreads) void keep_select(SelParams P) {
     bool by_mass = false;
     if (P.rule == VT_SELECT_TOP_P) {
       uint64_t s = 0;
+      uint32_t c[kSelPer], cn[kSelPer];
+      load_tile_raw<kVec>(P, 0, c);
       for (int tile = 0; tile < P.V; tile += kSelTile) {
-        uint32_t c[kSelPer];
-        load_tile<kVec>(P, tile, c);
+        load_tile_raw<kVec>(P, tile + kSelTile, cn);
+        const int nv = tile_valid(P, tile);
 #pragma unroll
-        for (int j = 0; j < kSelPer; ++j) s += c[j];
+        for (int j = 0; j < kSelPer; ++j) {
+          s += j < nv ? c[j] : 0u;
+          c[j] = cn[j];
+        }
       }
       uint64_t total;
       (void)sel_exclusive_scan<uint64_t>(s, red64, &total);
@@ -344,9 +361,11 @@ __global__ __launch_bounds__(kSelThreads) void keep_select(SelParams P) {
   // written contiguously by consecutive lanes.
   __shared__ int32_t kbuf[kSelTile];
   int tie_carry = 0, keep_carry = 0;
+  uint32_t c[kSelPer], cn[kSelPer];
+  load_tile_raw<kVec>(P, 0, c);
   for (int tile = 0; tile < P.V; tile += kSelTile) {
-    uint32_t c[kSelPer];
-    const int nv = load_tile<kVec>(P, tile, c);
+    load_tile_raw<kVec>(P, tile + kSelTile, cn);
+    const int nv = tile_valid(P, tile);
     int above = 0, ties = 0;
 #pragma unroll
     for (int j = 0; j < kSelPer; ++j) {
@@ -385,6 +404,8 @@ __global__ __launch_bounds__(kSelThreads) void keep_select(SelParams P) {
     __syncthreads();
     tie_carry += tie_total;
     keep_carry += kept_total;
+#pragma unroll
+    for (int j = 0; j < kSelPer; ++j) c[j] = cn[j];
   }
   if (threadIdx.x == 0) *P.num_kept = keep_carry;
 }
@@ -451,7 +472,8 @@ extern "C" vt_status_t vt_keep_select(const uint32_t *counts, int64_t V, vt_sele
   if (V > INT32_MAX) return VT_ERR_UNSUPPORTED;
   const SelParams P{counts, static_cast<int>(V), static_cast<int>(rule), k, p, min_count, keep_ids, full_to_trim,
                     num_kept};
-  return hip_status(aligned16(counts) && aligned16(full_to_trim)
+  // 16-byte loads need aligned buffers and whole 4-count pieces (load_tile_raw clamps piece indices)
+  return hip_status(aligned16(counts) && aligned16(full_to_trim) && V % 4 == 0
                         ? launch(keep_select<true>, dim3(1), dim3(kSelThreads), 0, stream, P)
                                       : launch(keep_select<false>, dim3(1), dim3(kSelThreads), 0, stream, P));
 }

@@ -94,11 +94,12 @@ def counts_cases():
     wide = rng.integers(0, 1 << 32, size=V, dtype=np.uint64).astype(np.uint32)  # every digit in play
     wide[rng.choice(V, 50, replace=False)] = wide[:50]                  # some equal large counts
     small = rng.integers(0, 9, size=1000).astype(np.uint32)
+    ragged = rng.integers(0, 50, size=1001).astype(np.uint32)  # V % 4 != 0 with non-zero tail counts
     return {"zipf": zipf, "ties": ties, "wide": wide, "small": small, "zeros": np.zeros(777, np.uint32),
-            "one": np.array([5], np.uint32)}
+            "one": np.array([5], np.uint32), "ragged": ragged}
 
 
-CASE_NAMES = ["zipf", "ties", "wide", "small", "zeros", "one"]
+CASE_NAMES = ["zipf", "ties", "wide", "small", "zeros", "one", "ragged"]
 
 
 @pytest.mark.parametrize("name", CASE_NAMES)
