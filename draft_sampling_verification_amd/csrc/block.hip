@@ -36,7 +36,7 @@ struct BlockPlan {
   int64_t nchunk_d;  // draft partial chunks per row (GEMV row blocks, or 4096-chunks)
   int chunk_d;
   int64_t nchunk_v;
-  size_t off_tpart, off_dpart, off_nbuf, off_vpart, bytes;
+  size_t off_tpart, off_dpart, off_nbuf, off_vpart, off_wbuf, bytes;
 };
 
 // greedy_t: the target is decoded greedily (no target softmax; verification compares argmaxes).
@@ -76,6 +76,8 @@ BlockPlan plan_block(int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt,
     p.off_vpart = off;
     off += align_up(static_cast<size_t>(B * (gamma + 1) * p.nchunk_v) * sizeof(float2), 256);
   }
+  p.off_wbuf = off;
+  if (p.fv) off += align_up(static_cast<size_t>(2 * B * V) * sizeof(float), 256);  // final-draw weights and p_n
   p.bytes = off;
   return p;
 }
@@ -98,7 +100,7 @@ hipError_t launch_combine(const SmParams &D, bool d_multi, const SmParams &T, bo
 template <typename TinT, bool kVecT>
 hipError_t run_block_small(const BlockPlan &pl, const SmParams &D, const SmParams &T, const VfParams &Vp,
                            const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int64_t H,
-                           int64_t Vt, float *logits, const float *u_draft, int64_t B, hipEvent_t ev0,
+                           int64_t Vt, float *logits, const float *u_draft, float *wbuf, int64_t B, hipEvent_t ev0,
                            hipEvent_t ev1, hipStream_t stream) {
   hipError_t e = hipSuccess;
   GemvParts gp{};
@@ -122,10 +124,12 @@ hipError_t run_block_small(const BlockPlan &pl, const SmParams &D, const SmParam
   F.dlse_out = D.lse;
   F.dids_out = D.sampled;
   F.tlse_out = T.lse;
+  F.wbuf = wbuf;
+  F.pbuf = wbuf + B * Vp.V;
   e = launch(verify_fused_chunk<TinT, kVecT>, dim3(static_cast<unsigned>(B * Vp.nchunk)), dim3(kFvBlock), 0, stream,
              F);
   if (e != hipSuccess) return e;
-  return launch(verify_fused_final<TinT, kVecT>, dim3(static_cast<unsigned>(B)), dim3(kBlock), 0, stream, Vp);
+  return launch(verify_fused_final<TinT, kVecT>, dim3(static_cast<unsigned>(B)), dim3(kBlock), 0, stream, F);
 }
 
 // Small batch, greedy both sides: 2 launches.  The GEMV launch leaves per-block argmax partials
@@ -161,9 +165,10 @@ hipError_t run_block_greedy_small(const BlockPlan &pl, const SmParams &D, const 
 template <typename TinT, bool kVecT, bool kVecD>
 hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, const VfParams &Vp,
                      const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int64_t H, int64_t Vt,
-                     float *logits, int64_t B, hipEvent_t ev0, hipEvent_t ev1, hipStream_t stream) {
-  if (pl.fv) return run_block_small<TinT, kVecT>(pl, D, T, Vp, hidden, weight, keep, H, Vt, logits, D.u, B, ev0, ev1,
-                                                 stream);
+                     float *logits, float *wbuf, int64_t B, hipEvent_t ev0, hipEvent_t ev1, hipStream_t stream) {
+  if (pl.fv)
+    return run_block_small<TinT, kVecT>(pl, D, T, Vp, hidden, weight, keep, H, Vt, logits, D.u, wbuf, B, ev0, ev1,
+                                        stream);
   if (pl.fg)
     return run_block_greedy_small<TinT, kVecT>(pl, D, T, Vp, hidden, weight, keep, H, Vt, logits, B, ev0, ev1, stream);
   hipError_t e = hipSuccess;
@@ -320,7 +325,8 @@ extern "C" vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *wei
   const bool vt_ = aligned16(target_logits) && V % vec_elems == 0;
   const bool vd = aligned16(draft_logits) && Vt % 4 == 0 && pl.chunk_d % 4 == 0;
   auto go = [&](auto run) {
-    return run(pl, D, T, P, hidden, weight, keep_ids, H, Vt, draft_logits, B, lmhead_begin, lmhead_end, stream);
+    return run(pl, D, T, P, hidden, weight, keep_ids, H, Vt, draft_logits,
+               pl.fv ? reinterpret_cast<float *>(ws + pl.off_wbuf) : nullptr, B, lmhead_begin, lmhead_end, stream);
   };
   hipError_t e;
   if (target_dtype == VT_F32) {

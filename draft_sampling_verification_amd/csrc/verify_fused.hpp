@@ -60,6 +60,7 @@ struct FvParams {
   double *dlse_out;      // [B * R]
   int32_t *dids_out;     // [B * R]
   double *tlse_out;      // [B * (gamma + 1)]
+  float *wbuf, *pbuf;    // [B][V]: the chunk pass's final-draw weights and p_n, for the final pass
 };
 
 // Raw bits of two consecutive elements [e0, e0 + 2) of a row (even e0), loaded unconditionally
@@ -395,20 +396,25 @@ __global__ __launch_bounds__(kFvBlock) void verify_fused_chunk(FvParams F) {
       if (!on[j]) d2[j] = kNegInf;
     }
     const RowExp pe = make_row_exp_inv(s_tlse[n], P.Tt, P.invTt, P.k2t);
+    float wj[kFvPer], pj[kFvPer];
     if (n < g) {
       const RowExp qe = make_row_exp_inv(s_dlse[n], P.Td, P.invTd, P.k2d);
 #pragma unroll
       for (int j = 0; j < kFvPer; ++j) {
-        const float p = pe(t2[j]);
-        sw += fmaxf(p - qe(d2[j]), 0.f);
-        sp += p;
+        pj[j] = pe(t2[j]);
+        wj[j] = fmaxf(pj[j] - qe(d2[j]), 0.f);
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < kFvPer; ++j) {
-        const float p = pe(t2[j]);
-        sw += p;
-        sp += p;
+      for (int j = 0; j < kFvPer; ++j) pj[j] = wj[j] = pe(t2[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kFvPer; ++j) {
+      sw += wj[j];
+      sp += pj[j];
+      if (x0 + j < P.V) {  // kept for the final pass's rescan of one chunk
+        F.wbuf[b * P.V + x0 + j] = wj[j];
+        F.pbuf[b * P.V + x0 + j] = pj[j];
       }
     }
   }
@@ -500,9 +506,11 @@ __global__ __launch_bounds__(kFvBlock) void verify_greedy_small(FvParams F) {
 }
 
 // Final pass: one 256-thread workgroup per sequence draws the final token from the chunk sums
-// and writes the outputs (the log-normalisers and draft ids were written by the chunk pass).
+// and writes the outputs (the log-normalisers and draft ids were written by the chunk pass); the
+// chunk it rescans comes from the weights the chunk pass kept, so no logit is read here.
 template <typename Tin, bool kVec>
-__global__ __launch_bounds__(kBlock) void verify_fused_final(VfParams P) {
+__global__ __launch_bounds__(kBlock) void verify_fused_final(FvParams F) {
+  const VfParams &P = F.v;
   __shared__ float redf[kWavesPerBlock];
   __shared__ int redi[kWavesPerBlock];
   __shared__ float bcast;
@@ -514,7 +522,15 @@ __global__ __launch_bounds__(kBlock) void verify_fused_final(VfParams P) {
     const float2 v = part[k];
     return use_p ? v.y : v.x;
   };
-  finish_sequence<Tin, kVec, decltype(mass), kFvFinalPer>(P, b, n, mass, redf, redi, &bcast);
+  auto weights = [&](int c, bool use_p, float(&wv)[kFvFinalPer]) {
+    const float *src = (use_p ? F.pbuf : F.wbuf) + b * P.V;
+#pragma unroll
+    for (int j = 0; j < kFvFinalPer; ++j) {
+      const int64_t x = static_cast<int64_t>(c) * kFvIds + static_cast<int64_t>(threadIdx.x) * kFvFinalPer + j;
+      wv[j] = x < P.V ? src[x] : 0.f;
+    }
+  };
+  finish_sequence<Tin, kVec, decltype(mass), kFvFinalPer>(P, b, n, mass, redf, redi, &bcast, weights);
 }
 
 }  // namespace

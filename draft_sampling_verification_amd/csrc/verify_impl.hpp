@@ -17,6 +17,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "vt_common.hpp"
 
@@ -186,9 +187,11 @@ __device__ __forceinline__ int accept_scan(const VfParams &P, int64_t b, int *sh
 
 // Final draw and outputs of sequence b, given n and the chunk sums of the residual (or bonus)
 // weights and of p (mass(k, use_p)); all threads of the workgroup must call.
-template <typename Tin, bool kVec, typename Mass, int PER = kPerThread>
+// weights (optional): a callable (chunk, use_p, float (&wv)[PER]) giving this thread's weights of
+// the chunk when they were kept from pass 1; otherwise they are recomputed from the logits.
+template <typename Tin, bool kVec, typename Mass, int PER = kPerThread, typename Weights = std::nullptr_t>
 __device__ __forceinline__ void finish_sequence(const VfParams &P, int64_t b, int n, Mass mass, float *redf,
-                                                int *redi, float *bcast) {
+                                                int *redi, float *bcast, Weights weights = nullptr) {
   const int gamma = P.gamma;
   int32_t *tok = P.out_tokens + b * (gamma + 1);
   if (n < 0) {
@@ -242,8 +245,13 @@ __device__ __forceinline__ void finish_sequence(const VfParams &P, int64_t b, in
     fallback = true;
   }
   // rescan chunk c*: running sum inside it, first id reaching t (else last positive id)
-  float wv[PER], pv[PER];
-  final_weights<Tin, kVec, PER>(P, b, n, cstar, use_p, wv, pv);
+  float wv[PER];
+  if constexpr (std::is_same<Weights, std::nullptr_t>::value) {
+    float pv[PER];
+    final_weights<Tin, kVec, PER>(P, b, n, cstar, use_p, wv, pv);
+  } else {
+    weights(cstar, use_p, wv);
+  }
   float loc[PER];
   float acc = 0.f;
 #pragma unroll
