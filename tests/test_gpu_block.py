@@ -57,6 +57,15 @@ def test_fused_block_parity_scaled(name):
     _check(make_workload(SCALED[name]))
 
 
+def test_fused_block_longest_draft():
+    # gamma = 64, the longest run the path takes (one lane per draft position), with a drafter that
+    # follows the target closely: runs of every length up to full acceptance and its bonus token
+    cfg = CONFIGS[4].scaled(B=6, gamma=64, R=65, V=6000, Vt=2500, H=256)
+    say("fused block parity gamma=64, following drafter")
+    _, orc = _check(make_workload(cfg, follow=0.03))
+    assert (orc["n"] == 64).any() and (orc["n"] < 64).any()
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_fused_block_parity_small_batch(name):
     say(f"fused block parity {name} (three-launch path)")

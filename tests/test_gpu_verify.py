@@ -84,6 +84,15 @@ def _verify_only(target, T, draft, ids, u_acc, u_fin, keep=None, f2t=None):
     return tok.cpu().numpy(), nacc.cpu().numpy()
 
 
+def test_block_parity_longest_draft():
+    # gamma = 64 through the separate calls (draft = target at the kept ids: deep accepts,
+    # full acceptance with the bonus draw from row 64)
+    say("aligned block parity gamma=64")
+    wl = make_workload(CONFIGS[4].scaled(B=4, gamma=64, R=65, V=6000, Vt=2500, H=256), aligned=True)
+    _, orc, _ = _check_block(wl)
+    assert (orc["n"] == 64).any()
+
+
 def test_worked_example_grid_on_gpu():
     # glossary two-token example (A 0.6 / B 0.4 target, 0.8 / 0.2 draft), 40 x 40 grid of
     # (u_draft, u_accept) as 1600 sequences: 960 keep A, 320 keep B, 320 are rejected -> B
@@ -108,9 +117,9 @@ def test_worked_example_grid_on_gpu():
         assert (tok[:, 0] == 0).sum() * 5 == B * 3  # final A mass 0.6
 
 
-def test_identical_draft_accepts_everything():
+@pytest.mark.parametrize("B,g,V", [(12, 5, 9000), (3, 64, 3000)])  # 64: the longest run taken
+def test_identical_draft_accepts_everything(B, g, V):
     rng = np.random.default_rng(1)
-    B, g, V = 12, 5, 9000
     target = (1.5 * rng.standard_normal((B, g + 1, V))).astype(np.float32)
     draft = target.copy()  # q == p bitwise at every position (R = gamma + 1)
     u_d = counter_uniforms(7, 4, B, g + 1)
