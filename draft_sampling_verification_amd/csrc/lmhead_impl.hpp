@@ -57,6 +57,62 @@ __device__ __forceinline__ float half_wave_reduce(float v, Op op) {
   return op(a, b);
 }
 
+// Reduce-scatter over each half-wave of 64 per-lane entries: afterwards v[k], k < 2, holds the
+// reduction over the half's 32 lanes of entry 2 (lane & 31) + k.  Each step pairs the lanes at
+// one distance (16: row swap; 8: rotation of the row by 8; 4: mirror of each group of 8, whose
+// lanes hold the same entries by then; 2 and 1: quad permutations) and halves the entries a lane
+// carries, each lane keeping the half its partner gives up: 62 exchanges for the 64 reductions
+// instead of 5 each.
+template <int CTRL, int BIT, int H, typename Op>
+__device__ __forceinline__ void scatter_step(float (&v)[64], Op op) {
+  const bool up = (lane_id() & BIT) != 0;
+#pragma unroll
+  for (int k = 0; k < H; ++k) {
+    const float send = up ? v[k] : v[k + H];
+    const float keep = up ? v[k + H] : v[k];
+    v[k] = op(keep, lane_swap<CTRL>(send));
+  }
+}
+template <typename Op>
+__device__ __forceinline__ void half_reduce_scatter(float (&v)[64], Op op) {
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    float a = v[k], b = v[k + 32];
+    swap16(a, b);
+    v[k] = op(a, b);
+  }
+  scatter_step<kDppRor8, 8, 16>(v, op);
+  scatter_step<kDppHalfMirror, 4, 8>(v, op);
+  scatter_step<kDppXor2, 2, 4>(v, op);
+  scatter_step<kDppXor1, 1, 2>(v, op);
+}
+// The movement of half_reduce_scatter reversed: from v[k] = entry 2 (lane & 31) + k (k < 2),
+// every lane of the half ends with all 64 entries in order.
+template <int CTRL, int BIT, int H>
+__device__ __forceinline__ void gather_step(float (&v)[64]) {
+  const bool up = (lane_id() & BIT) != 0;
+#pragma unroll
+  for (int k = 0; k < H; ++k) {
+    const float mine = v[k];
+    const float other = lane_swap<CTRL>(mine);
+    v[k] = up ? other : mine;
+    v[k + H] = up ? mine : other;
+  }
+}
+__device__ __forceinline__ void half_all_gather(float (&v)[64]) {
+  gather_step<kDppXor1, 1, 2>(v);
+  gather_step<kDppXor2, 2, 4>(v);
+  gather_step<kDppHalfMirror, 4, 8>(v);
+  gather_step<kDppRor8, 8, 16>(v);
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    float a = v[k], b = v[k];
+    swap16(a, b);
+    v[k] = a;
+    v[k + 32] = b;
+  }
+}
+
 // Transpose-reduction of NP (1, 2, 4 or 8) per-lane partial sums over the 64 lanes.  The steps
 // at lane distance 32, 16 and 8 halve the number of values each lane carries (each lane keeps
 // the half its partner gives up), the remaining steps add within groups of 64/NP lanes.  On
@@ -507,26 +563,47 @@ __device__ __forceinline__ void big_tile_store(const f32x16 (&acc)[4][NJ], int M
       }
     }
   if constexpr (PARTS) {
-    // per hidden row: max and sum of exp2((x - max) k2) over this wave's 32 NJ columns (32 lanes
-    // of a half-wave x NJ subtiles), then merged with the other waves covering the same rows
+    // per hidden row: max and sum of exp2((x - max) k2) over this wave's 32 NJ columns.  A lane
+    // holds 64 rows (entry e = 16 i + v) of its half-wave's rows; their maxima are reduced over
+    // the half's 32 lanes by a reduce-scatter and gathered back for the exponentials, the sums
+    // reduced by a second reduce-scatter; lane l then owns entries 2 (l & 31) + k and writes them
+    // for the merge with the other waves covering the same rows.
+    bool cin[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) cin[j] = n0 + wn + j * 32 + lr < Vt;
+    float mx[64];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        float x[NJ];
-        float mx = kNegInf;
+        float m = cin[0] ? acc[i][0][v] : kNegInf;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          x[j] = (n0 + wn + j * 32 + lr < Vt) ? acc[i][j][v] : kNegInf;
-          mx = fmaxf(mx, x[j]);
-        }
-        mx = half_wave_reduce(mx, [](float a, float b) { return fmaxf(a, b); });
-        float sm = 0.f;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) sm += x[j] == kNegInf ? 0.f : __builtin_amdgcn_exp2f((x[j] - mx) * parts.k2);
-        sm = half_wave_reduce(sm, [](float a, float b) { return a + b; });
-        if (lr == 0) wpart[slot][wm + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)] = make_float2(mx, sm);
+        for (int j = 1; j < NJ; ++j) m = fmaxf(m, cin[j] ? acc[i][j][v] : kNegInf);
+        mx[16 * i + v] = m;
       }
+    const auto fmax_op = [](float a, float b) { return fmaxf(a, b); };
+    half_reduce_scatter(mx, fmax_op);
+    const float own_m[2] = {mx[0], mx[1]};
+    half_all_gather(mx);
+    float sm[64];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        // a row with no column in range has max -inf: reference 0 there, so every term is exp2(-inf) = 0
+        const float ref = mx[16 * i + v] == kNegInf ? 0.f : mx[16 * i + v];
+        float t = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          t += __builtin_amdgcn_exp2f(((cin[j] ? acc[i][j][v] : kNegInf) - ref) * parts.k2);
+        sm[16 * i + v] = t;
+      }
+    half_reduce_scatter(sm, [](float a, float b) { return a + b; });
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int e = 2 * lr + k, i = e >> 4, v = e & 15;
+      wpart[slot][wm + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)] = make_float2(own_m[k], sm[k]);
+    }
     __syncthreads();
     const int r = tid;  // one thread per row of the tile
     const int gm = m0 + r;
