@@ -197,3 +197,21 @@ def test_block_shapes_and_remap_scaled():
     n = out["n"][0]
     assert list(out["tokens"][0, :n]) == [int(wl.keep_ids[z]) for z in out["draft_ids"][0, :n]]
     assert np.all(out["tokens"][0, n + 1:] == -1)
+
+
+def test_zero_residual_falls_back_to_p():
+    """Reading R5: after a rejection the residual max(0, p_n - q_n) has positive mass in exact
+    arithmetic ("Speculative decoding" glossary, "Why a rejection needs a special draw": it is a
+    real distribution once normalised), but rounding can leave q_n >= p_n at every id.  Then the
+    final token is drawn from p_n itself.  Here q_n = p_n except at id 0, where q_n is larger, so
+    draft 0 is rejected with ratio 2/3 when u = 1 and the residual is zero everywhere; the draw
+    must follow p_n's running sum (0.1, 0.3, 0.6, 1.0), not q_n's (0.15, 0.35, 0.65, 1.05)/1.05."""
+    p = np.array([[0.1, 0.2, 0.3, 0.4], [0.25, 0.25, 0.25, 0.25]])
+    q = np.array([[0.15, 0.2, 0.3, 0.4]])
+    for uf, want in [(0.05, 0), (0.12, 1), (0.29, 1), (0.45, 2), (0.62, 3), (0.8, 3), (1.0, 3)]:
+        tok, n, ratios, _ = ref.verify_sequence(p, q, [0], None, [1.0], uf, 1)
+        assert n == 0 and abs(ratios[0] - 2 / 3) < 1e-15
+        assert tok[0] == want and tok[1] == -1, (uf, tok)
+    # a ratio of exactly 1 (p = q at the drafted id) always accepts, even at u = 1
+    tok, n, ratios, _ = ref.verify_sequence(p, q, [2], None, [1.0], 0.5, 1)
+    assert n == 1 and ratios[0] == 1.0 and tok[0] == 2
