@@ -10,6 +10,8 @@ from .gen import (  # noqa: F401
     Config,
     ToyTables,
     Workload,
+    article_toy,
+    article_toy_counts,
     bf16_round,
     counter_uniforms,
     make_workload,

@@ -23,6 +23,8 @@ from __future__ import annotations
 
 import dataclasses
 import functools
+import json
+import os
 from typing import Optional
 
 import numpy as np
@@ -205,6 +207,44 @@ def toy_tables(cfg: Config = CONFIGS[1], w: float = 0.5) -> ToyTables:
     q0 /= q0.sum()
     q = w * p + (1.0 - w) * q0[None, :]
     return ToyTables(target_logits=tl, draft_logits=np.log(q).astype(np.float32), w=w)
+
+
+ARTICLE_TOY_FIXTURE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "tests", "golden",
+                                   "rr_toy.json")
+
+
+@functools.lru_cache(maxsize=1)
+def article_toy_counts():
+    """The rejection-rule article's toy models, as counts ("A target and a draft small enough to
+    print in full"): the vocabulary is the sorted set of the corpus's characters (18); the target is
+    an order-1 bigram model with one pseudo-count per (context, token) pair plus one count per
+    transition of the corpus, read from a start context before its first character (row 0 of the
+    table; row r + 1 is the context "previous token = r"); the unigram q0 has one pseudo-count per
+    token plus its occurrences.  Returns (vocabulary string, bigram counts [V+1, V], unigram counts [V])."""
+    with open(ARTICLE_TOY_FIXTURE) as f:
+        corpus = json.load(f)["corpus"]
+    vocab = "".join(sorted(set(corpus)))
+    index = {c: i for i, c in enumerate(vocab)}
+    V = len(vocab)
+    bigram = np.ones((V + 1, V), dtype=np.int64)
+    ctx = 0
+    for ch in corpus:
+        bigram[ctx, index[ch]] += 1
+        ctx = index[ch] + 1
+    unigram = np.ones(V, dtype=np.int64)
+    for ch in corpus:
+        unigram[index[ch]] += 1
+    return vocab, bigram, unigram
+
+
+def article_toy(w: float) -> ToyTables:
+    """The article's target p (normalised bigram counts) and draft q_w = w p + (1 - w) q0 (q0 the
+    normalised unigram counts), formed in float64 and handed over as fp32 log-weights (T = 1)."""
+    _, bigram, unigram = article_toy_counts()
+    p = bigram / bigram.sum(axis=1, keepdims=True)
+    q0 = unigram / unigram.sum()
+    q = w * p + (1.0 - w) * q0[None, :]
+    return ToyTables(target_logits=np.log(p).astype(np.float32), draft_logits=np.log(q).astype(np.float32), w=w)
 
 
 @dataclasses.dataclass
