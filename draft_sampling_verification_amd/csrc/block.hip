@@ -103,13 +103,14 @@ hipError_t run_block_small(const BlockPlan &pl, const SmParams &D, const SmParam
                            int64_t Vt, float *logits, const float *u_draft, float *wbuf, int64_t B, hipEvent_t ev0,
                            hipEvent_t ev1, hipStream_t stream) {
   hipError_t e = hipSuccess;
+  const int vrows = static_cast<int>(Vp.V);  // the head passed in is the full [V][H] one
   GemvParts gp{};
   gp.part = D.part;
   gp.k2 = D.k2;
   gp.tgt = T;
   gp.tsel = sizeof(TinT) == 4 ? (kVecT ? 1 : 2) : (kVecT ? 3 : 4);
   if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-  e = launch_gemv(pick_gemv<kPartsSoftmax>(pl.M, H, keep != nullptr), hidden, weight, keep, H, Vt, logits, gp, stream,
+  e = launch_gemv(pick_gemv<kPartsSoftmax>(pl.M, H, keep != nullptr), hidden, weight, keep, vrows, H, Vt, logits, gp, stream,
                   T.rows * T.nchunk);
   if (e != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
@@ -141,12 +142,13 @@ hipError_t run_block_greedy_small(const BlockPlan &pl, const SmParams &D, const 
                                   int64_t Vt, float *logits, int64_t B, hipEvent_t ev0, hipEvent_t ev1,
                                   hipStream_t stream) {
   hipError_t e = hipSuccess;
+  const int vrows = static_cast<int>(Vp.V);  // the head passed in is the full [V][H] one
   GemvParts gp{};
   gp.part = D.part;
   gp.tgt = T;
   gp.tsel = sizeof(TinT) == 4 ? (kVecT ? 1 : 2) : (kVecT ? 3 : 4);
   if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-  e = launch_gemv(pick_gemv<kPartsArgmax>(pl.M, H, keep != nullptr), hidden, weight, keep, H, Vt, logits, gp, stream,
+  e = launch_gemv(pick_gemv<kPartsArgmax>(pl.M, H, keep != nullptr), hidden, weight, keep, vrows, H, Vt, logits, gp, stream,
                   T.rows * T.nchunk);
   if (e != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
@@ -172,6 +174,7 @@ hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, 
   if (pl.fg)
     return run_block_greedy_small<TinT, kVecT>(pl, D, T, Vp, hidden, weight, keep, H, Vt, logits, B, ev0, ev1, stream);
   hipError_t e = hipSuccess;
+  const int vrows = static_cast<int>(Vp.V);  // the head passed in is the full [V][H] one
   const bool greedy_t = Vp.greedy;
   const bool t_multi = !greedy_t && pl.nchunk_t > 1;
   // 1. target partials (or a whole single-chunk target softmax); greedy verification needs none
@@ -186,17 +189,17 @@ hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, 
   bool d_multi = true;
   if (pl.fused) {
     const GemvFn fn = pick_gemv<kPartsSoftmax>(pl.M, H, keep != nullptr);
-    e = launch_gemv(fn, hidden, weight, keep, H, Vt, logits, GemvParts{D.part, D.k2}, stream);
+    e = launch_gemv(fn, hidden, weight, keep, vrows, H, Vt, logits, GemvParts{D.part, D.k2}, stream);
     if (e != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   } else if (pl.fused_mfma) {
-    e = launch_mfma_big<true>(hidden, weight, keep, pl.M, H, Vt, logits, GemvParts{D.part, D.k2}, stream);
+    e = launch_mfma_big<true>(hidden, weight, keep, vrows, pl.M, H, Vt, logits, GemvParts{D.part, D.k2}, stream);
     if (e != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   } else {
     const GemvFn plain = pick_gemv<kPartsNone>(pl.M, H, keep != nullptr);
-    e = plain ? launch_gemv(plain, hidden, weight, keep, H, Vt, logits, GemvParts{}, stream)
-              : launch_mfma(hidden, weight, keep, pl.M, H, Vt, logits, stream);
+    e = plain ? launch_gemv(plain, hidden, weight, keep, vrows, H, Vt, logits, GemvParts{}, stream)
+              : launch_mfma(hidden, weight, keep, vrows, pl.M, H, Vt, logits, stream);
     if (e != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
     if (pl.nchunk_d > 1) {

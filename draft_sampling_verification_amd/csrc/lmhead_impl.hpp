@@ -170,10 +170,13 @@ struct Pow2Ceil<1> {
   static constexpr int value = 1;
 };
 
-#ifndef VT_GEMV_PD
-#define VT_GEMV_PD 2
-#endif
-constexpr int kGemvPrefetch = VT_GEMV_PD;  // weight rows in flight per wavefront beyond the one in use
+// Row of the full head behind kept row j: keep_ids[j], clamped into [0, vrows) so that an id out of
+// range (a violated precondition) gives unspecified logits but never a read outside the head.
+__device__ __forceinline__ int64_t kept_row(const int32_t *__restrict__ keep, int j, int vrows) {
+  return static_cast<int64_t>(min(static_cast<uint32_t>(keep[j]), static_cast<uint32_t>(vrows - 1)));
+}
+
+constexpr int kGemvPrefetch = 2;  // weight rows in flight per wavefront beyond the one in use
 
 // Rows per workgroup block: the head is cut into contiguous blocks of `per` rows (a multiple of 4,
 // one block per workgroup), sized for one workgroup per CU of a 256-CU device.  The size depends
@@ -227,8 +230,8 @@ constexpr int kPartsNone = 0, kPartsSoftmax = 1, kPartsArgmax = 2;
 template <int M, int NIT, int PD, bool FULL, bool TRIM, int PARTS>
 __global__ __launch_bounds__(kBlock) void lmhead_gemv(const uint16_t *__restrict__ hidden,
                                                       const uint16_t *__restrict__ weight,
-                                                      const int32_t *__restrict__ keep, int H, int Vt, int per,
-                                                      float *__restrict__ logits, GemvParts parts) {
+                                                      const int32_t *__restrict__ keep, int vrows, int H, int Vt,
+                                                      int per, float *__restrict__ logits, GemvParts parts) {
   constexpr int NP = Pow2Ceil<M>::value;
   constexpr int kGroup = kWave / NP;
   const int nblk = (Vt + per - 1) / per;
@@ -268,7 +271,7 @@ __global__ __launch_bounds__(kBlock) void lmhead_gemv(const uint16_t *__restrict
   auto fetch = [&](int t, uint4(&dst)[NIT]) {
     const int j = row_of(min(t, nrows - 1));  // wave-uniform
     int64_t r = j;
-    if constexpr (TRIM) r = keep[j];
+    if constexpr (TRIM) r = kept_row(keep, j, vrows);
     const uint4 *src = reinterpret_cast<const uint4 *>(weight + r * H);
 #pragma unroll
     for (int it = 0; it < NIT; ++it) dst[it] = load_nt(src + piece(it));
@@ -361,8 +364,8 @@ constexpr int kLdsRow = kBK + kLdsPad;  // bf16 elements per LDS row (80 bytes)
 
 __global__ __launch_bounds__(kBlock) void lmhead_mfma(const uint16_t *__restrict__ hidden,
                                                       const uint16_t *__restrict__ weight,
-                                                      const int32_t *__restrict__ keep, int M, int H, int Vt,
-                                                      float *__restrict__ logits) {
+                                                      const int32_t *__restrict__ keep, int vrows, int M, int H,
+                                                      int Vt, float *__restrict__ logits) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM * kLdsRow];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBN * kLdsRow];
 
@@ -387,7 +390,7 @@ __global__ __launch_bounds__(kBlock) void lmhead_mfma(const uint16_t *__restrict
     a_src[s] = gm < M ? hidden + static_cast<int64_t>(gm) * H : nullptr;
     const int gn = n0 + b_row[s];
     if (gn < Vt) {
-      const int64_t r = keep ? static_cast<int64_t>(keep[gn]) : static_cast<int64_t>(gn);
+      const int64_t r = keep ? kept_row(keep, gn, vrows) : static_cast<int64_t>(gn);
       b_src[s] = weight + r * H;
     } else {
       b_src[s] = nullptr;
@@ -467,7 +470,7 @@ __global__ __launch_bounds__(kBlock) void lmhead_mfma(const uint16_t *__restrict
 }
 
 // ------------------------------------------------------------------------------ dispatch
-using GemvFn = void (*)(const uint16_t *, const uint16_t *, const int32_t *, int, int, int, float *, GemvParts);
+using GemvFn = void (*)(const uint16_t *, const uint16_t *, const int32_t *, int, int, int, int, float *, GemvParts);
 
 constexpr int kGemvMaxM = 8;
 constexpr int kGemvMaxNit = 8;
@@ -626,8 +629,8 @@ __device__ __forceinline__ void big_tile_store(const f32x16 (&acc)[4][NJ], int M
 template <bool TRIM, bool PARTS, bool KFULL>
 __global__ __launch_bounds__(kBlock, 1) void lmhead_mfma_big(const uint16_t *__restrict__ hidden,
                                                              const uint16_t *__restrict__ weight,
-                                                             const int32_t *__restrict__ keep, int M, int H, int Vt,
-                                                             float *__restrict__ logits, GemvParts parts) {
+                                                             const int32_t *__restrict__ keep, int vrows, int M, int H,
+                                                             int Vt, float *__restrict__ logits, GemvParts parts) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][(kBigBM + kBigBN) * kBigRow];
   const int nbm = (M + kBigBM - 1) / kBigBM;
   const int nbn = (Vt + kBigBN - 1) / kBigBN;
@@ -643,7 +646,7 @@ __global__ __launch_bounds__(kBlock, 1) void lmhead_mfma_big(const uint16_t *__r
   for (int i = 0; i < 8; ++i) {
     arow[i] = min(m0 + r0 + 32 * i, M - 1);
     const int n = min(n0 + r0 + 32 * i, Vt - 1);
-    brow[i] = TRIM ? keep[n] : n;
+    brow[i] = TRIM ? static_cast<int>(kept_row(keep, n, vrows)) : n;
   }
   uint4 ra[8], rb[8];
   uint32_t keepk = 0xffffffffu;  // all ones while the fetched pieces lie inside H; pieces past H are zeroed
@@ -746,28 +749,18 @@ __global__ __launch_bounds__(kBlock, 1) void lmhead_mfma_big(const uint16_t *__r
                         reinterpret_cast<float2(*)[kBigBM]>(&smem[0][0]));
 }
 
-// The same 256 x 256 tiles with the operands brought into LDS by the load units themselves
-// (global_load_lds_dwordx4: each lane's 16 bytes land at LDS base + 16 * lane), through a ring of
-// four K steps of 32, so a load has three steps of MFMA work to arrive and no register staging or
-// LDS write instructions are needed.  A wave's 64 pieces fill 16 rows x 64 bytes contiguously, so
-// rows cannot be padded; instead piece p of tile row r is stored at slot p ^ f(r),
-// f(r) = ((r >> 1) ^ (r >> 3)) & 3, which spreads the 16 rows of a fragment read over all banks.
-// The waits are explicit: before the barrier of step k a thread waits until at most the loads of
-// steps k + 1 and k + 2 are outstanding (vmcnt(16)); the barrier then makes every thread's pieces
-// of step k visible and frees the slot of step k - 1 for step k + 3.  Steps past the last re-fetch
-// the last step into the free slot (never read), so every step issues the same 8 loads per thread.
-// Needs H % 32 == 0 (a piece past H cannot be zeroed on the way into LDS).
+// Direct-to-LDS operand staging for 256 x 256 tiles: the load units write each lane's 16 bytes
+// straight into LDS (global_load_lds_dwordx4: lane L's piece lands at LDS base + 16 L), through a
+// ring of four K steps of 32, so a load has two to three steps of MFMA work to arrive and no
+// register staging or LDS write instructions are needed.  A wave's 64 pieces fill 16 rows x 64
+// bytes contiguously, so rows cannot be padded; instead piece p of tile row r is stored at slot
+// p ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3, which spreads the 16 rows of a fragment read over
+// all banks.  Needs H % 32 == 0 (a piece past H cannot be zeroed on the way into LDS).
 constexpr int kDmaBK = 32;
-#ifndef VT_DMA_STAGES
-#define VT_DMA_STAGES 4
-#endif
-constexpr int kDmaStages = VT_DMA_STAGES;
-#ifndef VT_MFMA_WAVES
-#define VT_MFMA_WAVES 8  // waves per 256 x 256 tile in the direct-to-LDS kernel: 4 or 8
-#endif  // ring depth: loads get kDmaStages - 2 steps to land
-constexpr int kDmaRowBytes = kDmaBK * 2;                          // 64
-constexpr int kDmaOperandBytes = kBigBM * kDmaRowBytes;           // 16 KB per operand per step
-constexpr int kDmaStageBytes = 2 * kDmaOperandBytes;              // 32 KB
+constexpr int kDmaStages = 4;                           // ring depth: loads get kDmaStages - 2 steps to land
+constexpr int kDmaRowBytes = kDmaBK * 2;                // 64
+constexpr int kDmaOperandBytes = kBigBM * kDmaRowBytes;  // 16 KB per operand per step
+constexpr int kDmaStageBytes = 2 * kDmaOperandBytes;    // 32 KB
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int dma_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
@@ -780,113 +773,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <bool TRIM, bool PARTS>
-__global__ __launch_bounds__(kBlock, 1) void lmhead_mfma_dma(const uint16_t *__restrict__ hidden,
-                                                             const uint16_t *__restrict__ weight,
-                                                             const int32_t *__restrict__ keep, int M, int H, int Vt,
-                                                             float *__restrict__ logits, GemvParts parts) {
-  __shared__ __attribute__((aligned(1024))) char smem[kDmaStages * kDmaStageBytes];
-  const int nbm = (M + kBigBM - 1) / kBigBM;
-  const int nbn = (Vt + kBigBN - 1) / kBigBN;
-  const int tile = static_cast<int>(xcd_remap(blockIdx.x, static_cast<int64_t>(nbm) * nbn));
-  const int bm = tile % nbm, bn = tile / nbm;
-  const int m0 = bm * kBigBM, n0 = bn * kBigBN;
-  const int w = wave_id(), lane = lane_id();
-
-  // loads: wave w fills 1 KB chunks q = 4 w + j (j < 4) of each operand, i.e. tile rows
-  // 16 q .. 16 q + 15; lane L writes row 16 q + L / 4, slot L % 4, and fetches piece slot ^ f(row)
-  const uint16_t *asrc[4], *bsrc[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 16 * (4 * w + j) + (lane >> 2);
-    const int piece = (lane & 3) ^ dma_swz(r);
-    const int am = min(m0 + r, M - 1);
-    const int n = min(n0 + r, Vt - 1);
-    const int64_t brow = TRIM ? static_cast<int64_t>(keep[n]) : static_cast<int64_t>(n);
-    asrc[j] = hidden + static_cast<int64_t>(am) * H + piece * 8;
-    bsrc[j] = weight + brow * H + piece * 8;
-  }
-  const int nk = H / kDmaBK;
-  auto issue = [&](int kstep, int slot) {
-    const int k0 = min(kstep, nk - 1) * kDmaBK;
-    char *base = smem + slot * kDmaStageBytes;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_global_load_lds(asrc[j] + k0, (lds_void *)(base + (4 * w + j) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_global_load_lds(bsrc[j] + k0, (lds_void *)(base + kDmaOperandBytes + (4 * w + j) * 1024),
-                                       16, 0, 0);
-  };
-
-  const int wm = (w >> 1) * 128, wn = (w & 1) * 128;
-  const int lr = lane & 31;
-  // fragment reads: tile row wm + 32 i + lr (f depends on lr only), pieces 2 s + lane / 32 of
-  // the step's 4, for the two 16-deep slices s
-  const int sw = dma_swz(lr);
-  const int off0 = lr * kDmaRowBytes + (((lane >> 5) ^ sw) << 4);
-  const int off1 = lr * kDmaRowBytes + (((2 + (lane >> 5)) ^ sw) << 4);
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  auto frags = [&](int slot, int off, bf16x8(&a)[4], bf16x8(&b)[4]) {
-    const char *sa = smem + slot * kDmaStageBytes + wm * kDmaRowBytes + off;
-    const char *sb = smem + slot * kDmaStageBytes + kDmaOperandBytes + wn * kDmaRowBytes + off;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(sa + i * 32 * kDmaRowBytes);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(sb + j * 32 * kDmaRowBytes);
-  };
-  auto mfmas = [&](const bf16x8(&a)[4], const bf16x8(&b)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-  };
-  auto interleave = [&]() {  // 8 LDS reads spread over the first 8 of 16 MFMAs
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-  };
-
-  // Each step k: the MFMAs of its first 16-deep slice run while the second slice's fragments are
-  // read; then (wait + barrier) step k + 1 is complete in LDS and the slot of step k - 1 is free,
-  // the loads of step k + 3 go into it, and the second slice's MFMAs run while the first slice of
-  // step k + 1 is read.  LDS reads never wait on an idle MFMA pipe; loads have two steps to land.
-  bf16x8 a0[4], b0[4], a1[4], b1[4];
-  constexpr int kAhead = kDmaStages - 1;  // steps in flight after each issue
-#pragma unroll
-  for (int s = 0; s < kAhead; ++s) issue(s, s);
-  wait_vmcnt<8 * (kAhead - 1)>();  // step 0 has landed (8 loads per step and wave)
-  __builtin_amdgcn_s_barrier();
-  frags(0, off0, a0, b0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int slot = kt % kDmaStages;
-    frags(slot, off1, a1, b1);
-    mfmas(a0, b0);
-    interleave();
-    wait_vmcnt<8 * (kAhead - 2)>();  // step kt + 1 has landed
-    __builtin_amdgcn_s_barrier();
-    issue(kt + kAhead, (kt + kAhead) % kDmaStages);
-    frags((kt + 1) % kDmaStages, off0, a0, b0);  // past the last step: unused reads of a re-fetch
-    mfmas(a1, b1);
-    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);
-    interleave();
-  }
-  wait_vmcnt<0>();  // the re-fetches past the last step land in a free slot: drain them
-  __syncthreads();
-  big_tile_store<PARTS>(acc, M, Vt, m0, n0, wm, wn, nbn, bn, logits, parts,
-                        reinterpret_cast<float2(*)[kBigBM]>(smem));
-}
-
 // The same 256 x 256 tile and LDS ring with eight waves (two per SIMD): wave w computes rows
 // 128 (w / 4) .. +127 and columns 64 (w % 4) .. +63 of the tile, 4 x 2 accumulator blocks (128
 // AGPRs), so each SIMD holds two waves and one issues MFMAs while the other waits on LDS or the
@@ -896,8 +782,8 @@ constexpr int kDma8Block = 512;
 template <bool TRIM, bool PARTS>
 __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_dma8(const uint16_t *__restrict__ hidden,
                                                                   const uint16_t *__restrict__ weight,
-                                                                  const int32_t *__restrict__ keep, int M, int H,
-                                                                  int Vt, float *__restrict__ logits,
+                                                                  const int32_t *__restrict__ keep, int vrows, int M,
+                                                                  int H, int Vt, float *__restrict__ logits,
                                                                   GemvParts parts) {
   __shared__ __attribute__((aligned(1024))) char smem[kDmaStages * kDmaStageBytes];
   const int nbm = (M + kBigBM - 1) / kBigBM;
@@ -916,7 +802,7 @@ __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_dma8(const uint16_t
     const int piece = (lane & 3) ^ dma_swz(r);
     const int am = min(m0 + r, M - 1);
     const int n = min(n0 + r, Vt - 1);
-    const int64_t brow = TRIM ? static_cast<int64_t>(keep[n]) : static_cast<int64_t>(n);
+    const int64_t brow = TRIM ? kept_row(keep, n, vrows) : static_cast<int64_t>(n);
     asrc[j] = hidden + static_cast<int64_t>(am) * H + piece * 8;
     bsrc[j] = weight + brow * H + piece * 8;
   }
@@ -969,7 +855,13 @@ __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_dma8(const uint16_t
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   };
 
-  // the step schedule of lmhead_mfma_dma, with 4 loads per step and wave
+  // Each step k: the MFMAs of its first 16-deep slice run while the second slice's fragments are
+  // read; then (wait + barrier) step k + 1 is complete in LDS and the slot of step k - 1 is free,
+  // the loads of step k + 3 go into it, and the second slice's MFMAs run while the first slice of
+  // step k + 1 is read.  LDS reads never wait on an idle MFMA pipe; loads have two steps to land.
+  // The waits are explicit: before the barrier of step k a thread waits until at most the loads
+  // of steps k + 2 and k + 3 are outstanding; steps past the last re-fetch the last step into the
+  // free slot (never read), so every step issues the same 4 loads per wave.
   bf16x8 a0[4], b0[2], a1[4], b1[2];
   constexpr int kAhead = kDmaStages - 1;
 #pragma unroll
@@ -999,40 +891,36 @@ __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_dma8(const uint16_t
 inline int64_t mfma_big_tiles_n(int64_t Vt) { return (Vt + kBigBN - 1) / kBigBN; }
 
 template <bool PARTS>
-inline hipError_t launch_mfma_big(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int64_t M,
-                                  int64_t H, int64_t Vt, float *logits, GemvParts parts, hipStream_t stream) {
+inline hipError_t launch_mfma_big(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int vrows,
+                                  int64_t M, int64_t H, int64_t Vt, float *logits, GemvParts parts,
+                                  hipStream_t stream) {
   const int64_t tiles = ((M + kBigBM - 1) / kBigBM) * mfma_big_tiles_n(Vt);
   if (H % kDmaBK == 0) {
-#if VT_MFMA_WAVES == 8
     auto fd = keep ? &lmhead_mfma_dma8<true, PARTS> : &lmhead_mfma_dma8<false, PARTS>;
     return launch(fd, dim3(static_cast<unsigned>(tiles)), dim3(kDma8Block), 0, stream, hidden, weight, keep,
-                  static_cast<int>(M), static_cast<int>(H), static_cast<int>(Vt), logits, parts);
-#else
-    auto fd = keep ? &lmhead_mfma_dma<true, PARTS> : &lmhead_mfma_dma<false, PARTS>;
-    return launch(fd, dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0, stream, hidden, weight, keep,
-                  static_cast<int>(M), static_cast<int>(H), static_cast<int>(Vt), logits, parts);
-#endif
+                  vrows, static_cast<int>(M), static_cast<int>(H), static_cast<int>(Vt), logits, parts);
   }
   auto fn = H % kBigBK == 0 ? (keep ? &lmhead_mfma_big<true, PARTS, true> : &lmhead_mfma_big<false, PARTS, true>)
                             : (keep ? &lmhead_mfma_big<true, PARTS, false> : &lmhead_mfma_big<false, PARTS, false>);
-  return launch(fn, dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0, stream, hidden, weight, keep,
+  return launch(fn, dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0, stream, hidden, weight, keep, vrows,
                 static_cast<int>(M), static_cast<int>(H), static_cast<int>(Vt), logits, parts);
 }
 
 // extra: workgroups past the head's row blocks (target partial chunks; PARTS kernels only).
 inline hipError_t launch_gemv(GemvFn fn, const uint16_t *hidden, const uint16_t *weight, const int32_t *keep,
-                              int64_t H, int64_t Vt, float *logits, GemvParts parts, hipStream_t stream,
+                              int vrows, int64_t H, int64_t Vt, float *logits, GemvParts parts, hipStream_t stream,
                               int64_t extra = 0) {
   return launch(fn, dim3(static_cast<unsigned>(gemv_blocks(Vt) + extra)), dim3(kBlock), 0, stream, hidden, weight, keep,
-                static_cast<int>(H), static_cast<int>(Vt), gemv_rows_per_block(Vt), logits, parts);
+                vrows, static_cast<int>(H), static_cast<int>(Vt), gemv_rows_per_block(Vt), logits, parts);
 }
 
-inline hipError_t launch_mfma(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int64_t M,
-                              int64_t H, int64_t Vt, float *logits, hipStream_t stream) {
-  if (M >= kBigMinM) return launch_mfma_big<false>(hidden, weight, keep, M, H, Vt, logits, GemvParts{}, stream);
+inline hipError_t launch_mfma(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int vrows,
+                              int64_t M, int64_t H, int64_t Vt, float *logits, hipStream_t stream) {
+  if (M >= kBigMinM)
+    return launch_mfma_big<false>(hidden, weight, keep, vrows, M, H, Vt, logits, GemvParts{}, stream);
   const int64_t tiles = ((M + kBM - 1) / kBM) * ((Vt + kBN - 1) / kBN);
   return launch(lmhead_mfma, dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0, stream, hidden, weight, keep,
-                static_cast<int>(M), static_cast<int>(H), static_cast<int>(Vt), logits);
+                vrows, static_cast<int>(M), static_cast<int>(H), static_cast<int>(Vt), logits);
 }
 
 }  // namespace

@@ -394,16 +394,19 @@ __global__ __launch_bounds__(kBlock) void verify_wave(VfParams P, int64_t B) {
   int n, fin;
   if (P.greedy) {
     // argmax of every target row (lowest id on ties), one row at a time over the lanes
-    int am = -1;  // lane i keeps row i's argmax
+    // lane i < gamma keeps row i's argmax; row gamma's (the bonus, which has no lane of its own
+    // when gamma = 64) is kept wave-uniform
+    int am = -1, am_g = -1;
     for (int i = 0; i <= g; ++i) {
       float bv = in ? tlogit(i, xs) : kNegInf;
       int bi = in ? lane : kNoIndex;
       wave_argmax(bv, bi);
       if (lane == i) am = bi;
+      if (i == g) am_g = bi;
     }
     const unsigned long long rej = __ballot(lane < g && !(valid && y == am));
     n = bad ? -1 : (rej ? __ffsll(static_cast<long long>(rej)) - 1 : g);
-    fin = n >= 0 ? lane_value(am, n) : -1;
+    fin = n < 0 ? -1 : (n == g ? am_g : lane_value(am, n));
   } else {
     bool accept = true;
     if (lane < g && valid) {
