@@ -17,7 +17,7 @@ import torch
 
 import draft_sampling_verification_amd as vt
 from oracle import ref
-from workloads import Workload
+from workloads import Workload, make_workload
 
 BAND = 1e-6
 
@@ -154,3 +154,43 @@ def lmhead_error_bound(hidden_bits, weight_bits, keep_ids):
     w = np.abs(ref.bf16_to_f64(rows))
     H = h.shape[1]
     return H * 2.0 ** -24 * (h @ w.T)
+
+
+def sequences_workload(cfg, seqs, **kw) -> Workload:
+    """One workload holding the listed sequences of a config (each sequence's inputs are those it
+    has in the full batch: hidden rows, target rows and uniforms are seeded per sequence)."""
+    parts = [make_workload(cfg, B=1, b0=int(s), **kw) for s in seqs]
+    wl = parts[0]
+    out = Workload(cfg=cfg, b0=-1, B=len(parts), T=wl.T, weight=wl.weight, keep_ids=wl.keep_ids,
+                   full_to_trim=wl.full_to_trim)
+    for k in ("hidden", "target", "draft_logits", "u_draft", "u_acc", "u_fin"):
+        if getattr(wl, k) is not None:
+            setattr(out, k, np.concatenate([getattr(p, k) for p in parts]))
+    return out
+
+
+def beta_z(gpu: dict, wl: Workload):
+    """z-score of the number of sequences whose first draft was accepted against its expectation
+    sum_b beta_b, beta_b = sum_x min(p_0(x), q_0(x)) ("A rejection rule keeps speculative
+    decoding's output exact", "What draft accuracy buys": beta is the chance that a draft survives),
+    with variance sum_b beta_b (1 - beta_b).  p_0 from the target row, q_0 from the GPU's own draft
+    logits (q = 0 off the kept set)."""
+    from oracle import stats
+
+    cfg = wl.cfg
+    B, R = wl.B, cfg.R
+    t = ref.as_f64(wl.target, cfg.target_dtype)[:, 0, :]
+    _, p0 = ref.softmax_temp(t, wl.T)
+    d = gpu["draft_logits"].reshape(B, R, cfg.Vt)[:, 0, :].astype(np.float64)
+    _, q0 = ref.softmax_temp(d, wl.T)
+    beta = np.empty(B)
+    for b in range(B):
+        qf = np.zeros(cfg.V)
+        if wl.keep_ids is None:
+            qf[:] = q0[b]
+        else:
+            qf[wl.keep_ids] = q0[b]
+        beta[b] = stats.beta(p0[b], qf)
+    acc = float((np.asarray(gpu["n"]) >= 1).sum())
+    var = float((beta * (1 - beta)).sum())
+    return (acc - beta.sum()) / np.sqrt(max(var, 1e-12)), acc, float(beta.sum())
