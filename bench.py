@@ -7,13 +7,20 @@ chunk pass that draws, accepts and sums the residual, one final draw; larger bat
 with the draft partials, target partials, one combine launch, two verify launches); with
 --calls the four separate calls
   vt_lmhead_trimmed -> vt_softmax_temp (draft, with draws) -> vt_softmax_temp (target) -> vt_spec_verify
-on synthetic inputs already resident in HBM.  Default workload: B=1, gamma=5, hidden 3072, full
-128256-row drafter head, fp32 target logits, T=1 (config 2 of the workload recipe).
+on synthetic inputs already resident in HBM.  Default workload: the large drafter, B=256,
+gamma=8, hidden 4096, 65536-row VocabTrim head of a 128256-id vocabulary, bf16 target logits,
+T=0.8 (config 5 of the workload recipe, the largest that fits one GPU); afterwards the batch-1
+VocabTrim block (B=1, gamma=5, hidden 3072, 32768 kept rows, config 3) is measured as a side
+record, so that its whole-block HBM fraction is reported too.
 
 Prints ONE JSON line on stdout (progress goes to stderr):
   value        verified draft positions / s = B * gamma / (seconds per step)
-  roofline     the LM-head kernel (the dominant kernel): algorithmic bytes per launch / its average
-               duration measured live with HIP events on the launch stream, against 8 TB/s
+  roofline     the LM-head kernel (the dominant kernel), from its average duration measured live
+               with HIP events on the launch stream: algorithmic flops per launch against the bf16
+               MFMA peak (2.5 PFLOP/s) when the head is a dense contraction (256+ hidden rows),
+               else algorithmic bytes per launch against 8 TB/s
+  config       also the LM head's and the whole block's HBM GB/s and fraction of 8 TB/s, and in
+               config.side the same for the side config
   cpu_baseline the float64 CPU oracle timed on a bounded sample of the same workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C] [--greedy] [--no-cpu-baseline] [--calls] [--graph]
@@ -48,7 +55,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--side-config", type=int, default=3, choices=[0, 2, 3, 4, 5],
+                    help="a second config measured after the main one, reported in config.side (0: none); "
+                         "by default the batch-1 VocabTrim block, whose whole-block HBM fraction is tracked")
+    ap.add_argument("--side-steps", type=int, default=200)
     ap.add_argument("--batch", type=int, default=1,
                     help="sequences per step for the toy (--config 1); the other configs fix their batch")
     ap.add_argument("--workload", default="block", choices=["block", "keepset", "generate"],
@@ -236,9 +247,9 @@ def write_traffic_record(config: int, fetch_csv, write_csv, copy_fetch_csv, copy
         "algorithmic_read_bytes": lmhead_launch_bytes(cfg) - alg_w, "algorithmic_write_bytes": alg_w,
         "commands": [
             f"rocprofv3 --pmc FETCH_SIZE -f csv -d <out> -o bench -- python3 bench.py --config {config} "
-            "--no-cpu-baseline --steps 10 --warmup 3",
+            "--side-config 0 --no-cpu-baseline --steps 10 --warmup 3",
             f"rocprofv3 --pmc WRITE_SIZE -f csv -d <out> -o bench -- python3 bench.py --config {config} "
-            "--no-cpu-baseline --steps 10 --warmup 3",
+            "--side-config 0 --no-cpu-baseline --steps 10 --warmup 3",
             "rocprofv3 --pmc FETCH_SIZE -f csv -d <out> -o copy -- python3 bench.py --copy-calibration",
             "rocprofv3 --pmc WRITE_SIZE -f csv -d <out> -o copy -- python3 bench.py --copy-calibration",
             f"python3 bench.py --config {config} --traffic-record <4 csv files>"],
@@ -592,37 +603,16 @@ def valu_record():
     return rec if rec.get("source_sha256") == generate_source_hash() else None
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
-              file=sys.stderr)
-        sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    if args.traffic_record:
-        print(write_traffic_record(args.config, *args.traffic_record))
-        return
-    if args.valu_record:
-        print(write_valu_record(args.valu_record))
-        return
-    if args.workload == "keepset":
-        bench_keepset(args)
-        return
-    if args.workload == "generate":
-        bench_generate(args)
-        return
-    if args.config == 1:
-        bench_toy(args)
-        return
-
+def bench_block(args, config: int, steps: int, warmup: int):
+    """Time `steps` speculative blocks of a config after `warmup` untimed ones.  Returns the fields
+    of the result line: step time, the LM-head launch time from HIP events on its own stream, the
+    algorithmic bytes and flops, and the side statistics."""
     import torch
 
     import draft_sampling_verification_amd as vt
     from workloads import CONFIGS, make_workload
 
-    cfg = CONFIGS[args.config]
+    cfg = CONFIGS[config]
     B, g, R = cfg.B, cfg.gamma, cfg.R
     log(f"workload: {cfg.name}")
     t0 = time.perf_counter()
@@ -731,9 +721,8 @@ def main():
         if not all(torch.equal(a, b) for a, b in zip(want, outs)):
             raise RuntimeError("graph replay differs from the eager step")
 
-    n_ev = args.steps
-    ev_a = [DeviceEvent() for _ in range(n_ev)]
-    ev_b = [DeviceEvent() for _ in range(n_ev)]
+    ev_a = [DeviceEvent() for _ in range(steps)]
+    ev_b = [DeviceEvent() for _ in range(steps)]
     if not args.calls:
         # the fused call must agree with the four separate calls on the LM head and the target
         # log-normalisers bit for bit (draws may differ only at rounding-level CDF boundaries)
@@ -745,7 +734,7 @@ def main():
             same = same and all(torch.equal(a, b) for a, b in zip(want[1:3] + want[4:], (dlse, dids, tokens, nacc)))
         if not same:
             raise RuntimeError("vt_spec_block differs from the separate calls")
-    for i in range(args.warmup):
+    for i in range(warmup):
         if args.calls:
             a, b = runners[i % n_sets]
             a()
@@ -757,7 +746,7 @@ def main():
     # bracketed by events on the stream it is launched on
     if args.calls:
         t0 = time.perf_counter()
-        for i in range(args.steps):
+        for i in range(steps):
             a, b = runners[i % n_sets]
             ev_a[i].record(main)
             a()
@@ -769,29 +758,92 @@ def main():
             e.record(main)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):
+        for i in range(steps):
             fused(sets[i % n_sets], (ev_a[i], ev_b[i]))
         torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = 1e3 * wall / args.steps
-    lm_ms = sum(x.elapsed_time(y) for x, y in zip(ev_a, ev_b)) / n_ev
-
-    value = B * g / (ms_per_step / 1e3)
+    ms_per_step = 1e3 * wall / steps
+    lm_ms = sum(x.elapsed_time(y) for x, y in zip(ev_a, ev_b)) / steps
     lmb = lmhead_launch_bytes(cfg, args.greedy, args.calls)
-    achieved = lmb / (lm_ms / 1e3) / 1e9
-    wl_key = f"config{args.config}"
-    traffic = measured_traffic(wl_key)
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": ("lmhead_gemv" if B * R <= 8 else "lmhead_mfma")
-                      + (" + target softmax partials" if small_batch_block(cfg, args.greedy) and not args.calls else ""),
-            "algorithmic_bytes_per_launch": lmb, "avg_launch_ms": round(lm_ms, 5)}
+    mean_acc = float(nacc.double().mean())
+    res = dict(cfg=cfg, wl=wl, n_sets=n_sets, ms_per_step=ms_per_step, lm_ms=lm_ms, lm_bytes=lmb,
+               lm_gbs=lmb / (lm_ms / 1e3) / 1e9, block_bytes=bb, block_gbs=bb / (ms_per_step / 1e3) / 1e9,
+               value=B * g / (ms_per_step / 1e3), mean_accepted=mean_acc,
+               mfma=B * R > 8 and not small_batch_block(cfg, args.greedy) and B * R >= 256)
     if B * R > 8:
-        tf = lmhead_flops(cfg) / (lm_ms / 1e3) / 1e12
-        roof["mfma_tflops"] = round(tf, 1)
-        roof["mfma_frac"] = round(tf / BF16_MFMA_PEAK_TFLOPS, 4)
-    log(f"step {ms_per_step:.4f} ms, LM head {lm_ms:.4f} ms = {achieved:.0f} GB/s; "
-        f"block {bb / (ms_per_step / 1e3) / 1e9:.0f} GB/s algorithmic")
+        res["lm_tflops"] = lmhead_flops(cfg) / (lm_ms / 1e3) / 1e12
+    log(f"step {ms_per_step:.4f} ms, LM head {lm_ms:.4f} ms = {res['lm_gbs']:.0f} GB/s"
+        + (f" = {res['lm_tflops']:.1f} TFLOP/s" if "lm_tflops" in res else "")
+        + f"; block {res['block_gbs']:.0f} GB/s algorithmic")
+    del sets, base, logits
+    torch.cuda.empty_cache()
+    return res
+
+
+def side_record(res) -> dict:
+    """The whole-block HBM figures of a config, for the line's side fields."""
+    cfg = res["cfg"]
+    return {"workload": cfg.name, "ms_per_step": round(res["ms_per_step"], 5),
+            "value": round(res["value"], 1), "unit": "verified draft positions/s",
+            "block_algorithmic_bytes": res["block_bytes"], "block_gbs": round(res["block_gbs"], 1),
+            "block_hbm_frac": round(res["block_gbs"] / HBM_PEAK_GBS, 4),
+            "lmhead_ms": round(res["lm_ms"], 5), "lmhead_gbs": round(res["lm_gbs"], 1),
+            "lmhead_hbm_frac": round(res["lm_gbs"] / HBM_PEAK_GBS, 4)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.traffic_record:
+        print(write_traffic_record(args.config, *args.traffic_record))
+        return
+    if args.valu_record:
+        print(write_valu_record(args.valu_record))
+        return
+    if args.workload == "keepset":
+        bench_keepset(args)
+        return
+    if args.workload == "generate":
+        bench_generate(args)
+        return
+    if args.config == 1:
+        bench_toy(args)
+        return
+
+    from workloads import make_workload
+
+    res = bench_block(args, args.config, args.steps, args.warmup)
+    cfg = res["cfg"]
+    B, g = cfg.B, cfg.gamma
+    traffic = measured_traffic(f"config{args.config}")
+    kernel = (("lmhead_gemv" if B * cfg.R <= 8 else "lmhead_mfma_dma8" if B * cfg.R >= 256 else "lmhead_mfma")
+              + (" + target softmax partials" if small_batch_block(cfg, args.greedy) and not args.calls else ""))
+    if res["mfma"]:
+        # a real dense contraction: the head is priced against the bf16 MFMA peak
+        tf = res["lm_tflops"]
+        roof = {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": traffic, "kernel": kernel,
+                "algorithmic_flops_per_launch": lmhead_flops(cfg), "algorithmic_bytes_per_launch": res["lm_bytes"],
+                "avg_launch_ms": round(res["lm_ms"], 5),
+                "hbm_gbs": round(res["lm_gbs"], 1), "hbm_frac": round(res["lm_gbs"] / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(res["lm_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(res["lm_gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
+                "algorithmic_bytes_per_launch": res["lm_bytes"], "avg_launch_ms": round(res["lm_ms"], 5)}
+        if "lm_tflops" in res:
+            roof["mfma_tflops"] = round(res["lm_tflops"], 1)
+            roof["mfma_frac"] = round(res["lm_tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)
+
+    side = {}
+    if args.side_config and args.side_config != args.config and not args.greedy and not args.calls:
+        side[f"config{args.side_config}"] = side_record(
+            bench_block(args, args.side_config, args.side_steps, max(5, args.warmup // 2)))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -799,9 +851,10 @@ def main():
         log("timing the CPU oracle ...")
         cpu = cpu_baseline(cfg, wl_one, args.cpu_seconds)
 
+    ms_per_step = res["ms_per_step"]
     out = {
         "metric": "verified draft positions/sec + LM-head HBM GB/s (% of 8 TB/s), 1 GPU",
-        "value": round(value, 1),
+        "value": round(res["value"], 1),
         "unit": "verified draft positions/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -810,22 +863,27 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if res["mfma"] else "f32",
         "data": "synthetic",
         "config": {"workload": cfg.name, "batch": B, "gamma": g, "hidden": cfg.H, "vocab": cfg.V,
-                   "kept_rows": cfg.Vt, "target_logits": cfg.target_dtype, "temperature": 0.0 if args.greedy else cfg.T,
-                   "weights": "bf16", "accumulate": "f32", "input_sets_rotated": n_sets,
+                   "kept_rows": cfg.Vt, "target_logits": cfg.target_dtype,
+                   "temperature": 0.0 if args.greedy else cfg.T,
+                   "weights": "bf16", "accumulate": "f32", "input_sets_rotated": res["n_sets"],
                    "verification": "greedy (temperature 0)" if args.greedy else "sampling",
                    "launch": ("vt_spec_block: one fused call per step" if not args.calls else
                               "four calls, hip graphs (LM head | rest) replayed" if args.graph else
                               "four calls, target softmax on a second stream" if args.overlap else
                               "four calls, eager, one stream"),
-                   "block_algorithmic_bytes": bb,
-                   "block_gbs": round(bb / (ms_per_step / 1e3) / 1e9, 1),
+                   "block_algorithmic_bytes": res["block_bytes"],
+                   "block_gbs": round(res["block_gbs"], 1),
+                   "block_hbm_frac": round(res["block_gbs"] / HBM_PEAK_GBS, 4),
+                   "lmhead_gbs": round(res["lm_gbs"], 1),
+                   "lmhead_hbm_frac": round(res["lm_gbs"] / HBM_PEAK_GBS, 4),
                    "drafter": f"follows the target, noise sd {args.follow}" if args.follow > 0 else
                               "unrelated random head (the recipe)",
-                   "mean_accepted": round(float(nacc.double().mean()), 4),
-                   "tokens_per_block": round(float(nacc.double().mean()) + 1.0, 4)},
+                   "mean_accepted": round(res["mean_accepted"], 4),
+                   "tokens_per_block": round(res["mean_accepted"] + 1.0, 4),
+                   "side": side or None},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
