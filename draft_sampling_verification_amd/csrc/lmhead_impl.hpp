@@ -536,6 +536,20 @@ constexpr int kBigBM = 256, kBigBN = 256, kBigBK = 64, kBigPad = 8;
 constexpr int kBigRow = kBigBK + kBigPad;  // bf16 per LDS row: 144 bytes
 constexpr int kBigMinM = 256;
 
+// Tile order of the 256 x 256 kernels.  Each XCD works through one contiguous range of logical
+// tiles (xcd_remap); logical tiles are ordered in groups of kTileGroup hidden-row blocks, walked
+// head-block-major inside a group, so the 32 tiles an XCD runs at once span about three hidden-row
+// blocks and eleven head-row blocks and share both in its L2.  Measured on the large-drafter
+// shape (9 x 256 tiles) against groups of 1, 2, 4 and 9 rows: 3 is the fastest (about 5% over 9).
+constexpr int kTileGroup = 3;
+__device__ __forceinline__ void big_tile_of(int tile, int nbm, int nbn, int &bm, int &bn) {
+  const int group = tile / (kTileGroup * nbn);
+  const int in = tile - group * kTileGroup * nbn;
+  const int rows = min(kTileGroup, nbm - group * kTileGroup);
+  bm = group * kTileGroup + in % rows;
+  bn = in / rows;
+}
+
 // Epilogue of a 256 x 256 tile held by four waves as 4 x 4 accumulators each: the logits, and
 // with PARTS the draft softmax partials of the tile's 256 columns per hidden row.  All threads of
 // the workgroup must call.
@@ -635,7 +649,8 @@ __global__ __launch_bounds__(kBlock, 1) void lmhead_mfma_big(const uint16_t *__r
   const int nbm = (M + kBigBM - 1) / kBigBM;
   const int nbn = (Vt + kBigBN - 1) / kBigBN;
   const int tile = static_cast<int>(xcd_remap(blockIdx.x, static_cast<int64_t>(nbm) * nbn));
-  const int bm = tile % nbm, bn = tile / nbm;
+  int bm, bn;
+  big_tile_of(tile, nbm, nbn, bm, bn);
   const int m0 = bm * kBigBM, n0 = bn * kBigBN;
   const int tid = threadIdx.x;
 
@@ -789,7 +804,8 @@ __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_dma8(const uint16_t
   const int nbm = (M + kBigBM - 1) / kBigBM;
   const int nbn = (Vt + kBigBN - 1) / kBigBN;
   const int tile = static_cast<int>(xcd_remap(blockIdx.x, static_cast<int64_t>(nbm) * nbn));
-  const int bm = tile % nbm, bn = tile / nbm;
+  int bm, bn;
+  big_tile_of(tile, nbm, nbn, bm, bn);
   const int m0 = bm * kBigBM, n0 = bn * kBigBN;
   const int w = wave_id(), lane = lane_id();
 
