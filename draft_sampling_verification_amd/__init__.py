@@ -14,13 +14,14 @@ Entry points (same names as the C ABI):
   vt_spec_block(hidden, weight, keep_ids, full_to_trim, target_logits, target_T, draft_T, u_draft, u_accept,
                 u_final, draft_logits, draft_lse, draft_ids, target_lse, out_tokens, out_num_accepted,
                 workspace=None, lmhead_events=None)
+  vt_spec_block_noalloc(... the same without workspace ...): the library's fixed device scratch instead
 Keep-set construction (include/vt_keepset.h):
   vt_token_histogram(tokens, V, counts, accumulate=False, workspace=None)
   vt_keep_select(counts, rule, keep_ids, full_to_trim, num_kept, k=0, p=0.0, min_count=0)
   vt_trim_head(weight, keep_ids, trimmed)
 Generation loop for table models (include/vt_generate.h):
   vt_spec_generate_markov(target_table, draft_table, target_T, draft_T, gamma, u, out_tokens, out_stats=None)
-Helpers: softmax_workspace(rows, n), verify_workspace(B, V), block_workspace(...), lib() (the raw ctypes handle).
+Helpers: softmax_workspace(rows, n), verify_workspace(B, gamma, V), block_workspace(...), lib() (the raw ctypes handle).
 """
 from __future__ import annotations
 
@@ -65,6 +66,9 @@ def lib() -> ctypes.CDLL:
         L.vt_spec_block.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I64, P, I, F, F, P, P, P, P, P, P, P, P, P,
                                     P, P, P, SZ, P]
         L.vt_spec_block.restype = I
+        L.vt_spec_block_noalloc.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I64, P, I, F, F, P, P, P, P, P, P,
+                                            P, P, P, P, P, P]
+        L.vt_spec_block_noalloc.restype = I
         L.vt_spec_block_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I64]
         L.vt_spec_block_workspace_bytes.restype = SZ
         L.vt_token_histogram.argtypes = [P, I64, I64, I, P, P, SZ, P]
@@ -84,7 +88,8 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTED = ("vt_lmhead_trimmed", "vt_softmax_temp", "vt_softmax_temp_workspace_bytes", "vt_spec_verify",
-            "vt_spec_verify_workspace_bytes", "vt_spec_block", "vt_spec_block_workspace_bytes", "vt_status_string",
+            "vt_spec_verify_workspace_bytes", "vt_spec_block", "vt_spec_block_workspace_bytes",
+            "vt_spec_block_noalloc", "vt_status_string",
             "vt_token_histogram", "vt_token_histogram_workspace_bytes", "vt_keep_select", "vt_trim_head",
             "vt_spec_generate_markov")
 
@@ -270,6 +275,44 @@ def vt_spec_block(hidden, weight, keep_ids, full_to_trim, target_logits, target_
                                                                                 torch.int32, B),
                              ev0, ev1, _ptr(workspace, "workspace"), wsb, _stream())
     _check("vt_spec_block", st)
+    return out_tokens, out_num_accepted
+
+
+def vt_spec_block_noalloc(hidden, weight, keep_ids, full_to_trim, target_logits, target_T, draft_T, u_draft,
+                          u_accept, u_final, draft_logits, draft_lse, draft_ids, target_lse, out_tokens,
+                          out_num_accepted, lmhead_events=None):
+    """vt_spec_block with the library's fixed per-device scratch instead of a workspace (nothing is
+    allocated; shapes needing more than 32 MiB of workspace are rejected).  Calls that overlap on
+    one device race on that scratch."""
+    torch = _torch()
+    _bits16(hidden, "hidden")
+    _bits16(weight, "weight")
+    B, g1, V = target_logits.shape
+    gamma = g1 - 1
+    M, H = hidden.shape
+    R = M // B
+    Vt = draft_logits.shape[1]
+    if M != B * R or weight.shape != (V, H) or tuple(draft_logits.shape) != (M, Vt) or \
+            tuple(out_tokens.shape) != (B, g1):
+        raise ValueError("vt_spec_block_noalloc: shape mismatch")
+    if target_logits.dtype == torch.float32:
+        dt = VT_F32
+    else:
+        _bits16(target_logits, "target_logits")
+        dt = VT_BF16
+    ev0 = ev1 = None
+    if lmhead_events is not None:
+        ev0, ev1 = (ctypes.c_void_p(e.cuda_event) for e in lmhead_events)
+    st = lib().vt_spec_block_noalloc(
+        _ptr(hidden, "hidden"), _ptr(weight, "weight"), _ptr(keep_ids, "keep_ids", torch.int32),
+        _ptr(full_to_trim, "full_to_trim", torch.int32, V), B, gamma, R, H, Vt, V, _ptr(target_logits, "target_logits"),
+        dt, float(target_T), float(draft_T), _ptr(u_draft, "u_draft", torch.float32, M),
+        _ptr(u_accept, "u_accept", torch.float32, B * gamma), _ptr(u_final, "u_final", torch.float32, B),
+        _ptr(draft_logits, "draft_logits", torch.float32), _ptr(draft_lse, "draft_lse", torch.float64, M),
+        _ptr(draft_ids, "draft_ids", torch.int32, M), _ptr(target_lse, "target_lse", torch.float64, B * g1),
+        _ptr(out_tokens, "out_tokens", torch.int32), _ptr(out_num_accepted, "out_num_accepted", torch.int32, B),
+        ev0, ev1, _stream())
+    _check("vt_spec_block_noalloc", st)
     return out_tokens, out_num_accepted
 
 

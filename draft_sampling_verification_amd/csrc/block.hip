@@ -15,6 +15,7 @@
 // partials ride in extra workgroups of the GEMV launch, and one chunk pass forms every
 // log-normaliser, draft draw, accept scan and residual chunk sum, followed by the final draw.
 #include <algorithm>
+#include <mutex>
 
 #include "lmhead_impl.hpp"
 #include "softmax_impl.hpp"
@@ -344,4 +345,61 @@ extern "C" vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *wei
       e = vd ? go(run_block<uint16_t, false, true>) : go(run_block<uint16_t, false, false>);
   }
   return hip_status(e);
+}
+
+// ------------------------------------------------------------------ variant without a workspace
+// For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+// loops, harnesses that forbid hipMalloc): vt_spec_block with its workspace in a fixed device
+// array of this file.  Each device the library runs on holds its own copy until the process ends.
+// The array's host-side name is only a stand-in for the symbol: its device address is looked up
+// once per device (hipGetSymbolAddress, with that device current) and only that address is
+// handed to kernels.  Nothing in the workspace has to start at zero: every launch of a call
+// writes the partials it reads later in the same call.
+namespace vt {
+namespace {
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;  // 32 MiB per device
+constexpr int kMaxDevices = 64;
+}  // namespace
+}  // namespace vt
+
+static __device__ __align__(256) char scratch[vt::kNoAllocScratchBytes];
+
+namespace vt {
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first call per device).
+vt_status_t scratch_on_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return VT_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return VT_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return VT_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return VT_OK;
+}
+}  // namespace
+}  // namespace vt
+
+extern "C" vt_status_t vt_spec_block_noalloc(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep_ids,
+                                             const int32_t *full_to_trim, int64_t B, int64_t gamma, int64_t R,
+                                             int64_t H, int64_t Vt, int64_t V, const void *target_logits,
+                                             vt_dtype_t target_dtype, float target_T, float draft_T,
+                                             const float *u_draft, const float *u_accept, const float *u_final,
+                                             float *draft_logits, double *draft_lse, int32_t *draft_ids,
+                                             double *target_lse, int32_t *out_tokens, int32_t *out_num_accepted,
+                                             hipEvent_t lmhead_begin, hipEvent_t lmhead_end, hipStream_t stream) {
+  void *ws = nullptr;
+  const vt_status_t st = vt::scratch_on_current_device(&ws);
+  if (st != VT_OK) return st;
+  // vt_spec_block validates every argument and returns VT_ERR_WORKSPACE when the shape needs more
+  // than the fixed scratch holds
+  return vt_spec_block(hidden, weight, keep_ids, full_to_trim, B, gamma, R, H, Vt, V, target_logits, target_dtype,
+                       target_T, draft_T, u_draft, u_accept, u_final, draft_logits, draft_lse, draft_ids, target_lse,
+                       out_tokens, out_num_accepted, lmhead_begin, lmhead_end, ws, vt::kNoAllocScratchBytes, stream);
 }

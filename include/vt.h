@@ -20,8 +20,8 @@
  *   - Every array pointer is a DEVICE pointer owned by the caller.  The library never allocates,
  *     frees or synchronises; it only enqueues kernels on `stream` (0 = the null stream) and
  *     returns.  Outputs are valid once the caller has synchronised the stream; inputs must stay
- *     unchanged until then.  There is no global state: calls on distinct streams (with distinct
- *     workspaces) may overlap.
+ *     unchanged until then.  There is no global state (apart from the fixed device scratch of
+ *     vt_spec_block_noalloc): calls on distinct streams (with distinct workspaces) may overlap.
  *   - Arguments are validated on the host before any HIP call.  A failed check returns an error
  *     code and enqueues nothing.  Nothing is thrown across the ABI and nothing aborts.
  *   - Random numbers the method draws are inputs: uniforms u in (0, 1].  Using u = (k+1) * 2^-24
@@ -209,6 +209,29 @@ vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *weight, const 
 
 /* Bytes of workspace vt_spec_block needs for this shape. */
 size_t vt_spec_block_workspace_bytes(int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt, int64_t V);
+
+/*
+ * vt_spec_block_noalloc -- vt_spec_block for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * results and errors as vt_spec_block, without workspace / workspace_bytes: the workspace is a
+ * fixed 32 MiB array of device memory inside the library, one per device, held until the process
+ * ends (its address is looked up once per device, on the first call with that device current).
+ * Nothing is allocated or freed by this call.
+ *   Limit: shapes whose vt_spec_block_workspace_bytes exceeds 32 MiB return VT_ERR_WORKSPACE
+ *   before anything is enqueued (for example B = 256, gamma = 8, H = 4096, Vt = 65536,
+ *   V = 128256 needs 5.6 MiB).
+ *   Calls that overlap on one device (two streams, or two host threads) share that device's array
+ *   and race: serialise them.  The array keeps the last call's partial results; no call depends on
+ *   its previous contents.  Errors: as vt_spec_block, plus VT_ERR_HIP if the device or the array's
+ *   address cannot be queried, VT_ERR_UNSUPPORTED for a device index of 64 or more.
+ */
+vt_status_t vt_spec_block_noalloc(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep_ids,
+                                  const int32_t *full_to_trim, int64_t B, int64_t gamma, int64_t R, int64_t H,
+                                  int64_t Vt, int64_t V, const void *target_logits, vt_dtype_t target_dtype,
+                                  float target_T, float draft_T, const float *u_draft, const float *u_accept,
+                                  const float *u_final, float *draft_logits, double *draft_lse, int32_t *draft_ids,
+                                  double *target_lse, int32_t *out_tokens, int32_t *out_num_accepted,
+                                  hipEvent_t lmhead_begin, hipEvent_t lmhead_end, hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char *vt_status_string(vt_status_t status);
