@@ -73,6 +73,13 @@ typedef enum { VT_F32 = 0, VT_BF16 = 1 } vt_dtype_t;
  *   logits   fp32 row-major [M][Vt], written in full
  *   Products of bf16 values are exact in fp32; sums are accumulated in fp32 in an order that does
  *   not depend on the row, so trimmed logits equal untrimmed logits gathered at keep_ids bit for bit.
+ *   The order does depend on M, which picks the kernel: a GEMV when M <= 8 and
+ *   M * ceil(H / 512) <= 48 (lanes hold partial sums over 16-byte pieces of a row, reduced across
+ *   lanes); otherwise 128 x 128 MFMA tiles when M < 256 and 256 x 256 MFMA tiles when M >= 256
+ *   (sums over K in MFMA steps of 16).  A hidden row's
+ *   logits may therefore differ in the last bits between batch sizes (each within the
+ *   recursive-summation bound H 2^-24 sum_k |h_k w_k|), and so may a decision taken on them, but
+ *   only where it lies within rounding of its uniform.
  *   Errors: INVALID_ARG for NULL hidden/weight/logits, M, H, Vt or V_rows <= 0, Vt > V_rows when
  *   keep_ids is NULL; UNSUPPORTED for H % 8 != 0 or a hidden/weight base not 16-byte aligned.
  */
@@ -185,7 +192,11 @@ size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
  *   the fused paths the draft running sums are chunked by the LM head's own blocks of head rows
  *   instead of 4096-element chunks: ceil(Vt / 256) rounded up to a multiple of 4 rows when B*R <= 8,
  *   256 rows when B*R >= 256.  Draws can then differ from the separate calls only where a CDF
- *   boundary lies within rounding of the uniform.
+ *   boundary lies within rounding of the uniform.  Sequences are independent: a sequence's
+ *   outputs are those it gets alone, up to the LM head's batch-size-dependent summation order
+ *   (see vt_lmhead_trimmed), i.e. they can differ only at a decision within rounding of its
+ *   uniform; every target-side quantity (target_lse, p, the residual) is computed per row in an
+ *   order that depends on neither B nor the row.
  *   target_T = 0 selects greedy verification as in vt_spec_verify ([VT] §4): no target softmax
  *   runs, target_lse is not written, u_accept and u_final are not read (all three may be NULL).
  *   draft_T = 0 (allowed only with target_T = 0) makes each draft the lowest id of its row's
