@@ -81,6 +81,8 @@ def parse():
     ap.add_argument("--follow", type=float, default=0.0, metavar="SIGMA",
                     help="a drafter that follows the target (target = the head's own two columns + N(0, SIGMA)): "
                          "drafts get accepted; the default is the recipe's unrelated random head")
+    ap.add_argument("--keep-order", default="id", choices=["id", "rank"],
+                    help="storage order of the kept ids: ascending id (the default) or rank order, best first")
     ap.add_argument("--greedy", action="store_true",
                     help="temperature 0 for target and draft: argmax drafts and greedy verification")
     ap.add_argument("--graph", action="store_true",
@@ -616,7 +618,7 @@ def bench_block(args, config: int, steps: int, warmup: int):
     B, g, R = cfg.B, cfg.gamma, cfg.R
     log(f"workload: {cfg.name}")
     t0 = time.perf_counter()
-    wl = make_workload(cfg, follow=args.follow)
+    wl = make_workload(cfg, follow=args.follow, keep_order=args.keep_order)
     log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
 
     def bf16(bits):
@@ -847,7 +849,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        wl_one = make_workload(cfg, B=1, follow=args.follow)
+        wl_one = make_workload(cfg, B=1, follow=args.follow, keep_order=args.keep_order)
         log("timing the CPU oracle ...")
         cpu = cpu_baseline(cfg, wl_one, args.cpu_seconds)
 
@@ -866,7 +868,7 @@ def main():
         "dtype": "bf16" if res["mfma"] else "f32",
         "data": "synthetic",
         "config": {"workload": cfg.name, "batch": B, "gamma": g, "hidden": cfg.H, "vocab": cfg.V,
-                   "kept_rows": cfg.Vt, "target_logits": cfg.target_dtype,
+                   "kept_rows": cfg.Vt, "keep_order": args.keep_order, "target_logits": cfg.target_dtype,
                    "temperature": 0.0 if args.greedy else cfg.T,
                    "weights": "bf16", "accumulate": "f32", "input_sets_rotated": res["n_sets"],
                    "verification": "greedy (temperature 0)" if args.greedy else "sampling",

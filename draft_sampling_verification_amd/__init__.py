@@ -282,7 +282,7 @@ def vt_spec_block_noalloc(hidden, weight, keep_ids, full_to_trim, target_logits,
                           u_accept, u_final, draft_logits, draft_lse, draft_ids, target_lse, out_tokens,
                           out_num_accepted, lmhead_events=None):
     """vt_spec_block with the library's fixed per-device scratch instead of a workspace (nothing is
-    allocated; shapes needing more than 32 MiB of workspace are rejected).  Calls that overlap on
+    allocated; shapes needing more than 64 MiB of workspace are rejected).  Calls that overlap on
     one device race on that scratch."""
     torch = _torch()
     _bits16(hidden, "hidden")

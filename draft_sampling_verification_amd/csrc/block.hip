@@ -37,7 +37,8 @@ struct BlockPlan {
   int64_t nchunk_d;  // draft partial chunks per row (GEMV row blocks, or 4096-chunks)
   int chunk_d;
   int64_t nchunk_v;
-  size_t off_tpart, off_dpart, off_nbuf, off_vpart, off_wbuf, bytes;
+  size_t off_tpart, off_dpart, off_nbuf, off_vpart, off_wbuf, off_hidt, bytes;
+  size_t hidt_bytes;  // K-tiled copy of the hidden rows for the large-batch head (0: none)
 };
 
 // greedy_t: the target is decoded greedily (no target softmax; verification compares argmaxes).
@@ -79,6 +80,9 @@ BlockPlan plan_block(int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt,
   }
   p.off_wbuf = off;
   if (p.fv) off += align_up(static_cast<size_t>(2 * B * V) * sizeof(float), 256);  // final-draw weights and p_n
+  p.off_hidt = off;
+  p.hidt_bytes = p.fused_mfma ? hidden_tiles_bytes(p.M, H) : 0;
+  off += align_up(p.hidt_bytes, 256);
   p.bytes = off;
   return p;
 }
@@ -168,7 +172,8 @@ hipError_t run_block_greedy_small(const BlockPlan &pl, const SmParams &D, const 
 template <typename TinT, bool kVecT, bool kVecD>
 hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, const VfParams &Vp,
                      const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int64_t H, int64_t Vt,
-                     float *logits, float *wbuf, int64_t B, hipEvent_t ev0, hipEvent_t ev1, hipStream_t stream) {
+                     float *logits, float *wbuf, int64_t B, hipEvent_t ev0, hipEvent_t ev1, hipStream_t stream,
+                     void *hidt_base) {
   if (pl.fv)
     return run_block_small<TinT, kVecT>(pl, D, T, Vp, hidden, weight, keep, H, Vt, logits, D.u, wbuf, B, ev0, ev1,
                                         stream);
@@ -178,13 +183,25 @@ hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, 
   const int vrows = static_cast<int>(Vp.V);  // the head passed in is the full [V][H] one
   const bool greedy_t = Vp.greedy;
   const bool t_multi = !greedy_t && pl.nchunk_t > 1;
+  // the large-batch head reads the hidden rows K-tiled (one contiguous 16 KB run per K step of a
+  // 256-row block); the copy rides in extra workgroups of the target partials launch when there is one
+  uint16_t *hidt = pl.hidt_bytes ? reinterpret_cast<uint16_t *>(hidt_base) : nullptr;
+  const TileParams tp = hidden_tiles_params(hidden, pl.M, H, hidt);
   // 1. target partials (or a whole single-chunk target softmax); greedy verification needs none
-  if (t_multi)
+  if (t_multi && hidt)
+    e = launch(softmax_partial_tiles<TinT, kVecT>,
+               dim3(static_cast<unsigned>(T.rows * T.nchunk + hidden_tiles_blocks(tp))), dim3(kBlock), 0, stream, T,
+               tp);
+  else if (t_multi)
     e = launch(softmax_partial<TinT, kVecT>, dim3(static_cast<unsigned>(T.rows * T.nchunk)), dim3(kBlock), 0,
                stream, T);
   else if (!greedy_t)
     e = launch(softmax_single<TinT, kVecT>, dim3(static_cast<unsigned>(T.rows)), dim3(kBlock), 0, stream, T);
   if (e != hipSuccess) return e;
+  if (hidt && !t_multi &&
+      (e = launch(hidden_tiles, dim3(static_cast<unsigned>(hidden_tiles_blocks(tp))), dim3(kBlock), 0, stream, tp)) !=
+          hipSuccess)
+    return e;
   // 2. LM head (+ draft partials), bracketed by the caller's timing events if any
   if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
   bool d_multi = true;
@@ -194,7 +211,8 @@ hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, 
     if (e != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   } else if (pl.fused_mfma) {
-    e = launch_mfma_big<true>(hidden, weight, keep, vrows, pl.M, H, Vt, logits, GemvParts{D.part, D.k2}, stream);
+    e = launch_mfma_big<true>(hidden, weight, keep, vrows, pl.M, H, Vt, logits, GemvParts{D.part, D.k2}, stream,
+                              hidt);
     if (e != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   } else {
@@ -258,7 +276,8 @@ extern "C" vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *wei
   if (H % 8 != 0 || !aligned16(hidden) || !aligned16(weight)) return VT_ERR_UNSUPPORTED;
   if (V > INT32_MAX || H > INT32_MAX || B * R > INT32_MAX) return VT_ERR_UNSUPPORTED;
   const BlockPlan pl = plan_block(B, gamma, R, H, Vt, V, keep_ids != nullptr, greedy_t, greedy_d);
-  if (pl.rows_t * pl.nchunk_t > static_cast<int64_t>(UINT32_MAX) ||
+  if (pl.rows_t * pl.nchunk_t + static_cast<int64_t>(pl.hidt_bytes / (16 * kBlock)) + 1 >
+          static_cast<int64_t>(UINT32_MAX) ||
       pl.M * pl.nchunk_d > static_cast<int64_t>(UINT32_MAX) || B * pl.nchunk_v > static_cast<int64_t>(UINT32_MAX))
     return VT_ERR_UNSUPPORTED;
   if (!pl.fused && ((pl.M + kBM - 1) / kBM) * ((Vt + kBN - 1) / kBN) > INT32_MAX) return VT_ERR_UNSUPPORTED;
@@ -330,7 +349,8 @@ extern "C" vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *wei
   const bool vd = aligned16(draft_logits) && Vt % 4 == 0 && pl.chunk_d % 4 == 0;
   auto go = [&](auto run) {
     return run(pl, D, T, P, hidden, weight, keep_ids, H, Vt, draft_logits,
-               pl.fv ? reinterpret_cast<float *>(ws + pl.off_wbuf) : nullptr, B, lmhead_begin, lmhead_end, stream);
+               pl.fv ? reinterpret_cast<float *>(ws + pl.off_wbuf) : nullptr, B, lmhead_begin, lmhead_end, stream,
+               pl.hidt_bytes ? static_cast<void *>(ws + pl.off_hidt) : nullptr);
   };
   hipError_t e;
   if (target_dtype == VT_F32) {
@@ -357,7 +377,7 @@ extern "C" vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *wei
 // writes the partials it reads later in the same call.
 namespace vt {
 namespace {
-constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;  // 32 MiB per device
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;  // 64 MiB per device
 constexpr int kMaxDevices = 64;
 }  // namespace
 }  // namespace vt

@@ -794,7 +794,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 // barrier.  Each wave loads two 1 KB chunks of each operand per K step.
 constexpr int kDma8Block = 512;
 
-template <bool TRIM, bool PARTS>
+// ATILED: the hidden rows come K-tiled (hidden_tiles below): each K step's 256 x 32 slice of a
+// hidden-row block is one contiguous 16 KB run instead of 256 rows 8 KB apart.  Measured on the
+// large-drafter shape, the kernel's loads then take about 15% less time and the kernel 4-6% less;
+// the products and their summation order are unchanged, so the logits are the same bits.
+template <bool TRIM, bool PARTS, bool ATILED = false>
 __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_dma8(const uint16_t *__restrict__ hidden,
                                                                   const uint16_t *__restrict__ weight,
                                                                   const int32_t *__restrict__ keep, int vrows, int M,
@@ -819,16 +823,18 @@ __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_dma8(const uint16_t
     const int am = min(m0 + r, M - 1);
     const int n = min(n0 + r, Vt - 1);
     const int64_t brow = TRIM ? kept_row(keep, n, vrows) : static_cast<int64_t>(n);
-    asrc[j] = hidden + static_cast<int64_t>(am) * H + piece * 8;
+    asrc[j] = ATILED ? hidden + (static_cast<int64_t>(bm) * (H / kDmaBK) * kBigBM + r) * kDmaBK + piece * 8
+                     : hidden + static_cast<int64_t>(am) * H + piece * 8;
     bsrc[j] = weight + brow * H + piece * 8;
   }
   const int nk = H / kDmaBK;
   auto issue = [&](int kstep, int slot) {
     const int k0 = min(kstep, nk - 1) * kDmaBK;
+    const int64_t ka = ATILED ? static_cast<int64_t>(min(kstep, nk - 1)) * kBigBM * kDmaBK : k0;
     char *base = smem + slot * kDmaStageBytes;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      __builtin_amdgcn_global_load_lds(asrc[j] + k0, (lds_void *)(base + (2 * w + j) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(asrc[j] + ka, (lds_void *)(base + (2 * w + j) * 1024), 16, 0, 0);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       __builtin_amdgcn_global_load_lds(bsrc[j] + k0, (lds_void *)(base + kDmaOperandBytes + (2 * w + j) * 1024),
@@ -906,12 +912,83 @@ __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_dma8(const uint16_t
 
 inline int64_t mfma_big_tiles_n(int64_t Vt) { return (Vt + kBigBN - 1) / kBigBN; }
 
+// K-tiled copy of the hidden rows for lmhead_mfma_dma8<..., ATILED>: out[bm][ks][r][32] =
+// hidden[min(256 bm + r, M - 1)][32 ks .. 32 ks + 31] (rows past M repeat the last row; their
+// logits are never stored).  One thread moves one 16-byte piece; a wave reads 16 rows x 64 bytes
+// and writes 1 KB contiguously.  Needs H % 32 == 0.
+// Bytes of the K-tiled hidden copy (0 when the direct-to-LDS kernel does not run).
+inline size_t hidden_tiles_bytes(int64_t M, int64_t H) {
+  if (M < kBigMinM || H % kDmaBK != 0) return 0;
+  return static_cast<size_t>((M + kBigBM - 1) / kBigBM) * kBigBM * static_cast<size_t>(H) * 2;
+}
+
+struct TileParams {
+  const uint16_t *hidden;
+  uint16_t *out;
+  int64_t pieces;
+  int M, H;
+};
+
+// Workgroup `blk` of the copy (kBlock pieces).
+__device__ __forceinline__ void hidden_tiles_block(const TileParams &T, int64_t blk) {
+  const uint16_t *__restrict__ hidden = T.hidden;
+  const int M = T.M, H = T.H;
+  const int64_t q = blk * kBlock + threadIdx.x;  // piece index in out
+  if (q >= T.pieces) return;
+  const int p = static_cast<int>(q & 3);
+  const int64_t rr = q >> 2;  // (bm, ks, r) flattened
+  const int r = static_cast<int>(rr % kBigBM);
+  const int64_t bk = rr / kBigBM;
+  const int nk = H / kDmaBK;
+  const int ks = static_cast<int>(bk % nk);
+  const int bm = static_cast<int>(bk / nk);
+  const int m = min(bm * kBigBM + r, M - 1);
+  const uint4 v = *reinterpret_cast<const uint4 *>(hidden + static_cast<int64_t>(m) * H + ks * kDmaBK + p * 8);
+  *reinterpret_cast<uint4 *>(T.out + q * 8) = v;
+}
+
+inline TileParams hidden_tiles_params(const uint16_t *hidden, int64_t M, int64_t H, uint16_t *out) {
+  TileParams T{};
+  T.hidden = hidden;
+  T.out = out;
+  T.M = static_cast<int>(M);
+  T.H = static_cast<int>(H);
+  T.pieces = static_cast<int64_t>(hidden_tiles_bytes(M, H) / 16);
+  return T;
+}
+
+inline int64_t hidden_tiles_blocks(const TileParams &T) { return (T.pieces + kBlock - 1) / kBlock; }
+
+__global__ __launch_bounds__(kBlock) void hidden_tiles(TileParams T) { hidden_tiles_block(T, blockIdx.x); }
+
+// The target rows' softmax partials (one workgroup per (row, 4096-chunk)) with the K-tiled copy of
+// the hidden rows in extra workgroups past them: both only read inputs of the block, so the copy
+// rides in the launch that precedes the head instead of taking one of its own.
+template <typename Tin, bool kVec>
+__global__ __launch_bounds__(kBlock) void softmax_partial_tiles(SmParams P, TileParams T) {
+  const int64_t nparts = P.rows * P.nchunk;
+  const int64_t bid = blockIdx.x;
+  if (bid < nparts)
+    partial_chunk<Tin, kVec>(P, bid);
+  else
+    hidden_tiles_block(T, bid - nparts);
+}
+
+
+
+
+// hidden_tiled: NULL, or the K-tiled copy of the hidden rows made by launch_hidden_tiles (H % 32 == 0).
 template <bool PARTS>
 inline hipError_t launch_mfma_big(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int vrows,
                                   int64_t M, int64_t H, int64_t Vt, float *logits, GemvParts parts,
-                                  hipStream_t stream) {
+                                  hipStream_t stream, const uint16_t *hidden_tiled = nullptr) {
   const int64_t tiles = ((M + kBigBM - 1) / kBigBM) * mfma_big_tiles_n(Vt);
   if (H % kDmaBK == 0) {
+    if (hidden_tiled) {
+      auto ft = keep ? &lmhead_mfma_dma8<true, PARTS, true> : &lmhead_mfma_dma8<false, PARTS, true>;
+      return launch(ft, dim3(static_cast<unsigned>(tiles)), dim3(kDma8Block), 0, stream, hidden_tiled, weight, keep,
+                    vrows, static_cast<int>(M), static_cast<int>(H), static_cast<int>(Vt), logits, parts);
+    }
     auto fd = keep ? &lmhead_mfma_dma8<true, PARTS> : &lmhead_mfma_dma8<false, PARTS>;
     return launch(fd, dim3(static_cast<unsigned>(tiles)), dim3(kDma8Block), 0, stream, hidden, weight, keep,
                   vrows, static_cast<int>(M), static_cast<int>(H), static_cast<int>(Vt), logits, parts);

@@ -177,7 +177,11 @@ size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
  * first pass and, in extra workgroups, the target rows' first pass; one chunk pass over the
  * full vocabulary forms the log-normalisers, draft draws, accept tests and residual chunk sums;
  * one final pass draws the last token.  Larger batches take 5 (LM head with the draft partials,
- * target partials, one combine launch for both row sets, two verify passes).
+ * target partials, one combine launch for both row sets, two verify passes).  When B*R >= 256 and
+ * H % 32 == 0 the target partials launch also copies the hidden rows K-tiled into the workspace
+ * (the head then reads each K step of a 256-row block as one contiguous run; same products, same
+ * logits); without target partials (V <= 4096 or greedy verification) the copy is a launch of its
+ * own.
  *   Pages: as for the four calls above.
  *
  *   hidden bf16 [B*R][H] (row b*R + i is sequence b's i-th draft position); weight bf16 [V][H]
@@ -225,12 +229,12 @@ size_t vt_spec_block_workspace_bytes(int64_t B, int64_t gamma, int64_t R, int64_
  * vt_spec_block_noalloc -- vt_spec_block for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
  * results and errors as vt_spec_block, without workspace / workspace_bytes: the workspace is a
- * fixed 32 MiB array of device memory inside the library, one per device, held until the process
+ * fixed 64 MiB array of device memory inside the library, one per device, held until the process
  * ends (its address is looked up once per device, on the first call with that device current).
  * Nothing is allocated or freed by this call.
- *   Limit: shapes whose vt_spec_block_workspace_bytes exceeds 32 MiB return VT_ERR_WORKSPACE
+ *   Limit: shapes whose vt_spec_block_workspace_bytes exceeds 64 MiB return VT_ERR_WORKSPACE
  *   before anything is enqueued (for example B = 256, gamma = 8, H = 4096, Vt = 65536,
- *   V = 128256 needs 5.6 MiB).
+ *   V = 128256 needs 24.5 MiB, most of it the K-tiled copy of the hidden rows).
  *   Calls that overlap on one device (two streams, or two host threads) share that device's array
  *   and race: serialise them.  The array keeps the last call's partial results; no call depends on
  *   its previous contents.  Errors: as vt_spec_block, plus VT_ERR_HIP if the device or the array's

@@ -111,8 +111,10 @@ def test_fused_block_rank_ordered_keep_set(name):
     _check(make_workload(SCALED[name], keep_order="rank"))
 
 
-@pytest.mark.parametrize("name", ["c3-trimmed", "c4-batched-mfma", "c4-big-tiles"])
+@pytest.mark.parametrize("name", ["c3-trimmed", "c4-batched-mfma", "c4-big-tiles", "c5-big-tiles"])
 def test_fused_matches_separate_calls(name):
+    # c5-big-tiles (M = 288, H = 256): the fused call's head reads a K-tiled copy of the hidden
+    # rows, the separate call reads them row-major; the logits must still be the same bits
     wl = make_workload(SCALED[name])
     a = gpu_block(wl)
     b = gpu_block_fused(wl)

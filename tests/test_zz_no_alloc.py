@@ -75,7 +75,7 @@ def test_noalloc_matches_block_on_two_calls(order):
 
 
 def test_noalloc_full_size_then_batch_one():
-    # the benchmark's large-drafter block (5.6 MiB of scratch) and then the batch-1 VocabTrim block
+    # the benchmark's large-drafter block (24.5 MiB of scratch) and then the batch-1 VocabTrim block
     for c in (5, 3):
         wl = make_workload(CONFIGS[c])
         say(f"noalloc full size config {c}")
@@ -85,7 +85,7 @@ def test_noalloc_full_size_then_batch_one():
 def test_noalloc_rejects_shapes_beyond_the_scratch():
     L = vt.lib()
     B, g, R, H, Vt, V = 4096, 8, 9, 4096, 65536, 128256
-    assert L.vt_spec_block_workspace_bytes(B, g, R, H, Vt, V) > 32 << 20
+    assert L.vt_spec_block_workspace_bytes(B, g, R, H, Vt, V) > 64 << 20
     # rejected on the host before anything is enqueued: the pointers are never dereferenced
     fake = ctypes.c_void_p(256)
     st = L.vt_spec_block_noalloc(fake, fake, fake, fake, B, g, R, H, Vt, V, fake, 1, 0.8, 0.8, fake, fake, fake,
