@@ -804,7 +804,10 @@ __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_dma8(const uint16_t
                                                                   const int32_t *__restrict__ keep, int vrows, int M,
                                                                   int H, int Vt, float *__restrict__ logits,
                                                                   GemvParts parts) {
-  __shared__ __attribute__((aligned(1024))) char smem[kDmaStages * kDmaStageBytes];
+  // with the K-tiled hidden rows a five-slot ring (the whole 160 KB of LDS) gives the loads three
+  // steps to land: ~3% faster on the large-drafter shape; row-major rows keep four slots
+  constexpr int kStages = ATILED ? 5 : kDmaStages;
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * kDmaStageBytes];
   const int nbm = (M + kBigBM - 1) / kBigBM;
   const int nbn = (Vt + kBigBN - 1) / kBigBN;
   const int tile = static_cast<int>(xcd_remap(blockIdx.x, static_cast<int64_t>(nbm) * nbn));
@@ -882,24 +885,25 @@ __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_dma8(const uint16_t
   // the loads of step k + 3 go into it, and the second slice's MFMAs run while the first slice of
   // step k + 1 is read.  LDS reads never wait on an idle MFMA pipe; loads have two steps to land.
   // The waits are explicit: before the barrier of step k a thread waits until at most the loads
-  // of steps k + 2 and k + 3 are outstanding; steps past the last re-fetch the last step into the
-  // free slot (never read), so every step issues the same 4 loads per wave.
+  // of the steps after k + 1 are outstanding (k + 2 and k + 3 with four slots, k + 2 .. k + 4 with
+  // five); steps past the last re-fetch the last step into the free slot (never read), so every
+  // step issues the same 4 loads per wave.
   bf16x8 a0[4], b0[2], a1[4], b1[2];
-  constexpr int kAhead = kDmaStages - 1;
+  constexpr int kAhead = kStages - 1;
 #pragma unroll
   for (int s = 0; s < kAhead; ++s) issue(s, s);
   wait_vmcnt<4 * (kAhead - 1)>();
   __builtin_amdgcn_s_barrier();
   frags(0, off0, a0, b0);
   for (int kt = 0; kt < nk; ++kt) {
-    const int slot = kt % kDmaStages;
+    const int slot = kt % kStages;
     frags(slot, off1, a1, b1);
     mfmas(a0, b0);
     interleave();
     wait_vmcnt<4 * (kAhead - 2)>();
     __builtin_amdgcn_s_barrier();
-    issue(kt + kAhead, (kt + kAhead) % kDmaStages);
-    frags((kt + 1) % kDmaStages, off0, a0, b0);  // past the last step: unused reads of a re-fetch
+    issue(kt + kAhead, (kt + kAhead) % kStages);
+    frags((kt + 1) % kStages, off0, a0, b0);  // past the last step: unused reads of a re-fetch
     mfmas(a1, b1);
     __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
     interleave();

@@ -20,6 +20,10 @@ SCALED = {
     "c4-big-tiles": CONFIGS[4].scaled(B=40, V=20000, Vt=5000, H=520),  # M = 320: fused 256x256 tiles
     "c5-big-tiles": CONFIGS[5].scaled(B=32, V=13000, Vt=6001, H=256),  # M = 288, ragged Vt
     "c3-one-chunk-target": CONFIGS[3].scaled(V=4000, Vt=1500, H=256),
+    # untrimmed head at 256+ hidden rows (M = 288): K-tiled hidden copy, no keep set
+    "c2-untrimmed-big-tiles": CONFIGS[2].scaled(B=48, V=6000, Vt=6000, H=256),
+    # 256+ hidden rows with a one-chunk target row: the hidden copy takes a launch of its own
+    "c5-big-tiles-one-chunk-target": CONFIGS[5].scaled(B=32, V=4000, Vt=1500, H=256),
 }
 
 
