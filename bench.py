@@ -87,6 +87,10 @@ def parse():
                     help="temperature 0 for target and draft: argmax drafts and greedy verification")
     ap.add_argument("--graph", action="store_true",
                     help="replay captured HIP graphs (LM head | rest) instead of launching the calls eagerly")
+    ap.add_argument("--head", default="tiled", choices=["tiled", "gather"],
+                    help="what the fused call's large-batch head reads: the K-tiled W^Trim built once per keep "
+                         "set by vt_trim_head_tiled (the default), or rows of the full head gathered through "
+                         "keep_ids")
     return ap.parse_args()
 
 
@@ -681,10 +685,20 @@ def bench_block(args, config: int, steps: int, warmup: int):
             ev_free.record(main)
 
     ws_blk = vt.block_workspace(B, g, R, cfg.H, cfg.Vt, cfg.V)
+    # W^Trim is built once per keep set, before decoding (VocabTrim §3): the K-tiled copy is made
+    # here, outside the timed region, one per input set; the fused call reads it only where its
+    # large-batch head runs
+    tiled = tiled_head_used(cfg, args)
+    if tiled:
+        for s in sets:
+            s["weight_tiled"] = vt.vt_trim_head_tiled(s["weight"], keep, k=cfg.Vt)
+        torch.cuda.synchronize()
+        log("K-tiled W^Trim built for each input set")
 
     def fused(s, events=None):
         vt.vt_spec_block(s["hidden"], s["weight"], keep, f2t, s["target"], T, T, s["u_draft"], s["u_acc"],
-                         s["u_fin"], logits, dlse, dids, tlse, tokens, nacc, workspace=ws_blk, lmhead_events=events)
+                         s["u_fin"], logits, dlse, dids, tlse, tokens, nacc, workspace=ws_blk, lmhead_events=events,
+                         weight_tiled=s.get("weight_tiled"))
 
     outs = (logits, dlse, dids, tlse, tokens, nacc)
     if not args.calls and (args.graph or args.overlap):
@@ -768,7 +782,7 @@ def bench_block(args, config: int, steps: int, warmup: int):
     lm_ms = sum(x.elapsed_time(y) for x, y in zip(ev_a, ev_b)) / steps
     lmb = lmhead_launch_bytes(cfg, args.greedy, args.calls)
     mean_acc = float(nacc.double().mean())
-    res = dict(cfg=cfg, wl=wl, n_sets=n_sets, ms_per_step=ms_per_step, lm_ms=lm_ms, lm_bytes=lmb,
+    res = dict(cfg=cfg, wl=wl, n_sets=n_sets, tiled=tiled, ms_per_step=ms_per_step, lm_ms=lm_ms, lm_bytes=lmb,
                lm_gbs=lmb / (lm_ms / 1e3) / 1e9, block_bytes=bb, block_gbs=bb / (ms_per_step / 1e3) / 1e9,
                value=B * g / (ms_per_step / 1e3), mean_accepted=mean_acc,
                mfma=B * R > 8 and not small_batch_block(cfg, args.greedy) and B * R >= 256)
@@ -780,6 +794,13 @@ def bench_block(args, config: int, steps: int, warmup: int):
     del sets, base, logits
     torch.cuda.empty_cache()
     return res
+
+
+def tiled_head_used(cfg, args) -> bool:
+    """Whether the fused call's head reads the K-tiled W^Trim: the sampled large-batch head
+    (256 x 256 tiles) with whole 32-column K steps, unless --head gather."""
+    return (not args.calls and args.head == "tiled" and not args.greedy and cfg.B * cfg.R >= 256
+            and cfg.H % 32 == 0)
 
 
 def side_record(res) -> dict:
@@ -871,6 +892,9 @@ def main():
                    "kept_rows": cfg.Vt, "keep_order": args.keep_order, "target_logits": cfg.target_dtype,
                    "temperature": 0.0 if args.greedy else cfg.T,
                    "weights": "bf16", "accumulate": "f32", "input_sets_rotated": res["n_sets"],
+                   "head_rows": ("K-tiled W^Trim, built once per keep set outside the timed region" if res["tiled"]
+                                 else "gathered from the full head through keep_ids" if cfg.trimmed
+                                 else "the full head"),
                    "verification": "greedy (temperature 0)" if args.greedy else "sampling",
                    "launch": ("vt_spec_block: one fused call per step" if not args.calls else
                               "four calls, hip graphs (LM head | rest) replayed" if args.graph else

@@ -63,11 +63,11 @@ def lib() -> ctypes.CDLL:
         L.vt_spec_verify.restype = I
         L.vt_spec_verify_workspace_bytes.argtypes = [I64, I64, I64]
         L.vt_spec_verify_workspace_bytes.restype = SZ
-        L.vt_spec_block.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I64, P, I, F, F, P, P, P, P, P, P, P, P, P,
-                                    P, P, P, SZ, P]
+        L.vt_spec_block.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, P, I, F, F, P, P, P, P, P, P, P, P,
+                                    P, P, P, P, SZ, P]
         L.vt_spec_block.restype = I
-        L.vt_spec_block_noalloc.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I64, P, I, F, F, P, P, P, P, P, P,
-                                            P, P, P, P, P, P]
+        L.vt_spec_block_noalloc.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, P, I, F, F, P, P, P, P, P,
+                                            P, P, P, P, P, P, P]
         L.vt_spec_block_noalloc.restype = I
         L.vt_spec_block_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I64]
         L.vt_spec_block_workspace_bytes.restype = SZ
@@ -79,6 +79,10 @@ def lib() -> ctypes.CDLL:
         L.vt_keep_select.restype = I
         L.vt_trim_head.argtypes = [P, I64, I64, P, I64, P, P]
         L.vt_trim_head.restype = I
+        L.vt_trim_head_tiled.argtypes = [P, I64, I64, P, I64, P, P]
+        L.vt_trim_head_tiled.restype = I
+        L.vt_trim_head_tiled_bytes.argtypes = [I64, I64]
+        L.vt_trim_head_tiled_bytes.restype = SZ
         L.vt_spec_generate_markov.argtypes = [P, P, I64, F, F, I64, I64, I64, P, P, P, P]
         L.vt_spec_generate_markov.restype = I
         L.vt_status_string.argtypes = [I]
@@ -91,7 +95,7 @@ EXPORTED = ("vt_lmhead_trimmed", "vt_softmax_temp", "vt_softmax_temp_workspace_b
             "vt_spec_verify_workspace_bytes", "vt_spec_block", "vt_spec_block_workspace_bytes",
             "vt_spec_block_noalloc", "vt_status_string",
             "vt_token_histogram", "vt_token_histogram_workspace_bytes", "vt_keep_select", "vt_trim_head",
-            "vt_spec_generate_markov")
+            "vt_trim_head_tiled", "vt_trim_head_tiled_bytes", "vt_spec_generate_markov")
 
 VT_SELECT_TOP_K, VT_SELECT_TOP_P, VT_SELECT_MIN_FREQ = range(3)
 
@@ -233,13 +237,25 @@ def block_workspace(B: int, gamma: int, R: int, H: int, Vt: int, V: int, device=
     return _torch().empty(nbytes, dtype=_torch().uint8, device=device) if nbytes else None
 
 
+def _weight_tiled(weight_tiled, Vt, H, fn):
+    if weight_tiled is None:
+        return None
+    _bits16(weight_tiled, "weight_tiled")
+    need = lib().vt_trim_head_tiled_bytes(Vt, H) // 2
+    if need == 0 or weight_tiled.numel() != need:
+        raise ValueError(f"{fn}: weight_tiled must hold the K-tiled W^Trim of {Vt} rows ({need} values)")
+    return _ptr(weight_tiled, "weight_tiled")
+
+
 def vt_spec_block(hidden, weight, keep_ids, full_to_trim, target_logits, target_T, draft_T, u_draft, u_accept,
                   u_final, draft_logits, draft_lse, draft_ids, target_lse, out_tokens, out_num_accepted,
-                  workspace=None, lmhead_events=None):
+                  workspace=None, lmhead_events=None, weight_tiled=None):
     """One whole block.  hidden [B*R, H] bf16, weight [V, H] bf16, target [B, gamma+1, V];
     outputs draft_logits [B*R, Vt] f32, draft_lse [B*R] f64, draft_ids [B*R] i32, target_lse
     [B*(gamma+1)] f64, out_tokens [B, gamma+1] i32, out_num_accepted [B] i32.
     lmhead_events: optional (start, end) torch.cuda.Event pair recorded around the LM-head kernel.
+    weight_tiled: optional K-tiled W^Trim from vt_trim_head_tiled(weight, keep_ids), read by the
+    large-batch head instead of gathering rows of weight (same logits).
     target_T = 0: greedy verification (target_lse, u_accept, u_final may be None); draft_T = 0 (with
     target_T = 0): argmax drafts (u_draft may be None)."""
     torch = _torch()
@@ -264,7 +280,9 @@ def vt_spec_block(hidden, weight, keep_ids, full_to_trim, target_logits, target_
     ev0 = ev1 = None
     if lmhead_events is not None:
         ev0, ev1 = (ctypes.c_void_p(e.cuda_event) for e in lmhead_events)
-    st = lib().vt_spec_block(_ptr(hidden, "hidden"), _ptr(weight, "weight"), _ptr(keep_ids, "keep_ids", torch.int32),
+    wt = _weight_tiled(weight_tiled, Vt, H, "vt_spec_block")
+    st = lib().vt_spec_block(_ptr(hidden, "hidden"), _ptr(weight, "weight"), wt,
+                             _ptr(keep_ids, "keep_ids", torch.int32),
                              _ptr(full_to_trim, "full_to_trim", torch.int32, V), B, gamma, R, H, Vt, V,
                              _ptr(target_logits, "target_logits"), dt, float(target_T), float(draft_T),
                              _ptr(u_draft, "u_draft", torch.float32, M), _ptr(u_accept, "u_accept", torch.float32, B * gamma),
@@ -280,7 +298,7 @@ def vt_spec_block(hidden, weight, keep_ids, full_to_trim, target_logits, target_
 
 def vt_spec_block_noalloc(hidden, weight, keep_ids, full_to_trim, target_logits, target_T, draft_T, u_draft,
                           u_accept, u_final, draft_logits, draft_lse, draft_ids, target_lse, out_tokens,
-                          out_num_accepted, lmhead_events=None):
+                          out_num_accepted, lmhead_events=None, weight_tiled=None):
     """vt_spec_block with the library's fixed per-device scratch instead of a workspace (nothing is
     allocated; shapes needing more than 64 MiB of workspace are rejected).  Calls that overlap on
     one device race on that scratch."""
@@ -303,8 +321,9 @@ def vt_spec_block_noalloc(hidden, weight, keep_ids, full_to_trim, target_logits,
     ev0 = ev1 = None
     if lmhead_events is not None:
         ev0, ev1 = (ctypes.c_void_p(e.cuda_event) for e in lmhead_events)
+    wt = _weight_tiled(weight_tiled, Vt, H, "vt_spec_block_noalloc")
     st = lib().vt_spec_block_noalloc(
-        _ptr(hidden, "hidden"), _ptr(weight, "weight"), _ptr(keep_ids, "keep_ids", torch.int32),
+        _ptr(hidden, "hidden"), _ptr(weight, "weight"), wt, _ptr(keep_ids, "keep_ids", torch.int32),
         _ptr(full_to_trim, "full_to_trim", torch.int32, V), B, gamma, R, H, Vt, V, _ptr(target_logits, "target_logits"),
         dt, float(target_T), float(draft_T), _ptr(u_draft, "u_draft", torch.float32, M),
         _ptr(u_accept, "u_accept", torch.float32, B * gamma), _ptr(u_final, "u_final", torch.float32, B),
@@ -368,6 +387,27 @@ def vt_trim_head(weight, keep_ids, trimmed):
                             _ptr(trimmed, "trimmed"), _stream())
     _check("vt_trim_head", st)
     return trimmed
+
+
+def vt_trim_head_tiled(weight, keep_ids, k=None, tiled=None):
+    """W^Trim = weight[keep_ids] (or rows 0..k-1 when keep_ids is None) in the K-tiled layout
+    [ceil(k/256)][H/32][256][32] of vt_trim_head_tiled, as a flat bf16-bits tensor (allocated when
+    tiled is None)."""
+    torch = _torch()
+    _bits16(weight, "weight")
+    V_rows, H = weight.shape
+    if keep_ids is not None:
+        k = keep_ids.numel()
+    nbytes = lib().vt_trim_head_tiled_bytes(k, H)
+    if tiled is None:
+        tiled = torch.empty(nbytes // 2, dtype=weight.dtype, device=weight.device)
+    _bits16(tiled, "tiled")
+    if tiled.numel() * 2 != nbytes:
+        raise ValueError("vt_trim_head_tiled: tiled must hold vt_trim_head_tiled_bytes(k, H) bytes")
+    st = lib().vt_trim_head_tiled(_ptr(weight, "weight"), V_rows, H, _ptr(keep_ids, "keep_ids", torch.int32), k,
+                                  _ptr(tiled, "tiled"), _stream())
+    _check("vt_trim_head_tiled", st)
+    return tiled
 
 
 # ---------------------------------------------------------------- generation loop

@@ -173,7 +173,7 @@ template <typename TinT, bool kVecT, bool kVecD>
 hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, const VfParams &Vp,
                      const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int64_t H, int64_t Vt,
                      float *logits, float *wbuf, int64_t B, hipEvent_t ev0, hipEvent_t ev1, hipStream_t stream,
-                     void *hidt_base) {
+                     void *hidt_base, const uint16_t *weight_tiled) {
   if (pl.fv)
     return run_block_small<TinT, kVecT>(pl, D, T, Vp, hidden, weight, keep, H, Vt, logits, D.u, wbuf, B, ev0, ev1,
                                         stream);
@@ -212,7 +212,7 @@ hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, 
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   } else if (pl.fused_mfma) {
     e = launch_mfma_big<true>(hidden, weight, keep, vrows, pl.M, H, Vt, logits, GemvParts{D.part, D.k2}, stream,
-                              hidt);
+                              hidt, weight_tiled);
     if (e != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   } else {
@@ -250,7 +250,8 @@ extern "C" size_t vt_spec_block_workspace_bytes(int64_t B, int64_t gamma, int64_
   return bytes;
 }
 
-extern "C" vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep_ids,
+extern "C" vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *weight, const uint16_t *weight_tiled,
+                                     const int32_t *keep_ids,
                                      const int32_t *full_to_trim, int64_t B, int64_t gamma, int64_t R, int64_t H,
                                      int64_t Vt, int64_t V, const void *target_logits, vt_dtype_t target_dtype,
                                      float target_T, float draft_T, const float *u_draft, const float *u_accept,
@@ -274,6 +275,7 @@ extern "C" vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *wei
   if (!keep_ids && Vt != V) return VT_ERR_INVALID_ARG;
   if (gamma > kWave) return VT_ERR_UNSUPPORTED;
   if (H % 8 != 0 || !aligned16(hidden) || !aligned16(weight)) return VT_ERR_UNSUPPORTED;
+  if (weight_tiled && (H % kTileK != 0 || !aligned16(weight_tiled))) return VT_ERR_UNSUPPORTED;
   if (V > INT32_MAX || H > INT32_MAX || B * R > INT32_MAX) return VT_ERR_UNSUPPORTED;
   const BlockPlan pl = plan_block(B, gamma, R, H, Vt, V, keep_ids != nullptr, greedy_t, greedy_d);
   if (pl.rows_t * pl.nchunk_t + static_cast<int64_t>(pl.hidt_bytes / (16 * kBlock)) + 1 >
@@ -350,7 +352,7 @@ extern "C" vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *wei
   auto go = [&](auto run) {
     return run(pl, D, T, P, hidden, weight, keep_ids, H, Vt, draft_logits,
                pl.fv ? reinterpret_cast<float *>(ws + pl.off_wbuf) : nullptr, B, lmhead_begin, lmhead_end, stream,
-               pl.hidt_bytes ? static_cast<void *>(ws + pl.off_hidt) : nullptr);
+               pl.hidt_bytes ? static_cast<void *>(ws + pl.off_hidt) : nullptr, weight_tiled);
   };
   hipError_t e;
   if (target_dtype == VT_F32) {
@@ -406,7 +408,8 @@ vt_status_t scratch_on_current_device(void **out) {
 }  // namespace
 }  // namespace vt
 
-extern "C" vt_status_t vt_spec_block_noalloc(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep_ids,
+extern "C" vt_status_t vt_spec_block_noalloc(const uint16_t *hidden, const uint16_t *weight,
+                                             const uint16_t *weight_tiled, const int32_t *keep_ids,
                                              const int32_t *full_to_trim, int64_t B, int64_t gamma, int64_t R,
                                              int64_t H, int64_t Vt, int64_t V, const void *target_logits,
                                              vt_dtype_t target_dtype, float target_T, float draft_T,
@@ -419,7 +422,8 @@ extern "C" vt_status_t vt_spec_block_noalloc(const uint16_t *hidden, const uint1
   if (st != VT_OK) return st;
   // vt_spec_block validates every argument and returns VT_ERR_WORKSPACE when the shape needs more
   // than the fixed scratch holds
-  return vt_spec_block(hidden, weight, keep_ids, full_to_trim, B, gamma, R, H, Vt, V, target_logits, target_dtype,
-                       target_T, draft_T, u_draft, u_accept, u_final, draft_logits, draft_lse, draft_ids, target_lse,
-                       out_tokens, out_num_accepted, lmhead_begin, lmhead_end, ws, vt::kNoAllocScratchBytes, stream);
+  return vt_spec_block(hidden, weight, weight_tiled, keep_ids, full_to_trim, B, gamma, R, H, Vt, V, target_logits,
+                       target_dtype, target_T, draft_T, u_draft, u_accept, u_final, draft_logits, draft_lse, draft_ids,
+                       target_lse, out_tokens, out_num_accepted, lmhead_begin, lmhead_end, ws,
+                       vt::kNoAllocScratchBytes, stream);
 }

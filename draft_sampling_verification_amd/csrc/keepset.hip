@@ -429,6 +429,30 @@ __global__ __launch_bounds__(kBlock) void trim_rows(const uint16_t *__restrict__
   for (int i = lane_id(); i < n16; i += kWave) dst[i] = src[i];
 }
 
+// K-tiled trimmed head: one thread per 16-byte piece of the output, out[b][s][r][32] = row
+// 256 b + r of W^Trim, columns 32 s .. 32 s + 31 (a wave reads 16 rows x 64 bytes and writes 1 KB
+// contiguously).  Rows past k and rows whose id lies outside [0, V_rows) are zeros.
+__global__ __launch_bounds__(kBlock) void trim_tiles(const uint16_t *__restrict__ weight, int V_rows, int H,
+                                                     const int32_t *__restrict__ keep, int k, int64_t pieces,
+                                                     uint16_t *__restrict__ out) {
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  if (q >= pieces) return;
+  const int p = static_cast<int>(q & 3);
+  const int64_t rr = q >> 2;
+  const int r = static_cast<int>(rr % kTileRows);
+  const int64_t bs = rr / kTileRows;
+  const int nk = H / kTileK;
+  const int s = static_cast<int>(bs % nk);
+  const int j = static_cast<int>(bs / nk) * kTileRows + r;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (j < k) {
+    const int id = keep ? keep[j] : j;
+    if (id >= 0 && id < V_rows)
+      v = *reinterpret_cast<const uint4 *>(weight + static_cast<int64_t>(id) * H + s * kTileK + p * 8);
+  }
+  *reinterpret_cast<uint4 *>(out + q * 8) = v;
+}
+
 }  // namespace
 }  // namespace vt
 
@@ -487,4 +511,23 @@ extern "C" vt_status_t vt_trim_head(const uint16_t *weight, int64_t V_rows, int6
   const unsigned grid = static_cast<unsigned>((k + kRowsPerBlock - 1) / kRowsPerBlock);
   return hip_status(launch(trim_rows, dim3(grid), dim3(kBlock), 0, stream, weight, static_cast<int>(V_rows),
                            static_cast<int>(H), keep_ids, static_cast<int>(k), trimmed));
+}
+
+extern "C" size_t vt_trim_head_tiled_bytes(int64_t k, int64_t H) {
+  if (k <= 0 || H <= 0 || H % vt::kTileK != 0) return 0;
+  return vt::tiled_rows_bytes(k, H);
+}
+
+extern "C" vt_status_t vt_trim_head_tiled(const uint16_t *weight, int64_t V_rows, int64_t H, const int32_t *keep_ids,
+                                          int64_t k, uint16_t *tiled, hipStream_t stream) {
+  using namespace vt;
+  if (!weight || !tiled || V_rows <= 0 || H <= 0 || k <= 0 || (!keep_ids && k > V_rows)) return VT_ERR_INVALID_ARG;
+  if (H % kTileK != 0 || !aligned16(weight) || !aligned16(tiled)) return VT_ERR_UNSUPPORTED;
+  if (k > INT32_MAX || V_rows > INT32_MAX || H > INT32_MAX) return VT_ERR_UNSUPPORTED;
+  const int64_t pieces = static_cast<int64_t>(tiled_rows_bytes(k, H) / 16);
+  const int64_t grid = (pieces + kBlock - 1) / kBlock;
+  if (grid > INT32_MAX) return VT_ERR_UNSUPPORTED;
+  return hip_status(launch(trim_tiles, dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, stream, weight,
+                           static_cast<int>(V_rows), static_cast<int>(H), keep_ids, static_cast<int>(k), pieces,
+                           tiled));
 }

@@ -772,6 +772,7 @@ __global__ __launch_bounds__(kBlock, 1) void lmhead_mfma_big(const uint16_t *__r
 // p ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3, which spreads the 16 rows of a fragment read over
 // all banks.  Needs H % 32 == 0 (a piece past H cannot be zeroed on the way into LDS).
 constexpr int kDmaBK = 32;
+static_assert(kDmaBK == kTileK && kBigBM == kTileRows && kBigBN == kTileRows, "K-tiled operand layout");
 constexpr int kDmaStages = 4;                           // ring depth: loads get kDmaStages - 2 steps to land
 constexpr int kDmaRowBytes = kDmaBK * 2;                // 64
 constexpr int kDmaOperandBytes = kBigBM * kDmaRowBytes;  // 16 KB per operand per step
@@ -798,7 +799,9 @@ constexpr int kDma8Block = 512;
 // hidden-row block is one contiguous 16 KB run instead of 256 rows 8 KB apart.  Measured on the
 // large-drafter shape, the kernel's loads then take about 15% less time and the kernel 4-6% less;
 // the products and their summation order are unchanged, so the logits are the same bits.
-template <bool TRIM, bool PARTS, bool ATILED = false>
+// BTILED: the head rows come from a K-tiled W^Trim (vt_trim_head_tiled) instead of being
+// gathered from the full head through keep; again the same products in the same order.
+template <bool TRIM, bool PARTS, bool ATILED = false, bool BTILED = false>
 __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_dma8(const uint16_t *__restrict__ hidden,
                                                                   const uint16_t *__restrict__ weight,
                                                                   const int32_t *__restrict__ keep, int vrows, int M,
@@ -807,6 +810,7 @@ __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_dma8(const uint16_t
   // with the K-tiled hidden rows a five-slot ring (the whole 160 KB of LDS) gives the loads three
   // steps to land: ~3% faster on the large-drafter shape; row-major rows keep four slots
   constexpr int kStages = ATILED ? 5 : kDmaStages;
+  static_assert(!(BTILED && TRIM), "a K-tiled head is already trimmed");
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kDmaStageBytes];
   const int nbm = (M + kBigBM - 1) / kBigBM;
   const int nbn = (Vt + kBigBN - 1) / kBigBN;
@@ -828,19 +832,22 @@ __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_dma8(const uint16_t
     const int64_t brow = TRIM ? kept_row(keep, n, vrows) : static_cast<int64_t>(n);
     asrc[j] = ATILED ? hidden + (static_cast<int64_t>(bm) * (H / kDmaBK) * kBigBM + r) * kDmaBK + piece * 8
                      : hidden + static_cast<int64_t>(am) * H + piece * 8;
-    bsrc[j] = weight + brow * H + piece * 8;
+    bsrc[j] = BTILED ? weight + (static_cast<int64_t>(bn) * (H / kDmaBK) * kBigBN + r) * kDmaBK + piece * 8
+                     : weight + brow * H + piece * 8;
   }
   const int nk = H / kDmaBK;
   auto issue = [&](int kstep, int slot) {
     const int k0 = min(kstep, nk - 1) * kDmaBK;
-    const int64_t ka = ATILED ? static_cast<int64_t>(min(kstep, nk - 1)) * kBigBM * kDmaBK : k0;
+    const int64_t kt = static_cast<int64_t>(min(kstep, nk - 1)) * kBigBM * kDmaBK;  // K-tiled step offset
+    const int64_t ka = ATILED ? kt : k0;
+    const int64_t kb = BTILED ? kt : k0;
     char *base = smem + slot * kDmaStageBytes;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       __builtin_amdgcn_global_load_lds(asrc[j] + ka, (lds_void *)(base + (2 * w + j) * 1024), 16, 0, 0);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      __builtin_amdgcn_global_load_lds(bsrc[j] + k0, (lds_void *)(base + kDmaOperandBytes + (2 * w + j) * 1024),
+      __builtin_amdgcn_global_load_lds(bsrc[j] + kb, (lds_void *)(base + kDmaOperandBytes + (2 * w + j) * 1024),
                                        16, 0, 0);
   };
 
@@ -923,7 +930,7 @@ inline int64_t mfma_big_tiles_n(int64_t Vt) { return (Vt + kBigBN - 1) / kBigBN;
 // Bytes of the K-tiled hidden copy (0 when the direct-to-LDS kernel does not run).
 inline size_t hidden_tiles_bytes(int64_t M, int64_t H) {
   if (M < kBigMinM || H % kDmaBK != 0) return 0;
-  return static_cast<size_t>((M + kBigBM - 1) / kBigBM) * kBigBM * static_cast<size_t>(H) * 2;
+  return tiled_rows_bytes(M, H);
 }
 
 struct TileParams {
@@ -981,13 +988,20 @@ __global__ __launch_bounds__(kBlock) void softmax_partial_tiles(SmParams P, Tile
 
 
 
-// hidden_tiled: NULL, or the K-tiled copy of the hidden rows made by launch_hidden_tiles (H % 32 == 0).
+// hidden_tiled: NULL, or the K-tiled copy of the hidden rows made by hidden_tiles (H % 32 == 0);
+// weight_tiled: NULL, or the K-tiled trimmed head of vt_trim_head_tiled (read only together with
+// hidden_tiled; weight and keep are then not read by the kernel).
 template <bool PARTS>
 inline hipError_t launch_mfma_big(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int vrows,
                                   int64_t M, int64_t H, int64_t Vt, float *logits, GemvParts parts,
-                                  hipStream_t stream, const uint16_t *hidden_tiled = nullptr) {
+                                  hipStream_t stream, const uint16_t *hidden_tiled = nullptr,
+                                  const uint16_t *weight_tiled = nullptr) {
   const int64_t tiles = ((M + kBigBM - 1) / kBigBM) * mfma_big_tiles_n(Vt);
   if (H % kDmaBK == 0) {
+    if (hidden_tiled && weight_tiled)
+      return launch(lmhead_mfma_dma8<false, PARTS, true, true>, dim3(static_cast<unsigned>(tiles)), dim3(kDma8Block),
+                    0, stream, hidden_tiled, weight_tiled, keep, vrows, static_cast<int>(M), static_cast<int>(H),
+                    static_cast<int>(Vt), logits, parts);
     if (hidden_tiled) {
       auto ft = keep ? &lmhead_mfma_dma8<true, PARTS, true> : &lmhead_mfma_dma8<false, PARTS, true>;
       return launch(ft, dim3(static_cast<unsigned>(tiles)), dim3(kDma8Block), 0, stream, hidden_tiled, weight, keep,

@@ -224,6 +224,15 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblocks) {
   return xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
 }
 
+// K-tiled layout of a matrix of rows of H bf16 values (the trimmed head made by
+// vt_trim_head_tiled, the hidden-row copy of the large-batch head): block b of kTileRows rows and
+// K step s of kTileK columns sit at out[b][s][r][kTileK], so each (b, s) slice is one contiguous
+// 16 KB run.  Rows past the matrix's end fill out its last block.
+constexpr int kTileRows = 256, kTileK = 32;
+inline size_t tiled_rows_bytes(int64_t rows, int64_t H) {
+  return static_cast<size_t>((rows + kTileRows - 1) / kTileRows) * kTileRows * static_cast<size_t>(H) * 2;
+}
+
 // Argmax with ties to the lowest index (padding carries index INT_MAX, so it never wins a tie).
 constexpr int kNoIndex = 0x7fffffff;
 __device__ __forceinline__ bool argmax_better(float v1, int i1, float v2, int i2) {

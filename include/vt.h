@@ -185,8 +185,12 @@ size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
  *   Pages: as for the four calls above.
  *
  *   hidden bf16 [B*R][H] (row b*R + i is sequence b's i-th draft position); weight bf16 [V][H]
- *   (the full head); keep_ids int32 [Vt] and full_to_trim int32 [V] (both NULL iff the head is
- *   untrimmed, Vt == V); target_logits [B][gamma+1][V] (fp32 or bf16); u_draft fp32 [B*R],
+ *   (the full head); weight_tiled: NULL, or W^Trim in the K-tiled layout vt_trim_head_tiled makes
+ *   from this weight and keep_ids (vt_keepset.h), which the 256 x 256 head then reads in place of
+ *   gathering rows of weight (only when B*R >= 256, both sides are sampled and H % 32 == 0; ignored
+ *   otherwise; same products in the same order, so the same logits bits; the library cannot check
+ *   that it matches weight and keep_ids); keep_ids int32 [Vt] and full_to_trim int32 [V] (both
+ *   NULL iff the head is untrimmed, Vt == V); target_logits [B][gamma+1][V] (fp32 or bf16); u_draft fp32 [B*R],
  *   u_accept fp32 [B][gamma], u_final fp32 [B].
  *   Outputs: draft_logits fp32 [B*R][Vt], draft_lse fp64 [B*R], draft_ids int32 [B*R] (trimmed
  *   ids), target_lse fp64 [B*(gamma+1)], out_tokens int32 [B][gamma+1], out_num_accepted int32 [B].
@@ -211,10 +215,12 @@ size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
  *   Errors: INVALID_ARG for NULL required pointers, B, gamma, H, V or Vt <= 0, R < gamma, Vt > V,
  *   a temperature not finite or < 0, draft_T = 0 with target_T > 0, keep_ids/full_to_trim
  *   inconsistent with Vt; UNSUPPORTED for
- *   gamma > 64, H % 8 != 0 or a hidden/weight base not 16-byte aligned; WORKSPACE if the workspace
+ *   gamma > 64, H % 8 != 0, a hidden/weight/weight_tiled base not 16-byte aligned, weight_tiled
+ *   with H % 32 != 0; WORKSPACE if the workspace
  *   is smaller than vt_spec_block_workspace_bytes.
  */
-vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep_ids,
+vt_status_t vt_spec_block(const uint16_t *hidden, const uint16_t *weight, const uint16_t *weight_tiled,
+                          const int32_t *keep_ids,
                           const int32_t *full_to_trim, int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt,
                           int64_t V, const void *target_logits, vt_dtype_t target_dtype, float target_T,
                           float draft_T, const float *u_draft, const float *u_accept, const float *u_final,
@@ -240,7 +246,8 @@ size_t vt_spec_block_workspace_bytes(int64_t B, int64_t gamma, int64_t R, int64_
  *   its previous contents.  Errors: as vt_spec_block, plus VT_ERR_HIP if the device or the array's
  *   address cannot be queried, VT_ERR_UNSUPPORTED for a device index of 64 or more.
  */
-vt_status_t vt_spec_block_noalloc(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep_ids,
+vt_status_t vt_spec_block_noalloc(const uint16_t *hidden, const uint16_t *weight, const uint16_t *weight_tiled,
+                                  const int32_t *keep_ids,
                                   const int32_t *full_to_trim, int64_t B, int64_t gamma, int64_t R, int64_t H,
                                   int64_t Vt, int64_t V, const void *target_logits, vt_dtype_t target_dtype,
                                   float target_T, float draft_T, const float *u_draft, const float *u_accept,

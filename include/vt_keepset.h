@@ -85,6 +85,27 @@ vt_status_t vt_keep_select(const uint32_t *counts, int64_t V, vt_select_t rule, 
 vt_status_t vt_trim_head(const uint16_t *weight, int64_t V_rows, int64_t H, const int32_t *keep_ids, int64_t k,
                          uint16_t *trimmed, hipStream_t stream);
 
+/*
+ * vt_trim_head_tiled -- the same W^Trim ([VT] §3 Eq. 1, second line: the kept rows in keep_ids
+ * order), stored K-tiled for the large-batch LM head of vt_spec_block: row j = 256 b + r,
+ * columns 32 s .. 32 s + 31 sit at tiled[b][s][r][0 .. 31], so each 256-row, 32-column slice is
+ * one contiguous 16 KB run.  [VT] §3 builds W^Trim once, from calibration counts, before any
+ * decoding, so its storage layout is a free choice; this one is what the head's loads read fastest.
+ *
+ *   weight    bf16 bit patterns, row-major [V_rows][H], 16-byte aligned
+ *   keep_ids  int32 [k], or NULL for rows 0 .. k-1 (then k <= V_rows); an id outside [0, V_rows)
+ *             yields a zero row (nothing is read for it)
+ *   tiled     bf16 bit patterns, [ceil(k / 256)][H / 32][256][32], 16-byte aligned, written in
+ *             full (rows k .. 256 ceil(k / 256) - 1 are zeros): vt_trim_head_tiled_bytes(k, H) bytes
+ *   Errors: INVALID_ARG for NULL weight/tiled, V_rows, H or k <= 0, k > V_rows without keep_ids;
+ *   UNSUPPORTED for H % 32 != 0, an unaligned base, or k, V_rows >= 2^31.
+ */
+vt_status_t vt_trim_head_tiled(const uint16_t *weight, int64_t V_rows, int64_t H, const int32_t *keep_ids,
+                               int64_t k, uint16_t *tiled, hipStream_t stream);
+
+/* Bytes of the K-tiled W^Trim of k rows (0 when k or H <= 0 or H % 32 != 0). */
+size_t vt_trim_head_tiled_bytes(int64_t k, int64_t H);
+
 #ifdef __cplusplus
 }
 #endif

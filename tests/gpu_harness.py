@@ -77,21 +77,24 @@ def gpu_block(wl: Workload, probs: bool = False, device_inputs=None) -> dict:
     return out
 
 
-def gpu_block_fused(wl: Workload, events=None) -> dict:
-    """The same block through the single fused call vt_spec_block."""
+def gpu_block_fused(wl: Workload, events=None, tiled: bool = False) -> dict:
+    """The same block through the single fused call vt_spec_block (tiled: with the K-tiled W^Trim
+    of vt_trim_head_tiled, which the large-batch head reads instead of gathering rows)."""
     cfg = wl.cfg
     B, R, g = wl.B, cfg.R, cfg.gamma
     keep = dev(wl.keep_ids) if wl.keep_ids is not None else None
     f2t = dev(wl.full_to_trim) if wl.full_to_trim is not None else None
+    weight = dev_bf16(wl.weight)
+    wt = vt.vt_trim_head_tiled(weight, keep, k=cfg.Vt) if tiled else None
     logits = torch.empty(B * R, cfg.Vt, dtype=torch.float32, device="cuda")
     dlse = torch.empty(B * R, dtype=torch.float64, device="cuda")
     dids = torch.empty(B * R, dtype=torch.int32, device="cuda")
     tlse = torch.empty(B * (g + 1), dtype=torch.float64, device="cuda")
     tokens = torch.empty(B, g + 1, dtype=torch.int32, device="cuda")
     nacc = torch.empty(B, dtype=torch.int32, device="cuda")
-    vt.vt_spec_block(dev_bf16(wl.hidden), dev_bf16(wl.weight), keep, f2t, target_tensor(wl), wl.T, wl.T,
+    vt.vt_spec_block(dev_bf16(wl.hidden), weight, keep, f2t, target_tensor(wl), wl.T, wl.T,
                      dev(wl.u_draft.reshape(-1)), dev(wl.u_acc), dev(wl.u_fin), logits, dlse, dids, tlse, tokens, nacc,
-                     lmhead_events=events)
+                     lmhead_events=events, weight_tiled=wt)
     torch.cuda.synchronize()
     return dict(draft_logits=logits.cpu().numpy(), draft_lse=dlse.cpu().numpy(),
                 draft_ids=dids.cpu().numpy().reshape(B, R), target_lse=tlse.cpu().numpy().reshape(B, g + 1),

@@ -147,10 +147,10 @@ def test_missing_library_fails_loudly(tmp_path):
 
 # ------------------------------------------------------------------ vt_spec_block
 
-def blk(hidden=A, weight=A2, keep=A, f2t=A, B=4, gamma=5, R=6, H=3072, Vt=32768, V=128256, target=A, tdt=F32,
-        Tt=1.0, Td=1.0, ud=A, ua=A, uf=A, dl=A, dlse=A, ids=A, tlse=A, tok=A, nacc=A, ws=A2, wsb=1 << 30):
-    return vt.lib().vt_spec_block(hidden, weight, keep, f2t, B, gamma, R, H, Vt, V, target, tdt, Tt, Td, ud, ua, uf,
-                                  dl, dlse, ids, tlse, tok, nacc, NUL, NUL, ws, wsb, NUL)
+def blk(hidden=A, weight=A2, wt=NUL, keep=A, f2t=A, B=4, gamma=5, R=6, H=3072, Vt=32768, V=128256, target=A,
+        tdt=F32, Tt=1.0, Td=1.0, ud=A, ua=A, uf=A, dl=A, dlse=A, ids=A, tlse=A, tok=A, nacc=A, ws=A2, wsb=1 << 30):
+    return vt.lib().vt_spec_block(hidden, weight, wt, keep, f2t, B, gamma, R, H, Vt, V, target, tdt, Tt, Td, ud, ua,
+                                  uf, dl, dlse, ids, tlse, tok, nacc, NUL, NUL, ws, wsb, NUL)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -164,6 +164,7 @@ def blk(hidden=A, weight=A2, keep=A, f2t=A, B=4, gamma=5, R=6, H=3072, Vt=32768,
     (dict(Tt=0.0, ua=NUL, uf=NUL, tlse=NUL, ud=NUL), INV),  # sampled drafts still need u_draft
     (dict(keep=NUL, f2t=NUL), INV), (dict(keep=NUL), INV), (dict(f2t=NUL), INV),
     (dict(gamma=65, R=65), UNS), (dict(H=3070), UNS), (dict(hidden=P(0x100004)), UNS),
+    (dict(wt=P(0x100004)), UNS), (dict(wt=A, H=3080), UNS),  # the K-tiled head needs whole 32-column steps
     (dict(ws=NUL), WS), (dict(wsb=64), WS),
 ])
 def test_block_rejects(kw, status):
@@ -225,6 +226,27 @@ def trim(w=A, V=128256, H=3072, keep=A2, k=10, out=A):
 ])
 def test_trim_head_rejects(kw, status):
     assert trim(**kw) == status
+
+
+def trim_tiled(w=A, V=128256, H=3072, keep=A2, k=10, out=A):
+    return vt.lib().vt_trim_head_tiled(w, V, H, keep, k, out, NUL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=NUL), INV), (dict(out=NUL), INV), (dict(V=0), INV), (dict(H=0), INV), (dict(k=0), INV),
+    (dict(keep=NUL, k=128257), INV),  # rows 0..k-1 of the head need k <= V_rows
+    (dict(H=3080), UNS), (dict(w=P(0x100008)), UNS), (dict(out=P(0x100004)), UNS), (dict(k=1 << 31), UNS),
+])
+def test_trim_head_tiled_rejects(kw, status):
+    assert trim_tiled(**kw) == status
+
+
+def test_trim_head_tiled_bytes():
+    L = vt.lib()
+    assert L.vt_trim_head_tiled_bytes(65536, 4096) == 65536 * 4096 * 2
+    assert L.vt_trim_head_tiled_bytes(300, 64) == 512 * 64 * 2   # the last 256-row block is filled out
+    assert L.vt_trim_head_tiled_bytes(300, 80) == 0             # H % 32 != 0
+    assert L.vt_trim_head_tiled_bytes(0, 64) == 0
 
 
 # ------------------------------------------------------------------ generation loop

@@ -129,17 +129,42 @@ def test_fused_matches_separate_calls(name):
     assert same.mean() >= 0.95, same.mean()
 
 
+@pytest.mark.parametrize("name,order", [("c5-big-tiles", "id"), ("c5-big-tiles", "rank"),
+                                        ("c2-untrimmed-big-tiles", "id"), ("c5-big-tiles-one-chunk-target", "id")])
+def test_tiled_head_gives_the_same_block(name, order):
+    # the K-tiled W^Trim holds the same rows as the gather through keep_ids: every output, the
+    # logits included, must be the same bits (M = 288, ragged Vt = 6001 in the first two)
+    wl = make_workload(SCALED[name], keep_order=order)
+    say(f"tiled head vs gathered rows: {name}, keep order {order}")
+    a = gpu_block_fused(wl)
+    b = gpu_block_fused(wl, tiled=True)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("c", [4, 5])
+def test_tiled_head_gives_the_same_block_full_size(c):
+    wl = make_workload(CONFIGS[c])
+    say(f"tiled head vs gathered rows: full size config {c}")
+    a = gpu_block_fused(wl)
+    b = gpu_block_fused(wl, tiled=True)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
 @pytest.mark.parametrize("c,order,follow", [(2, "id", 0.0), (3, "id", 0.0), (4, "id", 0.0), (5, "id", 0.0),
                                             (3, "rank", 0.0), (3, "id", 0.5)])
 def test_fused_block_full_size(c, order, follow):
+    # configs 4 and 5 run as the benchmark times them: with the K-tiled W^Trim
     cfg = CONFIGS[c]
-    say(f"fused block full size config {c}, keep order {order}, following drafter {follow}")
+    tiled = c in (4, 5)
+    say(f"fused block full size config {c}, keep order {order}, following drafter {follow}, tiled head {tiled}")
     wl = make_workload(cfg, keep_order=order, follow=follow)
     ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     for e in ev:
         e.record()  # materialise the events
     torch.cuda.synchronize()
-    gpu = gpu_block_fused(wl, events=ev)
+    gpu = gpu_block_fused(wl, events=ev, tiled=tiled)
     say(f"  LM head inside the call: {ev[0].elapsed_time(ev[1]) * 1e3:.1f} us")
     assert ev[0].elapsed_time(ev[1]) > 0
     R = cfg.R

@@ -154,6 +154,46 @@ def test_trim_head_rows_and_out_of_range_ids():
     assert not got[~ok].any()
 
 
+def _k_tiled(trimmed: np.ndarray) -> np.ndarray:
+    """The K-tiled layout of vt_trim_head_tiled, written as a reshape: [ceil(k/256)][H/32][256][32],
+    rows past k zero."""
+    k, H = trimmed.shape
+    nb = -(-k // 256)
+    x = np.zeros((nb * 256, H), trimmed.dtype)
+    x[:k] = trimmed
+    return x.reshape(nb, 256, H // 32, 32).transpose(0, 2, 1, 3).reshape(-1)
+
+
+@pytest.mark.parametrize("k,rank_order", [(1001, False), (256, False), (700, True)])
+def test_trim_head_tiled_layout(k, rank_order):
+    rng = np.random.default_rng(37 + k)
+    V, H = 3000, 96  # three 32-column K steps; k = 1001 and 700 leave a ragged last row block
+    W = bf16_round(rng.standard_normal((V, H), dtype=np.float32))
+    keep = rng.choice(V, k, replace=False).astype(np.int32)
+    if not rank_order:
+        keep = np.sort(keep)
+    keep[[3, k - 1]] = [-1, V]  # not rows of W: zero rows
+    want_rows = np.zeros((k, H), np.uint16)
+    ok = (keep >= 0) & (keep < V)
+    want_rows[ok] = keepset.trim_head(W, keep[ok])
+    say(f"tiled W^Trim: V={V} H={H} k={k} rank order {rank_order}")
+    out = torch.full((vt.lib().vt_trim_head_tiled_bytes(k, H) // 2,), 7, dtype=torch.int16,
+                     device="cuda").view(torch.bfloat16)
+    vt.vt_trim_head_tiled(dev_bf16(W), dev(keep), tiled=out)
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, _k_tiled(want_rows))
+
+
+def test_trim_head_tiled_without_keep_ids():
+    rng = np.random.default_rng(43)
+    V, H, k = 600, 64, 300
+    W = bf16_round(rng.standard_normal((V, H), dtype=np.float32))
+    got = vt.vt_trim_head_tiled(dev_bf16(W), None, k=k)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.view(torch.int16).cpu().numpy().view(np.uint16), _k_tiled(W[:k]))
+
+
 def test_stream_to_trimmed_head_end_to_end():
     """Counter -> Top-K -> W^Trim on the GPU; the trimmed head scored without keep_ids gives the
     same logits as the full head gathered through keep_ids (Eq. 1), bit for bit."""

@@ -41,7 +41,7 @@ def _run(wl, noalloc):
     o = _outs(cfg, B)
     dt = 0 if cfg.target_dtype == "f32" else 1
     T = float(wl.T)
-    args = [_p(ins["hidden"]), _p(ins["weight"]), _p(ins["keep"]), _p(ins["f2t"]), B, cfg.gamma, cfg.R, cfg.H, cfg.Vt,
+    args = [_p(ins["hidden"]), _p(ins["weight"]), None, _p(ins["keep"]), _p(ins["f2t"]), B, cfg.gamma, cfg.R, cfg.H, cfg.Vt,
             cfg.V, _p(ins["target"]), dt, T, T, _p(ins["ud"]), _p(ins["ua"]), _p(ins["uf"]), _p(o["logits"]),
             _p(o["dlse"]), _p(o["dids"]), _p(o["tlse"]), _p(o["tok"]), _p(o["nacc"]), None, None]
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -88,6 +88,6 @@ def test_noalloc_rejects_shapes_beyond_the_scratch():
     assert L.vt_spec_block_workspace_bytes(B, g, R, H, Vt, V) > 64 << 20
     # rejected on the host before anything is enqueued: the pointers are never dereferenced
     fake = ctypes.c_void_p(256)
-    st = L.vt_spec_block_noalloc(fake, fake, fake, fake, B, g, R, H, Vt, V, fake, 1, 0.8, 0.8, fake, fake, fake,
+    st = L.vt_spec_block_noalloc(fake, fake, None, fake, fake, B, g, R, H, Vt, V, fake, 1, 0.8, 0.8, fake, fake, fake,
                                  fake, fake, fake, fake, fake, fake, None, None, None)
     assert st == VT_ERR_WORKSPACE
