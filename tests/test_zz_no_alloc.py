@@ -31,17 +31,19 @@ def _outs(cfg, B):
                 nacc=torch.full((B,), -5, dtype=torch.int32, device="cuda"))
 
 
-def _run(wl, noalloc):
+def _run(wl, noalloc, tiled=False):
+    """tiled: also hand over the K-tiled W^Trim (as the benchmark does for the large-batch head)."""
     cfg, B = wl.cfg, wl.B
     L = vt.lib()
     ins = dict(hidden=dev_bf16(wl.hidden), weight=dev_bf16(wl.weight),
                keep=dev(wl.keep_ids) if wl.keep_ids is not None else None,
                f2t=dev(wl.full_to_trim) if wl.full_to_trim is not None else None, target=target_tensor(wl),
                ud=dev(wl.u_draft.reshape(-1)), ua=dev(wl.u_acc), uf=dev(wl.u_fin))
+    wt = vt.vt_trim_head_tiled(ins["weight"], ins["keep"], k=cfg.Vt) if tiled else None
     o = _outs(cfg, B)
     dt = 0 if cfg.target_dtype == "f32" else 1
     T = float(wl.T)
-    args = [_p(ins["hidden"]), _p(ins["weight"]), None, _p(ins["keep"]), _p(ins["f2t"]), B, cfg.gamma, cfg.R, cfg.H, cfg.Vt,
+    args = [_p(ins["hidden"]), _p(ins["weight"]), _p(wt), _p(ins["keep"]), _p(ins["f2t"]), B, cfg.gamma, cfg.R, cfg.H, cfg.Vt,
             cfg.V, _p(ins["target"]), dt, T, T, _p(ins["ud"]), _p(ins["ua"]), _p(ins["uf"]), _p(o["logits"]),
             _p(o["dlse"]), _p(o["dids"]), _p(o["tlse"]), _p(o["tok"]), _p(o["nacc"]), None, None]
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -75,11 +77,12 @@ def test_noalloc_matches_block_on_two_calls(order):
 
 
 def test_noalloc_full_size_then_batch_one():
-    # the benchmark's large-drafter block (24.5 MiB of scratch) and then the batch-1 VocabTrim block
+    # the benchmark's large-drafter block (24.5 MiB of scratch, K-tiled W^Trim) and then the
+    # batch-1 VocabTrim block
     for c in (5, 3):
         wl = make_workload(CONFIGS[c])
         say(f"noalloc full size config {c}")
-        _same(_run(wl, noalloc=False), _run(wl, noalloc=True))
+        _same(_run(wl, noalloc=False, tiled=c == 5), _run(wl, noalloc=True, tiled=c == 5))
 
 
 def test_noalloc_rejects_shapes_beyond_the_scratch():
