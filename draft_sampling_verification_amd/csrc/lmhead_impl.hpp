@@ -63,8 +63,8 @@ __device__ __forceinline__ float half_wave_reduce(float v, Op op) {
 // lanes hold the same entries by then; 2 and 1: quad permutations) and halves the entries a lane
 // carries, each lane keeping the half its partner gives up: 62 exchanges for the 64 reductions
 // instead of 5 each.
-template <int CTRL, int BIT, int H, typename Op>
-__device__ __forceinline__ void scatter_step(float (&v)[64], Op op) {
+template <int CTRL, int BIT, int H, typename Op, int N>
+__device__ __forceinline__ void scatter_step(float (&v)[N], Op op) {
   const bool up = (lane_id() & BIT) != 0;
 #pragma unroll
   for (int k = 0; k < H; ++k) {
@@ -88,8 +88,8 @@ __device__ __forceinline__ void half_reduce_scatter(float (&v)[64], Op op) {
 }
 // The movement of half_reduce_scatter reversed: from v[k] = entry 2 (lane & 31) + k (k < 2),
 // every lane of the half ends with all 64 entries in order.
-template <int CTRL, int BIT, int H>
-__device__ __forceinline__ void gather_step(float (&v)[64]) {
+template <int CTRL, int BIT, int H, int N>
+__device__ __forceinline__ void gather_step(float (&v)[N]) {
   const bool up = (lane_id() & BIT) != 0;
 #pragma unroll
   for (int k = 0; k < H; ++k) {
@@ -921,23 +921,261 @@ __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_dma8(const uint16_t
                            reinterpret_cast<float2(*)[kBigBM]>(smem));
 }
 
+// Reduce-scatter of 16 per-lane entries over each half-wave (the steps of half_reduce_scatter at
+// lane distances 16, 8, 4 and 2, each halving what a lane carries, then a plain reduction with
+// the lane at distance 1): afterwards v[0] holds the reduction over the half's 32 lanes of entry
+// (lane & 31) >> 1.  16 exchanges.
+template <typename Op>
+__device__ __forceinline__ void half_reduce_scatter16(float (&v)[16], Op op) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    float a = v[k], b = v[k + 8];
+    swap16(a, b);
+    v[k] = op(a, b);
+  }
+  scatter_step<kDppRor8, 8, 4>(v, op);
+  scatter_step<kDppHalfMirror, 4, 2>(v, op);
+  scatter_step<kDppXor2, 2, 1>(v, op);
+  v[0] = op(v[0], lane_swap<kDppXor1>(v[0]));
+}
+
+// The movement of half_reduce_scatter16 reversed: from v[0] = entry (lane & 31) >> 1, every lane
+// of the half ends with all 16 entries in order.  15 exchanges.
+__device__ __forceinline__ void half_all_gather16(float (&v)[16]) {
+  gather_step<kDppXor2, 2, 1>(v);
+  gather_step<kDppHalfMirror, 4, 2>(v);
+  gather_step<kDppRor8, 8, 4>(v);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    float a = v[k], b = v[k];
+    swap16(a, b);
+    v[k] = a;
+    v[k + 8] = b;
+  }
+}
+
+// 384 x 256 output tiles (384 hidden rows x 256 head rows) for batches whose hidden rows fill
+// 384-row blocks at least as tightly as 256-row ones (the large-drafter shape: 2304 = 6 x 384).
+// Per K step a CU loads 640 rows x 64 bytes for 384 x 256 x 32 multiply-adds, a sixth fewer
+// bytes per flop than the 256 x 256 tile, which is what bounds the loop.  Eight waves of 96 x 128
+// (3 x 4 accumulator blocks, 192 registers), so the fragments of a 16-deep slice are read into a
+// single buffer (a second one spills); the other wave on the SIMD covers the read latency.  The
+// hidden rows come K-tiled in 384-row blocks (hidden_tiles with kTallBM rows); the head rows
+// either gathered through keep or K-tiled (BTILED); a four-slot ring of 40 KB slices fills the
+// 160 KB of LDS.  Each output element sums the same products in the same K order as the 256 x
+// 256 kernels, so the logits are the same bits.
+constexpr int kTallBM = 384;
+constexpr int kTallStages = 4;
+constexpr int kTallStageBytes = (kTallBM + kBigBN) * kDmaRowBytes;  // 40 KB
+
+// Epilogue of a 384 x 256 tile held by eight waves as 3 x 4 accumulator blocks each: the logits,
+// and with PARTS the draft softmax partials of the tile's 256 columns per hidden row.  Per row
+// block of a wave the 16 row maxima (over the wave's 128 columns) are reduce-scattered over the
+// half-wave, gathered back for the exponentials, and the sums reduce-scattered; the two waves
+// covering the same rows merge through LDS.  All threads of the workgroup must call.
+template <bool PARTS>
+__device__ __forceinline__ void tall_tile_store(const f32x16 (&acc)[3][4], int M, int Vt, int m0, int n0, int wm,
+                                                int wn, int nbn, int bn, float *__restrict__ logits,
+                                                const GemvParts &parts, float2 (*wpart)[kTallBM]) {
+  constexpr int kMI = 3, kNJ = 4, kSlots = 2;
+  const int tid = threadIdx.x, lane = lane_id(), lr = lane & 31;
+  const int slot = wn / 128;
+#pragma unroll
+  for (int i = 0; i < kMI; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int gm = m0 + wm + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (gm < M) {
+        float *dst = logits + static_cast<int64_t>(gm) * Vt;
+#pragma unroll
+        for (int j = 0; j < kNJ; ++j) {
+          const int gn = n0 + wn + j * 32 + lr;
+          if (gn < Vt) __builtin_nontemporal_store(acc[i][j][v], dst + gn);  // streamed out, not re-read here
+        }
+      }
+    }
+  if constexpr (PARTS) {
+    bool cin[kNJ];
+#pragma unroll
+    for (int j = 0; j < kNJ; ++j) cin[j] = n0 + wn + j * 32 + lr < Vt;
+    const auto fmax_op = [](float a, float b) { return fmaxf(a, b); };
+#pragma unroll
+    for (int i = 0; i < kMI; ++i) {
+      float mx[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float m = cin[0] ? acc[i][0][v] : kNegInf;
+#pragma unroll
+        for (int j = 1; j < kNJ; ++j) m = fmaxf(m, cin[j] ? acc[i][j][v] : kNegInf);
+        mx[v] = m;
+      }
+      half_reduce_scatter16(mx, fmax_op);
+      const float own_m = mx[0];
+      half_all_gather16(mx);
+      float sm[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        // a row with no column in range has max -inf: reference 0 there, so every term is exp2(-inf) = 0
+        const float ref = mx[v] == kNegInf ? 0.f : mx[v];
+        float t = 0.f;
+#pragma unroll
+        for (int j = 0; j < kNJ; ++j) t += __builtin_amdgcn_exp2f(((cin[j] ? acc[i][j][v] : kNegInf) - ref) * parts.k2);
+        sm[v] = t;
+      }
+      half_reduce_scatter16(sm, [](float a, float b) { return a + b; });
+      if ((lane & 1) == 0) {
+        const int e = lr >> 1;
+        wpart[slot][wm + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)] = make_float2(own_m, sm[0]);
+      }
+    }
+    __syncthreads();
+    const int r = tid;  // one thread per row of the tile
+    const int gm = m0 + r;
+    if (r < kTallBM && gm < M) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int k = 0; k < kSlots; ++k) mx = fmaxf(mx, wpart[k][r].x);
+      float sm = 0.f;
+#pragma unroll
+      for (int k = 0; k < kSlots; ++k) {
+        const float2 p = wpart[k][r];
+        if (p.x != kNegInf) sm += p.y * __builtin_amdgcn_exp2f((p.x - mx) * parts.k2);
+      }
+      parts.part[static_cast<int64_t>(gm) * nbn + bn] = make_float2(mx, sm);
+    }
+  }
+}
+
+template <bool TRIM, bool PARTS, bool BTILED>
+__global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_tall(const uint16_t *__restrict__ hidden,
+                                                                  const uint16_t *__restrict__ weight,
+                                                                  const int32_t *__restrict__ keep, int vrows, int M,
+                                                                  int H, int Vt, float *__restrict__ logits,
+                                                                  GemvParts parts) {
+  static_assert(!(BTILED && TRIM), "a K-tiled head is already trimmed");
+  constexpr int kMI = 3, kNJ = 4;           // accumulator blocks per wave
+  constexpr int kLA = kTallBM / 128;        // 1 KB hidden-row loads per wave per step
+  constexpr int kLoads = kLA + 2;           // and two of head rows
+  constexpr int kOpA = kTallBM * kDmaRowBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[kTallStages * kTallStageBytes];
+  const int nbm = (M + kTallBM - 1) / kTallBM;
+  const int nbn = (Vt + kBigBN - 1) / kBigBN;
+  const int tile = static_cast<int>(xcd_remap(blockIdx.x, static_cast<int64_t>(nbm) * nbn));
+  int bm, bn;
+  big_tile_of(tile, nbm, nbn, bm, bn);
+  const int m0 = bm * kTallBM, n0 = bn * kBigBN;
+  const int w = wave_id(), lane = lane_id();
+  const int nk = H / kDmaBK;
+
+  // loads: wave w fills hidden chunks 3 w + j (tile rows 16 (3 w + j) + lane / 4) and head chunks
+  // 2 w + j.  Rows r and r + 32 share their swizzle, r + 16 does not: the hidden rows take one
+  // source pointer (at row ra, with the swizzle of row ra + 16 p) for the even chunks and one for
+  // the odd chunk, offset by 16 j rows when issued; each head chunk has its own.
+  const int ra = 16 * (kLA * w) + (lane >> 2), rb = 16 * (2 * w) + (lane >> 2);
+  const uint16_t *asrc[2], *bsrc[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    asrc[p] = hidden + (static_cast<int64_t>(bm) * nk * kTallBM + ra) * kDmaBK +
+              ((lane & 3) ^ dma_swz(ra + 16 * p)) * 8;
+    const int q = rb + 16 * p;
+    const int piece = (lane & 3) ^ dma_swz(q);
+    if (BTILED) {
+      bsrc[p] = weight + (static_cast<int64_t>(bn) * nk * kBigBN + q) * kDmaBK + piece * 8;
+    } else {
+      const int n = min(n0 + q, Vt - 1);
+      const int64_t brow = TRIM ? kept_row(keep, n, vrows) : static_cast<int64_t>(n);
+      bsrc[p] = weight + brow * H + piece * 8;
+    }
+  }
+  auto issue = [&](int kstep, int slot) {
+    const int k = min(kstep, nk - 1);
+    const int64_t ka = static_cast<int64_t>(k) * kTallBM * kDmaBK;
+    const int64_t kb = BTILED ? static_cast<int64_t>(k) * kBigBN * kDmaBK : static_cast<int64_t>(k) * kDmaBK;
+    char *base = smem + slot * kTallStageBytes;
+#pragma unroll
+    for (int j = 0; j < kLA; ++j)
+      __builtin_amdgcn_global_load_lds(asrc[j & 1] + ka + j * 16 * kDmaBK, (lds_void *)(base + (kLA * w + j) * 1024),
+                                       16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_global_load_lds(bsrc[j] + kb, (lds_void *)(base + kOpA + (2 * w + j) * 1024), 16, 0, 0);
+  };
+
+  const int wm = (w >> 1) * 96, wn = (w & 1) * 128;
+  const int lr = lane & 31;
+  const int sw = dma_swz(lr);
+  const int off0 = lr * kDmaRowBytes + (((lane >> 5) ^ sw) << 4);
+  const int off1 = lr * kDmaRowBytes + (((2 + (lane >> 5)) ^ sw) << 4);
+  f32x16 acc[kMI][kNJ];
+#pragma unroll
+  for (int i = 0; i < kMI; ++i)
+#pragma unroll
+    for (int j = 0; j < kNJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  bf16x8 a[kMI], b[kNJ];
+  auto slice = [&](int slot, int off) {
+    const char *sa = smem + slot * kTallStageBytes + wm * kDmaRowBytes + off;
+    const char *sb = smem + slot * kTallStageBytes + kOpA + wn * kDmaRowBytes + off;
+#pragma unroll
+    for (int i = 0; i < kMI; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(sa + i * 32 * kDmaRowBytes);
+#pragma unroll
+    for (int j = 0; j < kNJ; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(sb + j * 32 * kDmaRowBytes);
+#pragma unroll
+    for (int i = 0; i < kMI; ++i)
+#pragma unroll
+      for (int j = 0; j < kNJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  };
+
+  // step k: both 16-deep slices of slot k % 4; then (wait + barrier) step k + 1 is in LDS and the
+  // slot of step k - 1 is free, and the loads of step k + 3 go into it; past the last step the last
+  // step is fetched again into the free slot (never read), so every step issues the same loads
+  constexpr int kAhead = kTallStages - 1;
+#pragma unroll
+  for (int s = 0; s < kAhead; ++s) issue(s, s);
+  wait_vmcnt<kLoads * (kAhead - 1)>();
+  __builtin_amdgcn_s_barrier();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int slot = kt % kTallStages;
+    slice(slot, off0);
+    slice(slot, off1);
+    wait_vmcnt<kLoads * (kAhead - 2)>();
+    __builtin_amdgcn_s_barrier();
+    issue(kt + kAhead, (kt + kAhead) % kTallStages);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  tall_tile_store<PARTS>(acc, M, Vt, m0, n0, wm, wn, nbn, bn, logits, parts,
+                         reinterpret_cast<float2(*)[kTallBM]>(smem));
+}
+
 inline int64_t mfma_big_tiles_n(int64_t Vt) { return (Vt + kBigBN - 1) / kBigBN; }
 
-// K-tiled copy of the hidden rows for lmhead_mfma_dma8<..., ATILED>: out[bm][ks][r][32] =
-// hidden[min(256 bm + r, M - 1)][32 ks .. 32 ks + 31] (rows past M repeat the last row; their
-// logits are never stored).  One thread moves one 16-byte piece; a wave reads 16 rows x 64 bytes
-// and writes 1 KB contiguously.  Needs H % 32 == 0.
-// Bytes of the K-tiled hidden copy (0 when the direct-to-LDS kernel does not run).
+// Rows per hidden-row block of the large-batch head that reads a K-tiled copy: 384 (the tall
+// tiles) when padding M to 384-row blocks adds no more rows than padding it to 256-row blocks
+// (2304 = 6 x 384 = 9 x 256), else 256.
+inline int big_tile_rows(int64_t M) {
+  const int64_t p384 = (M + kTallBM - 1) / kTallBM * kTallBM, p256 = (M + kBigBM - 1) / kBigBM * kBigBM;
+  return p384 <= p256 ? kTallBM : kBigBM;
+}
+
+// K-tiled copy of the hidden rows for lmhead_mfma_dma8<..., ATILED> and lmhead_mfma_tall, in
+// blocks of R = big_tile_rows(M) rows: out[bm][ks][r][32] = hidden[min(R bm + r, M - 1)][32 ks ..
+// 32 ks + 31] (rows past M repeat the last row; their logits are never stored).  One thread moves
+// one 16-byte piece; a wave reads 16 rows x 64 bytes and writes 1 KB contiguously.  Needs
+// H % 32 == 0.
+// Bytes of the K-tiled hidden copy (0 when the direct-to-LDS kernels do not run).
 inline size_t hidden_tiles_bytes(int64_t M, int64_t H) {
   if (M < kBigMinM || H % kDmaBK != 0) return 0;
-  return tiled_rows_bytes(M, H);
+  const int64_t R = big_tile_rows(M);
+  return static_cast<size_t>((M + R - 1) / R) * R * static_cast<size_t>(H) * 2;
 }
 
 struct TileParams {
   const uint16_t *hidden;
   uint16_t *out;
   int64_t pieces;
-  int M, H;
+  int M, H, rows;  // rows: rows per block of the copy
 };
 
 // Workgroup `blk` of the copy (kBlock pieces).
@@ -948,12 +1186,12 @@ __device__ __forceinline__ void hidden_tiles_block(const TileParams &T, int64_t 
   if (q >= T.pieces) return;
   const int p = static_cast<int>(q & 3);
   const int64_t rr = q >> 2;  // (bm, ks, r) flattened
-  const int r = static_cast<int>(rr % kBigBM);
-  const int64_t bk = rr / kBigBM;
+  const int r = static_cast<int>(rr % T.rows);
+  const int64_t bk = rr / T.rows;
   const int nk = H / kDmaBK;
   const int ks = static_cast<int>(bk % nk);
   const int bm = static_cast<int>(bk / nk);
-  const int m = min(bm * kBigBM + r, M - 1);
+  const int m = min(bm * T.rows + r, M - 1);
   const uint4 v = *reinterpret_cast<const uint4 *>(hidden + static_cast<int64_t>(m) * H + ks * kDmaBK + p * 8);
   *reinterpret_cast<uint4 *>(T.out + q * 8) = v;
 }
@@ -964,6 +1202,7 @@ inline TileParams hidden_tiles_params(const uint16_t *hidden, int64_t M, int64_t
   T.out = out;
   T.M = static_cast<int>(M);
   T.H = static_cast<int>(H);
+  T.rows = big_tile_rows(M);
   T.pieces = static_cast<int64_t>(hidden_tiles_bytes(M, H) / 16);
   return T;
 }
@@ -988,15 +1227,26 @@ __global__ __launch_bounds__(kBlock) void softmax_partial_tiles(SmParams P, Tile
 
 
 
-// hidden_tiled: NULL, or the K-tiled copy of the hidden rows made by hidden_tiles (H % 32 == 0);
-// weight_tiled: NULL, or the K-tiled trimmed head of vt_trim_head_tiled (read only together with
-// hidden_tiled; weight and keep are then not read by the kernel).
+// hidden_tiled: NULL, or the K-tiled copy of the hidden rows made by hidden_tiles (H % 32 == 0),
+// in blocks of big_tile_rows(M) rows: 384-row blocks select the tall tiles (with PARTS, the
+// fused block's head); weight_tiled: NULL, or the K-tiled trimmed head of vt_trim_head_tiled
+// (read only together with hidden_tiled; weight and keep are then not read by the kernel).
 template <bool PARTS>
 inline hipError_t launch_mfma_big(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int vrows,
                                   int64_t M, int64_t H, int64_t Vt, float *logits, GemvParts parts,
                                   hipStream_t stream, const uint16_t *hidden_tiled = nullptr,
                                   const uint16_t *weight_tiled = nullptr) {
   const int64_t tiles = ((M + kBigBM - 1) / kBigBM) * mfma_big_tiles_n(Vt);
+  if (!PARTS && hidden_tiled && big_tile_rows(M) != kBigBM) return hipErrorInvalidValue;  // no tall kernel without PARTS
+  if constexpr (PARTS) {
+    if (hidden_tiled && H % kDmaBK == 0 && big_tile_rows(M) == kTallBM) {
+      const unsigned tall = static_cast<unsigned>(((M + kTallBM - 1) / kTallBM) * mfma_big_tiles_n(Vt));
+      auto f = weight_tiled ? &lmhead_mfma_tall<false, true, true>
+                            : (keep ? &lmhead_mfma_tall<true, true, false> : &lmhead_mfma_tall<false, true, false>);
+      return launch(f, dim3(tall), dim3(kDma8Block), 0, stream, hidden_tiled, weight_tiled ? weight_tiled : weight,
+                    keep, vrows, static_cast<int>(M), static_cast<int>(H), static_cast<int>(Vt), logits, parts);
+    }
+  }
   if (H % kDmaBK == 0) {
     if (hidden_tiled && weight_tiled)
       return launch(lmhead_mfma_dma8<false, PARTS, true, true>, dim3(static_cast<unsigned>(tiles)), dim3(kDma8Block),

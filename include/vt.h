@@ -179,14 +179,16 @@ size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
  * one final pass draws the last token.  Larger batches take 5 (LM head with the draft partials,
  * target partials, one combine launch for both row sets, two verify passes).  When B*R >= 256 and
  * H % 32 == 0 the target partials launch also copies the hidden rows K-tiled into the workspace
- * (the head then reads each K step of a 256-row block as one contiguous run; same products, same
- * logits); without target partials (V <= 4096 or greedy verification) the copy is a launch of its
- * own.
+ * (the head then reads each K step of a block of hidden rows as one contiguous run; same products,
+ * same logits); without target partials (V <= 4096 or greedy verification) the copy is a launch of
+ * its own.  With sampled drafts that head takes 384 x 256 tiles (384 hidden rows) when padding
+ * B*R to 384-row blocks adds no more rows than padding it to 256-row blocks (B*R = 2304, 288,
+ * 756 ...), else 256 x 256 tiles (B*R = 512 ...); both sum the same products in the same order.
  *   Pages: as for the four calls above.
  *
  *   hidden bf16 [B*R][H] (row b*R + i is sequence b's i-th draft position); weight bf16 [V][H]
  *   (the full head); weight_tiled: NULL, or W^Trim in the K-tiled layout vt_trim_head_tiled makes
- *   from this weight and keep_ids (vt_keepset.h), which the 256 x 256 head then reads in place of
+ *   from this weight and keep_ids (vt_keepset.h), which the large-batch head then reads in place of
  *   gathering rows of weight (only when B*R >= 256, both sides are sampled and H % 32 == 0; ignored
  *   otherwise; same products in the same order, so the same logits bits; the library cannot check
  *   that it matches weight and keep_ids); keep_ids int32 [Vt] and full_to_trim int32 [V] (both

@@ -24,6 +24,10 @@ SCALED = {
     "c2-untrimmed-big-tiles": CONFIGS[2].scaled(B=48, V=6000, Vt=6000, H=256),
     # 256+ hidden rows with a one-chunk target row: the hidden copy takes a launch of its own
     "c5-big-tiles-one-chunk-target": CONFIGS[5].scaled(B=32, V=4000, Vt=1500, H=256),
+    # the head's row blocks: 288 and 756 hidden rows take 384-row tiles (one block; two, the
+    # second ragged), 512 takes 256-row tiles (two blocks; 384-row blocks would pad to 768)
+    "c5-tall-two-blocks": CONFIGS[5].scaled(B=84, V=13000, Vt=6001, H=256),
+    "c4-square-two-blocks": CONFIGS[4].scaled(B=64, V=20000, Vt=5000, H=256),
 }
 
 
@@ -115,10 +119,13 @@ def test_fused_block_rank_ordered_keep_set(name):
     _check(make_workload(SCALED[name], keep_order="rank"))
 
 
-@pytest.mark.parametrize("name", ["c3-trimmed", "c4-batched-mfma", "c4-big-tiles", "c5-big-tiles"])
+@pytest.mark.parametrize("name", ["c3-trimmed", "c4-batched-mfma", "c4-big-tiles", "c5-big-tiles",
+                                  "c5-tall-two-blocks", "c4-square-two-blocks"])
 def test_fused_matches_separate_calls(name):
-    # c5-big-tiles (M = 288, H = 256): the fused call's head reads a K-tiled copy of the hidden
-    # rows, the separate call reads them row-major; the logits must still be the same bits
+    # c5-big-tiles (M = 288, H = 256) and c5-tall-two-blocks (M = 756): the fused call's head runs
+    # 384 x 256 tiles on a K-tiled copy of the hidden rows, the separate call 256 x 256 tiles on
+    # the rows as given; c4-square-two-blocks (M = 512): 256 x 256 tiles on both; the logits must
+    # be the same bits
     wl = make_workload(SCALED[name])
     a = gpu_block(wl)
     b = gpu_block_fused(wl)
@@ -130,7 +137,8 @@ def test_fused_matches_separate_calls(name):
 
 
 @pytest.mark.parametrize("name,order", [("c5-big-tiles", "id"), ("c5-big-tiles", "rank"),
-                                        ("c2-untrimmed-big-tiles", "id"), ("c5-big-tiles-one-chunk-target", "id")])
+                                        ("c2-untrimmed-big-tiles", "id"), ("c5-big-tiles-one-chunk-target", "id"),
+                                        ("c5-tall-two-blocks", "id"), ("c4-square-two-blocks", "id")])
 def test_tiled_head_gives_the_same_block(name, order):
     # the K-tiled W^Trim holds the same rows as the gather through keep_ids: every output, the
     # logits included, must be the same bits (M = 288, ragged Vt = 6001 in the first two)
