@@ -57,12 +57,10 @@ __device__ __forceinline__ float half_wave_reduce(float v, Op op) {
   return op(a, b);
 }
 
-// Reduce-scatter over each half-wave of 64 per-lane entries: afterwards v[k], k < 2, holds the
-// reduction over the half's 32 lanes of entry 2 (lane & 31) + k.  Each step pairs the lanes at
-// one distance (16: row swap; 8: rotation of the row by 8; 4: mirror of each group of 8, whose
-// lanes hold the same entries by then; 2 and 1: quad permutations) and halves the entries a lane
-// carries, each lane keeping the half its partner gives up: 62 exchanges for the 64 reductions
-// instead of 5 each.
+// One step of a reduce-scatter over a half-wave: the lanes at one distance (16: row swap; 8:
+// rotation of the row by 8; 4: mirror of each group of 8, whose lanes hold the same entries by
+// then; 2 and 1: quad permutations) pair up and each keeps the half of its N entries that its
+// partner gives up, reduced with the partner's copy.
 template <int CTRL, int BIT, int H, typename Op, int N>
 __device__ __forceinline__ void scatter_step(float (&v)[N], Op op) {
   const bool up = (lane_id() & BIT) != 0;
@@ -73,21 +71,7 @@ __device__ __forceinline__ void scatter_step(float (&v)[N], Op op) {
     v[k] = op(keep, lane_swap<CTRL>(send));
   }
 }
-template <typename Op>
-__device__ __forceinline__ void half_reduce_scatter(float (&v)[64], Op op) {
-#pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    float a = v[k], b = v[k + 32];
-    swap16(a, b);
-    v[k] = op(a, b);
-  }
-  scatter_step<kDppRor8, 8, 16>(v, op);
-  scatter_step<kDppHalfMirror, 4, 8>(v, op);
-  scatter_step<kDppXor2, 2, 4>(v, op);
-  scatter_step<kDppXor1, 1, 2>(v, op);
-}
-// The movement of half_reduce_scatter reversed: from v[k] = entry 2 (lane & 31) + k (k < 2),
-// every lane of the half ends with all 64 entries in order.
+// The movement of scatter_step reversed: each lane ends with its own H entries and its partner's.
 template <int CTRL, int BIT, int H, int N>
 __device__ __forceinline__ void gather_step(float (&v)[N]) {
   const bool up = (lane_id() & BIT) != 0;
@@ -99,17 +83,37 @@ __device__ __forceinline__ void gather_step(float (&v)[N]) {
     v[k + H] = up ? mine : other;
   }
 }
-__device__ __forceinline__ void half_all_gather(float (&v)[64]) {
-  gather_step<kDppXor1, 1, 2>(v);
-  gather_step<kDppXor2, 2, 4>(v);
-  gather_step<kDppHalfMirror, 4, 8>(v);
-  gather_step<kDppRor8, 8, 16>(v);
+
+// Reduce-scatter of 16 per-lane entries over each half-wave (the steps of half_reduce_scatter at
+// lane distances 16, 8, 4 and 2, each halving what a lane carries, then a plain reduction with
+// the lane at distance 1): afterwards v[0] holds the reduction over the half's 32 lanes of entry
+// (lane & 31) >> 1.  16 exchanges.
+template <typename Op>
+__device__ __forceinline__ void half_reduce_scatter16(float (&v)[16], Op op) {
 #pragma unroll
-  for (int k = 0; k < 32; ++k) {
+  for (int k = 0; k < 8; ++k) {
+    float a = v[k], b = v[k + 8];
+    swap16(a, b);
+    v[k] = op(a, b);
+  }
+  scatter_step<kDppRor8, 8, 4>(v, op);
+  scatter_step<kDppHalfMirror, 4, 2>(v, op);
+  scatter_step<kDppXor2, 2, 1>(v, op);
+  v[0] = op(v[0], lane_swap<kDppXor1>(v[0]));
+}
+
+// The movement of half_reduce_scatter16 reversed: from v[0] = entry (lane & 31) >> 1, every lane
+// of the half ends with all 16 entries in order.  15 exchanges.
+__device__ __forceinline__ void half_all_gather16(float (&v)[16]) {
+  gather_step<kDppXor2, 2, 1>(v);
+  gather_step<kDppHalfMirror, 4, 2>(v);
+  gather_step<kDppRor8, 8, 4>(v);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
     float a = v[k], b = v[k];
     swap16(a, b);
     v[k] = a;
-    v[k + 32] = b;
+    v[k + 8] = b;
   }
 }
 
@@ -550,23 +554,28 @@ __device__ __forceinline__ void big_tile_of(int tile, int nbm, int nbn, int &bm,
   bn = in / rows;
 }
 
-// Epilogue of a 256 x 256 tile held by four waves as 4 x 4 accumulators each: the logits, and
-// with PARTS the draft softmax partials of the tile's 256 columns per hidden row.  All threads of
-// the workgroup must call.
-// wpart: LDS scratch of 2 x 256 float2 that the caller no longer needs (its operand tiles), so
+// Epilogue of a TM x 256 tile (TM hidden rows x 256 head rows) whose waves hold MI x NJ
+// accumulator blocks of 32 x 32 each: the logits, and with PARTS the draft softmax partials of
+// the tile's 256 columns per hidden row (max and sum of 2^((x - max) k2)).  Per row block of a
+// wave the 16 row maxima over the wave's 32 NJ columns are reduce-scattered over the half-wave
+// (a lane holds 16 rows of its half in each block), gathered back for the exponentials, and the
+// sums reduce-scattered: 47 lane exchanges per block, 16 maxima and sums in registers at a time.
+// The 256 / (32 NJ) waves that cover the same rows merge through LDS.  All threads of the
+// workgroup must call.
+// wpart: LDS scratch of kSlots x TM float2 that the caller no longer needs (its operand tiles), so
 // that the kernel keeps a single LDS object (a second one makes the compiler wait for every
 // outstanding direct-to-LDS load before any LDS read in the main loop).
-template <bool PARTS, int NJ = 4>
-__device__ __forceinline__ void big_tile_store(const f32x16 (&acc)[4][NJ], int M, int Vt, int m0, int n0, int wm,
-                                               int wn, int nbn, int bn, float *__restrict__ logits,
-                                               const GemvParts &parts, float2 (*wpart)[kBigBM]) {
+template <bool PARTS, int MI, int NJ, int TM>
+__device__ __forceinline__ void tile_store(const f32x16 (&acc)[MI][NJ], int M, int Vt, int m0, int n0, int wm,
+                                           int wn, int nbn, int bn, float *__restrict__ logits,
+                                           const GemvParts &parts, float2 (*wpart)[TM]) {
   constexpr int kSlots = kBigBN / (32 * NJ);  // waves covering the same tile rows
   const int tid = threadIdx.x, lane = lane_id(), lr = lane & 31;
   const int slot = wn / (32 * NJ);
   // 32x32 accumulator layout: lane l holds column l % 32; register v holds row
   // 8 * (v / 4) + 4 * (l / 32) + v % 4.
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int gm = m0 + wm + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
@@ -580,51 +589,43 @@ __device__ __forceinline__ void big_tile_store(const f32x16 (&acc)[4][NJ], int M
       }
     }
   if constexpr (PARTS) {
-    // per hidden row: max and sum of exp2((x - max) k2) over this wave's 32 NJ columns.  A lane
-    // holds 64 rows (entry e = 16 i + v) of its half-wave's rows; their maxima are reduced over
-    // the half's 32 lanes by a reduce-scatter and gathered back for the exponentials, the sums
-    // reduced by a second reduce-scatter; lane l then owns entries 2 (l & 31) + k and writes them
-    // for the merge with the other waves covering the same rows.
     bool cin[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) cin[j] = n0 + wn + j * 32 + lr < Vt;
-    float mx[64];
+    const auto fmax_op = [](float a, float b) { return fmaxf(a, b); };
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i) {
+      float mx[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         float m = cin[0] ? acc[i][0][v] : kNegInf;
 #pragma unroll
         for (int j = 1; j < NJ; ++j) m = fmaxf(m, cin[j] ? acc[i][j][v] : kNegInf);
-        mx[16 * i + v] = m;
+        mx[v] = m;
       }
-    const auto fmax_op = [](float a, float b) { return fmaxf(a, b); };
-    half_reduce_scatter(mx, fmax_op);
-    const float own_m[2] = {mx[0], mx[1]};
-    half_all_gather(mx);
-    float sm[64];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
+      half_reduce_scatter16(mx, fmax_op);
+      const float own_m = mx[0];
+      half_all_gather16(mx);
+      float sm[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         // a row with no column in range has max -inf: reference 0 there, so every term is exp2(-inf) = 0
-        const float ref = mx[16 * i + v] == kNegInf ? 0.f : mx[16 * i + v];
+        const float ref = mx[v] == kNegInf ? 0.f : mx[v];
         float t = 0.f;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          t += __builtin_amdgcn_exp2f(((cin[j] ? acc[i][j][v] : kNegInf) - ref) * parts.k2);
-        sm[16 * i + v] = t;
+        for (int j = 0; j < NJ; ++j) t += __builtin_amdgcn_exp2f(((cin[j] ? acc[i][j][v] : kNegInf) - ref) * parts.k2);
+        sm[v] = t;
       }
-    half_reduce_scatter(sm, [](float a, float b) { return a + b; });
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int e = 2 * lr + k, i = e >> 4, v = e & 15;
-      wpart[slot][wm + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)] = make_float2(own_m[k], sm[k]);
+      half_reduce_scatter16(sm, [](float a, float b) { return a + b; });
+      if ((lane & 1) == 0) {  // lanes l and l ^ 1 hold the same row
+        const int e = lr >> 1;
+        wpart[slot][wm + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)] = make_float2(own_m, sm[0]);
+      }
     }
     __syncthreads();
     const int r = tid;  // one thread per row of the tile
     const int gm = m0 + r;
-    if (r < kBigBM && gm < M) {
+    if (r < TM && gm < M) {
       float mx = kNegInf;
 #pragma unroll
       for (int k = 0; k < kSlots; ++k) mx = fmaxf(mx, wpart[k][r].x);
@@ -760,7 +761,7 @@ __global__ __launch_bounds__(kBlock, 1) void lmhead_mfma_big(const uint16_t *__r
     __syncthreads();
   }
 
-  big_tile_store<PARTS>(acc, M, Vt, m0, n0, wm, wn, nbn, bn, logits, parts,
+  tile_store<PARTS, 4, 4, kBigBM>(acc, M, Vt, m0, n0, wm, wn, nbn, bn, logits, parts,
                         reinterpret_cast<float2(*)[kBigBM]>(&smem[0][0]));
 }
 
@@ -917,41 +918,8 @@ __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_dma8(const uint16_t
   }
   wait_vmcnt<0>();
   __syncthreads();
-  big_tile_store<PARTS, 2>(acc, M, Vt, m0, n0, wm, wn, nbn, bn, logits, parts,
+  tile_store<PARTS, 4, 2, kBigBM>(acc, M, Vt, m0, n0, wm, wn, nbn, bn, logits, parts,
                            reinterpret_cast<float2(*)[kBigBM]>(smem));
-}
-
-// Reduce-scatter of 16 per-lane entries over each half-wave (the steps of half_reduce_scatter at
-// lane distances 16, 8, 4 and 2, each halving what a lane carries, then a plain reduction with
-// the lane at distance 1): afterwards v[0] holds the reduction over the half's 32 lanes of entry
-// (lane & 31) >> 1.  16 exchanges.
-template <typename Op>
-__device__ __forceinline__ void half_reduce_scatter16(float (&v)[16], Op op) {
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    float a = v[k], b = v[k + 8];
-    swap16(a, b);
-    v[k] = op(a, b);
-  }
-  scatter_step<kDppRor8, 8, 4>(v, op);
-  scatter_step<kDppHalfMirror, 4, 2>(v, op);
-  scatter_step<kDppXor2, 2, 1>(v, op);
-  v[0] = op(v[0], lane_swap<kDppXor1>(v[0]));
-}
-
-// The movement of half_reduce_scatter16 reversed: from v[0] = entry (lane & 31) >> 1, every lane
-// of the half ends with all 16 entries in order.  15 exchanges.
-__device__ __forceinline__ void half_all_gather16(float (&v)[16]) {
-  gather_step<kDppXor2, 2, 1>(v);
-  gather_step<kDppHalfMirror, 4, 2>(v);
-  gather_step<kDppRor8, 8, 4>(v);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    float a = v[k], b = v[k];
-    swap16(a, b);
-    v[k] = a;
-    v[k + 8] = b;
-  }
 }
 
 // 384 x 256 output tiles (384 hidden rows x 256 head rows) for batches whose hidden rows fill
@@ -967,84 +935,6 @@ __device__ __forceinline__ void half_all_gather16(float (&v)[16]) {
 constexpr int kTallBM = 384;
 constexpr int kTallStages = 4;
 constexpr int kTallStageBytes = (kTallBM + kBigBN) * kDmaRowBytes;  // 40 KB
-
-// Epilogue of a 384 x 256 tile held by eight waves as 3 x 4 accumulator blocks each: the logits,
-// and with PARTS the draft softmax partials of the tile's 256 columns per hidden row.  Per row
-// block of a wave the 16 row maxima (over the wave's 128 columns) are reduce-scattered over the
-// half-wave, gathered back for the exponentials, and the sums reduce-scattered; the two waves
-// covering the same rows merge through LDS.  All threads of the workgroup must call.
-template <bool PARTS>
-__device__ __forceinline__ void tall_tile_store(const f32x16 (&acc)[3][4], int M, int Vt, int m0, int n0, int wm,
-                                                int wn, int nbn, int bn, float *__restrict__ logits,
-                                                const GemvParts &parts, float2 (*wpart)[kTallBM]) {
-  constexpr int kMI = 3, kNJ = 4, kSlots = 2;
-  const int tid = threadIdx.x, lane = lane_id(), lr = lane & 31;
-  const int slot = wn / 128;
-#pragma unroll
-  for (int i = 0; i < kMI; ++i)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int gm = m0 + wm + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (gm < M) {
-        float *dst = logits + static_cast<int64_t>(gm) * Vt;
-#pragma unroll
-        for (int j = 0; j < kNJ; ++j) {
-          const int gn = n0 + wn + j * 32 + lr;
-          if (gn < Vt) __builtin_nontemporal_store(acc[i][j][v], dst + gn);  // streamed out, not re-read here
-        }
-      }
-    }
-  if constexpr (PARTS) {
-    bool cin[kNJ];
-#pragma unroll
-    for (int j = 0; j < kNJ; ++j) cin[j] = n0 + wn + j * 32 + lr < Vt;
-    const auto fmax_op = [](float a, float b) { return fmaxf(a, b); };
-#pragma unroll
-    for (int i = 0; i < kMI; ++i) {
-      float mx[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float m = cin[0] ? acc[i][0][v] : kNegInf;
-#pragma unroll
-        for (int j = 1; j < kNJ; ++j) m = fmaxf(m, cin[j] ? acc[i][j][v] : kNegInf);
-        mx[v] = m;
-      }
-      half_reduce_scatter16(mx, fmax_op);
-      const float own_m = mx[0];
-      half_all_gather16(mx);
-      float sm[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        // a row with no column in range has max -inf: reference 0 there, so every term is exp2(-inf) = 0
-        const float ref = mx[v] == kNegInf ? 0.f : mx[v];
-        float t = 0.f;
-#pragma unroll
-        for (int j = 0; j < kNJ; ++j) t += __builtin_amdgcn_exp2f(((cin[j] ? acc[i][j][v] : kNegInf) - ref) * parts.k2);
-        sm[v] = t;
-      }
-      half_reduce_scatter16(sm, [](float a, float b) { return a + b; });
-      if ((lane & 1) == 0) {
-        const int e = lr >> 1;
-        wpart[slot][wm + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)] = make_float2(own_m, sm[0]);
-      }
-    }
-    __syncthreads();
-    const int r = tid;  // one thread per row of the tile
-    const int gm = m0 + r;
-    if (r < kTallBM && gm < M) {
-      float mx = kNegInf;
-#pragma unroll
-      for (int k = 0; k < kSlots; ++k) mx = fmaxf(mx, wpart[k][r].x);
-      float sm = 0.f;
-#pragma unroll
-      for (int k = 0; k < kSlots; ++k) {
-        const float2 p = wpart[k][r];
-        if (p.x != kNegInf) sm += p.y * __builtin_amdgcn_exp2f((p.x - mx) * parts.k2);
-      }
-      parts.part[static_cast<int64_t>(gm) * nbn + bn] = make_float2(mx, sm);
-    }
-  }
-}
 
 template <bool TRIM, bool PARTS, bool BTILED>
 __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_tall(const uint16_t *__restrict__ hidden,
@@ -1145,7 +1035,7 @@ __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_tall(const uint16_t
   }
   wait_vmcnt<0>();
   __syncthreads();
-  tall_tile_store<PARTS>(acc, M, Vt, m0, n0, wm, wn, nbn, bn, logits, parts,
+  tile_store<PARTS, kMI, kNJ, kTallBM>(acc, M, Vt, m0, n0, wm, wn, nbn, bn, logits, parts,
                          reinterpret_cast<float2(*)[kTallBM]>(smem));
 }
 
