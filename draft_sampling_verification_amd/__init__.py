@@ -398,7 +398,11 @@ def vt_trim_head_tiled(weight, keep_ids, k=None, tiled=None):
     V_rows, H = weight.shape
     if keep_ids is not None:
         k = keep_ids.numel()
+    elif k is None:
+        raise ValueError("vt_trim_head_tiled: give keep_ids or the row count k")
     nbytes = lib().vt_trim_head_tiled_bytes(k, H)
+    if nbytes == 0:
+        raise ValueError(f"vt_trim_head_tiled: no K-tiled layout for k={k}, H={H} (needs k > 0 and H % 32 == 0)")
     if tiled is None:
         tiled = torch.empty(nbytes // 2, dtype=weight.dtype, device=weight.device)
     _bits16(tiled, "tiled")
