@@ -84,10 +84,10 @@ __device__ __forceinline__ void gather_step(float (&v)[N]) {
   }
 }
 
-// Reduce-scatter of 16 per-lane entries over each half-wave (the steps of half_reduce_scatter at
-// lane distances 16, 8, 4 and 2, each halving what a lane carries, then a plain reduction with
-// the lane at distance 1): afterwards v[0] holds the reduction over the half's 32 lanes of entry
-// (lane & 31) >> 1.  16 exchanges.
+// Reduce-scatter of 16 per-lane entries over each half-wave: steps at lane distances 16 (the row
+// swap of v_permlane16_swap), 8, 4 and 2 (scatter_step), each halving what a lane carries, then a
+// plain reduction with the lane at distance 1; afterwards v[0] holds the reduction over the
+// half's 32 lanes of entry (lane & 31) >> 1.  16 exchanges instead of 5 for each of 16 entries.
 template <typename Op>
 __device__ __forceinline__ void half_reduce_scatter16(float (&v)[16], Op op) {
 #pragma unroll
