@@ -152,12 +152,18 @@ def test_tiled_head_gives_the_same_block(name, order):
 
 @pytest.mark.parametrize("c", [4, 5])
 def test_tiled_head_gives_the_same_block_full_size(c):
+    # the benchmark's launch configuration (config 5: 384 x 256 tiles on the K-tiled W^Trim;
+    # config 4: 256 x 256) against the same call gathering rows, and its logits and target
+    # log-normalisers against the separate calls (256 x 256 tiles on the rows as given)
     wl = make_workload(CONFIGS[c])
-    say(f"tiled head vs gathered rows: full size config {c}")
+    say(f"tiled head vs gathered rows and separate calls: full size config {c}")
     a = gpu_block_fused(wl)
     b = gpu_block_fused(wl, tiled=True)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+    sep = gpu_block(wl)
+    assert np.array_equal(b["draft_logits"], sep["draft_logits"])
+    assert np.array_equal(b["target_lse"], sep["target_lse"])
 
 
 @pytest.mark.parametrize("c,order,follow", [(2, "id", 0.0), (3, "id", 0.0), (4, "id", 0.0), (5, "id", 0.0),
