@@ -711,13 +711,14 @@ def bench_block(args, config: int, steps: int, warmup: int):
         # one graph for the LM head and one for the rest of the step, per input set: replaying
         # them leaves the GPU no host-side gaps; the events between the two replays still time
         # the LM head on the stream it runs on
-        side = torch.cuda.Stream()
-        side.wait_stream(main)
-        with torch.cuda.stream(side):
+        # (warm-up on a stream of its own; `side` stays None: no overlap inside the graphs)
+        warm = torch.cuda.Stream()
+        warm.wait_stream(main)
+        with torch.cuda.stream(warm):
             for s in sets:
                 lmhead(s)
                 rest(s)
-        main.wait_stream(side)
+        main.wait_stream(warm)
         torch.cuda.synchronize()
         runners = []
         for s in sets:
