@@ -798,10 +798,9 @@ def bench_block(args, config: int, steps: int, warmup: int):
 
 
 def tiled_head_used(cfg, args) -> bool:
-    """Whether the fused call's head reads the K-tiled W^Trim: the sampled large-batch head
-    (256 x 256 tiles) with whole 32-column K steps, unless --head gather."""
-    return (not args.calls and args.head == "tiled" and not args.greedy and cfg.B * cfg.R >= 256
-            and cfg.H % 32 == 0)
+    """Whether the fused call's head reads the K-tiled W^Trim: the large-batch head (256 x 256 or
+    384 x 256 tiles) with whole 32-column K steps, unless --head gather."""
+    return not args.calls and args.head == "tiled" and cfg.B * cfg.R >= 256 and cfg.H % 32 == 0
 
 
 def side_record(res) -> dict:
@@ -846,7 +845,10 @@ def main():
     cfg = res["cfg"]
     B, g = cfg.B, cfg.gamma
     traffic = measured_traffic(f"config{args.config}")
-    kernel = (("lmhead_gemv" if B * cfg.R <= 8 else "lmhead_mfma_dma8" if B * cfg.R >= 256 else "lmhead_mfma")
+    M = B * cfg.R
+    tall = not args.calls and cfg.H % 32 == 0 and -(-M // 384) * 384 <= -(-M // 256) * 256
+    kernel = (("lmhead_gemv" if M <= 8 else ("lmhead_mfma_tall" if tall else "lmhead_mfma_dma8") if M >= 256
+               else "lmhead_mfma")
               + (" + target softmax partials" if small_batch_block(cfg, args.greedy) and not args.calls else ""))
     if res["mfma"]:
         # a real dense contraction: the head is priced against the bf16 MFMA peak

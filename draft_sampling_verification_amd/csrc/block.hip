@@ -27,7 +27,7 @@ namespace {
 
 struct BlockPlan {
   bool fused;       // GEMV with draft partials in its epilogue
-  bool fused_mfma;  // large-batch MFMA tiles with draft partials in their epilogue
+  bool fused_mfma;  // large-batch MFMA tiles with draft partials (softmax or argmax) in their epilogue
   bool fv;          // small batch, sampling both sides: target partials ride in the GEMV launch,
                     // then one chunk pass and one final pass (verify_fused_chunk / _final)
   bool fg;          // small batch, greedy both sides: argmax partials in the GEMV launch (head
@@ -51,7 +51,9 @@ BlockPlan plan_block(int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt,
   p.fused = !greedy_d && pick_gemv<kPartsSoftmax>(p.M, H, trim) != nullptr;
   p.fg = greedy_t && greedy_d && R <= kFvMaxR && pick_gemv<kPartsArgmax>(p.M, H, trim) != nullptr;
   p.nchunk_t = greedy_t && !p.fg ? 1 : (V + kChunk - 1) / kChunk;
-  p.fused_mfma = !greedy_d && !p.fused && p.M >= kBigMinM;
+  // large batches: the MFMA head emits the draft partials in its epilogue (softmax partials, or
+  // argmax partials for argmax drafts)
+  p.fused_mfma = !p.fused && !p.fg && p.M >= kBigMinM;
   if (p.fused || p.fg) {
     p.nchunk_d = gemv_blocks(Vt);
     p.chunk_d = gemv_rows_per_block(Vt);
@@ -183,8 +185,8 @@ hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, 
   const int vrows = static_cast<int>(Vp.V);  // the head passed in is the full [V][H] one
   const bool greedy_t = Vp.greedy;
   const bool t_multi = !greedy_t && pl.nchunk_t > 1;
-  // the large-batch head reads the hidden rows K-tiled (one contiguous 16 KB run per K step of a
-  // 256-row block); the copy rides in extra workgroups of the target partials launch when there is one
+  // the large-batch head reads the hidden rows K-tiled (one contiguous run per K step of a block of
+  // hidden rows); the copy rides in extra workgroups of the target partials launch when there is one
   uint16_t *hidt = pl.hidt_bytes ? reinterpret_cast<uint16_t *>(hidt_base) : nullptr;
   const TileParams tp = hidden_tiles_params(hidden, pl.M, H, hidt);
   // 1. target partials (or a whole single-chunk target softmax); greedy verification needs none
@@ -211,8 +213,10 @@ hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, 
     if (e != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   } else if (pl.fused_mfma) {
-    e = launch_mfma_big<true>(hidden, weight, keep, vrows, pl.M, H, Vt, logits, GemvParts{D.part, D.k2}, stream,
-                              hidt, weight_tiled);
+    e = D.greedy ? launch_mfma_big<kPartsArgmax>(hidden, weight, keep, vrows, pl.M, H, Vt, logits,
+                                                 GemvParts{D.part, D.k2}, stream, hidt, weight_tiled)
+                 : launch_mfma_big<kPartsSoftmax>(hidden, weight, keep, vrows, pl.M, H, Vt, logits,
+                                                  GemvParts{D.part, D.k2}, stream, hidt, weight_tiled);
     if (e != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   } else {

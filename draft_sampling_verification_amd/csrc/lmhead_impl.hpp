@@ -117,6 +117,45 @@ __device__ __forceinline__ void half_all_gather16(float (&v)[16]) {
   }
 }
 
+// Argmax over each half-wave of 16 per-lane (value, index) entries, by the same steps as
+// half_reduce_scatter16 with the pair moved together: afterwards (v[0], ix[0]) is the largest
+// value of entry (lane & 31) >> 1 over the half's 32 lanes, the lowest index among equal values.
+template <int CTRL, int BIT, int H>
+__device__ __forceinline__ void argmax_step(float (&v)[16], int (&ix)[16]) {
+  const bool up = (lane_id() & BIT) != 0;
+#pragma unroll
+  for (int k = 0; k < H; ++k) {
+    const float sv = up ? v[k] : v[k + H], kv = up ? v[k + H] : v[k];
+    const int si = up ? ix[k] : ix[k + H], ki = up ? ix[k + H] : ix[k];
+    const float ov = lane_swap<CTRL>(sv);
+    const int oi = lane_swap<CTRL>(si);
+    const bool take = argmax_better(ov, oi, kv, ki);
+    v[k] = take ? ov : kv;
+    ix[k] = take ? oi : ki;
+  }
+}
+__device__ __forceinline__ void half_argmax_scatter16(float (&v)[16], int (&ix)[16]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    float a = v[k], b = v[k + 8];
+    float ia = __int_as_float(ix[k]), ib = __int_as_float(ix[k + 8]);
+    swap16(a, b);
+    swap16(ia, ib);
+    const bool take = argmax_better(b, __float_as_int(ib), a, __float_as_int(ia));
+    v[k] = take ? b : a;
+    ix[k] = take ? __float_as_int(ib) : __float_as_int(ia);
+  }
+  argmax_step<kDppRor8, 8, 4>(v, ix);
+  argmax_step<kDppHalfMirror, 4, 2>(v, ix);
+  argmax_step<kDppXor2, 2, 1>(v, ix);
+  const float ov = lane_swap<kDppXor1>(v[0]);
+  const int oi = lane_swap<kDppXor1>(ix[0]);
+  if (argmax_better(ov, oi, v[0], ix[0])) {
+    v[0] = ov;
+    ix[0] = oi;
+  }
+}
+
 // Transpose-reduction of NP (1, 2, 4 or 8) per-lane partial sums over the 64 lanes.  The steps
 // at lane distance 32, 16 and 8 halve the number of values each lane carries (each lane keeps
 // the half its partner gives up), the remaining steps add within groups of 64/NP lanes.  On
@@ -555,8 +594,9 @@ __device__ __forceinline__ void big_tile_of(int tile, int nbm, int nbn, int &bm,
 }
 
 // Epilogue of a TM x 256 tile (TM hidden rows x 256 head rows) whose waves hold MI x NJ
-// accumulator blocks of 32 x 32 each: the logits, and with PARTS the draft softmax partials of
-// the tile's 256 columns per hidden row (max and sum of 2^((x - max) k2)).  Per row block of a
+// accumulator blocks of 32 x 32 each: the logits, and per hidden row the draft partials of the
+// tile's 256 columns: with PARTS = kPartsSoftmax the max and sum of 2^((x - max) k2), with
+// kPartsArgmax the max and the lowest column index holding it (for argmax drafts).  Per row block of a
 // wave the 16 row maxima over the wave's 32 NJ columns are reduce-scattered over the half-wave
 // (a lane holds 16 rows of its half in each block), gathered back for the exponentials, and the
 // sums reduce-scattered: 47 lane exchanges per block, 16 maxima and sums in registers at a time.
@@ -565,7 +605,7 @@ __device__ __forceinline__ void big_tile_of(int tile, int nbm, int nbn, int &bm,
 // wpart: LDS scratch of kSlots x TM float2 that the caller no longer needs (its operand tiles), so
 // that the kernel keeps a single LDS object (a second one makes the compiler wait for every
 // outstanding direct-to-LDS load before any LDS read in the main loop).
-template <bool PARTS, int MI, int NJ, int TM>
+template <int PARTS, int MI, int NJ, int TM>
 __device__ __forceinline__ void tile_store(const f32x16 (&acc)[MI][NJ], int M, int Vt, int m0, int n0, int wm,
                                            int wn, int nbn, int bn, float *__restrict__ logits,
                                            const GemvParts &parts, float2 (*wpart)[TM]) {
@@ -588,7 +628,50 @@ __device__ __forceinline__ void tile_store(const f32x16 (&acc)[MI][NJ], int M, i
         }
       }
     }
-  if constexpr (PARTS) {
+  if constexpr (PARTS == kPartsArgmax) {
+    // per row: the wave's best (value, column) over its 32 NJ columns, reduce-scattered over the
+    // half-wave, then merged across the waves that cover the same rows
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      float bv[16];
+      int bi[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        bv[v] = kNegInf;
+        bi[v] = kNoIndex;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int gn = n0 + wn + j * 32 + lr;
+          if (gn < Vt && argmax_better(acc[i][j][v], gn, bv[v], bi[v])) {
+            bv[v] = acc[i][j][v];
+            bi[v] = gn;
+          }
+        }
+      }
+      half_argmax_scatter16(bv, bi);
+      if ((lane & 1) == 0) {  // lanes l and l ^ 1 hold the same row
+        const int e = lr >> 1;
+        wpart[slot][wm + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)] = make_float2(bv[0], __int_as_float(bi[0]));
+      }
+    }
+    __syncthreads();
+    const int r = tid;
+    const int gm = m0 + r;
+    if (r < TM && gm < M) {
+      float v = kNegInf;
+      int ix = kNoIndex;
+#pragma unroll
+      for (int k = 0; k < kSlots; ++k) {
+        const float2 p = wpart[k][r];
+        if (argmax_better(p.x, __float_as_int(p.y), v, ix)) {
+          v = p.x;
+          ix = __float_as_int(p.y);
+        }
+      }
+      parts.part[static_cast<int64_t>(gm) * nbn + bn] = make_float2(v, __int_as_float(ix));
+    }
+  }
+  if constexpr (PARTS == kPartsSoftmax) {
     bool cin[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) cin[j] = n0 + wn + j * 32 + lr < Vt;
@@ -641,7 +724,7 @@ __device__ __forceinline__ void tile_store(const f32x16 (&acc)[MI][NJ], int M, i
 }
 
 
-template <bool TRIM, bool PARTS, bool KFULL>
+template <bool TRIM, int PARTS, bool KFULL>
 __global__ __launch_bounds__(kBlock, 1) void lmhead_mfma_big(const uint16_t *__restrict__ hidden,
                                                              const uint16_t *__restrict__ weight,
                                                              const int32_t *__restrict__ keep, int vrows, int M, int H,
@@ -802,7 +885,7 @@ constexpr int kDma8Block = 512;
 // the products and their summation order are unchanged, so the logits are the same bits.
 // BTILED: the head rows come from a K-tiled W^Trim (vt_trim_head_tiled) instead of being
 // gathered from the full head through keep; again the same products in the same order.
-template <bool TRIM, bool PARTS, bool ATILED = false, bool BTILED = false>
+template <bool TRIM, int PARTS, bool ATILED = false, bool BTILED = false>
 __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_dma8(const uint16_t *__restrict__ hidden,
                                                                   const uint16_t *__restrict__ weight,
                                                                   const int32_t *__restrict__ keep, int vrows, int M,
@@ -936,7 +1019,7 @@ constexpr int kTallBM = 384;
 constexpr int kTallStages = 4;
 constexpr int kTallStageBytes = (kTallBM + kBigBN) * kDmaRowBytes;  // 40 KB
 
-template <bool TRIM, bool PARTS, bool BTILED>
+template <bool TRIM, int PARTS, bool BTILED>
 __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_tall(const uint16_t *__restrict__ hidden,
                                                                   const uint16_t *__restrict__ weight,
                                                                   const int32_t *__restrict__ keep, int vrows, int M,
@@ -1117,44 +1200,45 @@ __global__ __launch_bounds__(kBlock) void softmax_partial_tiles(SmParams P, Tile
 
 
 
-// hidden_tiled: NULL, or the K-tiled copy of the hidden rows made by hidden_tiles (H % 32 == 0),
-// in blocks of big_tile_rows(M) rows: 384-row blocks select the tall tiles (with PARTS, the
-// fused block's head); weight_tiled: NULL, or the K-tiled trimmed head of vt_trim_head_tiled
-// (read only together with hidden_tiled; weight and keep are then not read by the kernel).
-template <bool PARTS>
+// PARTS = kPartsNone (the separate LM-head call): the hidden rows as given, 256 x 256 tiles.
+// kPartsSoftmax / kPartsArgmax (the fused block's head, with its draft partials): when H % 32 == 0
+// hidden_tiled must hold the K-tiled copy of the hidden rows made by hidden_tiles, in blocks of
+// big_tile_rows(M) rows, whose 384-row blocks select the tall tiles; weight_tiled: NULL, or the
+// K-tiled trimmed head of vt_trim_head_tiled (weight and keep are then not read by the kernel).
+// Other H take the register-staged kernel on the rows as given.
+template <int PARTS>
 inline hipError_t launch_mfma_big(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int vrows,
                                   int64_t M, int64_t H, int64_t Vt, float *logits, GemvParts parts,
                                   hipStream_t stream, const uint16_t *hidden_tiled = nullptr,
                                   const uint16_t *weight_tiled = nullptr) {
   const int64_t tiles = ((M + kBigBM - 1) / kBigBM) * mfma_big_tiles_n(Vt);
-  if (!PARTS && hidden_tiled && big_tile_rows(M) != kBigBM) return hipErrorInvalidValue;  // no tall kernel without PARTS
-  if constexpr (PARTS) {
-    if (hidden_tiled && H % kDmaBK == 0 && big_tile_rows(M) == kTallBM) {
-      const unsigned tall = static_cast<unsigned>(((M + kTallBM - 1) / kTallBM) * mfma_big_tiles_n(Vt));
-      auto f = weight_tiled ? &lmhead_mfma_tall<false, true, true>
-                            : (keep ? &lmhead_mfma_tall<true, true, false> : &lmhead_mfma_tall<false, true, false>);
-      return launch(f, dim3(tall), dim3(kDma8Block), 0, stream, hidden_tiled, weight_tiled ? weight_tiled : weight,
-                    keep, vrows, static_cast<int>(M), static_cast<int>(H), static_cast<int>(Vt), logits, parts);
-    }
-  }
+  const int iM = static_cast<int>(M), iH = static_cast<int>(H), iV = static_cast<int>(Vt);
   if (H % kDmaBK == 0) {
-    if (hidden_tiled && weight_tiled)
-      return launch(lmhead_mfma_dma8<false, PARTS, true, true>, dim3(static_cast<unsigned>(tiles)), dim3(kDma8Block),
-                    0, stream, hidden_tiled, weight_tiled, keep, vrows, static_cast<int>(M), static_cast<int>(H),
-                    static_cast<int>(Vt), logits, parts);
-    if (hidden_tiled) {
-      auto ft = keep ? &lmhead_mfma_dma8<true, PARTS, true> : &lmhead_mfma_dma8<false, PARTS, true>;
-      return launch(ft, dim3(static_cast<unsigned>(tiles)), dim3(kDma8Block), 0, stream, hidden_tiled, weight, keep,
-                    vrows, static_cast<int>(M), static_cast<int>(H), static_cast<int>(Vt), logits, parts);
+    if constexpr (PARTS == kPartsNone) {
+      if (hidden_tiled || weight_tiled) return hipErrorInvalidValue;
+      auto fd = keep ? &lmhead_mfma_dma8<true, PARTS> : &lmhead_mfma_dma8<false, PARTS>;
+      return launch(fd, dim3(static_cast<unsigned>(tiles)), dim3(kDma8Block), 0, stream, hidden, weight, keep, vrows,
+                    iM, iH, iV, logits, parts);
+    } else {
+      if (!hidden_tiled) return hipErrorInvalidValue;
+      if (big_tile_rows(M) == kTallBM) {
+        const unsigned tall = static_cast<unsigned>(((M + kTallBM - 1) / kTallBM) * mfma_big_tiles_n(Vt));
+        auto f = weight_tiled ? &lmhead_mfma_tall<false, PARTS, true>
+                              : (keep ? &lmhead_mfma_tall<true, PARTS, false> : &lmhead_mfma_tall<false, PARTS, false>);
+        return launch(f, dim3(tall), dim3(kDma8Block), 0, stream, hidden_tiled, weight_tiled ? weight_tiled : weight,
+                      keep, vrows, iM, iH, iV, logits, parts);
+      }
+      auto ft = weight_tiled ? &lmhead_mfma_dma8<false, PARTS, true, true>
+                             : (keep ? &lmhead_mfma_dma8<true, PARTS, true> : &lmhead_mfma_dma8<false, PARTS, true>);
+      return launch(ft, dim3(static_cast<unsigned>(tiles)), dim3(kDma8Block), 0, stream, hidden_tiled,
+                    weight_tiled ? weight_tiled : weight, keep, vrows, iM, iH, iV, logits, parts);
     }
-    auto fd = keep ? &lmhead_mfma_dma8<true, PARTS> : &lmhead_mfma_dma8<false, PARTS>;
-    return launch(fd, dim3(static_cast<unsigned>(tiles)), dim3(kDma8Block), 0, stream, hidden, weight, keep,
-                  vrows, static_cast<int>(M), static_cast<int>(H), static_cast<int>(Vt), logits, parts);
   }
+  if (hidden_tiled || weight_tiled) return hipErrorInvalidValue;
   auto fn = H % kBigBK == 0 ? (keep ? &lmhead_mfma_big<true, PARTS, true> : &lmhead_mfma_big<false, PARTS, true>)
                             : (keep ? &lmhead_mfma_big<true, PARTS, false> : &lmhead_mfma_big<false, PARTS, false>);
-  return launch(fn, dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0, stream, hidden, weight, keep, vrows,
-                static_cast<int>(M), static_cast<int>(H), static_cast<int>(Vt), logits, parts);
+  return launch(fn, dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0, stream, hidden, weight, keep, vrows, iM, iH,
+                iV, logits, parts);
 }
 
 // extra: workgroups past the head's row blocks (target partial chunks; PARTS kernels only).
@@ -1168,7 +1252,7 @@ inline hipError_t launch_gemv(GemvFn fn, const uint16_t *hidden, const uint16_t 
 inline hipError_t launch_mfma(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int vrows,
                               int64_t M, int64_t H, int64_t Vt, float *logits, hipStream_t stream) {
   if (M >= kBigMinM)
-    return launch_mfma_big<false>(hidden, weight, keep, vrows, M, H, Vt, logits, GemvParts{}, stream);
+    return launch_mfma_big<kPartsNone>(hidden, weight, keep, vrows, M, H, Vt, logits, GemvParts{}, stream);
   const int64_t tiles = ((M + kBM - 1) / kBM) * ((Vt + kBN - 1) / kBN);
   return launch(lmhead_mfma, dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0, stream, hidden, weight, keep,
                 vrows, static_cast<int>(M), static_cast<int>(H), static_cast<int>(Vt), logits);

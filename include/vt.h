@@ -181,7 +181,7 @@ size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
  * H % 32 == 0 the target partials launch also copies the hidden rows K-tiled into the workspace
  * (the head then reads each K step of a block of hidden rows as one contiguous run; same products,
  * same logits); without target partials (V <= 4096 or greedy verification) the copy is a launch of
- * its own.  With sampled drafts that head takes 384 x 256 tiles (384 hidden rows) when padding
+ * its own.  That head takes 384 x 256 tiles (384 hidden rows) when padding
  * B*R to 384-row blocks adds no more rows than padding it to 256-row blocks (B*R = 2304, 288,
  * 756 ...), else 256 x 256 tiles (B*R = 512 ...); both sum the same products in the same order.
  *   Pages: as for the four calls above.
@@ -189,8 +189,7 @@ size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
  *   hidden bf16 [B*R][H] (row b*R + i is sequence b's i-th draft position); weight bf16 [V][H]
  *   (the full head); weight_tiled: NULL, or W^Trim in the K-tiled layout vt_trim_head_tiled makes
  *   from this weight and keep_ids (vt_keepset.h), which the large-batch head then reads in place of
- *   gathering rows of weight (only when B*R >= 256, both sides are sampled and H % 32 == 0; ignored
- *   otherwise; same products in the same order, so the same logits bits; the library cannot check
+ *   gathering rows of weight (only when B*R >= 256 and H % 32 == 0; ignored otherwise; same products in the same order, so the same logits bits; the library cannot check
  *   that it matches weight and keep_ids); keep_ids int32 [Vt] and full_to_trim int32 [V] (both
  *   NULL iff the head is untrimmed, Vt == V); target_logits [B][gamma+1][V] (fp32 or bf16); u_draft fp32 [B*R],
  *   u_accept fp32 [B][gamma], u_final fp32 [B].
@@ -211,9 +210,12 @@ size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
  *   runs, target_lse is not written, u_accept and u_final are not read (all three may be NULL).
  *   draft_T = 0 (allowed only with target_T = 0) makes each draft the lowest id of its row's
  *   maximum, draft_lse the row maximum, and u_draft is not read (may be NULL); the LM head then
- *   runs without the fused softmax partials, except at decode sizes (B*R <= 8), where it emits
- *   per-block argmax partials of the draft rows and, in extra workgroups, per-chunk argmaxes of
- *   the target rows, and one more launch finishes the block (2 launches).
+ *   emits argmax partials instead of softmax partials: at decode sizes (B*R <= 8) per block of
+ *   head rows for the draft rows and, in extra workgroups, per 4096-chunk for the target rows,
+ *   and one more launch finishes the block (2 launches); from B*R >= 256 per 256 head rows (the
+ *   same large-batch head, K-tiled copies and weight_tiled as with sampled drafts), finished by
+ *   the combine launch; in between the head runs without partials and a separate pass finds the
+ *   draft rows' argmaxes.
  *   Errors: INVALID_ARG for NULL required pointers, B, gamma, H, V or Vt <= 0, R < gamma, Vt > V,
  *   a temperature not finite or < 0, draft_T = 0 with target_T > 0, keep_ids/full_to_trim
  *   inconsistent with Vt; UNSUPPORTED for

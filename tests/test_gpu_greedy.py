@@ -99,7 +99,7 @@ def test_greedy_flags_bad_ids():
     assert n[1] == -1 and (tok[1] == -1).all() and n[0] >= 0 and n[2] >= 0
 
 
-def _block_greedy(wl, draft_T):
+def _block_greedy(wl, draft_T, tiled=False):
     cfg = wl.cfg
     B, R, g = wl.B, cfg.R, cfg.gamma
     keep = dev(wl.keep_ids) if wl.keep_ids is not None else None
@@ -111,8 +111,10 @@ def _block_greedy(wl, draft_T):
     tok = torch.full((B, g + 1), -9, dtype=torch.int32, device="cuda")
     nacc = torch.empty(B, dtype=torch.int32, device="cuda")
     ud = dev(wl.u_draft.reshape(-1)) if draft_T > 0 else None
-    vt.vt_spec_block(dev_bf16(wl.hidden), dev_bf16(wl.weight), keep, f2t, target, 0.0, draft_T, ud, None, None,
-                     logits, dlse, dids, None, tok, nacc)
+    weight = dev_bf16(wl.weight)
+    wt = vt.vt_trim_head_tiled(weight, keep, k=cfg.Vt) if tiled else None
+    vt.vt_spec_block(dev_bf16(wl.hidden), weight, keep, f2t, target, 0.0, draft_T, ud, None, None,
+                     logits, dlse, dids, None, tok, nacc, weight_tiled=wt)
     torch.cuda.synchronize()
     return (logits.cpu().numpy(), dlse.cpu().numpy(), dids.cpu().numpy().reshape(B, R), tok.cpu().numpy(),
             nacc.cpu().numpy())
@@ -123,6 +125,12 @@ def _block_greedy(wl, draft_T):
     ("c3-scaled sampled drafts", CONFIGS[3].scaled(B=4, V=20000, Vt=5000, H=512), 1.0),
     ("c4-scaled argmax drafts", CONFIGS[4].scaled(B=24, V=9001, Vt=3000, H=256), 0.0),
     ("c4 big tiles argmax drafts", CONFIGS[4].scaled(B=40, V=20000, Vt=5000, H=256), 0.0),
+    # argmax partials from the large-batch heads' epilogues: 512 hidden rows on 256 x 256 tiles,
+    # 756 on 384 x 256 tiles (two row blocks, ragged Vt), H = 520 on the register-staged tiles
+    ("c4 square tiles argmax drafts", CONFIGS[4].scaled(B=64, V=20000, Vt=5000, H=256), 0.0),
+    ("c5 tall tiles argmax drafts", CONFIGS[5].scaled(B=84, V=13000, Vt=6001, H=256), 0.0),
+    ("c4 register-staged tiles argmax drafts", CONFIGS[4].scaled(B=40, V=20000, Vt=5000, H=520), 0.0),
+    ("c5 full size argmax drafts, K-tiled head", CONFIGS[5], 0.0),
     ("c5-scaled sampled drafts", CONFIGS[5].scaled(B=32, V=13000, Vt=6001, H=256), 0.8),
     ("c2 full size argmax drafts", CONFIGS[2], 0.0),
     ("c3-scaled argmax drafts, following drafter", CONFIGS[3].scaled(B=4, V=20000, Vt=5000, H=512), 0.0),
@@ -135,7 +143,7 @@ def test_block_greedy(name, cfg, draft_T):
     following drafter (draft argmax mostly the target's) reaches long accepted runs."""
     say(f"fused block, greedy target: {name}")
     wl = make_workload(cfg, follow=0.5 if "following" in name else 0.0)
-    logits, dlse, ids, tok, n = _block_greedy(wl, draft_T)
+    logits, dlse, ids, tok, n = _block_greedy(wl, draft_T, tiled="K-tiled" in name)
     B, R, g = wl.B, cfg.R, cfg.gamma
     if draft_T == 0.0:
         want_ids = np.array([ref.argmax_lowest(row) for row in logits]).reshape(B, R)
