@@ -88,11 +88,11 @@ def _merge(parts):
     return {k: np.concatenate([p[k] for p in parts]) for k in ("tokens", "n", "draft_ids")}
 
 
-@pytest.mark.parametrize("c,B,follow", [(4, 40, 0.5), (5, 32, 0.5), (4, 40, 0.0)])
+@pytest.mark.parametrize("c,B,follow", [(4, 40, 0.5), (5, 32, 0.5), (4, 40, 0.0), (4, 64, 0.5)])
 def test_batch_independence_across_head_kernels(c, B, follow):
     """The same sequences alone (B = 1: the GEMV head and the three-launch path for 8 draft rows,
     128 x 128 MFMA tiles for 9), in batches of at most 16 (128 x 128 MFMA tiles) and in a batch of
-    256+ hidden rows (256 x 256 direct-to-LDS tiles).
+    256+ hidden rows (direct-to-LDS tiles: 384 x 256 for 320 and 288 rows, 256 x 256 for 512).
     The logits' fp32 summation order differs between the three head kernels, so a decision may
     differ only where the oracle places it within the band; every other output must be the same,
     and each run must match the oracle."""
