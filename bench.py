@@ -44,6 +44,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20
+# hidden rows from which the LM head takes the 256 x 256 / 384 x 256 tiles (more than one 128-row block)
+BIG_MIN_M = 129
 
 
 def log(*a):
@@ -800,7 +802,7 @@ def bench_block(args, config: int, steps: int, warmup: int):
 def tiled_head_used(cfg, args) -> bool:
     """Whether the fused call's head reads the K-tiled W^Trim: the large-batch head (256 x 256 or
     384 x 256 tiles) with whole 32-column K steps, unless --head gather."""
-    return not args.calls and args.head == "tiled" and cfg.B * cfg.R >= 256 and cfg.H % 32 == 0
+    return not args.calls and args.head == "tiled" and cfg.B * cfg.R >= BIG_MIN_M and cfg.H % 32 == 0
 
 
 def side_record(res) -> dict:
@@ -847,7 +849,7 @@ def main():
     traffic = measured_traffic(f"config{args.config}")
     M = B * cfg.R
     tall = not args.calls and cfg.H % 32 == 0 and -(-M // 384) * 384 <= -(-M // 256) * 256
-    kernel = (("lmhead_gemv" if M <= 8 else ("lmhead_mfma_tall" if tall else "lmhead_mfma_dma8") if M >= 256
+    kernel = (("lmhead_gemv" if M <= 8 else ("lmhead_mfma_tall" if tall else "lmhead_mfma_dma8") if M >= BIG_MIN_M
                else "lmhead_mfma")
               + (" + target softmax partials" if small_batch_block(cfg, args.greedy) and not args.calls else ""))
     if res["mfma"]:

@@ -577,7 +577,7 @@ GemvFn pick_gemv(int64_t M, int64_t H, bool trim) {
 // row (max and sum of 2^((x - max) k2)), combined across the two waves that share rows.
 constexpr int kBigBM = 256, kBigBN = 256, kBigBK = 64, kBigPad = 8;
 constexpr int kBigRow = kBigBK + kBigPad;  // bf16 per LDS row: 144 bytes
-constexpr int kBigMinM = 256;
+constexpr int kBigMinM = 129;  // more than one 128-row block: the 256 x 256 or tall tiles
 
 // Tile order of the 256 x 256 kernels.  Each XCD works through one contiguous range of logical
 // tiles (xcd_remap); logical tiles are ordered in groups of kTileGroup hidden-row blocks, walked

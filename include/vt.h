@@ -75,7 +75,7 @@ typedef enum { VT_F32 = 0, VT_BF16 = 1 } vt_dtype_t;
  *   not depend on the row, so trimmed logits equal untrimmed logits gathered at keep_ids bit for bit.
  *   The order does depend on M, which picks the kernel: a GEMV when M <= 8 and
  *   M * ceil(H / 512) <= 48 (lanes hold partial sums over 16-byte pieces of a row, reduced across
- *   lanes); otherwise 128 x 128 MFMA tiles when M < 256 and 256 x 256 MFMA tiles when M >= 256
+ *   lanes); otherwise 128 x 128 MFMA tiles when M <= 128 and 256 x 256 MFMA tiles when M > 128
  *   (sums over K in MFMA steps of 16).  A hidden row's
  *   logits may therefore differ in the last bits between batch sizes (each within the
  *   recursive-summation bound H 2^-24 sum_k |h_k w_k|), and so may a decision taken on them, but
@@ -177,19 +177,19 @@ size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
  * first pass and, in extra workgroups, the target rows' first pass; one chunk pass over the
  * full vocabulary forms the log-normalisers, draft draws, accept tests and residual chunk sums;
  * one final pass draws the last token.  Larger batches take 5 (LM head with the draft partials,
- * target partials, one combine launch for both row sets, two verify passes).  When B*R >= 256 and
+ * target partials, one combine launch for both row sets, two verify passes).  When B*R > 128 and
  * H % 32 == 0 the target partials launch also copies the hidden rows K-tiled into the workspace
  * (the head then reads each K step of a block of hidden rows as one contiguous run; same products,
  * same logits); without target partials (V <= 4096 or greedy verification) the copy is a launch of
  * its own.  That head takes 384 x 256 tiles (384 hidden rows) when padding
  * B*R to 384-row blocks adds no more rows than padding it to 256-row blocks (B*R = 2304, 288,
- * 756 ...), else 256 x 256 tiles (B*R = 512 ...); both sum the same products in the same order.
+ * 756 ...), else 256 x 256 tiles (B*R = 144, 512 ...); both sum the same products in the same order.
  *   Pages: as for the four calls above.
  *
  *   hidden bf16 [B*R][H] (row b*R + i is sequence b's i-th draft position); weight bf16 [V][H]
  *   (the full head); weight_tiled: NULL, or W^Trim in the K-tiled layout vt_trim_head_tiled makes
  *   from this weight and keep_ids (vt_keepset.h), which the large-batch head then reads in place of
- *   gathering rows of weight (only when B*R >= 256 and H % 32 == 0; ignored otherwise; same products in the same order, so the same logits bits; the library cannot check
+ *   gathering rows of weight (only when B*R > 128 and H % 32 == 0; ignored otherwise; same products in the same order, so the same logits bits; the library cannot check
  *   that it matches weight and keep_ids); keep_ids int32 [Vt] and full_to_trim int32 [V] (both
  *   NULL iff the head is untrimmed, Vt == V); target_logits [B][gamma+1][V] (fp32 or bf16); u_draft fp32 [B*R],
  *   u_accept fp32 [B][gamma], u_final fp32 [B].
@@ -200,7 +200,7 @@ size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
  *   Results are those of the four calls (the logits and target_lse bit for bit), except that on
  *   the fused paths the draft running sums are chunked by the LM head's own blocks of head rows
  *   instead of 4096-element chunks: ceil(Vt / 256) rounded up to a multiple of 4 rows when B*R <= 8,
- *   256 rows when B*R >= 256.  Draws can then differ from the separate calls only where a CDF
+ *   256 rows when B*R > 128.  Draws can then differ from the separate calls only where a CDF
  *   boundary lies within rounding of the uniform.  Sequences are independent: a sequence's
  *   outputs are those it gets alone, up to the LM head's batch-size-dependent summation order
  *   (see vt_lmhead_trimmed), i.e. they can differ only at a decision within rounding of its
@@ -212,7 +212,7 @@ size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
  *   maximum, draft_lse the row maximum, and u_draft is not read (may be NULL); the LM head then
  *   emits argmax partials instead of softmax partials: at decode sizes (B*R <= 8) per block of
  *   head rows for the draft rows and, in extra workgroups, per 4096-chunk for the target rows,
- *   and one more launch finishes the block (2 launches); from B*R >= 256 per 256 head rows (the
+ *   and one more launch finishes the block (2 launches); from B*R > 128 per 256 head rows (the
  *   same large-batch head, K-tiled copies and weight_tiled as with sampled drafts), finished by
  *   the combine launch; in between the head runs without partials and a separate pass finds the
  *   draft rows' argmaxes.

@@ -28,6 +28,10 @@ SCALED = {
     # second ragged), 512 takes 256-row tiles (two blocks; 384-row blocks would pad to 768)
     "c5-tall-two-blocks": CONFIGS[5].scaled(B=84, V=13000, Vt=6001, H=256),
     "c4-square-two-blocks": CONFIGS[4].scaled(B=64, V=20000, Vt=5000, H=256),
+    # the two sides of the switch to the fused 256 x 256 tiles: 128 hidden rows take 128 x 128
+    # tiles and a separate draft softmax, 129 take one 256-row block, 127 of its rows padding
+    "c4-128-rows": CONFIGS[4].scaled(B=16, V=20000, Vt=5000, H=256),
+    "c4-129-rows": CONFIGS[4].scaled(B=43, gamma=2, R=3, V=20000, Vt=5000, H=256),
 }
 
 

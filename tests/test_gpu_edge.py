@@ -91,8 +91,9 @@ def _merge(parts):
 @pytest.mark.parametrize("c,B,follow", [(4, 40, 0.5), (5, 32, 0.5), (4, 40, 0.0), (4, 64, 0.5)])
 def test_batch_independence_across_head_kernels(c, B, follow):
     """The same sequences alone (B = 1: the GEMV head and the three-launch path for 8 draft rows,
-    128 x 128 MFMA tiles for 9), in batches of at most 16 (128 x 128 MFMA tiles) and in a batch of
-    256+ hidden rows (direct-to-LDS tiles: 384 x 256 for 320 and 288 rows, 256 x 256 for 512).
+    128 x 128 MFMA tiles for 9), in batches of at most 128 hidden rows (128 x 128 MFMA tiles) and in
+    a batch of 256+ hidden rows (direct-to-LDS tiles: 384 x 256 for 320 and 288 rows, 256 x 256 for
+    512).
     The logits' fp32 summation order differs between the three head kernels, so a decision may
     differ only where the oracle places it within the band; every other output must be the same,
     and each run must match the oracle."""
@@ -105,10 +106,11 @@ def test_batch_independence_across_head_kernels(c, B, follow):
     st = compare_tokens(gbig, orc, big)
     say(f"  batch of {B}: {st}")
     assert st["full_match"] >= 0.95 * B
-    gmid = _merge([gpu_block_fused(make_workload(cfg.scaled(B=min(16, B - b0)), b0=b0, follow=follow))
-                   for b0 in range(0, B, 16)])
+    mb = 128 // cfg.R
+    gmid = _merge([gpu_block_fused(make_workload(cfg.scaled(B=min(mb, B - b0)), b0=b0, follow=follow))
+                   for b0 in range(0, B, mb)])
     st = compare_tokens(gmid, orc, big)
-    say(f"  batches of 16: {st}")
+    say(f"  batches of {mb}: {st}")
     assert st["full_match"] >= 0.95 * B
     one = cfg.scaled(B=1)
     singles = [gpu_block_fused(make_workload(one, b0=b, follow=follow)) for b in range(B)]
