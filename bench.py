@@ -44,8 +44,29 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20
-# hidden rows from which the LM head takes the 256 x 256 / 384 x 256 tiles (more than one 128-row block)
+# the LM head's MFMA kernels (past the GEMV's 8 rows): with H % 32 == 0 all rows in one block up
+# to ROWS_MAX_M rows, then 256 x 256 or (fused call, rows filling 384-row blocks) 384 x 256 tiles;
+# otherwise 128 x 128 tiles below BIG_MIN_M rows and register-staged 256 x 256 tiles from there
+ROWS_MAX_M = 192
 BIG_MIN_M = 129
+
+
+def gemv_head(M: int, H: int) -> bool:
+    """Whether the LM head is the GEMV: at most 8 rows whose 512-column slices fit its registers."""
+    nit = -(-H // 512)
+    return M <= 8 and nit <= 8 and M * nit <= 48
+
+
+def head_kernel(M: int, H: int, calls: bool) -> str:
+    """Name of the LM-head kernel vt_spec_block (calls=False) or vt_lmhead_trimmed runs."""
+    if gemv_head(M, H):
+        return "lmhead_gemv"
+    if H % 32 == 0:
+        if M <= ROWS_MAX_M:
+            return "lmhead_mfma_rows"
+        tall = not calls and -(-M // 384) * 384 <= -(-M // 256) * 256
+        return "lmhead_mfma_tall" if tall else "lmhead_mfma_dma8"
+    return "lmhead_mfma_big" if M >= BIG_MIN_M else "lmhead_mfma"
 
 
 def log(*a):
@@ -800,9 +821,9 @@ def bench_block(args, config: int, steps: int, warmup: int):
 
 
 def tiled_head_used(cfg, args) -> bool:
-    """Whether the fused call's head reads the K-tiled W^Trim: the large-batch head (256 x 256 or
-    384 x 256 tiles) with whole 32-column K steps, unless --head gather."""
-    return not args.calls and args.head == "tiled" and cfg.B * cfg.R >= BIG_MIN_M and cfg.H % 32 == 0
+    """Whether the fused call's head reads the K-tiled W^Trim: an MFMA head (past the GEMV's sizes)
+    with whole 32-column K steps, unless --head gather."""
+    return not args.calls and args.head == "tiled" and not gemv_head(cfg.B * cfg.R, cfg.H) and cfg.H % 32 == 0
 
 
 def side_record(res) -> dict:
@@ -848,9 +869,7 @@ def main():
     B, g = cfg.B, cfg.gamma
     traffic = measured_traffic(f"config{args.config}")
     M = B * cfg.R
-    tall = not args.calls and cfg.H % 32 == 0 and -(-M // 384) * 384 <= -(-M // 256) * 256
-    kernel = (("lmhead_gemv" if M <= 8 else ("lmhead_mfma_tall" if tall else "lmhead_mfma_dma8") if M >= BIG_MIN_M
-               else "lmhead_mfma")
+    kernel = (head_kernel(M, cfg.H, args.calls)
               + (" + target softmax partials" if small_batch_block(cfg, args.greedy) and not args.calls else ""))
     if res["mfma"]:
         # a real dense contraction: the head is priced against the bf16 MFMA peak

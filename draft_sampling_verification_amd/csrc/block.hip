@@ -51,9 +51,10 @@ BlockPlan plan_block(int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt,
   p.fused = !greedy_d && pick_gemv<kPartsSoftmax>(p.M, H, trim) != nullptr;
   p.fg = greedy_t && greedy_d && R <= kFvMaxR && pick_gemv<kPartsArgmax>(p.M, H, trim) != nullptr;
   p.nchunk_t = greedy_t && !p.fg ? 1 : (V + kChunk - 1) / kChunk;
-  // large batches: the MFMA head emits the draft partials in its epilogue (softmax partials, or
-  // argmax partials for argmax drafts)
-  p.fused_mfma = !p.fused && !p.fg && p.M >= kBigMinM;
+  // past the GEMV sizes: the direct-to-LDS MFMA heads (and the register-staged one from kBigMinM
+  // rows) emit the draft partials in their epilogue (softmax partials, or argmax partials for
+  // argmax drafts); the head kernel is the one the separate call takes for the same M and H
+  p.fused_mfma = !p.fused && !p.fg && pick_gemv<kPartsNone>(p.M, H, trim) == nullptr && mfma_head_direct(p.M, H);
   if (p.fused || p.fg) {
     p.nchunk_d = gemv_blocks(Vt);
     p.chunk_d = gemv_rows_per_block(Vt);
@@ -213,10 +214,10 @@ hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, 
     if (e != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   } else if (pl.fused_mfma) {
-    e = D.greedy ? launch_mfma_big<kPartsArgmax>(hidden, weight, keep, vrows, pl.M, H, Vt, logits,
-                                                 GemvParts{D.part, D.k2}, stream, hidt, weight_tiled)
-                 : launch_mfma_big<kPartsSoftmax>(hidden, weight, keep, vrows, pl.M, H, Vt, logits,
-                                                  GemvParts{D.part, D.k2}, stream, hidt, weight_tiled);
+    e = D.greedy ? launch_mfma_head<kPartsArgmax>(hidden, weight, keep, vrows, pl.M, H, Vt, logits,
+                                                  GemvParts{D.part, D.k2}, stream, hidt, weight_tiled)
+                 : launch_mfma_head<kPartsSoftmax>(hidden, weight, keep, vrows, pl.M, H, Vt, logits,
+                                                   GemvParts{D.part, D.k2}, stream, hidt, weight_tiled);
     if (e != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   } else {

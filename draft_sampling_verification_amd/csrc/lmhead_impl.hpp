@@ -565,7 +565,7 @@ GemvFn pick_gemv(int64_t M, int64_t H, bool trim) {
   }
 }
 
-// ---------------------------------------------------------------- large batches (M >= 256)
+// ------------------------------------------------- batches past the GEMV (256-column tiles)
 //
 // 256 x 256 output tiles (hidden rows x head rows), K in steps of 64, one workgroup of four waves
 // per CU (the double-buffered tiles take 144 KB of LDS).  Each wave owns a 128 x 128 quarter as
@@ -577,7 +577,7 @@ GemvFn pick_gemv(int64_t M, int64_t H, bool trim) {
 // row (max and sum of 2^((x - max) k2)), combined across the two waves that share rows.
 constexpr int kBigBM = 256, kBigBN = 256, kBigBK = 64, kBigPad = 8;
 constexpr int kBigRow = kBigBK + kBigPad;  // bf16 per LDS row: 144 bytes
-constexpr int kBigMinM = 129;  // more than one 128-row block: the 256 x 256 or tall tiles
+constexpr int kBigMinM = 129;  // with H % 32 != 0: register-staged 256 x 256 tiles from here, 128 x 128 below
 
 // Tile order of the 256 x 256 kernels.  Each XCD works through one contiguous range of logical
 // tiles (xcd_remap); logical tiles are ordered in groups of kTileGroup hidden-row blocks, walked
@@ -1122,6 +1122,160 @@ __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_tall(const uint16_t
                          reinterpret_cast<float2(*)[kTallBM]>(smem));
 }
 
+// Up to kRowsMaxM hidden rows (decode batches of a few to a few dozen sequences): the head is
+// bound by streaming W^Trim once, so a tile holds every hidden row, padded only to the next
+// multiple of 32, against 256 head rows: one workgroup per 256 head rows streams its 2 MB (H =
+// 4096) of the head once while the hidden rows come from L2.  The 256-row tiles would multiply
+// up to 256 rows whatever M is.  Eight waves, wave w holding all 32 MB tile rows against head
+// columns 32 w .. 32 w + 31 (MB accumulator blocks), so the epilogue merges eight column slots per
+// row.  The loads of a K step are 2 MB hidden-row chunks and 16 head-row chunks of 1 KB (16 rows
+// x 64 bytes, swizzled as in the 256 x 256 kernel), dealt out to the waves in turn; a wave with
+// fewer distinct chunks fetches one of the others again, which writes the same bytes to the same
+// place, so every wave issues the same number of loads per step and one wait count serves all.
+// The ring holds as many K steps as fit in the 160 KB of LDS, at most eight.  Each output sums the
+// same products in the same K order as the other direct-to-LDS kernels: the same logits bits.
+constexpr int kRowsMaxMB = 6;
+constexpr int kRowsMaxM = 32 * kRowsMaxMB;
+
+template <int MB>
+struct RowsTile {
+  static constexpr int kTM = 32 * MB;
+  static constexpr int kChunks = 2 * MB + kBigBN / 16;  // 1 KB loads per K step
+  static constexpr int kLoads = (kChunks + 7) / 8;      // per wave
+  static constexpr int kStageBytes = kChunks * 1024;
+  static constexpr int kFit = (160 * 1024) / kStageBytes;
+  static constexpr int kStages = kFit < 8 ? kFit : 8;
+  static_assert(kStages >= 3 && kLoads * (kStages - 2) < 64, "ring and wait counts");
+};
+
+// One lane's 16-byte direct-to-LDS load (the wave's 64 lanes fill dst .. dst + 1 KB).  A plain
+// device function, so that the builtin's operands never depend on a kernel's template parameters
+// (the host pass checks such a call against its own target and rejects the 16-byte size).
+__device__ __forceinline__ void lds_load16(const uint16_t *src, char *dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 16, 0, 0);
+}
+
+template <int MB, bool TRIM, int PARTS, bool ATILED, bool BTILED>
+__global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_rows(const uint16_t *__restrict__ hidden,
+                                                                  const uint16_t *__restrict__ weight,
+                                                                  const int32_t *__restrict__ keep, int vrows, int M,
+                                                                  int H, int Vt, float *__restrict__ logits,
+                                                                  GemvParts parts) {
+  static_assert(!(BTILED && TRIM), "a K-tiled head is already trimmed");
+  using G = RowsTile<MB>;
+  constexpr int kTM = G::kTM, kS = G::kStages, kL = G::kLoads, kOpA = kTM * kDmaRowBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[kS * G::kStageBytes];
+  const int nbm = (M + kTM - 1) / kTM;
+  const int nbn = (Vt + kBigBN - 1) / kBigBN;
+  const int tile = static_cast<int>(xcd_remap(blockIdx.x, static_cast<int64_t>(nbm) * nbn));
+  int bm, bn;
+  big_tile_of(tile, nbm, nbn, bm, bn);
+  const int m0 = bm * kTM, n0 = bn * kBigBN;
+  const int w = wave_id(), lane = lane_id();
+  const int nk = H / kDmaBK;
+
+  // load j of wave w: chunk q = w + 8 j (wrapped), lane L writing row 16 q + L / 4 of the stage,
+  // slot L % 4, with piece slot ^ f(row) of that row; per K step the source advances by step[j]
+  const uint16_t *src[kL];
+  int64_t step[kL];
+  int dst[kL];
+#pragma unroll
+  for (int j = 0; j < kL; ++j) {
+    int q = w + 8 * j;
+    if (q >= G::kChunks) q -= G::kChunks;
+    dst[j] = q * 1024;
+    if (q < 2 * MB) {
+      const int r = 16 * q + (lane >> 2);
+      const int piece = (lane & 3) ^ dma_swz(r);
+      if (ATILED) {
+        src[j] = hidden + (static_cast<int64_t>(bm) * nk * kTM + r) * kDmaBK + piece * 8;
+        step[j] = static_cast<int64_t>(kTM) * kDmaBK;
+      } else {
+        src[j] = hidden + static_cast<int64_t>(min(m0 + r, M - 1)) * H + piece * 8;
+        step[j] = kDmaBK;
+      }
+    } else {
+      const int r = 16 * (q - 2 * MB) + (lane >> 2);
+      const int piece = (lane & 3) ^ dma_swz(r);
+      if (BTILED) {
+        src[j] = weight + (static_cast<int64_t>(bn) * nk * kBigBN + r) * kDmaBK + piece * 8;
+        step[j] = static_cast<int64_t>(kBigBN) * kDmaBK;
+      } else {
+        const int n = min(n0 + r, Vt - 1);
+        const int64_t brow = TRIM ? kept_row(keep, n, vrows) : static_cast<int64_t>(n);
+        src[j] = weight + brow * H + piece * 8;
+        step[j] = kDmaBK;
+      }
+    }
+  }
+  auto issue = [&](int kstep, int slot) {
+    const int64_t k = min(kstep, nk - 1);
+    char *base = smem + slot * G::kStageBytes;
+#pragma unroll
+    for (int j = 0; j < kL; ++j)
+      lds_load16(src[j] + k * step[j], base + dst[j]);
+  };
+
+  const int wn = 32 * w;
+  const int lr = lane & 31;
+  const int sw = dma_swz(lr);
+  const int off0 = lr * kDmaRowBytes + (((lane >> 5) ^ sw) << 4);
+  const int off1 = lr * kDmaRowBytes + (((2 + (lane >> 5)) ^ sw) << 4);
+  f32x16 acc[MB][1];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[i][0][v] = 0.f;
+  auto slice = [&](int slot, int off) {
+    const char *sa = smem + slot * G::kStageBytes + off;
+    const char *sb = smem + slot * G::kStageBytes + kOpA + wn * kDmaRowBytes + off;
+    bf16x8 a[MB];
+    const bf16x8 b = *reinterpret_cast<const bf16x8 *>(sb);
+#pragma unroll
+    for (int i = 0; i < MB; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(sa + i * 32 * kDmaRowBytes);
+#pragma unroll
+    for (int i = 0; i < MB; ++i) acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, acc[i][0], 0, 0, 0);
+  };
+
+  // step k: both 16-deep slices of slot k % kS; then (wait + barrier) step k + 1 is in LDS and the
+  // slot of step k - 1 is free for the loads of step k + kS - 1; past the last step the last step
+  // is fetched again into the free slot (never read), so every step issues the same loads
+  constexpr int kAhead = kS - 1;
+#pragma unroll
+  for (int s = 0; s < kAhead; ++s) issue(s, s);
+  wait_vmcnt<kL * (kAhead - 1)>();
+  __builtin_amdgcn_s_barrier();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int slot = kt % kS;
+    slice(slot, off0);
+    slice(slot, off1);
+    wait_vmcnt<kL * (kAhead - 2)>();
+    __builtin_amdgcn_s_barrier();
+    issue(kt + kAhead, (kt + kAhead) % kS);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  tile_store<PARTS, MB, 1, kTM>(acc, M, Vt, m0, n0, 0, wn, nbn, bn, logits, parts,
+                               reinterpret_cast<float2(*)[kTM]>(smem));
+}
+
+typedef void (*HeadKernel)(const uint16_t *, const uint16_t *, const int32_t *, int, int, int, int, float *,
+                           GemvParts);
+
+template <bool TRIM, int PARTS, bool ATILED, bool BTILED>
+HeadKernel pick_rows(int mb) {
+  switch (mb) {
+    case 1: return &lmhead_mfma_rows<1, TRIM, PARTS, ATILED, BTILED>;
+    case 2: return &lmhead_mfma_rows<2, TRIM, PARTS, ATILED, BTILED>;
+    case 3: return &lmhead_mfma_rows<3, TRIM, PARTS, ATILED, BTILED>;
+    case 4: return &lmhead_mfma_rows<4, TRIM, PARTS, ATILED, BTILED>;
+    case 5: return &lmhead_mfma_rows<5, TRIM, PARTS, ATILED, BTILED>;
+    case 6: return &lmhead_mfma_rows<6, TRIM, PARTS, ATILED, BTILED>;
+    default: return nullptr;
+  }
+}
+static_assert(kRowsMaxMB == 6, "pick_rows covers 1 .. kRowsMaxMB row blocks");
+
 inline int64_t mfma_big_tiles_n(int64_t Vt) { return (Vt + kBigBN - 1) / kBigBN; }
 
 // Rows per hidden-row block of the large-batch head that reads a K-tiled copy: 384 (the tall
@@ -1132,15 +1286,21 @@ inline int big_tile_rows(int64_t M) {
   return p384 <= p256 ? kTallBM : kBigBM;
 }
 
-// K-tiled copy of the hidden rows for lmhead_mfma_dma8<..., ATILED> and lmhead_mfma_tall, in
-// blocks of R = big_tile_rows(M) rows: out[bm][ks][r][32] = hidden[min(R bm + r, M - 1)][32 ks ..
-// 32 ks + 31] (rows past M repeat the last row; their logits are never stored).  One thread moves
-// one 16-byte piece; a wave reads 16 rows x 64 bytes and writes 1 KB contiguously.  Needs
-// H % 32 == 0.
-// Bytes of the K-tiled hidden copy (0 when the direct-to-LDS kernels do not run).
+// Rows per hidden-row block of the direct-to-LDS heads: all M rows padded to a multiple of 32 up
+// to kRowsMaxM (lmhead_mfma_rows), else big_tile_rows(M).
+inline int head_tile_rows(int64_t M) {
+  return M <= kRowsMaxM ? static_cast<int>((M + 31) / 32 * 32) : big_tile_rows(M);
+}
+
+// K-tiled copy of the hidden rows for the direct-to-LDS heads (lmhead_mfma_rows, _dma8 and _tall
+// with ATILED), in blocks of R = head_tile_rows(M) rows: out[bm][ks][r][32] = hidden[min(R bm + r,
+// M - 1)][32 ks .. 32 ks + 31] (rows past M repeat the last row; their logits are never stored).
+// One thread moves one 16-byte piece; a wave reads 16 rows x 64 bytes and writes 1 KB
+// contiguously.  Needs H % 32 == 0.
+// Bytes of the K-tiled hidden copy (0 when H % 32 != 0: the direct-to-LDS kernels do not run).
 inline size_t hidden_tiles_bytes(int64_t M, int64_t H) {
-  if (M < kBigMinM || H % kDmaBK != 0) return 0;
-  const int64_t R = big_tile_rows(M);
+  if (H % kDmaBK != 0) return 0;
+  const int64_t R = head_tile_rows(M);
   return static_cast<size_t>((M + R - 1) / R) * R * static_cast<size_t>(H) * 2;
 }
 
@@ -1175,7 +1335,7 @@ inline TileParams hidden_tiles_params(const uint16_t *hidden, int64_t M, int64_t
   T.out = out;
   T.M = static_cast<int>(M);
   T.H = static_cast<int>(H);
-  T.rows = big_tile_rows(M);
+  T.rows = head_tile_rows(M);
   T.pieces = static_cast<int64_t>(hidden_tiles_bytes(M, H) / 16);
   return T;
 }
@@ -1200,19 +1360,37 @@ __global__ __launch_bounds__(kBlock) void softmax_partial_tiles(SmParams P, Tile
 
 
 
-// PARTS = kPartsNone (the separate LM-head call): the hidden rows as given, 256 x 256 tiles.
-// kPartsSoftmax / kPartsArgmax (the fused block's head, with its draft partials): when H % 32 == 0
-// hidden_tiled must hold the K-tiled copy of the hidden rows made by hidden_tiles, in blocks of
-// big_tile_rows(M) rows, whose 384-row blocks select the tall tiles; weight_tiled: NULL, or the
-// K-tiled trimmed head of vt_trim_head_tiled (weight and keep are then not read by the kernel).
-// Other H take the register-staged kernel on the rows as given.
+// The MFMA heads with whole 32-column K steps (any M), or with M >= kBigMinM (any H).
+// PARTS = kPartsNone (the separate LM-head call): the hidden rows as given; up to kRowsMaxM rows
+// in one block of all of them, else 256 x 256 tiles.  kPartsSoftmax / kPartsArgmax (the fused
+// block's head, with its draft partials): when H % 32 == 0 hidden_tiled must hold the K-tiled copy
+// of the hidden rows made by hidden_tiles, in blocks of head_tile_rows(M) rows, which select the
+// kernel (all rows up to kRowsMaxM, 384-row tall tiles or 256 x 256 tiles); weight_tiled: NULL, or
+// the K-tiled trimmed head of vt_trim_head_tiled (weight and keep are then not read by the
+// kernel).  Other H take the register-staged kernel on the rows as given.
 template <int PARTS>
-inline hipError_t launch_mfma_big(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int vrows,
-                                  int64_t M, int64_t H, int64_t Vt, float *logits, GemvParts parts,
-                                  hipStream_t stream, const uint16_t *hidden_tiled = nullptr,
-                                  const uint16_t *weight_tiled = nullptr) {
+inline hipError_t launch_mfma_head(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int vrows,
+                                   int64_t M, int64_t H, int64_t Vt, float *logits, GemvParts parts,
+                                   hipStream_t stream, const uint16_t *hidden_tiled = nullptr,
+                                   const uint16_t *weight_tiled = nullptr) {
   const int64_t tiles = ((M + kBigBM - 1) / kBigBM) * mfma_big_tiles_n(Vt);
   const int iM = static_cast<int>(M), iH = static_cast<int>(H), iV = static_cast<int>(Vt);
+  if (H % kDmaBK == 0 && M <= kRowsMaxM) {
+    const int mb = static_cast<int>((M + 31) / 32);
+    const unsigned grid = static_cast<unsigned>(mfma_big_tiles_n(Vt));
+    if constexpr (PARTS == kPartsNone) {
+      if (hidden_tiled || weight_tiled) return hipErrorInvalidValue;
+      const HeadKernel f = keep ? pick_rows<true, PARTS, false, false>(mb) : pick_rows<false, PARTS, false, false>(mb);
+      return launch(f, dim3(grid), dim3(kDma8Block), 0, stream, hidden, weight, keep, vrows, iM, iH, iV, logits, parts);
+    } else {
+      if (!hidden_tiled) return hipErrorInvalidValue;
+      const HeadKernel f = weight_tiled ? pick_rows<false, PARTS, true, true>(mb)
+                                        : (keep ? pick_rows<true, PARTS, true, false>(mb)
+                                                : pick_rows<false, PARTS, true, false>(mb));
+      return launch(f, dim3(grid), dim3(kDma8Block), 0, stream, hidden_tiled, weight_tiled ? weight_tiled : weight,
+                    keep, vrows, iM, iH, iV, logits, parts);
+    }
+  }
   if (H % kDmaBK == 0) {
     if constexpr (PARTS == kPartsNone) {
       if (hidden_tiled || weight_tiled) return hipErrorInvalidValue;
@@ -1249,10 +1427,14 @@ inline hipError_t launch_gemv(GemvFn fn, const uint16_t *hidden, const uint16_t 
                 vrows, static_cast<int>(H), static_cast<int>(Vt), gemv_rows_per_block(Vt), logits, parts);
 }
 
+// Whether the MFMA head for M hidden rows is one of launch_mfma_head's kernels (else the 128 x
+// 128 tiles).
+inline bool mfma_head_direct(int64_t M, int64_t H) { return H % kDmaBK == 0 || M >= kBigMinM; }
+
 inline hipError_t launch_mfma(const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int vrows,
                               int64_t M, int64_t H, int64_t Vt, float *logits, hipStream_t stream) {
-  if (M >= kBigMinM)
-    return launch_mfma_big<kPartsNone>(hidden, weight, keep, vrows, M, H, Vt, logits, GemvParts{}, stream);
+  if (mfma_head_direct(M, H))
+    return launch_mfma_head<kPartsNone>(hidden, weight, keep, vrows, M, H, Vt, logits, GemvParts{}, stream);
   const int64_t tiles = ((M + kBM - 1) / kBM) * ((Vt + kBN - 1) / kBN);
   return launch(lmhead_mfma, dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0, stream, hidden, weight, keep,
                 vrows, static_cast<int>(M), static_cast<int>(H), static_cast<int>(Vt), logits);

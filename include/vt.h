@@ -75,11 +75,13 @@ typedef enum { VT_F32 = 0, VT_BF16 = 1 } vt_dtype_t;
  *   not depend on the row, so trimmed logits equal untrimmed logits gathered at keep_ids bit for bit.
  *   The order does depend on M, which picks the kernel: a GEMV when M <= 8 and
  *   M * ceil(H / 512) <= 48 (lanes hold partial sums over 16-byte pieces of a row, reduced across
- *   lanes); otherwise 128 x 128 MFMA tiles when M <= 128 and 256 x 256 MFMA tiles when M > 128
- *   (sums over K in MFMA steps of 16).  A hidden row's
- *   logits may therefore differ in the last bits between batch sizes (each within the
- *   recursive-summation bound H 2^-24 sum_k |h_k w_k|), and so may a decision taken on them, but
- *   only where it lies within rounding of its uniform.
+ *   lanes); otherwise an MFMA kernel: when H % 32 == 0 one block of all M rows (padded to a
+ *   multiple of 32) per 256 head rows up to M = 192, 256 x 256 tiles beyond; for other H 128 x 128
+ *   tiles up to M = 128, register-staged 256 x 256 tiles beyond.  Every MFMA kernel sums a
+ *   logit's products in MFMA steps of 16 in ascending K, so they all give the same bits; between
+ *   the GEMV and the MFMA kernels a hidden row's logits may differ in the last bits (each within
+ *   the recursive-summation bound H 2^-24 sum_k |h_k w_k|), and so may a decision taken on them,
+ *   but only where it lies within rounding of its uniform.
  *   Errors: INVALID_ARG for NULL hidden/weight/logits, M, H, Vt or V_rows <= 0, Vt > V_rows when
  *   keep_ids is NULL; UNSUPPORTED for H % 8 != 0 or a hidden/weight base not 16-byte aligned.
  */
@@ -177,33 +179,36 @@ size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
  * first pass and, in extra workgroups, the target rows' first pass; one chunk pass over the
  * full vocabulary forms the log-normalisers, draft draws, accept tests and residual chunk sums;
  * one final pass draws the last token.  Larger batches take 5 (LM head with the draft partials,
- * target partials, one combine launch for both row sets, two verify passes).  When B*R > 128 and
- * H % 32 == 0 the target partials launch also copies the hidden rows K-tiled into the workspace
- * (the head then reads each K step of a block of hidden rows as one contiguous run; same products,
- * same logits); without target partials (V <= 4096 or greedy verification) the copy is a launch of
- * its own.  That head takes 384 x 256 tiles (384 hidden rows) when padding
- * B*R to 384-row blocks adds no more rows than padding it to 256-row blocks (B*R = 2304, 288,
- * 756 ...), else 256 x 256 tiles (B*R = 144, 512 ...); both sum the same products in the same order.
+ * target partials, one combine launch for both row sets, two verify passes).  Past the GEMV
+ * sizes with H % 32 == 0 the target partials launch also copies the hidden rows K-tiled into the
+ * workspace (the head then reads each K step of a block of hidden rows as one contiguous run; same
+ * products, same logits); without target partials (V <= 4096 or greedy verification) the copy is
+ * a launch of its own.  That head takes one block of all hidden rows up to B*R = 192, and beyond
+ * 384 x 256 tiles (384 hidden rows) when padding B*R to 384-row blocks adds no more rows than
+ * padding it to 256-row blocks (B*R = 2304, 288, 756 ...), else 256 x 256 tiles (B*R = 224, 512
+ * ...); all sum the same products in the same order as the separate call's kernel.
  *   Pages: as for the four calls above.
  *
  *   hidden bf16 [B*R][H] (row b*R + i is sequence b's i-th draft position); weight bf16 [V][H]
  *   (the full head); weight_tiled: NULL, or W^Trim in the K-tiled layout vt_trim_head_tiled makes
- *   from this weight and keep_ids (vt_keepset.h), which the large-batch head then reads in place of
- *   gathering rows of weight (only when B*R > 128 and H % 32 == 0; ignored otherwise; same products in the same order, so the same logits bits; the library cannot check
+ *   from this weight and keep_ids (vt_keepset.h), which the MFMA head then reads in place of
+ *   gathering rows of weight (only past the GEMV sizes and when H % 32 == 0; ignored otherwise;
+ *   same products in the same order, so the same logits bits; the library cannot check
  *   that it matches weight and keep_ids); keep_ids int32 [Vt] and full_to_trim int32 [V] (both
- *   NULL iff the head is untrimmed, Vt == V); target_logits [B][gamma+1][V] (fp32 or bf16); u_draft fp32 [B*R],
- *   u_accept fp32 [B][gamma], u_final fp32 [B].
+ *   NULL iff the head is untrimmed, Vt == V); target_logits [B][gamma+1][V] (fp32 or bf16);
+ *   u_draft fp32 [B*R], u_accept fp32 [B][gamma], u_final fp32 [B].
  *   Outputs: draft_logits fp32 [B*R][Vt], draft_lse fp64 [B*R], draft_ids int32 [B*R] (trimmed
  *   ids), target_lse fp64 [B*(gamma+1)], out_tokens int32 [B][gamma+1], out_num_accepted int32 [B].
  *   lmhead_begin / lmhead_end: optional (NULL) events, recorded on `stream` immediately before and
  *   after the LM-head kernel, for timing it inside the call.
  *   Results are those of the four calls (the logits and target_lse bit for bit), except that on
  *   the fused paths the draft running sums are chunked by the LM head's own blocks of head rows
- *   instead of 4096-element chunks: ceil(Vt / 256) rounded up to a multiple of 4 rows when B*R <= 8,
- *   256 rows when B*R > 128.  Draws can then differ from the separate calls only where a CDF
- *   boundary lies within rounding of the uniform.  Sequences are independent: a sequence's
- *   outputs are those it gets alone, up to the LM head's batch-size-dependent summation order
- *   (see vt_lmhead_trimmed), i.e. they can differ only at a decision within rounding of its
+ *   instead of 4096-element chunks: ceil(Vt / 256) rounded up to a multiple of 4 rows on the GEMV,
+ *   256 rows on the MFMA heads with partials (H % 32 == 0, or B*R > 128).  Draws can then differ
+ *   from the separate calls only where a CDF boundary lies within rounding of the uniform.
+ *   Sequences are independent: a sequence's outputs are those it gets alone, up to the LM head's
+ *   batch-size-dependent summation order and draft chunking (GEMV or MFMA head, see
+ *   vt_lmhead_trimmed), i.e. they can differ only at a decision within rounding of its
  *   uniform; every target-side quantity (target_lse, p, the residual) is computed per row in an
  *   order that depends on neither B nor the row.
  *   target_T = 0 selects greedy verification as in vt_spec_verify ([VT] §4): no target softmax
@@ -212,10 +217,10 @@ size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
  *   maximum, draft_lse the row maximum, and u_draft is not read (may be NULL); the LM head then
  *   emits argmax partials instead of softmax partials: at decode sizes (B*R <= 8) per block of
  *   head rows for the draft rows and, in extra workgroups, per 4096-chunk for the target rows,
- *   and one more launch finishes the block (2 launches); from B*R > 128 per 256 head rows (the
- *   same large-batch head, K-tiled copies and weight_tiled as with sampled drafts), finished by
- *   the combine launch; in between the head runs without partials and a separate pass finds the
- *   draft rows' argmaxes.
+ *   and one more launch finishes the block (2 launches); on the MFMA heads with partials per 256
+ *   head rows (the same kernels, K-tiled copies and weight_tiled as with sampled drafts), finished
+ *   by the combine launch; otherwise (the GEMV without the decode path, or H % 32 != 0 with
+ *   B*R <= 128) the head runs without partials and a separate pass finds the draft rows' argmaxes.
  *   Errors: INVALID_ARG for NULL required pointers, B, gamma, H, V or Vt <= 0, R < gamma, Vt > V,
  *   a temperature not finite or < 0, draft_T = 0 with target_T > 0, keep_ids/full_to_trim
  *   inconsistent with Vt; UNSUPPORTED for

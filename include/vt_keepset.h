@@ -87,7 +87,7 @@ vt_status_t vt_trim_head(const uint16_t *weight, int64_t V_rows, int64_t H, cons
 
 /*
  * vt_trim_head_tiled -- the same W^Trim ([VT] §3 Eq. 1, second line: the kept rows in keep_ids
- * order), stored K-tiled for the large-batch LM head of vt_spec_block: row j = 256 b + r,
+ * order), stored K-tiled for the MFMA LM head of vt_spec_block: row j = 256 b + r,
  * columns 32 s .. 32 s + 31 sit at tiled[b][s][r][0 .. 31], so each 256-row, 32-column slice is
  * one contiguous 16 KB run.  [VT] §3 builds W^Trim once, from calibration counts, before any
  * decoding, so its storage layout is a free choice; this one is what the head's loads read fastest.

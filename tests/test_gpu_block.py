@@ -28,10 +28,16 @@ SCALED = {
     # second ragged), 512 takes 256-row tiles (two blocks; 384-row blocks would pad to 768)
     "c5-tall-two-blocks": CONFIGS[5].scaled(B=84, V=13000, Vt=6001, H=256),
     "c4-square-two-blocks": CONFIGS[4].scaled(B=64, V=20000, Vt=5000, H=256),
-    # the two sides of the switch to the fused 256 x 256 tiles: 128 hidden rows take 128 x 128
-    # tiles and a separate draft softmax, 129 take one 256-row block, 127 of its rows padding
-    "c4-128-rows": CONFIGS[4].scaled(B=16, V=20000, Vt=5000, H=256),
-    "c4-129-rows": CONFIGS[4].scaled(B=43, gamma=2, R=3, V=20000, Vt=5000, H=256),
+    # past the GEMV sizes, up to 192 hidden rows: one block of all rows padded to a multiple of
+    # 32 (9 rows: one 32-row block; 96: three; 128, 129: four, five; 192: six), then 256 x 256
+    # tiles from 193; with H % 32 != 0 below 129 rows, 128 x 128 tiles and a separate draft softmax
+    "rows-9": CONFIGS[4].scaled(B=3, gamma=2, R=3, V=20000, Vt=5000, H=256),
+    "rows-96": CONFIGS[4].scaled(B=12, V=20000, Vt=5000, H=256),
+    "rows-128": CONFIGS[4].scaled(B=16, V=20000, Vt=5000, H=256),
+    "rows-129": CONFIGS[4].scaled(B=43, gamma=2, R=3, V=20000, Vt=5000, H=256),
+    "rows-192": CONFIGS[4].scaled(B=24, V=20000, Vt=5000, H=256),
+    "square-194": CONFIGS[4].scaled(B=97, gamma=1, R=2, V=20000, Vt=5000, H=256),
+    "small-batch-odd-H": CONFIGS[4].scaled(B=4, V=9001, Vt=1234, H=520),
 }
 
 

@@ -91,12 +91,11 @@ def _merge(parts):
 @pytest.mark.parametrize("c,B,follow", [(4, 40, 0.5), (5, 32, 0.5), (4, 40, 0.0), (4, 64, 0.5)])
 def test_batch_independence_across_head_kernels(c, B, follow):
     """The same sequences alone (B = 1: the GEMV head and the three-launch path for 8 draft rows,
-    128 x 128 MFMA tiles for 9), in batches of at most 128 hidden rows (128 x 128 MFMA tiles) and in
-    a batch of 256+ hidden rows (direct-to-LDS tiles: 384 x 256 for 320 and 288 rows, 256 x 256 for
-    512).
-    The logits' fp32 summation order differs between the three head kernels, so a decision may
-    differ only where the oracle places it within the band; every other output must be the same,
-    and each run must match the oracle."""
+    a one-block MFMA head for 9), in batches of at most 128 hidden rows (one block of all rows) and
+    in a batch of 256+ hidden rows (384 x 256 tiles for 320 and 288 rows, 256 x 256 for 512).
+    The MFMA kernels sum in one order, the GEMV in another, and the draft running sums are chunked
+    by the head's blocks, so a decision may differ only where the oracle places it within the
+    band; every other output must be the same, and each run must match the oracle."""
     cfg = CONFIGS[c].scaled(B=B, V=20000, Vt=6000, H=512)
     assert cfg.B * cfg.R >= 256
     say(f"batch independence config {c}: B={B} (M={cfg.B * cfg.R}), follow={follow}")

@@ -2,8 +2,9 @@
 
 Tolerance: |gpu - oracle| <= H * 2^-24 * sum_k |h_k w_k| per logit (the recursive-summation
 bound for fp32 accumulation of exact bf16 products) -- the observed error is also reported.
-Shapes cover the dot2 GEMV (M <= 8) and the MFMA tiles (M > 8 or large H), ragged row and K
-tails, trimmed and untrimmed heads."""
+Shapes cover the dot2 GEMV (M <= 8) and the MFMA kernels (M > 8 or large H: all rows in one
+block up to 192 rows, 256 x 256 tiles beyond; 128 x 128 and register-staged tiles when H is not a
+multiple of 32), ragged row and K tails, trimmed and untrimmed heads."""
 import numpy as np
 import pytest
 import torch
@@ -38,7 +39,13 @@ CASES = [
     (8, 1024, 777, 300, True),
     (3, 4096, 2000, 999, True),     # GEMV at H = 4096
     (9, 520, 1000, 513, True),      # MFMA (M > 8), K tail inside a 32-wide step
-    (130, 256, 1500, 1300, True),   # MFMA, M spans two 128-row tiles, ragged
+    (130, 256, 1500, 1300, True),   # MFMA, all rows in one block (160), ragged
+    (33, 512, 3001, 2500, True),    # one block of 64 rows, ragged rows and head rows
+    (64, 1024, 3000, 3000, False),  # one block of exactly 64 rows, untrimmed
+    (96, 256, 2000, 777, True),     # 96 rows
+    (192, 512, 1200, 1100, True),   # the largest all-rows block (192)
+    (193, 512, 1200, 1100, True),   # one row past it: 256 x 256 tiles
+    (100, 520, 1000, 700, True),    # H % 32 != 0 at 100 rows: 128 x 128 tiles
     (512, 3072, 2000, 1000, True),  # MFMA at config 4's M and H
     (7, 8192, 700, 700, False),     # M * ceil(H/512) too large for registers: MFMA
     (2304, 512, 300, 257, True),    # MFMA at config 5's M
@@ -77,3 +84,17 @@ def test_pre_gathered_head_equals_gather():
     a = _run(h, w, keep, 1500)
     b = _run(h, np.ascontiguousarray(w[keep]), None, 1500)
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("H,rows", [(1024, (9, 40, 96, 130, 192, 193, 256)), (520, (9, 100, 128, 129, 256))])
+def test_mfma_kernels_sum_in_one_order(H, rows):
+    # every MFMA kernel sums a logit's products in the same K order, so a hidden row's logits are
+    # the same bits whatever the batch's row count selects (H % 32 == 0: all-rows blocks of 32 ..
+    # 192 rows, 256 x 256 tiles; other H: 128 x 128 and register-staged 256 x 256 tiles); only the
+    # GEMV (M <= 8) sums differently
+    V, Vt = 2500, 2100
+    h, w, keep = _inputs(300, H, V, Vt, True, seed=13)
+    want = _run(h, w, keep, Vt)
+    for M in rows:
+        say(f"rows 0..{M - 1} alone against the 300-row call")
+        assert np.array_equal(_run(np.ascontiguousarray(h[:M]), w, keep, Vt), want[:M])
