@@ -59,8 +59,8 @@ BlockPlan plan_block(int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt,
     p.nchunk_d = gemv_blocks(Vt);
     p.chunk_d = gemv_rows_per_block(Vt);
   } else if (p.fused_mfma) {
-    p.nchunk_d = mfma_big_tiles_n(Vt);
-    p.chunk_d = kBigBN;
+    p.chunk_d = head_tile_cols(p.M, H, Vt);
+    p.nchunk_d = (Vt + p.chunk_d - 1) / p.chunk_d;
   } else {
     p.nchunk_d = (Vt + kChunk - 1) / kChunk;
     p.chunk_d = kChunk;
@@ -84,7 +84,7 @@ BlockPlan plan_block(int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt,
   p.off_wbuf = off;
   if (p.fv) off += align_up(static_cast<size_t>(2 * B * V) * sizeof(float), 256);  // final-draw weights and p_n
   p.off_hidt = off;
-  p.hidt_bytes = p.fused_mfma ? hidden_tiles_bytes(p.M, H) : 0;
+  p.hidt_bytes = p.fused_mfma ? hidden_tiles_bytes(p.M, H, Vt) : 0;
   off += align_up(p.hidt_bytes, 256);
   p.bytes = off;
   return p;
@@ -189,7 +189,7 @@ hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, 
   // the large-batch head reads the hidden rows K-tiled (one contiguous run per K step of a block of
   // hidden rows); the copy rides in extra workgroups of the target partials launch when there is one
   uint16_t *hidt = pl.hidt_bytes ? reinterpret_cast<uint16_t *>(hidt_base) : nullptr;
-  const TileParams tp = hidden_tiles_params(hidden, pl.M, H, hidt);
+  const TileParams tp = hidden_tiles_params(hidden, pl.M, H, Vt, hidt);
   // 1. target partials (or a whole single-chunk target softmax); greedy verification needs none
   if (t_multi && hidt)
     e = launch(softmax_partial_tiles<TinT, kVecT>,

@@ -593,23 +593,23 @@ __device__ __forceinline__ void big_tile_of(int tile, int nbm, int nbn, int &bm,
   bn = in / rows;
 }
 
-// Epilogue of a TM x 256 tile (TM hidden rows x 256 head rows) whose waves hold MI x NJ
+// Epilogue of a TM x BN tile (TM hidden rows x BN head rows) whose waves hold MI x NJ
 // accumulator blocks of 32 x 32 each: the logits, and per hidden row the draft partials of the
-// tile's 256 columns: with PARTS = kPartsSoftmax the max and sum of 2^((x - max) k2), with
-// kPartsArgmax the max and the lowest column index holding it (for argmax drafts).  Per row block of a
-// wave the 16 row maxima over the wave's 32 NJ columns are reduce-scattered over the half-wave
-// (a lane holds 16 rows of its half in each block), gathered back for the exponentials, and the
-// sums reduce-scattered: 47 lane exchanges per block, 16 maxima and sums in registers at a time.
-// The 256 / (32 NJ) waves that cover the same rows merge through LDS.  All threads of the
-// workgroup must call.
+// tile's BN columns: with PARTS = kPartsSoftmax the max and sum of 2^((x - max) k2), with
+// kPartsArgmax the max and the lowest column index holding it (for argmax drafts).  Per row block
+// of a wave the 16 row maxima over the wave's 32 NJ columns are reduce-scattered over the
+// half-wave (a lane holds 16 rows of its half in each block), gathered back for the exponentials,
+// and the sums reduce-scattered: 47 lane exchanges per block, 16 maxima and sums in registers at a
+// time.  The BN / (32 NJ) waves that cover the same rows merge through LDS.  All threads of the
+// workgroup must call (at least TM of them).
 // wpart: LDS scratch of kSlots x TM float2 that the caller no longer needs (its operand tiles), so
 // that the kernel keeps a single LDS object (a second one makes the compiler wait for every
 // outstanding direct-to-LDS load before any LDS read in the main loop).
-template <int PARTS, int MI, int NJ, int TM>
+template <int PARTS, int MI, int NJ, int TM, int BN = kBigBN>
 __device__ __forceinline__ void tile_store(const f32x16 (&acc)[MI][NJ], int M, int Vt, int m0, int n0, int wm,
                                            int wn, int nbn, int bn, float *__restrict__ logits,
                                            const GemvParts &parts, float2 (*wpart)[TM]) {
-  constexpr int kSlots = kBigBN / (32 * NJ);  // waves covering the same tile rows
+  constexpr int kSlots = BN / (32 * NJ);  // waves covering the same tile rows
   const int tid = threadIdx.x, lane = lane_id(), lr = lane & 31;
   const int slot = wn / (32 * NJ);
   // 32x32 accumulator layout: lane l holds column l % 32; register v holds row
@@ -1124,27 +1124,34 @@ __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_tall(const uint16_t
 
 // Up to kRowsMaxM hidden rows (decode batches of a few to a few dozen sequences): the head is
 // bound by streaming W^Trim once, so a tile holds every hidden row, padded only to the next
-// multiple of 32, against 256 head rows: one workgroup per 256 head rows streams its 2 MB (H =
-// 4096) of the head once while the hidden rows come from L2.  The 256-row tiles would multiply
-// up to 256 rows whatever M is.  Eight waves, wave w holding all 32 MB tile rows against head
-// columns 32 w .. 32 w + 31 (MB accumulator blocks), so the epilogue merges eight column slots per
-// row.  The loads of a K step are 2 MB hidden-row chunks and 16 head-row chunks of 1 KB (16 rows
-// x 64 bytes, swizzled as in the 256 x 256 kernel), dealt out to the waves in turn; a wave with
-// fewer distinct chunks fetches one of the others again, which writes the same bytes to the same
-// place, so every wave issues the same number of loads per step and one wait count serves all.
-// The ring holds as many K steps as fit in the 160 KB of LDS, at most eight.  Each output sums the
-// same products in the same K order as the other direct-to-LDS kernels: the same logits bits.
+// multiple of 32, against BN head rows: one workgroup per BN head rows streams its share of the
+// head once while the hidden rows come from L2.  The 256-row tiles would multiply up to 256 rows
+// whatever M is.  BN / 32 waves, wave w holding all 32 MB tile rows against head columns 32 w ..
+// 32 w + 31 (MB accumulator blocks), so the epilogue merges BN / 32 column slots per row.  BN =
+// 256 (eight waves, one workgroup per CU and 160 KB of LDS) when the head has at least kCUs
+// blocks of 256 rows, else BN = 128 (four waves, two workgroups per CU and 80 KB each), so that a
+// 32768-row head still spreads over every CU.  The loads of a K step are 2 MB hidden-row chunks
+// and BN / 16 head-row chunks of 1 KB (16 rows x 64 bytes, swizzled as in the 256 x 256 kernel),
+// dealt out to the waves in turn; a wave with fewer distinct chunks fetches one of the others
+// again, which writes the same bytes to the same place, so every wave issues the same number of
+// loads per step and one wait count serves all.  The ring holds as many K steps as fit the
+// workgroup's LDS, at most eight.  Each output sums the same products in the same K order as the
+// other direct-to-LDS kernels: the same logits bits.
 constexpr int kRowsMaxMB = 6;
 constexpr int kRowsMaxM = 32 * kRowsMaxMB;
+constexpr int kCUs = 256;  // compute units of the part
 
-template <int MB>
+template <int MB, int BN>
 struct RowsTile {
   static constexpr int kTM = 32 * MB;
-  static constexpr int kChunks = 2 * MB + kBigBN / 16;  // 1 KB loads per K step
-  static constexpr int kLoads = (kChunks + 7) / 8;      // per wave
+  static constexpr int kWaves = BN / 32;
+  static constexpr int kThreads = kWave * kWaves;
+  static constexpr int kChunks = 2 * MB + BN / 16;  // 1 KB loads per K step
+  static constexpr int kLoads = (kChunks + kWaves - 1) / kWaves;  // per wave
   static constexpr int kStageBytes = kChunks * 1024;
-  static constexpr int kFit = (160 * 1024) / kStageBytes;
+  static constexpr int kFit = (160 * 1024 / (256 / BN)) / kStageBytes;
   static constexpr int kStages = kFit < 8 ? kFit : 8;
+  static_assert(BN == 128 || BN == 256, "tile widths");
   static_assert(kStages >= 3 && kLoads * (kStages - 2) < 64, "ring and wait counts");
 };
 
@@ -1155,33 +1162,35 @@ __device__ __forceinline__ void lds_load16(const uint16_t *src, char *dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 16, 0, 0);
 }
 
-template <int MB, bool TRIM, int PARTS, bool ATILED, bool BTILED>
-__global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_rows(const uint16_t *__restrict__ hidden,
-                                                                  const uint16_t *__restrict__ weight,
-                                                                  const int32_t *__restrict__ keep, int vrows, int M,
-                                                                  int H, int Vt, float *__restrict__ logits,
-                                                                  GemvParts parts) {
+template <int MB, int BN, bool TRIM, int PARTS, bool ATILED, bool BTILED>
+__global__ __launch_bounds__(kWave * (BN / 32)) void lmhead_mfma_rows(const uint16_t *__restrict__ hidden,
+                                                                               const uint16_t *__restrict__ weight,
+                                                                               const int32_t *__restrict__ keep,
+                                                                               int vrows, int M, int H, int Vt,
+                                                                               float *__restrict__ logits,
+                                                                               GemvParts parts) {
   static_assert(!(BTILED && TRIM), "a K-tiled head is already trimmed");
-  using G = RowsTile<MB>;
-  constexpr int kTM = G::kTM, kS = G::kStages, kL = G::kLoads, kOpA = kTM * kDmaRowBytes;
+  using G = RowsTile<MB, BN>;
+  constexpr int kTM = G::kTM, kS = G::kStages, kL = G::kLoads, kW = G::kWaves, kOpA = kTM * kDmaRowBytes;
   __shared__ __attribute__((aligned(1024))) char smem[kS * G::kStageBytes];
   const int nbm = (M + kTM - 1) / kTM;
-  const int nbn = (Vt + kBigBN - 1) / kBigBN;
+  const int nbn = (Vt + BN - 1) / BN;
   const int tile = static_cast<int>(xcd_remap(blockIdx.x, static_cast<int64_t>(nbm) * nbn));
   int bm, bn;
   big_tile_of(tile, nbm, nbn, bm, bn);
-  const int m0 = bm * kTM, n0 = bn * kBigBN;
+  const int m0 = bm * kTM, n0 = bn * BN;
   const int w = wave_id(), lane = lane_id();
   const int nk = H / kDmaBK;
 
-  // load j of wave w: chunk q = w + 8 j (wrapped), lane L writing row 16 q + L / 4 of the stage,
-  // slot L % 4, with piece slot ^ f(row) of that row; per K step the source advances by step[j]
+  // load j of wave w: chunk q = w + kW j (wrapped), lane L writing row 16 q + L / 4 of the stage,
+  // slot L % 4, with piece slot ^ f(row) of that row; per K step the source advances by step[j].
+  // The K-tiled W^Trim comes in 256-row blocks: a 128-row tile is one half of one.
   const uint16_t *src[kL];
   int64_t step[kL];
   int dst[kL];
 #pragma unroll
   for (int j = 0; j < kL; ++j) {
-    int q = w + 8 * j;
+    int q = w + kW * j;
     if (q >= G::kChunks) q -= G::kChunks;
     dst[j] = q * 1024;
     if (q < 2 * MB) {
@@ -1198,8 +1207,9 @@ __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_rows(const uint16_t
       const int r = 16 * (q - 2 * MB) + (lane >> 2);
       const int piece = (lane & 3) ^ dma_swz(r);
       if (BTILED) {
-        src[j] = weight + (static_cast<int64_t>(bn) * nk * kBigBN + r) * kDmaBK + piece * 8;
-        step[j] = static_cast<int64_t>(kBigBN) * kDmaBK;
+        src[j] = weight + (static_cast<int64_t>(n0 / kTileRows) * nk * kTileRows + n0 % kTileRows + r) * kDmaBK +
+                 piece * 8;
+        step[j] = static_cast<int64_t>(kTileRows) * kDmaBK;
       } else {
         const int n = min(n0 + r, Vt - 1);
         const int64_t brow = TRIM ? kept_row(keep, n, vrows) : static_cast<int64_t>(n);
@@ -1212,8 +1222,7 @@ __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_rows(const uint16_t
     const int64_t k = min(kstep, nk - 1);
     char *base = smem + slot * G::kStageBytes;
 #pragma unroll
-    for (int j = 0; j < kL; ++j)
-      lds_load16(src[j] + k * step[j], base + dst[j]);
+    for (int j = 0; j < kL; ++j) lds_load16(src[j] + k * step[j], base + dst[j]);
   };
 
   const int wn = 32 * w;
@@ -1255,52 +1264,69 @@ __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_rows(const uint16_t
   }
   wait_vmcnt<0>();
   __syncthreads();
-  tile_store<PARTS, MB, 1, kTM>(acc, M, Vt, m0, n0, 0, wn, nbn, bn, logits, parts,
-                               reinterpret_cast<float2(*)[kTM]>(smem));
+  tile_store<PARTS, MB, 1, kTM, BN>(acc, M, Vt, m0, n0, 0, wn, nbn, bn, logits, parts,
+                                   reinterpret_cast<float2(*)[kTM]>(smem));
 }
 
 typedef void (*HeadKernel)(const uint16_t *, const uint16_t *, const int32_t *, int, int, int, int, float *,
                            GemvParts);
 
-template <bool TRIM, int PARTS, bool ATILED, bool BTILED>
-HeadKernel pick_rows(int mb) {
+template <int BN, bool TRIM, int PARTS, bool ATILED, bool BTILED>
+HeadKernel pick_rows_bn(int mb) {
   switch (mb) {
-    case 1: return &lmhead_mfma_rows<1, TRIM, PARTS, ATILED, BTILED>;
-    case 2: return &lmhead_mfma_rows<2, TRIM, PARTS, ATILED, BTILED>;
-    case 3: return &lmhead_mfma_rows<3, TRIM, PARTS, ATILED, BTILED>;
-    case 4: return &lmhead_mfma_rows<4, TRIM, PARTS, ATILED, BTILED>;
-    case 5: return &lmhead_mfma_rows<5, TRIM, PARTS, ATILED, BTILED>;
-    case 6: return &lmhead_mfma_rows<6, TRIM, PARTS, ATILED, BTILED>;
+    case 1: return &lmhead_mfma_rows<1, BN, TRIM, PARTS, ATILED, BTILED>;
+    case 2: return &lmhead_mfma_rows<2, BN, TRIM, PARTS, ATILED, BTILED>;
+    case 3: return &lmhead_mfma_rows<3, BN, TRIM, PARTS, ATILED, BTILED>;
+    case 4: return &lmhead_mfma_rows<4, BN, TRIM, PARTS, ATILED, BTILED>;
+    case 5: return &lmhead_mfma_rows<5, BN, TRIM, PARTS, ATILED, BTILED>;
+    case 6: return &lmhead_mfma_rows<6, BN, TRIM, PARTS, ATILED, BTILED>;
     default: return nullptr;
   }
 }
-static_assert(kRowsMaxMB == 6, "pick_rows covers 1 .. kRowsMaxMB row blocks");
+static_assert(kRowsMaxMB == 6, "pick_rows_bn covers 1 .. kRowsMaxMB row blocks");
+
+template <bool TRIM, int PARTS, bool ATILED, bool BTILED>
+HeadKernel pick_rows(int mb, int bn) {
+  return bn == 128 ? pick_rows_bn<128, TRIM, PARTS, ATILED, BTILED>(mb)
+                   : pick_rows_bn<256, TRIM, PARTS, ATILED, BTILED>(mb);
+}
 
 inline int64_t mfma_big_tiles_n(int64_t Vt) { return (Vt + kBigBN - 1) / kBigBN; }
 
 // Rows per hidden-row block of the large-batch head that reads a K-tiled copy: 384 (the tall
-// tiles) when padding M to 384-row blocks adds no more rows than padding it to 256-row blocks
-// (2304 = 6 x 384 = 9 x 256), else 256.
-inline int big_tile_rows(int64_t M) {
-  const int64_t p384 = (M + kTallBM - 1) / kTallBM * kTallBM, p256 = (M + kBigBM - 1) / kBigBM * kBigBM;
-  return p384 <= p256 ? kTallBM : kBigBM;
+// tiles) or 256, whichever needs fewer hidden rows per CU: one tile per CU at a time, so a launch
+// of t tiles of R rows takes about ceil(t / kCUs) R row-steps (2304 rows and 256 head blocks: 6
+// waves of 384 against 9 of 256, a tie, and the tall tiles move fewer bytes per flop; 384 rows
+// and 128 head blocks: one wave of 128 tall tiles, 384 row-steps on half the CUs, against one of
+// 256 square tiles, 256).
+inline int big_tile_rows(int64_t M, int64_t Vt) {
+  const int64_t nbn = mfma_big_tiles_n(Vt);
+  const int64_t t384 = (M + kTallBM - 1) / kTallBM * nbn, t256 = (M + kBigBM - 1) / kBigBM * nbn;
+  return (t384 + kCUs - 1) / kCUs * kTallBM <= (t256 + kCUs - 1) / kCUs * kBigBM ? kTallBM : kBigBM;
 }
 
 // Rows per hidden-row block of the direct-to-LDS heads: all M rows padded to a multiple of 32 up
-// to kRowsMaxM (lmhead_mfma_rows), else big_tile_rows(M).
-inline int head_tile_rows(int64_t M) {
-  return M <= kRowsMaxM ? static_cast<int>((M + 31) / 32 * 32) : big_tile_rows(M);
+// to kRowsMaxM (lmhead_mfma_rows), else big_tile_rows(M, Vt).
+inline int head_tile_rows(int64_t M, int64_t Vt) {
+  return M <= kRowsMaxM ? static_cast<int>((M + 31) / 32 * 32) : big_tile_rows(M, Vt);
+}
+
+// Head rows per column block of the MFMA heads with whole 32-column K steps, which is also the
+// chunk of their draft partials: 128 for the all-rows kernel when fewer than kCUs blocks of 256
+// head rows would leave CUs idle, else 256.
+inline int head_tile_cols(int64_t M, int64_t H, int64_t Vt) {
+  return H % kDmaBK == 0 && M <= kRowsMaxM && mfma_big_tiles_n(Vt) < kCUs ? 128 : kBigBN;
 }
 
 // K-tiled copy of the hidden rows for the direct-to-LDS heads (lmhead_mfma_rows, _dma8 and _tall
-// with ATILED), in blocks of R = head_tile_rows(M) rows: out[bm][ks][r][32] = hidden[min(R bm + r,
+// with ATILED), in blocks of R = head_tile_rows(M, Vt) rows: out[bm][ks][r][32] = hidden[min(R bm + r,
 // M - 1)][32 ks .. 32 ks + 31] (rows past M repeat the last row; their logits are never stored).
 // One thread moves one 16-byte piece; a wave reads 16 rows x 64 bytes and writes 1 KB
 // contiguously.  Needs H % 32 == 0.
 // Bytes of the K-tiled hidden copy (0 when H % 32 != 0: the direct-to-LDS kernels do not run).
-inline size_t hidden_tiles_bytes(int64_t M, int64_t H) {
+inline size_t hidden_tiles_bytes(int64_t M, int64_t H, int64_t Vt) {
   if (H % kDmaBK != 0) return 0;
-  const int64_t R = head_tile_rows(M);
+  const int64_t R = head_tile_rows(M, Vt);
   return static_cast<size_t>((M + R - 1) / R) * R * static_cast<size_t>(H) * 2;
 }
 
@@ -1329,14 +1355,14 @@ __device__ __forceinline__ void hidden_tiles_block(const TileParams &T, int64_t 
   *reinterpret_cast<uint4 *>(T.out + q * 8) = v;
 }
 
-inline TileParams hidden_tiles_params(const uint16_t *hidden, int64_t M, int64_t H, uint16_t *out) {
+inline TileParams hidden_tiles_params(const uint16_t *hidden, int64_t M, int64_t H, int64_t Vt, uint16_t *out) {
   TileParams T{};
   T.hidden = hidden;
   T.out = out;
   T.M = static_cast<int>(M);
   T.H = static_cast<int>(H);
-  T.rows = head_tile_rows(M);
-  T.pieces = static_cast<int64_t>(hidden_tiles_bytes(M, H) / 16);
+  T.rows = head_tile_rows(M, Vt);
+  T.pieces = static_cast<int64_t>(hidden_tiles_bytes(M, H, Vt) / 16);
   return T;
 }
 
@@ -1362,10 +1388,11 @@ __global__ __launch_bounds__(kBlock) void softmax_partial_tiles(SmParams P, Tile
 
 // The MFMA heads with whole 32-column K steps (any M), or with M >= kBigMinM (any H).
 // PARTS = kPartsNone (the separate LM-head call): the hidden rows as given; up to kRowsMaxM rows
-// in one block of all of them, else 256 x 256 tiles.  kPartsSoftmax / kPartsArgmax (the fused
-// block's head, with its draft partials): when H % 32 == 0 hidden_tiled must hold the K-tiled copy
-// of the hidden rows made by hidden_tiles, in blocks of head_tile_rows(M) rows, which select the
-// kernel (all rows up to kRowsMaxM, 384-row tall tiles or 256 x 256 tiles); weight_tiled: NULL, or
+// in one block of all of them (head_tile_cols(M, H, Vt) head rows per workgroup), else 256 x 256
+// tiles.  kPartsSoftmax / kPartsArgmax (the fused block's head, with its draft partials per
+// head_tile_cols(M, H, Vt) head rows): when H % 32 == 0 hidden_tiled must hold the K-tiled copy
+// of the hidden rows made by hidden_tiles, in blocks of head_tile_rows(M, Vt) rows, which select
+// the kernel (all rows up to kRowsMaxM, 384-row tall tiles or 256 x 256 tiles); weight_tiled: NULL, or
 // the K-tiled trimmed head of vt_trim_head_tiled (weight and keep are then not read by the
 // kernel).  Other H take the register-staged kernel on the rows as given.
 template <int PARTS>
@@ -1376,19 +1403,20 @@ inline hipError_t launch_mfma_head(const uint16_t *hidden, const uint16_t *weigh
   const int64_t tiles = ((M + kBigBM - 1) / kBigBM) * mfma_big_tiles_n(Vt);
   const int iM = static_cast<int>(M), iH = static_cast<int>(H), iV = static_cast<int>(Vt);
   if (H % kDmaBK == 0 && M <= kRowsMaxM) {
-    const int mb = static_cast<int>((M + 31) / 32);
-    const unsigned grid = static_cast<unsigned>(mfma_big_tiles_n(Vt));
+    const int mb = static_cast<int>((M + 31) / 32), bn = head_tile_cols(M, H, Vt);
+    const dim3 grid(static_cast<unsigned>((Vt + bn - 1) / bn)), block(static_cast<unsigned>(kWave * (bn / 32)));
     if constexpr (PARTS == kPartsNone) {
       if (hidden_tiled || weight_tiled) return hipErrorInvalidValue;
-      const HeadKernel f = keep ? pick_rows<true, PARTS, false, false>(mb) : pick_rows<false, PARTS, false, false>(mb);
-      return launch(f, dim3(grid), dim3(kDma8Block), 0, stream, hidden, weight, keep, vrows, iM, iH, iV, logits, parts);
+      const HeadKernel f =
+          keep ? pick_rows<true, PARTS, false, false>(mb, bn) : pick_rows<false, PARTS, false, false>(mb, bn);
+      return launch(f, grid, block, 0, stream, hidden, weight, keep, vrows, iM, iH, iV, logits, parts);
     } else {
       if (!hidden_tiled) return hipErrorInvalidValue;
-      const HeadKernel f = weight_tiled ? pick_rows<false, PARTS, true, true>(mb)
-                                        : (keep ? pick_rows<true, PARTS, true, false>(mb)
-                                                : pick_rows<false, PARTS, true, false>(mb));
-      return launch(f, dim3(grid), dim3(kDma8Block), 0, stream, hidden_tiled, weight_tiled ? weight_tiled : weight,
-                    keep, vrows, iM, iH, iV, logits, parts);
+      const HeadKernel f = weight_tiled ? pick_rows<false, PARTS, true, true>(mb, bn)
+                                        : (keep ? pick_rows<true, PARTS, true, false>(mb, bn)
+                                                : pick_rows<false, PARTS, true, false>(mb, bn));
+      return launch(f, grid, block, 0, stream, hidden_tiled, weight_tiled ? weight_tiled : weight, keep, vrows, iM, iH,
+                    iV, logits, parts);
     }
   }
   if (H % kDmaBK == 0) {
@@ -1399,7 +1427,7 @@ inline hipError_t launch_mfma_head(const uint16_t *hidden, const uint16_t *weigh
                     iM, iH, iV, logits, parts);
     } else {
       if (!hidden_tiled) return hipErrorInvalidValue;
-      if (big_tile_rows(M) == kTallBM) {
+      if (big_tile_rows(M, Vt) == kTallBM) {
         const unsigned tall = static_cast<unsigned>(((M + kTallBM - 1) / kTallBM) * mfma_big_tiles_n(Vt));
         auto f = weight_tiled ? &lmhead_mfma_tall<false, PARTS, true>
                               : (keep ? &lmhead_mfma_tall<true, PARTS, false> : &lmhead_mfma_tall<false, PARTS, false>);

@@ -17,25 +17,28 @@ SCALED = {
     "c3-ragged": CONFIGS[3].scaled(V=9001, Vt=1234, H=520),
     "c4-batched-mfma": CONFIGS[4].scaled(B=24, V=20000, Vt=5000, H=256),
     "c5-mfma": CONFIGS[5].scaled(B=16, V=13000, Vt=6000, H=256),
-    "c4-big-tiles": CONFIGS[4].scaled(B=40, V=20000, Vt=5000, H=520),  # M = 320: fused 256x256 tiles
-    "c5-big-tiles": CONFIGS[5].scaled(B=32, V=13000, Vt=6001, H=256),  # M = 288, ragged Vt
+    "c4-big-tiles": CONFIGS[4].scaled(B=40, V=20000, Vt=5000, H=520),  # M = 320: register-staged tiles
+    "c5-big-tiles": CONFIGS[5].scaled(B=32, V=13000, Vt=6001, H=256),  # M = 288: 256 x 256, ragged Vt
     "c3-one-chunk-target": CONFIGS[3].scaled(V=4000, Vt=1500, H=256),
-    # untrimmed head at 256+ hidden rows (M = 288): K-tiled hidden copy, no keep set
+    # untrimmed head at 288 hidden rows: K-tiled hidden copy, no keep set
     "c2-untrimmed-big-tiles": CONFIGS[2].scaled(B=48, V=6000, Vt=6000, H=256),
-    # 256+ hidden rows with a one-chunk target row: the hidden copy takes a launch of its own
+    # 288 hidden rows with a one-chunk target row: the hidden copy takes a launch of its own
     "c5-big-tiles-one-chunk-target": CONFIGS[5].scaled(B=32, V=4000, Vt=1500, H=256),
-    # the head's row blocks: 288 and 756 hidden rows take 384-row tiles (one block; two, the
-    # second ragged), 512 takes 256-row tiles (two blocks; 384-row blocks would pad to 768)
-    "c5-tall-two-blocks": CONFIGS[5].scaled(B=84, V=13000, Vt=6001, H=256),
+    # the head's row blocks: 756 hidden rows against 126 head blocks take 384-row tiles (two
+    # blocks, the second ragged: 252 tiles, one per CU, against 378 of 256 rows), 512 rows take
+    # 256-row tiles (two blocks)
+    "c5-tall-two-blocks": CONFIGS[5].scaled(B=84, V=40000, Vt=32001, H=256),
     "c4-square-two-blocks": CONFIGS[4].scaled(B=64, V=20000, Vt=5000, H=256),
     # past the GEMV sizes, up to 192 hidden rows: one block of all rows padded to a multiple of
-    # 32 (9 rows: one 32-row block; 96: three; 128, 129: four, five; 192: six), then 256 x 256
-    # tiles from 193; with H % 32 != 0 below 129 rows, 128 x 128 tiles and a separate draft softmax
+    # 32 (9 rows: one 32-row block; 96: three; 128, 129: four, five; 192: six) per 128 head rows
+    # (fewer than 256 blocks of 256) or per 256 (66000 head rows), then 256 x 256 tiles from 193;
+    # with H % 32 != 0 below 129 rows, 128 x 128 tiles and a separate draft softmax
     "rows-9": CONFIGS[4].scaled(B=3, gamma=2, R=3, V=20000, Vt=5000, H=256),
     "rows-96": CONFIGS[4].scaled(B=12, V=20000, Vt=5000, H=256),
     "rows-128": CONFIGS[4].scaled(B=16, V=20000, Vt=5000, H=256),
     "rows-129": CONFIGS[4].scaled(B=43, gamma=2, R=3, V=20000, Vt=5000, H=256),
     "rows-192": CONFIGS[4].scaled(B=24, V=20000, Vt=5000, H=256),
+    "rows-36-wide-head": CONFIGS[5].scaled(B=4, V=70000, Vt=66000, H=256),
     "square-194": CONFIGS[4].scaled(B=97, gamma=1, R=2, V=20000, Vt=5000, H=256),
     "small-batch-odd-H": CONFIGS[4].scaled(B=4, V=9001, Vt=1234, H=520),
 }

@@ -46,6 +46,7 @@ CASES = [
     (192, 512, 1200, 1100, True),   # the largest all-rows block (192)
     (193, 512, 1200, 1100, True),   # one row past it: 256 x 256 tiles
     (100, 520, 1000, 700, True),    # H % 32 != 0 at 100 rows: 128 x 128 tiles
+    (40, 256, 70000, 66000, True),  # all rows per 256 head rows (258 blocks of 256: one per CU)
     (512, 3072, 2000, 1000, True),  # MFMA at config 4's M and H
     (7, 8192, 700, 700, False),     # M * ceil(H/512) too large for registers: MFMA
     (2304, 512, 300, 257, True),    # MFMA at config 5's M
@@ -86,13 +87,14 @@ def test_pre_gathered_head_equals_gather():
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("H,rows", [(1024, (9, 40, 96, 130, 192, 193, 256)), (520, (9, 100, 128, 129, 256))])
-def test_mfma_kernels_sum_in_one_order(H, rows):
+@pytest.mark.parametrize("H,V,Vt,rows", [(1024, 2500, 2100, (9, 40, 96, 130, 192, 193, 256)),
+                                        (256, 70000, 66000, (9, 100, 192, 193, 256)),
+                                        (520, 2500, 2100, (9, 100, 128, 129, 256))])
+def test_mfma_kernels_sum_in_one_order(H, V, Vt, rows):
     # every MFMA kernel sums a logit's products in the same K order, so a hidden row's logits are
     # the same bits whatever the batch's row count selects (H % 32 == 0: all-rows blocks of 32 ..
-    # 192 rows, 256 x 256 tiles; other H: 128 x 128 and register-staged 256 x 256 tiles); only the
-    # GEMV (M <= 8) sums differently
-    V, Vt = 2500, 2100
+    # 192 rows per 128 or 256 head rows, 256 x 256 tiles; other H: 128 x 128 and register-staged
+    # 256 x 256 tiles); only the GEMV (M <= 8) sums differently
     h, w, keep = _inputs(300, H, V, Vt, True, seed=13)
     want = _run(h, w, keep, Vt)
     for M in rows:
