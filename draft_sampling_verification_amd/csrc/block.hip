@@ -5,15 +5,16 @@
 // "Extending the rule from one token to a drafted run"), launched as few kernels as the
 // dependencies allow:
 //   1. target rows' chunk partials (max, sum of exp)                       [if V > 4096]
-//   2. LM head; on the GEMV path and on the large-batch MFMA path its epilogue also emits the
-//      draft rows' partials per row block or column tile (no second pass over the logits); on
-//      the small MFMA path a partials launch follows
+//   2. LM head; on the GEMV path and on the MFMA paths with whole 32-column K steps its epilogue
+//      also emits the draft rows' partials per row block or column tile (no second pass over the
+//      logits); otherwise a partials launch follows
 //   3. one combine launch for the draft rows (lse + draws) and the target rows (lse)
 //   4. verify pass 1 (accept scans, residual chunk sums) and pass 2 (final draws, outputs)
 // Launch order never lets an independent kernel sit between the LM head and its consumers.
-// Small batches (the GEMV head, both sides sampled) take 3 launches instead: the target
-// partials ride in extra workgroups of the GEMV launch, and one chunk pass forms every
-// log-normaliser, draft draw, accept scan and residual chunk sum, followed by the final draw.
+// Small batches with both sides sampled and at most 8 draft rows per sequence replace 3 and 4
+// with two launches: one chunk pass forms every log-normaliser, draft draw, accept scan and
+// residual chunk sum from the partials, and the final pass draws the last token; on the GEMV path
+// the target partials also ride in extra workgroups of the head launch (3 launches in all).
 #include <algorithm>
 #include <mutex>
 
@@ -24,6 +25,12 @@
 
 namespace vt {
 namespace {
+
+// Hidden rows up to which the MFMA head is followed by the two-pass verification: each chunk
+// workgroup of a sequence repeats the sequence's draft draws and target log-normalisers, which
+// pays at a few sequences and not beyond (batched shape, H = 3072, Vt = 32768, 8 draft rows:
+// 2 sequences 55.0 -> 49.6 us per block, 4: 56.3 -> 54.4 us, 8: 59.4 -> 66.8 us).
+constexpr int64_t kFvMfmaMaxM = 32;
 
 struct BlockPlan {
   bool fused;       // GEMV with draft partials in its epilogue
@@ -65,7 +72,9 @@ BlockPlan plan_block(int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt,
     p.nchunk_d = (Vt + kChunk - 1) / kChunk;
     p.chunk_d = kChunk;
   }
-  p.fv = p.fused && !greedy_t && R <= kFvMaxR && p.nchunk_d <= kFvMaxParts;
+  // the two-pass verification (chunk pass + final pass) after the GEMV head, and after the MFMA
+  // head up to kFvMfmaMaxM hidden rows
+  p.fv = !greedy_t && R <= kFvMaxR && p.nchunk_d <= kFvMaxParts && (p.fused || (p.fused_mfma && p.M <= kFvMfmaMaxM));
   p.nchunk_v = (V + (p.fv ? kFvIds : kChunk) - 1) / (p.fv ? kFvIds : kChunk);
   size_t off = 0;
   p.off_tpart = off;
@@ -102,6 +111,31 @@ hipError_t launch_combine(const SmParams &D, bool d_multi, const SmParams &T, bo
   return hipSuccess;
 }
 
+// The chunk pass and the final pass of the two-pass verification: every log-normaliser and draft
+// draw is formed from the partials the earlier launches left (draft rows per head block, target
+// rows per 4096-chunk), then the accept scan, the residual chunk sums and the last token.
+template <typename TinT, bool kVecT>
+hipError_t launch_fused_verify(const BlockPlan &pl, const SmParams &D, const SmParams &T, const VfParams &Vp,
+                               const float *u_draft, float *wbuf, int64_t B, hipStream_t stream) {
+  FvParams F{};
+  F.v = Vp;
+  F.dpart = D.part;
+  F.nd = static_cast<int>(pl.nchunk_d);
+  F.dper = pl.chunk_d;
+  F.udraft = u_draft;
+  F.tpart = T.part;
+  F.nt = T.nchunk;
+  F.dlse_out = D.lse;
+  F.dids_out = D.sampled;
+  F.tlse_out = T.lse;
+  F.wbuf = wbuf;
+  F.pbuf = wbuf + B * Vp.V;
+  const hipError_t e = launch(verify_fused_chunk<TinT, kVecT>, dim3(static_cast<unsigned>(B * Vp.nchunk)),
+                              dim3(kFvBlock), 0, stream, F);
+  if (e != hipSuccess) return e;
+  return launch(verify_fused_final<TinT, kVecT>, dim3(static_cast<unsigned>(B)), dim3(kBlock), 0, stream, F);
+}
+
 // Small batch, sampling both sides: 3 launches.  The GEMV launch carries the target rows'
 // chunk partials in extra workgroups; the chunk pass forms every log-normaliser and draft draw
 // itself from the partials; the final pass draws the last token.
@@ -122,23 +156,36 @@ hipError_t run_block_small(const BlockPlan &pl, const SmParams &D, const SmParam
                   T.rows * T.nchunk);
   if (e != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
-  FvParams F{};
-  F.v = Vp;
-  F.dpart = D.part;
-  F.nd = static_cast<int>(pl.nchunk_d);
-  F.dper = pl.chunk_d;
-  F.udraft = u_draft;
-  F.tpart = T.part;
-  F.nt = T.nchunk;
-  F.dlse_out = D.lse;
-  F.dids_out = D.sampled;
-  F.tlse_out = T.lse;
-  F.wbuf = wbuf;
-  F.pbuf = wbuf + B * Vp.V;
-  e = launch(verify_fused_chunk<TinT, kVecT>, dim3(static_cast<unsigned>(B * Vp.nchunk)), dim3(kFvBlock), 0, stream,
-             F);
+  return launch_fused_verify<TinT, kVecT>(pl, D, T, Vp, u_draft, wbuf, B, stream);
+}
+
+// Small batch past the GEMV sizes, sampling both sides: 4 launches.  The target rows' chunk
+// partials (with the K-tiled hidden copy in extra workgroups), the MFMA head with the draft
+// partials, then the chunk pass and the final pass as after the GEMV head.
+template <typename TinT, bool kVecT>
+hipError_t run_block_small_mfma(const BlockPlan &pl, const SmParams &D, const SmParams &T, const VfParams &Vp,
+                                const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int64_t H,
+                                int64_t Vt, float *logits, const float *u_draft, float *wbuf, int64_t B,
+                                hipEvent_t ev0, hipEvent_t ev1, hipStream_t stream, void *hidt_base,
+                                const uint16_t *weight_tiled) {
+  hipError_t e = hipSuccess;
+  const int vrows = static_cast<int>(Vp.V);  // the head passed in is the full [V][H] one
+  uint16_t *hidt = pl.hidt_bytes ? reinterpret_cast<uint16_t *>(hidt_base) : nullptr;
+  const TileParams tp = hidden_tiles_params(hidden, pl.M, H, Vt, hidt);
+  if (hidt)
+    e = launch(softmax_partial_tiles<TinT, kVecT>,
+               dim3(static_cast<unsigned>(T.rows * T.nchunk + hidden_tiles_blocks(tp))), dim3(kBlock), 0, stream, T,
+               tp);
+  else
+    e = launch(softmax_partial<TinT, kVecT>, dim3(static_cast<unsigned>(T.rows * T.nchunk)), dim3(kBlock), 0,
+               stream, T);
   if (e != hipSuccess) return e;
-  return launch(verify_fused_final<TinT, kVecT>, dim3(static_cast<unsigned>(B)), dim3(kBlock), 0, stream, F);
+  if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
+  e = launch_mfma_head<kPartsSoftmax>(hidden, weight, keep, vrows, pl.M, H, Vt, logits, GemvParts{D.part, D.k2}, stream,
+                                      hidt, weight_tiled);
+  if (e != hipSuccess) return e;
+  if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
+  return launch_fused_verify<TinT, kVecT>(pl, D, T, Vp, u_draft, wbuf, B, stream);
 }
 
 // Small batch, greedy both sides: 2 launches.  The GEMV launch leaves per-block argmax partials
@@ -177,9 +224,12 @@ hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, 
                      const uint16_t *hidden, const uint16_t *weight, const int32_t *keep, int64_t H, int64_t Vt,
                      float *logits, float *wbuf, int64_t B, hipEvent_t ev0, hipEvent_t ev1, hipStream_t stream,
                      void *hidt_base, const uint16_t *weight_tiled) {
-  if (pl.fv)
+  if (pl.fv && pl.fused)
     return run_block_small<TinT, kVecT>(pl, D, T, Vp, hidden, weight, keep, H, Vt, logits, D.u, wbuf, B, ev0, ev1,
                                         stream);
+  if (pl.fv)
+    return run_block_small_mfma<TinT, kVecT>(pl, D, T, Vp, hidden, weight, keep, H, Vt, logits, D.u, wbuf, B, ev0,
+                                             ev1, stream, hidt_base, weight_tiled);
   if (pl.fg)
     return run_block_greedy_small<TinT, kVecT>(pl, D, T, Vp, hidden, weight, keep, H, Vt, logits, B, ev0, ev1, stream);
   hipError_t e = hipSuccess;

@@ -1,4 +1,5 @@
-// Verification of small batches in the single-call block, after the GEMV head (gfx950).
+// Verification of small batches in the single-call block, after the GEMV head or a small MFMA
+// head (gfx950).
 //
 // What is computed is what the separate softmax and verify calls compute ("Speculative
 // decoding" glossary, "Propose a block, keep a prefix" and "Why a rejection needs a special
@@ -42,7 +43,7 @@ constexpr int kFvBlock = 512;
 constexpr int kFvWaves = kFvBlock / kWave;      // 8: one draft row per wavefront
 constexpr int kFvIds = 1024;                    // full-vocabulary ids per chunk workgroup
 constexpr int kFvPer = kFvIds / kFvBlock;       // 2 ids per thread
-constexpr int kFvMaxR = 8;                      // draft rows per sequence (the GEMV head takes M <= 8)
+constexpr int kFvMaxR = 8;                      // draft rows per sequence (one wavefront each)
 constexpr int kFvMaxT = kFvMaxR + 1;            // target rows per sequence
 constexpr int kFvFinalPer = kFvIds / kBlock;    // 4 ids per thread in the final rescan
 constexpr int kFvMaxParts = 4 * kWave;          // head row blocks per row (gemv_blocks <= 256)

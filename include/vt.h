@@ -178,8 +178,10 @@ size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
  * sampled) take 3 launches instead of 7: the LM head launch also emits the draft softmax's
  * first pass and, in extra workgroups, the target rows' first pass; one chunk pass over the
  * full vocabulary forms the log-normalisers, draft draws, accept tests and residual chunk sums;
- * one final pass draws the last token.  Larger batches take 5 (LM head with the draft partials,
- * target partials, one combine launch for both row sets, two verify passes).  Past the GEMV
+ * one final pass draws the last token.  Past the GEMV sizes, up to 32 hidden rows with at most 8
+ * per sequence, the same two passes follow the target partials and the MFMA head (4 launches).
+ * Larger batches take 5 (target partials, LM head with the draft partials, one combine launch
+ * for both row sets, two verify passes).  Past the GEMV
  * sizes with H % 32 == 0 the target partials launch also copies the hidden rows K-tiled into the
  * workspace (the head then reads each K step of a block of hidden rows as one contiguous run; same
  * products, same logits); without target partials (V <= 4096 or greedy verification) the copy is

@@ -39,6 +39,9 @@ SCALED = {
     "rows-129": CONFIGS[4].scaled(B=43, gamma=2, R=3, V=20000, Vt=5000, H=256),
     "rows-192": CONFIGS[4].scaled(B=24, V=20000, Vt=5000, H=256),
     "rows-36-wide-head": CONFIGS[5].scaled(B=4, V=70000, Vt=66000, H=256),
+    # up to 32 hidden rows of at most 8 per sequence the MFMA head is followed by the two-pass
+    # verification (chunk pass and final pass) instead of the combine and verify launches
+    "rows-32-two-pass": CONFIGS[4].scaled(B=4, V=20000, Vt=5000, H=256),
     "square-194": CONFIGS[4].scaled(B=97, gamma=1, R=2, V=20000, Vt=5000, H=256),
     "small-batch-odd-H": CONFIGS[4].scaled(B=4, V=9001, Vt=1234, H=520),
 }
@@ -106,7 +109,7 @@ def test_fused_block_small_batch_long_runs(name):
     assert len(seen) >= 2 and max(seen) > 0
 
 
-@pytest.mark.parametrize("name", ["c4-batched-mfma", "c4-big-tiles", "c5-mfma", "c5-big-tiles"])
+@pytest.mark.parametrize("name", ["c4-batched-mfma", "c4-big-tiles", "c5-mfma", "c5-big-tiles", "rows-32-two-pass"])
 def test_fused_block_following_drafter(name):
     say(f"fused block parity {name}, following drafter")
     _, orc = _check(make_workload(SCALED[name], follow=0.5))
