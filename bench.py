@@ -29,10 +29,12 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C] [--greed
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -85,6 +87,10 @@ def parse():
     ap.add_argument("--side-steps", type=int, default=200)
     ap.add_argument("--batch", type=int, default=1,
                     help="sequences per step for the toy (--config 1); the other configs fix their batch")
+    ap.add_argument("--sequences", type=int, default=None,
+                    help="sequences per step for --config 2-5 in place of the config's own batch (the same "
+                         "recipe at another batch size, e.g. the medium batches of a serving loop); the "
+                         "configs' own batches are the reference workloads")
     ap.add_argument("--workload", default="block", choices=["block", "keepset", "generate"],
                     help="block: one speculative block per step (the default); keepset: token counter -> "
                          "Top-K -> trimmed head over a Zipf calibration stream; generate: the chained "
@@ -172,7 +178,7 @@ def lmhead_bytes(cfg) -> int:
 def small_batch_block(cfg, greedy: bool = False) -> bool:
     """Batch-1-sized blocks (at most 8 draft rows, both sides sampled): the GEMV head launch also
     runs the target rows' first softmax pass in extra workgroups."""
-    return cfg.B * cfg.R <= 8 and not greedy
+    return gemv_head(cfg.B * cfg.R, cfg.H) and cfg.R <= 8 and not greedy
 
 
 def lmhead_launch_bytes(cfg, greedy: bool = False, calls: bool = False) -> int:
@@ -632,7 +638,7 @@ def valu_record():
     return rec if rec.get("source_sha256") == generate_source_hash() else None
 
 
-def bench_block(args, config: int, steps: int, warmup: int):
+def bench_block(args, config: int, steps: int, warmup: int, sequences: int | None = None):
     """Time `steps` speculative blocks of a config after `warmup` untimed ones.  Returns the fields
     of the result line: step time, the LM-head launch time from HIP events on its own stream, the
     algorithmic bytes and flops, and the side statistics."""
@@ -642,6 +648,8 @@ def bench_block(args, config: int, steps: int, warmup: int):
     from workloads import CONFIGS, make_workload
 
     cfg = CONFIGS[config]
+    if sequences:
+        cfg = dataclasses.replace(cfg.scaled(B=sequences), name=re.sub(r"B=\d+", f"B={sequences}", cfg.name))
     B, g, R = cfg.B, cfg.gamma, cfg.R
     log(f"workload: {cfg.name}")
     t0 = time.perf_counter()
@@ -852,6 +860,8 @@ def main():
     if args.valu_record:
         print(write_valu_record(args.valu_record))
         return
+    if args.sequences is not None and (args.config == 1 or args.workload != "block" or args.sequences < 1):
+        raise SystemExit("--sequences takes a positive count and applies to --config 2-5")
     if args.workload == "keepset":
         bench_keepset(args)
         return
@@ -864,10 +874,11 @@ def main():
 
     from workloads import make_workload
 
-    res = bench_block(args, args.config, args.steps, args.warmup)
+    res = bench_block(args, args.config, args.steps, args.warmup, args.sequences)
     cfg = res["cfg"]
     B, g = cfg.B, cfg.gamma
-    traffic = measured_traffic(f"config{args.config}")
+    # PMC records are per config at the config's own batch
+    traffic = None if args.sequences else measured_traffic(f"config{args.config}")
     M = B * cfg.R
     kernel = (head_kernel(M, cfg.H, args.calls)
               + (" + target softmax partials" if small_batch_block(cfg, args.greedy) and not args.calls else ""))
