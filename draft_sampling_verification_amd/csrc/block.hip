@@ -26,11 +26,15 @@
 namespace vt {
 namespace {
 
-// Hidden rows up to which the MFMA head is followed by the two-pass verification: each chunk
-// workgroup of a sequence repeats the sequence's draft draws and target log-normalisers, which
-// pays at a few sequences and not beyond (batched shape, H = 3072, Vt = 32768, 8 draft rows:
-// 2 sequences 55.0 -> 49.6 us per block, 4: 56.3 -> 54.4 us, 8: 59.4 -> 66.8 us).
+// Batches after whose MFMA head the two-pass verification runs: at most kFvMfmaMaxM hidden rows and
+// 16 draft rows per sequence, and at most kFvMfmaMaxB sequences, counted twice when each chunk-pass
+// wavefront draws two rows.  Each chunk workgroup of a sequence repeats the sequence's draft draws
+// and target log-normalisers, which pays at a few sequences and not beyond (batched shape, H =
+// 3072, Vt = 32768, 8 draft rows: 2 sequences 55.0 -> 49.6 us per block, 4: 56.3 -> 54.4 us, 8:
+// 59.4 -> 66.8 us; large-drafter shape, 9 draft rows: 1 sequence 116.1 -> 112.6 us, 2: 116.0 ->
+// 115.1 us, 3: 124.7 us against 120.5 us for 4 without it).
 constexpr int64_t kFvMfmaMaxM = 32;
+constexpr int64_t kFvMfmaMaxB = 4;
 
 struct BlockPlan {
   bool fused;       // GEMV with draft partials in its epilogue
@@ -73,8 +77,10 @@ BlockPlan plan_block(int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt,
     p.chunk_d = kChunk;
   }
   // the two-pass verification (chunk pass + final pass) after the GEMV head, and after the MFMA
-  // head up to kFvMfmaMaxM hidden rows
-  p.fv = !greedy_t && R <= kFvMaxR && p.nchunk_d <= kFvMaxParts && (p.fused || (p.fused_mfma && p.M <= kFvMfmaMaxM));
+  // head for the small batches above
+  const int64_t rows_per_wave = R > kFvMaxR ? 2 : 1;
+  p.fv = !greedy_t && R <= kFvMaxR2 && p.nchunk_d <= kFvMaxParts &&
+         (p.fused || (p.fused_mfma && p.M <= kFvMfmaMaxM && B * rows_per_wave <= kFvMfmaMaxB));
   p.nchunk_v = (V + (p.fv ? kFvIds : kChunk) - 1) / (p.fv ? kFvIds : kChunk);
   size_t off = 0;
   p.off_tpart = off;
@@ -130,8 +136,9 @@ hipError_t launch_fused_verify(const BlockPlan &pl, const SmParams &D, const SmP
   F.tlse_out = T.lse;
   F.wbuf = wbuf;
   F.pbuf = wbuf + B * Vp.V;
-  const hipError_t e = launch(verify_fused_chunk<TinT, kVecT>, dim3(static_cast<unsigned>(B * Vp.nchunk)),
-                              dim3(kFvBlock), 0, stream, F);
+  const dim3 grid(static_cast<unsigned>(B * Vp.nchunk));
+  const hipError_t e = Vp.R > kFvMaxR ? launch(verify_fused_chunk<TinT, kVecT, 2>, grid, dim3(kFvBlock), 0, stream, F)
+                                      : launch(verify_fused_chunk<TinT, kVecT, 1>, grid, dim3(kFvBlock), 0, stream, F);
   if (e != hipSuccess) return e;
   return launch(verify_fused_final<TinT, kVecT>, dim3(static_cast<unsigned>(B)), dim3(kBlock), 0, stream, F);
 }

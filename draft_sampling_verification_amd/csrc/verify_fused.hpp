@@ -14,8 +14,9 @@
 //      launch left behind (per head row block for the draft rows, per 4096-chunk for the target
 //      rows).
 //   1. Wave w draws draft row w (log-normaliser from the partials, the block whose running mass
-//      reaches u Z, then a scan of that block's logits and keep ids), forms the log-normaliser
-//      of target rows w and w + 8, and runs the accept test of draft w (fp64 ratio).  Every
+//      reaches u Z, then a scan of that block's logits and keep ids), and row w + 8 as well when a
+//      sequence has more than 8 draft rows, forms the log-normaliser of target rows w, w + 8
+//      (and w + 16), and runs the accept tests of its drafts (fp64 ratio).  Every
 //      workgroup of the sequence repeats this small amount of work, so no workgroup waits for
 //      another; the first chunk's workgroup writes the outputs.
 //   2. After one barrier every thread reads the verdicts: n = first rejection.
@@ -43,8 +44,9 @@ constexpr int kFvBlock = 512;
 constexpr int kFvWaves = kFvBlock / kWave;      // 8: one draft row per wavefront
 constexpr int kFvIds = 1024;                    // full-vocabulary ids per chunk workgroup
 constexpr int kFvPer = kFvIds / kFvBlock;       // 2 ids per thread
-constexpr int kFvMaxR = 8;                      // draft rows per sequence (one wavefront each)
+constexpr int kFvMaxR = 8;                      // draft rows per sequence at one per wavefront
 constexpr int kFvMaxT = kFvMaxR + 1;            // target rows per sequence
+constexpr int kFvMaxR2 = 2 * kFvMaxR;           // draft rows per sequence at two per wavefront
 constexpr int kFvFinalPer = kFvIds / kBlock;    // 4 ids per thread in the final rescan
 constexpr int kFvMaxParts = 4 * kWave;          // head row blocks per row (gemv_blocks <= 256)
 constexpr int kFvScanBatch = 8;                 // 64-logit groups loaded at once when rescanning a row block
@@ -263,10 +265,15 @@ __device__ __forceinline__ double fv_target_lse(const FvParams &F, int64_t r, fl
   return static_cast<double>(M) * F.v.invTt + log(static_cast<double>(carry));
 }
 
-template <typename Tin, bool kVec>
+// RPW draft rows per wavefront (wave w: rows w + 8 r, r < RPW; target rows w + 8 s): RPW = 1 up to
+// 8 draft rows per sequence, 2 up to kFvMaxR2 (the second draw of a wave runs after its first).
+template <typename Tin, bool kVec, int RPW>
 __global__ __launch_bounds__(kFvBlock) void verify_fused_chunk(FvParams F) {
-  __shared__ double s_tlse[kFvMaxT], s_dlse[kFvMaxR];
-  __shared__ int s_acc[kFvMaxR];  // accept test of draft i: 1 kept, 0 rejected, -1 invalid id
+  constexpr int kMaxR = kFvWaves * RPW;  // draft rows per sequence
+  constexpr int kMaxT = kMaxR + 1;       // target rows per sequence
+  constexpr int kTPW = (kMaxT + kFvWaves - 1) / kFvWaves;  // target rows per wavefront
+  __shared__ double s_tlse[kMaxT], s_dlse[kMaxR];
+  __shared__ int s_acc[kMaxR];  // accept test of draft i: 1 kept, 0 rejected, -1 invalid id
   __shared__ float2 s_red[kFvWaves];
   const VfParams &P = F.v;
   // all chunks of a sequence on one XCD: the gathered draft rows meet in that XCD's L2
@@ -285,83 +292,101 @@ __global__ __launch_bounds__(kFvBlock) void verify_fused_chunk(FvParams F) {
     const int64_t x = x0 + j;
     ti[j] = P.f2t ? P.f2t[x < P.V ? x : P.V - 1] : static_cast<int32_t>(x);
   }
-  const bool my_draft = w < R && (w < g || c == 0);  // rows past gamma only feed the outputs
-  const int64_t m = b * R + w;
-  float2 pv[4];
-  float ud = 0.f;
-  if (my_draft) {
+  bool my_draft[RPW];  // rows past gamma only feed the outputs
+  float2 pv[RPW][4];
+  float ud[RPW], ua[RPW];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = 4 * lane + j;
-      pv[j] = F.dpart[m * F.nd + (k < F.nd ? k : F.nd - 1)];
+  for (int r = 0; r < RPW; ++r) {
+    const int i = w + kFvWaves * r;
+    my_draft[r] = i < R && (i < g || c == 0);
+    ud[r] = 0.f;
+    if (my_draft[r]) {
+      const int64_t m = b * R + i;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = 4 * lane + j;
+        pv[r][j] = F.dpart[m * F.nd + (k < F.nd ? k : F.nd - 1)];
+      }
+      ud[r] = F.udraft[m];
     }
-    ud = F.udraft[m];
+    ua[r] = i < g ? P.uacc[b * g + i] : 0.f;
   }
-  const float ua = w < g ? P.uacc[b * g + w] : 0.f;
-  float2 tp[2];
+  float2 tp[kTPW];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < kTPW; ++s) {
     const int i = w + kFvWaves * s;
     tp[s] = make_float2(kNegInf, 0.f);
     if (i <= g) tp[s] = F.tpart[(b * (g + 1) + i) * F.nt + (lane < F.nt ? lane : F.nt - 1)];
   }
-  RawPair<Tin> tg[kFvMaxT];
+  RawPair<Tin> tg[kMaxT];
 #pragma unroll
-  for (int i = 0; i < kFvMaxT; ++i) {
+  for (int i = 0; i < kMaxT; ++i) {
     const int ri = i <= g ? i : g;  // rows past gamma repeat row gamma (never selected)
     tg[i] = load_pair_raw<Tin, kVec>(reinterpret_cast<const Tin *>(P.target) + (b * (g + 1) + ri) * P.V, P.V, x0);
   }
   bool on[kFvPer];  // id inside the vocabulary and kept
 #pragma unroll
   for (int j = 0; j < kFvPer; ++j) on[j] = x0 + j < P.V && ti[j] >= 0 && ti[j] < P.Vt;
-  float dg[kFvMaxR][kFvPer];
+  float dg[kMaxR][kFvPer];
 #pragma unroll
-  for (int i = 0; i < kFvMaxR; ++i) {
+  for (int i = 0; i < kMaxR; ++i) {
     const int ri = i < g ? i : g - 1;  // rows past gamma - 1 repeat row gamma - 1 (never selected)
     const float *drow = P.draft + (b * R + ri) * P.Vt;
 #pragma unroll
     for (int j = 0; j < kFvPer; ++j) dg[i][j] = drow[on[j] ? ti[j] : 0];
   }
 
-  // 1. wave w: draw of draft row w; log-normalisers of target rows w and w + 8; accept test of
-  //    draft w (fp64 ratio exp(a - d), a and d the two log-probabilities of the drafted token)
-  DraftDraw dd{};
-  bool valid = false;
-  float tl = 0.f;
-  if (my_draft) {
-    dd = fv_draft_row(F, m, pv, ud);
-    valid = dd.x >= 0 && dd.x < P.Vt && dd.y >= 0 && dd.y < P.V;
-    if (w < g && valid)  // the target logit of the drafted token, in flight during the target lse
-      tl = load_logit(reinterpret_cast<const Tin *>(P.target) + (b * (g + 1) + w) * P.V, dd.y);
-    if (lane == 0) {
-      s_dlse[w] = dd.lse;
-      if (c == 0) {
-        F.dlse_out[m] = dd.lse;
-        F.dids_out[m] = dd.x;
-      }
-    }
-  }
-  double tl_w = 0.0;
+  // 1. wave w: draws of its draft rows; log-normalisers of its target rows; accept tests of its
+  //    drafts (fp64 ratio exp(a - d), a and d the two log-probabilities of the drafted token)
+  DraftDraw dd[RPW];
+  bool valid[RPW];
+  float tl[RPW];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int i = w + kFvWaves * s;
-    if (i <= g) {
-      const double l = fv_target_lse(F, b * (g + 1) + i, tp[s]);
-      if (s == 0) tl_w = l;
+  for (int r = 0; r < RPW; ++r) {
+    const int i = w + kFvWaves * r;
+    dd[r] = DraftDraw{};
+    valid[r] = false;
+    tl[r] = 0.f;
+    if (my_draft[r]) {
+      const int64_t m = b * R + i;
+      dd[r] = fv_draft_row(F, m, pv[r], ud[r]);
+      valid[r] = dd[r].x >= 0 && dd[r].x < P.Vt && dd[r].y >= 0 && dd[r].y < P.V;
+      if (i < g && valid[r])  // the target logit of the drafted token, in flight during the target lse
+        tl[r] = load_logit(reinterpret_cast<const Tin *>(P.target) + (b * (g + 1) + i) * P.V, dd[r].y);
       if (lane == 0) {
-        s_tlse[i] = l;
-        if (c == 0) F.tlse_out[b * (g + 1) + i] = l;
+        s_dlse[i] = dd[r].lse;
+        if (c == 0) {
+          F.dlse_out[m] = dd[r].lse;
+          F.dids_out[m] = dd[r].x;
+        }
       }
     }
   }
-  if (w < g && lane == 0) {
-    int verdict = -1;
-    if (valid) {
-      const double a = static_cast<double>(tl) * P.invTt - tl_w;
-      const double d = static_cast<double>(dd.xl) * P.invTd - dd.lse;
-      verdict = accept_ratio(ua, a - d) ? 1 : 0;
+  double tl_w[kTPW];  // log-normalisers of target rows w + 8 s
+#pragma unroll
+  for (int s = 0; s < kTPW; ++s) {
+    const int i = w + kFvWaves * s;
+    tl_w[s] = 0.0;
+    if (i <= g) {
+      tl_w[s] = fv_target_lse(F, b * (g + 1) + i, tp[s]);
+      if (lane == 0) {
+        s_tlse[i] = tl_w[s];
+        if (c == 0) F.tlse_out[b * (g + 1) + i] = tl_w[s];
+      }
     }
-    s_acc[w] = verdict;
+  }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int i = w + kFvWaves * r;
+    if (i < g && lane == 0) {
+      int verdict = -1;
+      if (valid[r]) {
+        const double a = static_cast<double>(tl[r]) * P.invTt - tl_w[r];
+        const double d = static_cast<double>(dd[r].xl) * P.invTd - dd[r].lse;
+        verdict = accept_ratio(ua[r], a - d) ? 1 : 0;
+      }
+      s_acc[i] = verdict;
+    }
   }
   __syncthreads();
 
@@ -383,12 +408,12 @@ __global__ __launch_bounds__(kFvBlock) void verify_fused_chunk(FvParams F) {
 #pragma unroll
     for (int j = 0; j < kFvPer; ++j) d2[j] = dg[0][j];
 #pragma unroll
-    for (int i = 1; i < kFvMaxT; ++i)
+    for (int i = 1; i < kMaxT; ++i)
       if (i == n) {
         tn = tg[i];
 #pragma unroll
         for (int j = 0; j < kFvPer; ++j)
-          if (i < kFvMaxR) d2[j] = dg[i][j];
+          if (i < kMaxR) d2[j] = dg[i][j];
       }
     float t2[kFvPer];
 #pragma unroll

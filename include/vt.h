@@ -178,8 +178,9 @@ size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
  * sampled) take 3 launches instead of 7: the LM head launch also emits the draft softmax's
  * first pass and, in extra workgroups, the target rows' first pass; one chunk pass over the
  * full vocabulary forms the log-normalisers, draft draws, accept tests and residual chunk sums;
- * one final pass draws the last token.  Past the GEMV sizes, up to 32 hidden rows with at most 8
- * per sequence, the same two passes follow the target partials and the MFMA head (4 launches).
+ * one final pass draws the last token.  Past the GEMV sizes, for up to 32 hidden rows in at most 4
+ * sequences of up to 8 draft rows or 2 of up to 16, the same two passes follow the target partials
+ * and the MFMA head (4 launches).
  * Larger batches take 5 (target partials, LM head with the draft partials, one combine launch
  * for both row sets, two verify passes).  Past the GEMV
  * sizes with H % 32 == 0 the target partials launch also copies the hidden rows K-tiled into the

@@ -42,6 +42,10 @@ SCALED = {
     # up to 32 hidden rows of at most 8 per sequence the MFMA head is followed by the two-pass
     # verification (chunk pass and final pass) instead of the combine and verify launches
     "rows-32-two-pass": CONFIGS[4].scaled(B=4, V=20000, Vt=5000, H=256),
+    # more than 8 draft rows per sequence: each chunk-pass wavefront draws two rows (9 and 16 rows,
+    # the latter with 16 target rows)
+    "rows-18-two-pass-9-rows": CONFIGS[5].scaled(B=2, V=20000, Vt=5000, H=256),
+    "rows-32-two-pass-16-rows": CONFIGS[4].scaled(B=2, gamma=15, R=16, V=20000, Vt=5000, H=256),
     "square-194": CONFIGS[4].scaled(B=97, gamma=1, R=2, V=20000, Vt=5000, H=256),
     "small-batch-odd-H": CONFIGS[4].scaled(B=4, V=9001, Vt=1234, H=520),
 }
@@ -109,11 +113,22 @@ def test_fused_block_small_batch_long_runs(name):
     assert len(seen) >= 2 and max(seen) > 0
 
 
-@pytest.mark.parametrize("name", ["c4-batched-mfma", "c4-big-tiles", "c5-mfma", "c5-big-tiles", "rows-32-two-pass"])
+@pytest.mark.parametrize("name", ["c4-batched-mfma", "c4-big-tiles", "c5-mfma", "c5-big-tiles", "rows-32-two-pass",
+                                  "rows-18-two-pass-9-rows"])
 def test_fused_block_following_drafter(name):
     say(f"fused block parity {name}, following drafter")
     _, orc = _check(make_workload(SCALED[name], follow=0.5))
     say(f"  accepted counts: {np.bincount(orc['n'], minlength=SCALED[name].gamma + 1).tolist()}")
+    assert orc["n"].max() > 0
+
+
+def test_two_pass_sixteen_draft_rows_following_drafter():
+    # two sequences of 16 draft rows whose drafts the oracle accepts in part (sequences 8 and 9 of
+    # the recipe: 1 and 3 accepted), so the chunk pass's second row per wavefront feeds a residual
+    cfg = SCALED["rows-32-two-pass-16-rows"]
+    say("fused block parity rows-32-two-pass-16-rows, following drafter, sequences 8 and 9")
+    _, orc = _check(make_workload(cfg, follow=0.5, b0=8))
+    say(f"  accepted: {orc['n'].tolist()}")
     assert orc["n"].max() > 0
 
 
