@@ -46,6 +46,9 @@ SCALED = {
     # the latter with 16 target rows)
     "rows-18-two-pass-9-rows": CONFIGS[5].scaled(B=2, V=20000, Vt=5000, H=256),
     "rows-32-two-pass-16-rows": CONFIGS[4].scaled(B=2, gamma=15, R=16, V=20000, Vt=5000, H=256),
+    # a 64-row head past the GEMV sizes (one partial per draft row) and H = 32 (one K step)
+    "rows-tiny-head": CONFIGS[4].scaled(B=8, V=3000, Vt=64, H=256),
+    "rows-one-k-step": CONFIGS[4].scaled(B=6, V=5000, Vt=1500, H=32),
     "square-194": CONFIGS[4].scaled(B=97, gamma=1, R=2, V=20000, Vt=5000, H=256),
     "small-batch-odd-H": CONFIGS[4].scaled(B=4, V=9001, Vt=1234, H=520),
 }

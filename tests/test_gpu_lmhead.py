@@ -47,6 +47,8 @@ CASES = [
     (193, 512, 1200, 1100, True),   # one row past it: 256 x 256 tiles
     (100, 520, 1000, 700, True),    # H % 32 != 0 at 100 rows: 128 x 128 tiles
     (40, 256, 70000, 66000, True),  # all rows per 256 head rows (258 blocks of 256: one per CU)
+    (40, 256, 3000, 64, True),      # a head of 64 rows: one 128-column block, half of it past Vt
+    (70, 32, 500, 300, True),       # H = 32: a single K step (the ring re-fetches it)
     (512, 3072, 2000, 1000, True),  # MFMA at config 4's M and H
     (7, 8192, 700, 700, False),     # M * ceil(H/512) too large for registers: MFMA
     (2304, 512, 300, 257, True),    # MFMA at config 5's M
