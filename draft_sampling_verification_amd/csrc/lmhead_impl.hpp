@@ -1126,8 +1126,10 @@ __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_tall(const uint16_t
 // bound by streaming W^Trim once, so a tile holds every hidden row, padded only to the next
 // multiple of 32, against BN head rows: one workgroup per BN head rows streams its share of the
 // head once while the hidden rows come from L2.  The 256-row tiles would multiply up to 256 rows
-// whatever M is.  BN / 32 waves, wave w holding all 32 MB tile rows against head columns 32 w ..
-// 32 w + 31 (MB accumulator blocks), so the epilogue merges BN / 32 column slots per row.  BN =
+// whatever M is.  BN / 32 waves: for an odd number MB of 32-row blocks wave w holds all 32 MB tile
+// rows against head columns 32 w .. 32 w + 31 (MB accumulator blocks); for an even one the waves
+// form two rows, each wave holding half the tile rows against 64 columns (MB / 2 x 2 blocks, fewer
+// fragment reads per MFMA); the epilogue merges the column slots per row.  BN =
 // 256 (eight waves, one workgroup per CU and 160 KB of LDS) when the head has at least kCUs
 // blocks of 256 rows, else BN = 128 (four waves, two workgroups per CU and 80 KB each), so that a
 // 32768-row head still spreads over every CU.  The loads of a K step are 2 MB hidden-row chunks
@@ -1172,6 +1174,9 @@ __global__ __launch_bounds__(kWave * (BN / 32)) void lmhead_mfma_rows(const uint
   static_assert(!(BTILED && TRIM), "a K-tiled head is already trimmed");
   using G = RowsTile<MB, BN>;
   constexpr int kTM = G::kTM, kS = G::kStages, kL = G::kLoads, kW = G::kWaves, kOpA = kTM * kDmaRowBytes;
+  // even row-block counts: waves in two rows of kW / 2, each holding half the rows against 64
+  // columns (fewer fragment reads per MFMA); odd: one row of kW waves against 32 columns each
+  constexpr int kWM = MB % 2 == 0 ? 2 : 1, kNJ = kWM, kMI = MB / kWM, kWN = kW / kWM;
   __shared__ __attribute__((aligned(1024))) char smem[kS * G::kStageBytes];
   const int nbm = (M + kTM - 1) / kTM;
   const int nbn = (Vt + BN - 1) / BN;
@@ -1225,25 +1230,30 @@ __global__ __launch_bounds__(kWave * (BN / 32)) void lmhead_mfma_rows(const uint
     for (int j = 0; j < kL; ++j) lds_load16(src[j] + k * step[j], base + dst[j]);
   };
 
-  const int wn = 32 * w;
+  const int wn = (w % kWN) * 32 * kNJ, wm = (w / kWN) * 32 * kMI;
   const int lr = lane & 31;
   const int sw = dma_swz(lr);
   const int off0 = lr * kDmaRowBytes + (((lane >> 5) ^ sw) << 4);
   const int off1 = lr * kDmaRowBytes + (((2 + (lane >> 5)) ^ sw) << 4);
-  f32x16 acc[MB][1];
+  f32x16 acc[kMI][kNJ];
 #pragma unroll
-  for (int i = 0; i < MB; ++i)
+  for (int i = 0; i < kMI; ++i)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[i][0][v] = 0.f;
+    for (int j = 0; j < kNJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
   auto slice = [&](int slot, int off) {
-    const char *sa = smem + slot * G::kStageBytes + off;
+    const char *sa = smem + slot * G::kStageBytes + wm * kDmaRowBytes + off;
     const char *sb = smem + slot * G::kStageBytes + kOpA + wn * kDmaRowBytes + off;
-    bf16x8 a[MB];
-    const bf16x8 b = *reinterpret_cast<const bf16x8 *>(sb);
+    bf16x8 a[kMI], b[kNJ];
 #pragma unroll
-    for (int i = 0; i < MB; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(sa + i * 32 * kDmaRowBytes);
+    for (int j = 0; j < kNJ; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(sb + j * 32 * kDmaRowBytes);
 #pragma unroll
-    for (int i = 0; i < MB; ++i) acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, acc[i][0], 0, 0, 0);
+    for (int i = 0; i < kMI; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(sa + i * 32 * kDmaRowBytes);
+#pragma unroll
+    for (int i = 0; i < kMI; ++i)
+#pragma unroll
+      for (int j = 0; j < kNJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   };
 
   // step k: both 16-deep slices of slot k % kS; then (wait + barrier) step k + 1 is in LDS and the
@@ -1264,8 +1274,8 @@ __global__ __launch_bounds__(kWave * (BN / 32)) void lmhead_mfma_rows(const uint
   }
   wait_vmcnt<0>();
   __syncthreads();
-  tile_store<PARTS, MB, 1, kTM, BN>(acc, M, Vt, m0, n0, 0, wn, nbn, bn, logits, parts,
-                                   reinterpret_cast<float2(*)[kTM]>(smem));
+  tile_store<PARTS, kMI, kNJ, kTM, BN>(acc, M, Vt, m0, n0, wm, wn, nbn, bn, logits, parts,
+                                       reinterpret_cast<float2(*)[kTM]>(smem));
 }
 
 typedef void (*HeadKernel)(const uint16_t *, const uint16_t *, const int32_t *, int, int, int, int, float *,
