@@ -1129,11 +1129,11 @@ __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_tall(const uint16_t
 // whatever M is.  BN / 32 waves: for an odd number MB of 32-row blocks wave w holds all 32 MB tile
 // rows against head columns 32 w .. 32 w + 31 (MB accumulator blocks); for an even one the waves
 // form two rows, each wave holding half the tile rows against 64 columns (MB / 2 x 2 blocks, fewer
-// fragment reads per MFMA); the epilogue merges the column slots per row.  BN =
-// 256 (eight waves, one workgroup per CU and 160 KB of LDS) when the head has at least kCUs
-// blocks of 256 rows, else BN = 128 (four waves, two workgroups per CU and 80 KB each), so that a
-// 32768-row head still spreads over every CU.  The loads of a K step are 2 MB hidden-row chunks
-// and BN / 16 head-row chunks of 1 KB (16 rows x 64 bytes, swizzled as in the 256 x 256 kernel),
+// fragment reads per MFMA); the epilogue merges the column slots per row.  BN = 256 (eight waves,
+// one workgroup per CU and 160 KB of LDS) when the head has at least kCUs blocks of 256 rows,
+// else BN = 128 (four waves and 80 KB, so up to two workgroups per CU), so that a 32768-row head
+// still spreads over every CU.  The loads of a K step are two 1 KB chunks (16 rows x 64 bytes,
+// swizzled as in the 256 x 256 kernel) per 32-row block of hidden rows and BN / 16 of head rows,
 // dealt out to the waves in turn; a wave with fewer distinct chunks fetches one of the others
 // again, which writes the same bytes to the same place, so every wave issues the same number of
 // loads per step and one wait count serves all.  The ring holds as many K steps as fit the
@@ -1166,11 +1166,10 @@ __device__ __forceinline__ void lds_load16(const uint16_t *src, char *dst) {
 
 template <int MB, int BN, bool TRIM, int PARTS, bool ATILED, bool BTILED>
 __global__ __launch_bounds__(kWave * (BN / 32)) void lmhead_mfma_rows(const uint16_t *__restrict__ hidden,
-                                                                               const uint16_t *__restrict__ weight,
-                                                                               const int32_t *__restrict__ keep,
-                                                                               int vrows, int M, int H, int Vt,
-                                                                               float *__restrict__ logits,
-                                                                               GemvParts parts) {
+                                                                      const uint16_t *__restrict__ weight,
+                                                                      const int32_t *__restrict__ keep, int vrows,
+                                                                      int M, int H, int Vt, float *__restrict__ logits,
+                                                                      GemvParts parts) {
   static_assert(!(BTILED && TRIM), "a K-tiled head is already trimmed");
   using G = RowsTile<MB, BN>;
   constexpr int kTM = G::kTM, kS = G::kStages, kL = G::kLoads, kW = G::kWaves, kOpA = kTM * kDmaRowBytes;

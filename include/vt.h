@@ -190,6 +190,8 @@ size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
  * 384 x 256 tiles (384 hidden rows) when padding B*R to 384-row blocks adds no more rows than
  * padding it to 256-row blocks (B*R = 2304, 288, 756 ...), else 256 x 256 tiles (B*R = 224, 512
  * ...); all sum the same products in the same order as the separate call's kernel.
+ *   The call issues kernel launches (and the optional events) only: no allocation, memset or copy,
+ *   so it can be captured into a HIP graph with its workspace and replayed.
  *   Pages: as for the four calls above.
  *
  *   hidden bf16 [B*R][H] (row b*R + i is sequence b's i-th draft position); weight bf16 [V][H]
