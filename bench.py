@@ -115,7 +115,8 @@ def parse():
     ap.add_argument("--greedy", action="store_true",
                     help="temperature 0 for target and draft: argmax drafts and greedy verification")
     ap.add_argument("--graph", action="store_true",
-                    help="replay captured HIP graphs (LM head | rest) instead of launching the calls eagerly")
+                    help="replay captured HIP graphs instead of launching eagerly: with --calls the LM head | "
+                         "the rest; for the toy (--config 1) the whole step")
     ap.add_argument("--head", default="tiled", choices=["tiled", "gather"],
                     help="what the fused call's large-batch head reads: the K-tiled W^Trim built once per keep "
                          "set by vt_trim_head_tiled (the default), or rows of the full head gathered through "
@@ -392,10 +393,43 @@ def bench_toy(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
+    if args.graph:
+        # the verify kernel timed on eager steps; the step itself as replays of one captured graph
+        # (the toy's inner loop is launch-bound: ~20 small launches per step)
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(main_s)
+        with torch.cuda.stream(side):
+            step()
+        main_s.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        step()
+        torch.cuda.synchronize()
+        want = (tok.clone(), nacc.clone())
+        for _ in range(3):
+            tok.fill_(-3)
+            nacc.fill_(-3)
+            graph.replay()
+            torch.cuda.synchronize()
+            if not (torch.equal(tok, want[0]) and torch.equal(nacc, want[1])):
+                raise SystemExit("toy graph replay differs from the eager step")
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+    else:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = 1e3 * wall / args.steps
     v_ms = sum(a.elapsed_time(b) for a, b in zip(ev_a, ev_b)) / args.steps
@@ -421,7 +455,8 @@ def bench_toy(args):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{cfg.name}; batch {B}", "batch": B, "gamma": g, "vocab": V,
-                   "launch": "gamma draft draws + target softmax + verify, separate calls (toy rows gathered by torch)",
+                   "launch": "gamma draft draws + target softmax + verify, separate calls (toy rows gathered by torch)"
+                             + ("; the step replayed as one captured HIP graph" if args.graph else ""),
                    "us_per_step": round(1e3 * ms, 2),
                    "mean_accepted": round(float(nacc.double().mean()), 4)},
         "roofline": {"bound": "hbm", "achieved": round(vb / (v_ms / 1e3) / 1e9, 2), "peak": HBM_PEAK_GBS,
