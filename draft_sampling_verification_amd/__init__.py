@@ -255,7 +255,7 @@ def vt_spec_block(hidden, weight, keep_ids, full_to_trim, target_logits, target_
     [B*(gamma+1)] f64, out_tokens [B, gamma+1] i32, out_num_accepted [B] i32.
     lmhead_events: optional (start, end) torch.cuda.Event pair recorded around the LM-head kernel.
     weight_tiled: optional K-tiled W^Trim from vt_trim_head_tiled(weight, keep_ids), read by the
-    large-batch head instead of gathering rows of weight (same logits).
+    MFMA head instead of gathering rows of weight (same logits).
     target_T = 0: greedy verification (target_lse, u_accept, u_final may be None); draft_T = 0 (with
     target_T = 0): argmax drafts (u_draft may be None)."""
     torch = _torch()

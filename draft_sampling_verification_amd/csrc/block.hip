@@ -38,18 +38,19 @@ constexpr int64_t kFvMfmaMaxB = 4;
 
 struct BlockPlan {
   bool fused;       // GEMV with draft partials in its epilogue
-  bool fused_mfma;  // large-batch MFMA tiles with draft partials (softmax or argmax) in their epilogue
-  bool fv;          // small batch, sampling both sides: target partials ride in the GEMV launch,
-                    // then one chunk pass and one final pass (verify_fused_chunk / _final)
+  bool fused_mfma;  // MFMA head with draft partials (softmax or argmax) in its epilogue
+  bool fv;          // small batch, sampling both sides: target partials (in the GEMV launch, or a
+                    // launch of their own before an MFMA head), then one chunk pass and one final
+                    // pass (verify_fused_chunk / _final)
   bool fg;          // small batch, greedy both sides: argmax partials in the GEMV launch (head
                     // blocks and, in extra workgroups, target chunks), then verify_greedy_small
   int64_t M, rows_t;
   int64_t nchunk_t;  // 4096-chunks of a target row
-  int64_t nchunk_d;  // draft partial chunks per row (GEMV row blocks, or 4096-chunks)
+  int64_t nchunk_d;  // draft partial chunks per row (GEMV row blocks, MFMA column blocks, or 4096-chunks)
   int chunk_d;
   int64_t nchunk_v;
   size_t off_tpart, off_dpart, off_nbuf, off_vpart, off_wbuf, off_hidt, bytes;
-  size_t hidt_bytes;  // K-tiled copy of the hidden rows for the large-batch head (0: none)
+  size_t hidt_bytes;  // K-tiled copy of the hidden rows for the MFMA head (0: none)
 };
 
 // greedy_t: the target is decoded greedily (no target softmax; verification compares argmaxes).
@@ -243,7 +244,7 @@ hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, 
   const int vrows = static_cast<int>(Vp.V);  // the head passed in is the full [V][H] one
   const bool greedy_t = Vp.greedy;
   const bool t_multi = !greedy_t && pl.nchunk_t > 1;
-  // the large-batch head reads the hidden rows K-tiled (one contiguous run per K step of a block of
+  // the MFMA head reads the hidden rows K-tiled (one contiguous run per K step of a block of
   // hidden rows); the copy rides in extra workgroups of the target partials launch when there is one
   uint16_t *hidt = pl.hidt_bytes ? reinterpret_cast<uint16_t *>(hidt_base) : nullptr;
   const TileParams tp = hidden_tiles_params(hidden, pl.M, H, Vt, hidt);

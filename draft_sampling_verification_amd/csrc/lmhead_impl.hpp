@@ -565,7 +565,7 @@ GemvFn pick_gemv(int64_t M, int64_t H, bool trim) {
   }
 }
 
-// ------------------------------------------------- batches past the GEMV (256-column tiles)
+// ---------------------------------------------------------- batches past the GEMV (MFMA tiles)
 //
 // 256 x 256 output tiles (hidden rows x head rows), K in steps of 64, one workgroup of four waves
 // per CU (the double-buffered tiles take 144 KB of LDS).  Each wave owns a 128 x 128 quarter as
@@ -1302,7 +1302,7 @@ HeadKernel pick_rows(int mb, int bn) {
 
 inline int64_t mfma_big_tiles_n(int64_t Vt) { return (Vt + kBigBN - 1) / kBigBN; }
 
-// Rows per hidden-row block of the large-batch head that reads a K-tiled copy: 384 (the tall
+// Rows per hidden-row block of the 256-column heads that read a K-tiled copy: 384 (the tall
 // tiles) or 256, whichever needs fewer hidden rows per CU: one tile per CU at a time, so a launch
 // of t tiles of R rows takes about ceil(t / kCUs) R row-steps (2304 rows and 256 head blocks: 6
 // waves of 384 against 9 of 256, a tie, and the tall tiles move fewer bytes per flop; 384 rows

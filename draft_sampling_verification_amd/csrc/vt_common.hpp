@@ -225,9 +225,10 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblocks) {
 }
 
 // K-tiled layout of a matrix of rows of H bf16 values (the trimmed head made by
-// vt_trim_head_tiled, the hidden-row copy of the large-batch head): block b of kTileRows rows and
-// K step s of kTileK columns sit at out[b][s][r][kTileK], so each (b, s) slice is one contiguous
-// 16 KB run.  Rows past the matrix's end fill out its last block.
+// vt_trim_head_tiled; the MFMA heads' hidden-row copy takes the same layout with blocks of their
+// own tile rows): block b of kTileRows rows and K step s of kTileK columns sit at
+// out[b][s][r][kTileK], so each (b, s) slice is one contiguous 16 KB run.  Rows past the matrix's
+// end fill out its last block.
 constexpr int kTileRows = 256, kTileK = 32;
 inline size_t tiled_rows_bytes(int64_t rows, int64_t H) {
   return static_cast<size_t>((rows + kTileRows - 1) / kTileRows) * kTileRows * static_cast<size_t>(H) * 2;

@@ -79,7 +79,7 @@ def gpu_block(wl: Workload, probs: bool = False, device_inputs=None) -> dict:
 
 def gpu_block_fused(wl: Workload, events=None, tiled: bool = False) -> dict:
     """The same block through the single fused call vt_spec_block (tiled: with the K-tiled W^Trim
-    of vt_trim_head_tiled, which the large-batch head reads instead of gathering rows)."""
+    of vt_trim_head_tiled, which the MFMA heads read instead of gathering rows)."""
     cfg = wl.cfg
     B, R, g = wl.B, cfg.R, cfg.gamma
     keep = dev(wl.keep_ids) if wl.keep_ids is not None else None
