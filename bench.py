@@ -47,10 +47,12 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20
 # the LM head's MFMA kernels (past the GEMV's 8 rows): with H % 32 == 0 all rows in one block up
-# to ROWS_MAX_M rows, then 256 x 256 or (fused call, rows filling 384-row blocks) 384 x 256 tiles;
-# otherwise 128 x 128 tiles below BIG_MIN_M rows and register-staged 256 x 256 tiles from there
-ROWS_MAX_M = 192
+# to ROWS_MAX_M rows (ROWS_MAX_M_NARROW when W^Trim has fewer than 256 blocks of 256 rows), then
+# 256 x 256 or (fused call, when they give fewer rows per CU) 384 x 256 tiles; otherwise 128 x 128
+# tiles below BIG_MIN_M rows and register-staged 256 x 256 tiles from there
+ROWS_MAX_M, ROWS_MAX_M_NARROW = 192, 256
 BIG_MIN_M = 129
+CUS = 256
 
 
 def gemv_head(M: int, H: int) -> bool:
@@ -59,14 +61,16 @@ def gemv_head(M: int, H: int) -> bool:
     return M <= 8 and nit <= 8 and M * nit <= 48
 
 
-def head_kernel(M: int, H: int, calls: bool) -> str:
+def head_kernel(M: int, H: int, calls: bool, Vt: int) -> str:
     """Name of the LM-head kernel vt_spec_block (calls=False) or vt_lmhead_trimmed runs."""
     if gemv_head(M, H):
         return "lmhead_gemv"
     if H % 32 == 0:
-        if M <= ROWS_MAX_M:
+        nbn = -(-Vt // 256)
+        if M <= (ROWS_MAX_M_NARROW if nbn < CUS else ROWS_MAX_M):
             return "lmhead_mfma_rows"
-        tall = not calls and -(-M // 384) * 384 <= -(-M // 256) * 256
+        # 384- or 256-row tiles, whichever gives fewer rows per CU (one tile per CU at a time)
+        tall = not calls and -(-(-(-M // 384) * nbn) // CUS) * 384 <= -(-(-(-M // 256) * nbn) // CUS) * 256
         return "lmhead_mfma_tall" if tall else "lmhead_mfma_dma8"
     return "lmhead_mfma_big" if M >= BIG_MIN_M else "lmhead_mfma"
 
@@ -915,7 +919,7 @@ def main():
     # PMC records are per config at the config's own batch
     traffic = None if args.sequences else measured_traffic(f"config{args.config}")
     M = B * cfg.R
-    kernel = (head_kernel(M, cfg.H, args.calls)
+    kernel = (head_kernel(M, cfg.H, args.calls, cfg.Vt)
               + (" + target softmax partials" if small_batch_block(cfg, args.greedy) and not args.calls else ""))
     if res["mfma"]:
         # a real dense contraction: the head is priced against the bf16 MFMA peak

@@ -1122,7 +1122,7 @@ __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_tall(const uint16_t
                          reinterpret_cast<float2(*)[kTallBM]>(smem));
 }
 
-// Up to kRowsMaxM hidden rows (decode batches of a few to a few dozen sequences): the head is
+// Up to rows_max(Vt) hidden rows (decode batches of a few to a few dozen sequences): the head is
 // bound by streaming W^Trim once, so a tile holds every hidden row, padded only to the next
 // multiple of 32, against BN head rows: one workgroup per BN head rows streams its share of the
 // head once while the hidden rows come from L2.  The 256-row tiles would multiply up to 256 rows
@@ -1138,8 +1138,10 @@ __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_tall(const uint16_t
 // again, which writes the same bytes to the same place, so every wave issues the same number of
 // loads per step and one wait count serves all.  The ring holds as many K steps as fit the
 // workgroup's LDS, at most eight.  Each output sums the same products in the same K order as the
-// other direct-to-LDS kernels: the same logits bits.
-constexpr int kRowsMaxMB = 6;
+// other direct-to-LDS kernels: the same logits bits.  Up to 192 rows (six blocks) in general; with
+// 128-column blocks up to 256 (seven or eight blocks, each workgroup then taking the whole 160 KB
+// of LDS), where the 256 x 256 tiles would leave CUs idle.
+constexpr int kRowsMaxMB = 6, kRowsMaxMB128 = 8;
 constexpr int kRowsMaxM = 32 * kRowsMaxMB;
 constexpr int kCUs = 256;  // compute units of the part
 
@@ -1151,9 +1153,11 @@ struct RowsTile {
   static constexpr int kChunks = 2 * MB + BN / 16;  // 1 KB loads per K step
   static constexpr int kLoads = (kChunks + kWaves - 1) / kWaves;  // per wave
   static constexpr int kStageBytes = kChunks * 1024;
-  static constexpr int kFit = (160 * 1024 / (256 / BN)) / kStageBytes;
+  static constexpr int kLdsBytes = MB > kRowsMaxMB ? 160 * 1024 : 160 * 1024 / (256 / BN);
+  static constexpr int kFit = kLdsBytes / kStageBytes;
   static constexpr int kStages = kFit < 8 ? kFit : 8;
   static_assert(BN == 128 || BN == 256, "tile widths");
+  static_assert(MB <= (BN == 128 ? kRowsMaxMB128 : kRowsMaxMB), "row blocks");
   static_assert(kStages >= 3 && kLoads * (kStages - 2) < 64, "ring and wait counts");
 };
 
@@ -1289,10 +1293,16 @@ HeadKernel pick_rows_bn(int mb) {
     case 4: return &lmhead_mfma_rows<4, BN, TRIM, PARTS, ATILED, BTILED>;
     case 5: return &lmhead_mfma_rows<5, BN, TRIM, PARTS, ATILED, BTILED>;
     case 6: return &lmhead_mfma_rows<6, BN, TRIM, PARTS, ATILED, BTILED>;
+    case 7:
+      if constexpr (BN == 128) return &lmhead_mfma_rows<7, BN, TRIM, PARTS, ATILED, BTILED>;
+      return nullptr;
+    case 8:
+      if constexpr (BN == 128) return &lmhead_mfma_rows<8, BN, TRIM, PARTS, ATILED, BTILED>;
+      return nullptr;
     default: return nullptr;
   }
 }
-static_assert(kRowsMaxMB == 6, "pick_rows_bn covers 1 .. kRowsMaxMB row blocks");
+static_assert(kRowsMaxMB == 6 && kRowsMaxMB128 == 8, "pick_rows_bn covers the row blocks");
 
 template <bool TRIM, int PARTS, bool ATILED, bool BTILED>
 HeadKernel pick_rows(int mb, int bn) {
@@ -1314,17 +1324,21 @@ inline int big_tile_rows(int64_t M, int64_t Vt) {
   return (t384 + kCUs - 1) / kCUs * kTallBM <= (t256 + kCUs - 1) / kCUs * kBigBM ? kTallBM : kBigBM;
 }
 
+// Hidden rows up to which the all-rows kernel runs: 256 when its column blocks are 128 rows (fewer
+// than kCUs blocks of 256 head rows), else 192.
+inline int64_t rows_max(int64_t Vt) { return mfma_big_tiles_n(Vt) < kCUs ? 32 * kRowsMaxMB128 : kRowsMaxM; }
+
 // Rows per hidden-row block of the direct-to-LDS heads: all M rows padded to a multiple of 32 up
-// to kRowsMaxM (lmhead_mfma_rows), else big_tile_rows(M, Vt).
+// to rows_max(Vt) (lmhead_mfma_rows), else big_tile_rows(M, Vt).
 inline int head_tile_rows(int64_t M, int64_t Vt) {
-  return M <= kRowsMaxM ? static_cast<int>((M + 31) / 32 * 32) : big_tile_rows(M, Vt);
+  return M <= rows_max(Vt) ? static_cast<int>((M + 31) / 32 * 32) : big_tile_rows(M, Vt);
 }
 
 // Head rows per column block of the MFMA heads with whole 32-column K steps, which is also the
 // chunk of their draft partials: 128 for the all-rows kernel when fewer than kCUs blocks of 256
 // head rows would leave CUs idle, else 256.
 inline int head_tile_cols(int64_t M, int64_t H, int64_t Vt) {
-  return H % kDmaBK == 0 && M <= kRowsMaxM && mfma_big_tiles_n(Vt) < kCUs ? 128 : kBigBN;
+  return H % kDmaBK == 0 && M <= rows_max(Vt) && mfma_big_tiles_n(Vt) < kCUs ? 128 : kBigBN;
 }
 
 // K-tiled copy of the hidden rows for the direct-to-LDS heads (lmhead_mfma_rows, _dma8 and _tall
@@ -1396,12 +1410,12 @@ __global__ __launch_bounds__(kBlock) void softmax_partial_tiles(SmParams P, Tile
 
 
 // The MFMA heads with whole 32-column K steps (any M), or with M >= kBigMinM (any H).
-// PARTS = kPartsNone (the separate LM-head call): the hidden rows as given; up to kRowsMaxM rows
+// PARTS = kPartsNone (the separate LM-head call): the hidden rows as given; up to rows_max(Vt) rows
 // in one block of all of them (head_tile_cols(M, H, Vt) head rows per workgroup), else 256 x 256
 // tiles.  kPartsSoftmax / kPartsArgmax (the fused block's head, with its draft partials per
 // head_tile_cols(M, H, Vt) head rows): when H % 32 == 0 hidden_tiled must hold the K-tiled copy
 // of the hidden rows made by hidden_tiles, in blocks of head_tile_rows(M, Vt) rows, which select
-// the kernel (all rows up to kRowsMaxM, 384-row tall tiles or 256 x 256 tiles); weight_tiled: NULL, or
+// the kernel (all rows up to rows_max(Vt), 384-row tall tiles or 256 x 256 tiles); weight_tiled: NULL, or
 // the K-tiled trimmed head of vt_trim_head_tiled (weight and keep are then not read by the
 // kernel).  Other H take the register-staged kernel on the rows as given.
 template <int PARTS>
@@ -1411,7 +1425,7 @@ inline hipError_t launch_mfma_head(const uint16_t *hidden, const uint16_t *weigh
                                    const uint16_t *weight_tiled = nullptr) {
   const int64_t tiles = ((M + kBigBM - 1) / kBigBM) * mfma_big_tiles_n(Vt);
   const int iM = static_cast<int>(M), iH = static_cast<int>(H), iV = static_cast<int>(Vt);
-  if (H % kDmaBK == 0 && M <= kRowsMaxM) {
+  if (H % kDmaBK == 0 && M <= rows_max(Vt)) {
     const int mb = static_cast<int>((M + 31) / 32), bn = head_tile_cols(M, H, Vt);
     const dim3 grid(static_cast<unsigned>((Vt + bn - 1) / bn)), block(static_cast<unsigned>(kWave * (bn / 32)));
     if constexpr (PARTS == kPartsNone) {

@@ -12,20 +12,24 @@ from workloads import CONFIGS
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-@pytest.mark.parametrize("M,H,calls,kernel", [
-    (6, 3072, False, "lmhead_gemv"),          # configs 2 and 3
-    (8, 4096, False, "lmhead_mfma_rows"),     # 8 rows of 4096 exceed the GEMV's registers
-    (9, 4096, False, "lmhead_mfma_rows"),     # config 5's shape at one sequence
-    (192, 3072, False, "lmhead_mfma_rows"),   # the largest all-rows block
-    (193, 3072, False, "lmhead_mfma_dma8"),
-    (512, 3072, False, "lmhead_mfma_dma8"),   # config 4
-    (2304, 4096, False, "lmhead_mfma_tall"),  # config 5, fused call
-    (2304, 4096, True, "lmhead_mfma_dma8"),   # config 5, separate calls
-    (100, 520, False, "lmhead_mfma"),         # H % 32 != 0 up to 128 rows
-    (300, 520, False, "lmhead_mfma_big"),
+@pytest.mark.parametrize("M,H,Vt,calls,kernel", [
+    (6, 3072, 32768, False, "lmhead_gemv"),          # configs 2 and 3
+    (8, 4096, 65536, False, "lmhead_mfma_rows"),     # 8 rows of 4096 exceed the GEMV's registers
+    (9, 4096, 65536, False, "lmhead_mfma_rows"),     # config 5's shape at one sequence
+    (192, 4096, 65536, False, "lmhead_mfma_rows"),   # the largest all-rows block on 256 columns
+    (193, 4096, 65536, False, "lmhead_mfma_dma8"),
+    (256, 3072, 32768, False, "lmhead_mfma_rows"),   # 128-column blocks: up to 256 rows
+    (257, 3072, 32768, False, "lmhead_mfma_dma8"),
+    (512, 3072, 32768, False, "lmhead_mfma_dma8"),   # config 4
+    (384, 3072, 32768, False, "lmhead_mfma_dma8"),   # 256 square tiles beat 128 tall ones
+    (288, 4096, 65536, False, "lmhead_mfma_tall"),   # 256 tall tiles against 512 square ones
+    (2304, 4096, 65536, False, "lmhead_mfma_tall"),  # config 5, fused call
+    (2304, 4096, 65536, True, "lmhead_mfma_dma8"),   # config 5, separate calls
+    (100, 520, 32768, False, "lmhead_mfma"),         # H % 32 != 0 up to 128 rows
+    (300, 520, 32768, False, "lmhead_mfma_big"),
 ])
-def test_head_kernel_names(M, H, calls, kernel):
-    assert bench.head_kernel(M, H, calls) == kernel
+def test_head_kernel_names(M, H, Vt, calls, kernel):
+    assert bench.head_kernel(M, H, calls, Vt) == kernel
 
 
 def test_gemv_register_limit():

@@ -29,15 +29,19 @@ SCALED = {
     # 256-row tiles (two blocks)
     "c5-tall-two-blocks": CONFIGS[5].scaled(B=84, V=40000, Vt=32001, H=256),
     "c4-square-two-blocks": CONFIGS[4].scaled(B=64, V=20000, Vt=5000, H=256),
-    # past the GEMV sizes, up to 192 hidden rows: one block of all rows padded to a multiple of
-    # 32 (9 rows: one 32-row block; 96: three; 128, 129: four, five; 192: six) per 128 head rows
-    # (fewer than 256 blocks of 256) or per 256 (66000 head rows), then 256 x 256 tiles from 193;
-    # with H % 32 != 0 below 129 rows, 128 x 128 tiles and a separate draft softmax
+    # past the GEMV sizes: one block of all rows padded to a multiple of 32 (9 rows: one 32-row
+    # block; 96: three; 128, 129: four, five; 192: six) per 256 head rows (66000 head rows) up to
+    # 192 rows, or per 128 (fewer than 256 blocks of 256) up to 256 rows (194: seven; 256:
+    # eight), then 256 x 256 tiles; with H % 32 != 0 below 129 rows, 128 x 128 tiles and a
+    # separate draft softmax
     "rows-9": CONFIGS[4].scaled(B=3, gamma=2, R=3, V=20000, Vt=5000, H=256),
     "rows-96": CONFIGS[4].scaled(B=12, V=20000, Vt=5000, H=256),
     "rows-128": CONFIGS[4].scaled(B=16, V=20000, Vt=5000, H=256),
     "rows-129": CONFIGS[4].scaled(B=43, gamma=2, R=3, V=20000, Vt=5000, H=256),
     "rows-192": CONFIGS[4].scaled(B=24, V=20000, Vt=5000, H=256),
+    "rows-194-seven-blocks": CONFIGS[4].scaled(B=97, gamma=1, R=2, V=20000, Vt=5000, H=256),
+    "rows-256-eight-blocks": CONFIGS[4].scaled(B=32, V=20000, Vt=5000, H=256),
+    "square-258": CONFIGS[4].scaled(B=129, gamma=1, R=2, V=20000, Vt=5000, H=256),
     "rows-36-wide-head": CONFIGS[5].scaled(B=4, V=70000, Vt=66000, H=256),
     # up to 32 hidden rows of at most 8 per sequence the MFMA head is followed by the two-pass
     # verification (chunk pass and final pass) instead of the combine and verify launches
@@ -49,7 +53,6 @@ SCALED = {
     # a 64-row head past the GEMV sizes (one partial per draft row) and H = 32 (one K step)
     "rows-tiny-head": CONFIGS[4].scaled(B=8, V=3000, Vt=64, H=256),
     "rows-one-k-step": CONFIGS[4].scaled(B=6, V=5000, Vt=1500, H=32),
-    "square-194": CONFIGS[4].scaled(B=97, gamma=1, R=2, V=20000, Vt=5000, H=256),
     "small-batch-odd-H": CONFIGS[4].scaled(B=4, V=9001, Vt=1234, H=520),
 }
 

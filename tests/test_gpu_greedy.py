@@ -125,11 +125,11 @@ def _block_greedy(wl, draft_T, tiled=False):
     ("c3-scaled sampled drafts", CONFIGS[3].scaled(B=4, V=20000, Vt=5000, H=512), 1.0),
     ("c4-scaled argmax drafts", CONFIGS[4].scaled(B=24, V=9001, Vt=3000, H=256), 0.0),
     ("c4 big tiles argmax drafts", CONFIGS[4].scaled(B=40, V=20000, Vt=5000, H=256), 0.0),
-    # argmax partials from the all-rows blocks (96 and 192 rows), from 256 x 256 tiles at 225
-    # rows, and with H % 32 != 0 at 32 rows a separate argmax pass after 128 x 128 tiles
+    # argmax partials from the all-rows blocks (96, 192 and 225 rows), and with H % 32 != 0 at 32
+    # rows a separate argmax pass after 128 x 128 tiles
     ("rows 96 argmax drafts", CONFIGS[4].scaled(B=12, V=20000, Vt=5000, H=256), 0.0),
     ("rows 192 argmax drafts", CONFIGS[4].scaled(B=24, V=20000, Vt=5000, H=256), 0.0),
-    ("square 225 rows argmax drafts", CONFIGS[4].scaled(B=75, gamma=2, R=3, V=20000, Vt=5000, H=256), 0.0),
+    ("rows 225 argmax drafts", CONFIGS[4].scaled(B=75, gamma=2, R=3, V=20000, Vt=5000, H=256), 0.0),
     ("odd H 32 rows argmax drafts", CONFIGS[4].scaled(B=4, V=9001, Vt=1234, H=520), 0.0),
     # argmax partials from the large-batch heads' epilogues: 512 hidden rows on 256 x 256 tiles,
     # 756 on 384 x 256 tiles (two row blocks, ragged Vt), H = 520 on the register-staged tiles

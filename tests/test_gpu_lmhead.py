@@ -3,8 +3,9 @@
 Tolerance: |gpu - oracle| <= H * 2^-24 * sum_k |h_k w_k| per logit (the recursive-summation
 bound for fp32 accumulation of exact bf16 products) -- the observed error is also reported.
 Shapes cover the dot2 GEMV (M <= 8) and the MFMA kernels (M > 8 or large H: all rows in one
-block up to 192 rows, 256 x 256 tiles beyond; 128 x 128 and register-staged tiles when H is not a
-multiple of 32), ragged row and K tails, trimmed and untrimmed heads."""
+block up to 192 rows, or 256 on heads of fewer than 256 blocks of 256 rows, 256 x 256 tiles
+beyond; 128 x 128 and register-staged tiles when H is not a multiple of 32), ragged row and K
+tails, trimmed and untrimmed heads."""
 import numpy as np
 import pytest
 import torch
@@ -43,8 +44,11 @@ CASES = [
     (33, 512, 3001, 2500, True),    # one block of 64 rows, ragged rows and head rows
     (64, 1024, 3000, 3000, False),  # one block of exactly 64 rows, untrimmed
     (96, 256, 2000, 777, True),     # 96 rows
-    (192, 512, 1200, 1100, True),   # the largest all-rows block (192)
-    (193, 512, 1200, 1100, True),   # one row past it: 256 x 256 tiles
+    (192, 512, 1200, 1100, True),   # six row blocks
+    (224, 512, 1200, 1100, True),   # seven and eight row blocks: only on 128-column blocks
+    (256, 512, 1200, 1100, True),
+    (257, 512, 1200, 1100, True),   # one row past them: 256 x 256 tiles
+    (193, 256, 70000, 66000, True), # 256 x 256 tiles past 192 rows when the head has 256+ blocks
     (100, 520, 1000, 700, True),    # H % 32 != 0 at 100 rows: 128 x 128 tiles
     (40, 256, 70000, 66000, True),  # all rows per 256 head rows (258 blocks of 256: one per CU)
     (40, 256, 3000, 64, True),      # a head of 64 rows: one 128-column block, half of it past Vt
@@ -95,7 +99,7 @@ def test_pre_gathered_head_equals_gather():
 def test_mfma_kernels_sum_in_one_order(H, V, Vt, rows):
     # every MFMA kernel sums a logit's products in the same K order, so a hidden row's logits are
     # the same bits whatever the batch's row count selects (H % 32 == 0: all-rows blocks of 32 ..
-    # 192 rows per 128 or 256 head rows, 256 x 256 tiles; other H: 128 x 128 and register-staged
+    # 256 rows per 128 head rows or 32 .. 192 per 256, 256 x 256 tiles; other H: 128 x 128 and register-staged
     # 256 x 256 tiles); only the GEMV (M <= 8) sums differently
     h, w, keep = _inputs(300, H, V, Vt, True, seed=13)
     want = _run(h, w, keep, Vt)
