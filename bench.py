@@ -47,7 +47,8 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20
 # the LM head's MFMA kernels (past the GEMV's 8 rows): with H % 32 == 0 all rows in one block up
-# to ROWS_MAX_M rows (ROWS_MAX_M_NARROW when W^Trim has fewer than 256 blocks of 256 rows), then
+# to ROWS_MAX_M rows (when W^Trim has fewer than 256 blocks of 256 rows: up to ROWS_MAX_M_NARROW
+# rows in one block and up to 2 ROWS_MAX_M in two), then
 # 256 x 256 or (fused call, when they give fewer rows per CU) 384 x 256 tiles; otherwise 128 x 128
 # tiles below BIG_MIN_M rows and register-staged 256 x 256 tiles from there
 ROWS_MAX_M, ROWS_MAX_M_NARROW = 192, 256
@@ -67,7 +68,8 @@ def head_kernel(M: int, H: int, calls: bool, Vt: int) -> str:
         return "lmhead_gemv"
     if H % 32 == 0:
         nbn = -(-Vt // 256)
-        if M <= (ROWS_MAX_M_NARROW if nbn < CUS else ROWS_MAX_M):
+        # one block of all rows, or on narrow heads up to two blocks of at most ROWS_MAX_M rows
+        if M <= (ROWS_MAX_M_NARROW if nbn < CUS else ROWS_MAX_M) or (nbn < CUS and M <= 2 * ROWS_MAX_M):
             return "lmhead_mfma_rows"
         # 384- or 256-row tiles, whichever gives fewer rows per CU (one tile per CU at a time)
         tall = not calls and -(-(-(-M // 384) * nbn) // CUS) * 384 <= -(-(-(-M // 256) * nbn) // CUS) * 256

@@ -1139,8 +1139,9 @@ __global__ __launch_bounds__(kDma8Block, 1) void lmhead_mfma_tall(const uint16_t
 // loads per step and one wait count serves all.  The ring holds as many K steps as fit the
 // workgroup's LDS, at most eight.  Each output sums the same products in the same K order as the
 // other direct-to-LDS kernels: the same logits bits.  Up to 192 rows (six blocks) in general; with
-// 128-column blocks up to 256 (seven or eight blocks, each workgroup then taking the whole 160 KB
-// of LDS), where the 256 x 256 tiles would leave CUs idle.
+// 128-column blocks, where the 256 x 256 tiles would leave CUs idle, up to 256 (seven or eight
+// blocks, each workgroup then taking the whole 160 KB of LDS), and up to 384 in two row blocks of
+// at most six (two workgroups per CU, one of each block).
 constexpr int kRowsMaxMB = 6, kRowsMaxMB128 = 8;
 constexpr int kRowsMaxM = 32 * kRowsMaxMB;
 constexpr int kCUs = 256;  // compute units of the part
@@ -1328,17 +1329,29 @@ inline int big_tile_rows(int64_t M, int64_t Vt) {
 // than kCUs blocks of 256 head rows), else 192.
 inline int64_t rows_max(int64_t Vt) { return mfma_big_tiles_n(Vt) < kCUs ? 32 * kRowsMaxMB128 : kRowsMaxM; }
 
-// Rows per hidden-row block of the direct-to-LDS heads: all M rows padded to a multiple of 32 up
-// to rows_max(Vt) (lmhead_mfma_rows), else big_tile_rows(M, Vt).
+// Whether the all-rows kernel takes M rows: in one block up to rows_max(Vt), and on heads of fewer
+// than kCUs blocks of 256 rows in two blocks of at most kRowsMaxM rows (the batched shape's head
+// at 264 to 384 rows: 88-93 us against 101-104 us on 256 x 256 tiles).  rows_block: its rows per
+// block.
+inline bool rows_kernel(int64_t M, int64_t Vt) {
+  return M <= rows_max(Vt) || (mfma_big_tiles_n(Vt) < kCUs && M <= 2 * kRowsMaxM);
+}
+inline int rows_block(int64_t M, int64_t Vt) {
+  const int64_t per = M <= rows_max(Vt) ? M : (M + 1) / 2;
+  return static_cast<int>((per + 31) / 32 * 32);
+}
+
+// Rows per hidden-row block of the direct-to-LDS heads: rows_block(M, Vt) for the all-rows kernel,
+// else big_tile_rows(M, Vt).
 inline int head_tile_rows(int64_t M, int64_t Vt) {
-  return M <= rows_max(Vt) ? static_cast<int>((M + 31) / 32 * 32) : big_tile_rows(M, Vt);
+  return rows_kernel(M, Vt) ? rows_block(M, Vt) : big_tile_rows(M, Vt);
 }
 
 // Head rows per column block of the MFMA heads with whole 32-column K steps, which is also the
 // chunk of their draft partials: 128 for the all-rows kernel when fewer than kCUs blocks of 256
 // head rows would leave CUs idle, else 256.
 inline int head_tile_cols(int64_t M, int64_t H, int64_t Vt) {
-  return H % kDmaBK == 0 && M <= rows_max(Vt) && mfma_big_tiles_n(Vt) < kCUs ? 128 : kBigBN;
+  return H % kDmaBK == 0 && rows_kernel(M, Vt) && mfma_big_tiles_n(Vt) < kCUs ? 128 : kBigBN;
 }
 
 // K-tiled copy of the hidden rows for the direct-to-LDS heads (lmhead_mfma_rows, _dma8 and _tall
@@ -1410,12 +1423,12 @@ __global__ __launch_bounds__(kBlock) void softmax_partial_tiles(SmParams P, Tile
 
 
 // The MFMA heads with whole 32-column K steps (any M), or with M >= kBigMinM (any H).
-// PARTS = kPartsNone (the separate LM-head call): the hidden rows as given; up to rows_max(Vt) rows
-// in one block of all of them (head_tile_cols(M, H, Vt) head rows per workgroup), else 256 x 256
-// tiles.  kPartsSoftmax / kPartsArgmax (the fused block's head, with its draft partials per
+// PARTS = kPartsNone (the separate LM-head call): the hidden rows as given; the all-rows kernel
+// where rows_kernel(M, Vt) (blocks of rows_block(M, Vt) rows, head_tile_cols(M, H, Vt) head rows
+// per workgroup), else 256 x 256 tiles.  kPartsSoftmax / kPartsArgmax (the fused block's head, with its draft partials per
 // head_tile_cols(M, H, Vt) head rows): when H % 32 == 0 hidden_tiled must hold the K-tiled copy
 // of the hidden rows made by hidden_tiles, in blocks of head_tile_rows(M, Vt) rows, which select
-// the kernel (all rows up to rows_max(Vt), 384-row tall tiles or 256 x 256 tiles); weight_tiled: NULL, or
+// the kernel (all-rows blocks, 384-row tall tiles or 256 x 256 tiles); weight_tiled: NULL, or
 // the K-tiled trimmed head of vt_trim_head_tiled (weight and keep are then not read by the
 // kernel).  Other H take the register-staged kernel on the rows as given.
 template <int PARTS>
@@ -1425,9 +1438,10 @@ inline hipError_t launch_mfma_head(const uint16_t *hidden, const uint16_t *weigh
                                    const uint16_t *weight_tiled = nullptr) {
   const int64_t tiles = ((M + kBigBM - 1) / kBigBM) * mfma_big_tiles_n(Vt);
   const int iM = static_cast<int>(M), iH = static_cast<int>(H), iV = static_cast<int>(Vt);
-  if (H % kDmaBK == 0 && M <= rows_max(Vt)) {
-    const int mb = static_cast<int>((M + 31) / 32), bn = head_tile_cols(M, H, Vt);
-    const dim3 grid(static_cast<unsigned>((Vt + bn - 1) / bn)), block(static_cast<unsigned>(kWave * (bn / 32)));
+  if (H % kDmaBK == 0 && rows_kernel(M, Vt)) {
+    const int tm = rows_block(M, Vt), mb = tm / 32, bn = head_tile_cols(M, H, Vt);
+    const int64_t nbm = (M + tm - 1) / tm;
+    const dim3 grid(static_cast<unsigned>(nbm * ((Vt + bn - 1) / bn))), block(static_cast<unsigned>(kWave * (bn / 32)));
     if constexpr (PARTS == kPartsNone) {
       if (hidden_tiled || weight_tiled) return hipErrorInvalidValue;
       const HeadKernel f =

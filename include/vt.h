@@ -76,8 +76,9 @@ typedef enum { VT_F32 = 0, VT_BF16 = 1 } vt_dtype_t;
  *   The order does depend on M, which picks the kernel: a GEMV when M <= 8 and
  *   M * ceil(H / 512) <= 48 (lanes hold partial sums over 16-byte pieces of a row, reduced across
  *   lanes); otherwise an MFMA kernel: when H % 32 == 0 one block of all M rows (padded to a
- *   multiple of 32) per 256 head rows up to M = 192 (per 128 head rows up to M = 256 when the
- *   head has fewer than 256 blocks of 256 rows), 256 x 256 tiles beyond; for other H 128 x 128
+ *   multiple of 32) per 256 head rows up to M = 192 (when the head has fewer than 256 blocks of
+ *   256 rows: per 128 head rows up to M = 256, and in two row blocks up to M = 384), 256 x 256
+ *   tiles beyond; for other H 128 x 128
  *   tiles up to M = 128, register-staged 256 x 256 tiles beyond.  Every MFMA kernel sums a
  *   logit's products in MFMA steps of 16 in ascending K, so they all give the same bits; between
  *   the GEMV and the MFMA kernels a hidden row's logits may differ in the last bits (each within
@@ -187,12 +188,12 @@ size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
  * sizes with H % 32 == 0 the target partials launch also copies the hidden rows K-tiled into the
  * workspace (the head then reads each K step of a block of hidden rows as one contiguous run; same
  * products, same logits); without target partials (V <= 4096 or greedy verification) the copy is
- * a launch of its own.  That head takes one block of all hidden rows up to B*R = 192 (256 when
- * the head has fewer than 256 blocks of 256 rows), and beyond 384 x 256 tiles (384 hidden rows)
- * when they give each CU no more hidden rows than 256 x 256 tiles, counting one tile per CU at a
- * time (B*R = 2304 or 288 against 256 head blocks), else 256 x 256 tiles (B*R = 512, or 384
- * against 128 head blocks); all sum the same products in the same order as the separate call's
- * kernel.
+ * a launch of its own.  That head takes one block of all hidden rows up to B*R = 192 (on heads
+ * of fewer than 256 blocks of 256 rows: one block up to 256 rows, two up to 384), and beyond
+ * 384 x 256 tiles (384 hidden rows) when they give each CU no more hidden rows than 256 x 256
+ * tiles, counting one tile per CU at a time (B*R = 2304 or 288 against 256 head blocks), else
+ * 256 x 256 tiles (B*R = 512 against 128 head blocks); all sum the same products in the same
+ * order as the separate call's kernel.
  *   The call issues kernel launches (and the optional events) only: no allocation, memset or copy,
  *   so it can be captured into a HIP graph with its workspace and replayed.
  *   Pages: as for the four calls above.

@@ -18,10 +18,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     (9, 4096, 65536, False, "lmhead_mfma_rows"),     # config 5's shape at one sequence
     (192, 4096, 65536, False, "lmhead_mfma_rows"),   # the largest all-rows block on 256 columns
     (193, 4096, 65536, False, "lmhead_mfma_dma8"),
-    (256, 3072, 32768, False, "lmhead_mfma_rows"),   # 128-column blocks: up to 256 rows
-    (257, 3072, 32768, False, "lmhead_mfma_dma8"),
+    (256, 3072, 32768, False, "lmhead_mfma_rows"),   # 128-column blocks: one block up to 256 rows
+    (384, 3072, 32768, False, "lmhead_mfma_rows"),   # and two up to 384
+    (385, 3072, 32768, False, "lmhead_mfma_dma8"),   # 256 square tiles beat 128 tall ones
     (512, 3072, 32768, False, "lmhead_mfma_dma8"),   # config 4
-    (384, 3072, 32768, False, "lmhead_mfma_dma8"),   # 256 square tiles beat 128 tall ones
     (288, 4096, 65536, False, "lmhead_mfma_tall"),   # 256 tall tiles against 512 square ones
     (2304, 4096, 65536, False, "lmhead_mfma_tall"),  # config 5, fused call
     (2304, 4096, 65536, True, "lmhead_mfma_dma8"),   # config 5, separate calls

@@ -18,7 +18,7 @@ SCALED = {
     "c4-batched-mfma": CONFIGS[4].scaled(B=24, V=20000, Vt=5000, H=256),
     "c5-mfma": CONFIGS[5].scaled(B=16, V=13000, Vt=6000, H=256),
     "c4-big-tiles": CONFIGS[4].scaled(B=40, V=20000, Vt=5000, H=520),  # M = 320: register-staged tiles
-    "c5-big-tiles": CONFIGS[5].scaled(B=32, V=13000, Vt=6001, H=256),  # M = 288: 256 x 256, ragged Vt
+    "c5-big-tiles": CONFIGS[5].scaled(B=32, V=13000, Vt=6001, H=256),  # M = 288: two all-rows blocks, ragged Vt
     "c3-one-chunk-target": CONFIGS[3].scaled(V=4000, Vt=1500, H=256),
     # untrimmed head at 288 hidden rows: K-tiled hidden copy, no keep set
     "c2-untrimmed-big-tiles": CONFIGS[2].scaled(B=48, V=6000, Vt=6000, H=256),
@@ -32,8 +32,8 @@ SCALED = {
     # past the GEMV sizes: one block of all rows padded to a multiple of 32 (9 rows: one 32-row
     # block; 96: three; 128, 129: four, five; 192: six) per 256 head rows (66000 head rows) up to
     # 192 rows, or per 128 (fewer than 256 blocks of 256) up to 256 rows (194: seven; 256:
-    # eight), then 256 x 256 tiles; with H % 32 != 0 below 129 rows, 128 x 128 tiles and a
-    # separate draft softmax
+    # eight) and in two blocks up to 384 (258: two of 160), then 256 x 256 tiles; with
+    # H % 32 != 0 below 129 rows, 128 x 128 tiles and a separate draft softmax
     "rows-9": CONFIGS[4].scaled(B=3, gamma=2, R=3, V=20000, Vt=5000, H=256),
     "rows-96": CONFIGS[4].scaled(B=12, V=20000, Vt=5000, H=256),
     "rows-128": CONFIGS[4].scaled(B=16, V=20000, Vt=5000, H=256),
@@ -41,7 +41,7 @@ SCALED = {
     "rows-192": CONFIGS[4].scaled(B=24, V=20000, Vt=5000, H=256),
     "rows-194-seven-blocks": CONFIGS[4].scaled(B=97, gamma=1, R=2, V=20000, Vt=5000, H=256),
     "rows-256-eight-blocks": CONFIGS[4].scaled(B=32, V=20000, Vt=5000, H=256),
-    "square-258": CONFIGS[4].scaled(B=129, gamma=1, R=2, V=20000, Vt=5000, H=256),
+    "rows-258-two-blocks": CONFIGS[4].scaled(B=129, gamma=1, R=2, V=20000, Vt=5000, H=256),
     "rows-36-wide-head": CONFIGS[5].scaled(B=4, V=70000, Vt=66000, H=256),
     # up to 32 hidden rows of at most 8 per sequence the MFMA head is followed by the two-pass
     # verification (chunk pass and final pass) instead of the combine and verify launches

@@ -92,7 +92,8 @@ def _merge(parts):
 def test_batch_independence_across_head_kernels(c, B, follow):
     """The same sequences alone (B = 1: the GEMV head and the three-launch path for 8 draft rows,
     a one-block MFMA head for 9), in batches of at most 128 hidden rows (one block of all rows) and
-    in a batch of 256+ hidden rows (256 x 256 tiles for 320, 288 and 512 rows).
+    in a batch of 256+ hidden rows (two all-rows blocks for 320 and 288 rows, 256 x 256 tiles for
+    512).
     The MFMA kernels sum in one order, the GEMV in another, and the draft running sums are chunked
     by the head's blocks, so a decision may differ only where the oracle places it within the
     band; every other output must be the same, and each run must match the oracle."""

@@ -3,8 +3,8 @@
 Tolerance: |gpu - oracle| <= H * 2^-24 * sum_k |h_k w_k| per logit (the recursive-summation
 bound for fp32 accumulation of exact bf16 products) -- the observed error is also reported.
 Shapes cover the dot2 GEMV (M <= 8) and the MFMA kernels (M > 8 or large H: all rows in one
-block up to 192 rows, or 256 on heads of fewer than 256 blocks of 256 rows, 256 x 256 tiles
-beyond; 128 x 128 and register-staged tiles when H is not a multiple of 32), ragged row and K
+block up to 192 rows, or on heads of fewer than 256 blocks of 256 rows in one block up to 256
+and two up to 384, 256 x 256 tiles beyond; 128 x 128 and register-staged tiles when H is not a multiple of 32), ragged row and K
 tails, trimmed and untrimmed heads."""
 import numpy as np
 import pytest
@@ -47,7 +47,8 @@ CASES = [
     (192, 512, 1200, 1100, True),   # six row blocks
     (224, 512, 1200, 1100, True),   # seven and eight row blocks: only on 128-column blocks
     (256, 512, 1200, 1100, True),
-    (257, 512, 1200, 1100, True),   # one row past them: 256 x 256 tiles
+    (257, 512, 1200, 1100, True),   # one row past them: two all-rows blocks of 160
+    (385, 512, 1200, 1100, True),   # past two blocks of 192: 256 x 256 tiles
     (193, 256, 70000, 66000, True), # 256 x 256 tiles past 192 rows when the head has 256+ blocks
     (100, 520, 1000, 700, True),    # H % 32 != 0 at 100 rows: 128 x 128 tiles
     (40, 256, 70000, 66000, True),  # all rows per 256 head rows (258 blocks of 256: one per CU)
