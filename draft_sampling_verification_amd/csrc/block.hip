@@ -42,8 +42,10 @@ struct BlockPlan {
   bool fv;          // small batch, sampling both sides: target partials (in the GEMV launch, or a
                     // launch of their own before an MFMA head), then one chunk pass and one final
                     // pass (verify_fused_chunk / _final)
-  bool fg;          // small batch, greedy both sides: argmax partials in the GEMV launch (head
-                    // blocks and, in extra workgroups, target chunks), then verify_greedy_small
+  bool fg;          // greedy both sides, at most 8 draft rows per sequence after the GEMV or 16
+                    // after an MFMA head: argmax partials of the head blocks and of the target
+                    // chunks (in extra workgroups of the GEMV launch, or a launch of their own
+                    // before the MFMA head), then verify_greedy_small
   int64_t M, rows_t;
   int64_t nchunk_t;  // 4096-chunks of a target row
   int64_t nchunk_d;  // draft partial chunks per row (GEMV row blocks, MFMA column blocks, or 4096-chunks)
@@ -60,14 +62,16 @@ BlockPlan plan_block(int64_t B, int64_t gamma, int64_t R, int64_t H, int64_t Vt,
   BlockPlan p{};
   p.M = B * R;
   p.rows_t = B * (gamma + 1);
-  p.fused = !greedy_d && pick_gemv<kPartsSoftmax>(p.M, H, trim) != nullptr;
-  p.fg = greedy_t && greedy_d && R <= kFvMaxR && pick_gemv<kPartsArgmax>(p.M, H, trim) != nullptr;
-  p.nchunk_t = greedy_t && !p.fg ? 1 : (V + kChunk - 1) / kChunk;
   // past the GEMV sizes: the direct-to-LDS MFMA heads (and the register-staged one from kBigMinM
   // rows) emit the draft partials in their epilogue (softmax partials, or argmax partials for
   // argmax drafts); the head kernel is the one the separate call takes for the same M and H
-  p.fused_mfma = !p.fused && !p.fg && pick_gemv<kPartsNone>(p.M, H, trim) == nullptr && mfma_head_direct(p.M, H);
-  if (p.fused || p.fg) {
+  const bool mfma_ok = pick_gemv<kPartsNone>(p.M, H, trim) == nullptr && mfma_head_direct(p.M, H);
+  p.fused = !greedy_d && pick_gemv<kPartsSoftmax>(p.M, H, trim) != nullptr;
+  const bool fg_gemv = greedy_t && greedy_d && R <= kFvMaxR && pick_gemv<kPartsArgmax>(p.M, H, trim) != nullptr;
+  p.fg = fg_gemv || (greedy_t && greedy_d && R <= kFvMaxR2 && mfma_ok);
+  p.nchunk_t = greedy_t && !p.fg ? 1 : (V + kChunk - 1) / kChunk;
+  p.fused_mfma = !p.fused && !fg_gemv && mfma_ok;
+  if (p.fused || fg_gemv) {
     p.nchunk_d = gemv_blocks(Vt);
     p.chunk_d = gemv_rows_per_block(Vt);
   } else if (p.fused_mfma) {
@@ -196,6 +200,51 @@ hipError_t run_block_small_mfma(const BlockPlan &pl, const SmParams &D, const Sm
   return launch_fused_verify<TinT, kVecT>(pl, D, T, Vp, u_draft, wbuf, B, stream);
 }
 
+// The greedy compare pass: one workgroup per sequence reduces the argmax partials of the draft
+// rows (per head block) and of the target rows (per 4096-chunk), compares and writes the outputs.
+inline hipError_t launch_greedy_verify(const BlockPlan &pl, const SmParams &D, const SmParams &T, const VfParams &Vp,
+                                       int64_t B, hipStream_t stream) {
+  FvParams F{};
+  F.v = Vp;
+  F.dpart = D.part;
+  F.nd = static_cast<int>(pl.nchunk_d);
+  F.dper = pl.chunk_d;
+  F.tpart = T.part;
+  F.nt = T.nchunk;
+  F.dlse_out = D.lse;
+  F.dids_out = D.sampled;
+  return launch(verify_greedy_small, dim3(static_cast<unsigned>(B)), dim3(kFvBlock), 0, stream, F);
+}
+
+// Greedy both sides past the GEMV sizes: 3 launches.  The target rows' per-chunk argmaxes (with
+// the K-tiled hidden copy in extra workgroups), the MFMA head with the draft rows' argmax
+// partials, and the compare pass.
+template <typename TinT, bool kVecT>
+hipError_t run_block_greedy_small_mfma(const BlockPlan &pl, const SmParams &D, const SmParams &T,
+                                       const VfParams &Vp, const uint16_t *hidden, const uint16_t *weight,
+                                       const int32_t *keep, int64_t H, int64_t Vt, float *logits, int64_t B,
+                                       hipEvent_t ev0, hipEvent_t ev1, hipStream_t stream, void *hidt_base,
+                                       const uint16_t *weight_tiled) {
+  hipError_t e = hipSuccess;
+  const int vrows = static_cast<int>(Vp.V);  // the head passed in is the full [V][H] one
+  uint16_t *hidt = pl.hidt_bytes ? reinterpret_cast<uint16_t *>(hidt_base) : nullptr;
+  const TileParams tp = hidden_tiles_params(hidden, pl.M, H, Vt, hidt);
+  if (hidt)
+    e = launch(softmax_partial_tiles<TinT, kVecT>,
+               dim3(static_cast<unsigned>(T.rows * T.nchunk + hidden_tiles_blocks(tp))), dim3(kBlock), 0, stream, T,
+               tp);
+  else
+    e = launch(softmax_partial<TinT, kVecT>, dim3(static_cast<unsigned>(T.rows * T.nchunk)), dim3(kBlock), 0,
+               stream, T);
+  if (e != hipSuccess) return e;
+  if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
+  e = launch_mfma_head<kPartsArgmax>(hidden, weight, keep, vrows, pl.M, H, Vt, logits, GemvParts{D.part, D.k2}, stream,
+                                     hidt, weight_tiled);
+  if (e != hipSuccess) return e;
+  if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
+  return launch_greedy_verify(pl, D, T, Vp, B, stream);
+}
+
 // Small batch, greedy both sides: 2 launches.  The GEMV launch leaves per-block argmax partials
 // of the draft rows and, in extra workgroups, per-chunk argmaxes of the target rows; one
 // workgroup per sequence reduces, compares and writes the outputs.
@@ -215,16 +264,7 @@ hipError_t run_block_greedy_small(const BlockPlan &pl, const SmParams &D, const 
                   T.rows * T.nchunk);
   if (e != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
-  FvParams F{};
-  F.v = Vp;
-  F.dpart = D.part;
-  F.nd = static_cast<int>(pl.nchunk_d);
-  F.dper = pl.chunk_d;
-  F.tpart = T.part;
-  F.nt = T.nchunk;
-  F.dlse_out = D.lse;
-  F.dids_out = D.sampled;
-  return launch(verify_greedy_small, dim3(static_cast<unsigned>(B)), dim3(kFvBlock), 0, stream, F);
+  return launch_greedy_verify(pl, D, T, Vp, B, stream);
 }
 
 template <typename TinT, bool kVecT, bool kVecD>
@@ -238,6 +278,9 @@ hipError_t run_block(const BlockPlan &pl, const SmParams &D, const SmParams &T, 
   if (pl.fv)
     return run_block_small_mfma<TinT, kVecT>(pl, D, T, Vp, hidden, weight, keep, H, Vt, logits, D.u, wbuf, B, ev0,
                                              ev1, stream, hidt_base, weight_tiled);
+  if (pl.fg && pl.fused_mfma)
+    return run_block_greedy_small_mfma<TinT, kVecT>(pl, D, T, Vp, hidden, weight, keep, H, Vt, logits, B, ev0, ev1,
+                                                    stream, hidt_base, weight_tiled);
   if (pl.fg)
     return run_block_greedy_small<TinT, kVecT>(pl, D, T, Vp, hidden, weight, keep, H, Vt, logits, B, ev0, ev1, stream);
   hipError_t e = hipSuccess;

@@ -460,11 +460,12 @@ __global__ __launch_bounds__(kFvBlock) void verify_fused_chunk(FvParams F) {
   }
 }
 
-// Greedy blocks at decode sizes (both temperatures 0; "VocabTrim" §4 and Appendix C.1,
-// Algorithm 2: a draft is kept only while it equals the target's most likely token, and the
-// target's own token follows the first mismatch).  The head launch leaves per-block (max, lowest
-// index of the max) of every draft row and per-4096-chunk argmaxes of every target row; one
-// 512-thread workgroup per sequence reduces them (wave w: draft row w, target rows w and w + 8),
+// Greedy blocks (both temperatures 0; "VocabTrim" §4 and Appendix C.1, Algorithm 2: a draft is
+// kept only while it equals the target's most likely token, and the target's own token follows
+// the first mismatch).  The head launch leaves per-block (max, lowest index of the max) of every
+// draft row, and per-4096-chunk argmaxes of every target row come from extra workgroups of the
+// GEMV launch or from a launch of their own before an MFMA head; one 512-thread workgroup per
+// sequence reduces them (wave w: draft rows w and w + 8, target rows w, w + 8 and w + 16),
 // compares, and writes every output.  No logits are read here.
 __device__ __forceinline__ void partial_argmax(const float2 *p, int n, float &bv, int &bi) {
   bv = kNegInf;
@@ -480,19 +481,19 @@ __device__ __forceinline__ void partial_argmax(const float2 *p, int n, float &bv
 }
 
 __global__ __launch_bounds__(kFvBlock) void verify_greedy_small(FvParams F) {
-  __shared__ int s_x[kFvMaxR];
-  __shared__ int s_a[kFvMaxT];
+  __shared__ int s_x[kFvMaxR2];
+  __shared__ int s_a[kFvMaxR2 + 1];
   const VfParams &P = F.v;
   const int64_t b = blockIdx.x;
   const int lane = lane_id(), w = static_cast<int>(threadIdx.x) / kWave;
   const int g = P.gamma, R = static_cast<int>(P.R);
-  if (w < R) {
-    const int64_t m = b * R + w;
+  for (int i = w; i < R; i += kFvWaves) {
+    const int64_t m = b * R + i;
     float bv;
     int bi;
     partial_argmax(F.dpart + m * F.nd, F.nd, bv, bi);
     if (lane == 0) {
-      s_x[w] = bi;
+      s_x[i] = bi;
       F.dlse_out[m] = static_cast<double>(bv);  // the greedy limit of the log-normaliser: the row max
       F.dids_out[m] = bi;
     }

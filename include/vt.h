@@ -226,10 +226,12 @@ size_t vt_spec_verify_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
  *   maximum, draft_lse the row maximum, and u_draft is not read (may be NULL); the LM head then
  *   emits argmax partials instead of softmax partials: at decode sizes (B*R <= 8) per block of
  *   head rows for the draft rows and, in extra workgroups, per 4096-chunk for the target rows,
- *   and one more launch finishes the block (2 launches); on the MFMA heads with partials per 256
- *   head rows (the same kernels, K-tiled copies and weight_tiled as with sampled drafts), finished
- *   by the combine launch; otherwise (the GEMV without the decode path, or H % 32 != 0 with
- *   B*R <= 128) the head runs without partials and a separate pass finds the draft rows' argmaxes.
+ *   and one more launch finishes the block (2 launches); on the MFMA heads per column block of
+ *   head rows (the same kernels, K-tiled copies and weight_tiled as with sampled drafts), after a
+ *   launch that takes the target rows' per-4096-chunk argmaxes, and one more launch finishes the
+ *   block (3 launches; with more than 16 draft rows per sequence the combine and the verify passes
+ *   finish it); otherwise (the GEMV without the decode path, or H % 32 != 0 with B*R <= 128) the
+ *   head runs without partials and a separate pass finds the draft rows' argmaxes.
  *   Errors: INVALID_ARG for NULL required pointers, B, gamma, H, V or Vt <= 0, R < gamma, Vt > V,
  *   a temperature not finite or < 0, draft_T = 0 with target_T > 0, keep_ids/full_to_trim
  *   inconsistent with Vt; UNSUPPORTED for
