@@ -29,6 +29,9 @@ SCALED = {
     # 256-row tiles (two blocks)
     "c5-tall-two-blocks": CONFIGS[5].scaled(B=84, V=40000, Vt=32001, H=256),
     "c4-square-two-blocks": CONFIGS[4].scaled(B=64, V=20000, Vt=5000, H=256),
+    # 2250 hidden rows against 128 head blocks: 768 tall tiles in three waves (six row blocks, the
+    # last ragged; ragged Vt)
+    "c5-tall-ragged": CONFIGS[5].scaled(B=250, V=34000, Vt=32700, H=128),
     # past the GEMV sizes: one block of all rows padded to a multiple of 32 (9 rows: one 32-row
     # block; 96: three; 128, 129: four, five; 192: six) per 256 head rows (66000 head rows) up to
     # 192 rows, or per 128 (fewer than 256 blocks of 256) up to 256 rows (194: seven; 256:
@@ -157,7 +160,7 @@ def test_fused_block_rank_ordered_keep_set(name):
 
 
 @pytest.mark.parametrize("name", ["c3-trimmed", "c4-batched-mfma", "c4-big-tiles", "c5-big-tiles",
-                                  "c5-tall-two-blocks", "c4-square-two-blocks"])
+                                  "c5-tall-two-blocks", "c4-square-two-blocks", "c5-tall-ragged"])
 def test_fused_matches_separate_calls(name):
     # c5-big-tiles (M = 288, H = 256) and c5-tall-two-blocks (M = 756): the fused call's head runs
     # 384 x 256 tiles on a K-tiled copy of the hidden rows, the separate call 256 x 256 tiles on
@@ -175,7 +178,8 @@ def test_fused_matches_separate_calls(name):
 
 @pytest.mark.parametrize("name,order", [("c5-big-tiles", "id"), ("c5-big-tiles", "rank"),
                                         ("c2-untrimmed-big-tiles", "id"), ("c5-big-tiles-one-chunk-target", "id"),
-                                        ("c5-tall-two-blocks", "id"), ("c4-square-two-blocks", "id")])
+                                        ("c5-tall-two-blocks", "id"), ("c4-square-two-blocks", "id"),
+                                        ("c5-tall-ragged", "id"), ("c5-tall-ragged", "rank")])
 def test_tiled_head_gives_the_same_block(name, order):
     # the K-tiled W^Trim holds the same rows as the gather through keep_ids: every output, the
     # logits included, must be the same bits (M = 288, ragged Vt = 6001 in the first two)

@@ -135,6 +135,8 @@ def _block_greedy(wl, draft_T, tiled=False):
     # 756 on 384 x 256 tiles (two row blocks, ragged Vt), H = 520 on the register-staged tiles
     ("c4 square tiles argmax drafts", CONFIGS[4].scaled(B=64, V=20000, Vt=5000, H=256), 0.0),
     ("c5 tall tiles argmax drafts", CONFIGS[5].scaled(B=84, V=40000, Vt=32001, H=256), 0.0),
+    # 2250 rows against 128 head blocks: three waves of tall tiles, ragged rows and head
+    ("c5 ragged tall tiles argmax drafts", CONFIGS[5].scaled(B=250, V=34000, Vt=32700, H=128), 0.0),
     ("c4 register-staged tiles argmax drafts", CONFIGS[4].scaled(B=40, V=20000, Vt=5000, H=520), 0.0),
     ("c5 full size argmax drafts, K-tiled head", CONFIGS[5], 0.0),
     ("c5-scaled sampled drafts", CONFIGS[5].scaled(B=32, V=13000, Vt=6001, H=256), 0.8),
