@@ -21,13 +21,13 @@ from workloads import CONFIGS, counter_uniforms, make_workload
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("V,B,gamma", [(18, 37, 4), (3000, 24, 3), (20000, 16, 5)])
+@pytest.mark.parametrize("V,B,gamma", [(18, 37, 4), (3000, 24, 3), (20000, 16, 5), (20000, 64, 5)])
 def test_zero_residual_draws_from_p(V, B, gamma):
     """Draft rows equal to the target rows, but draft_lse = target_lse - delta: then q = p e^delta
     at every id, every accept ratio is e^-delta < 1, u = 1 rejects draft 0, and the fp32 residual
     max(0, p - q) is zero everywhere, so the final token is drawn from p_0 (verify_wave for V <= 64,
-    verify_single for one chunk, verify_partial + verify_final otherwise).  The oracle's
-    verify_sequence is fed the same q."""
+    verify_single for one chunk, verify_partial + verify_final otherwise, also at 64 sequences).
+    The oracle's verify_sequence is fed the same q."""
     say(f"zero residual V={V} B={B} gamma={gamma}")
     rng = np.random.default_rng(V)
     T = np.float32(0.9)
